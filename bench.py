@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA decode step on one MI355X.
+
+A step is one whole mla_decode call (query absorption, split attention over
+the paged latent cache, log-sum-exp merge, W_UV up-projection) for a batch of
+B sequences: it produces one new token per sequence, so tokens/s = B / step.
+
+Inputs are seeded and synthetic (mla_inputs) and resident in HBM before the
+timed region.  Several copies of the cache pool are rotated from step to step
+so that the steps together touch more than 2x the 256 MB Infinity Cache and
+the latent-cache reads come from HBM.
+
+The attention kernel is timed alone with HIP events recorded on its own
+stream around its launch (mla_decode_timed); `roofline.achieved` is the
+algorithmic latent-cache bytes of one launch over that average duration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), DSV3 shape @32K ctx"
+ATTN_SOURCE = os.path.join(ROOT, "head_latent_attention_10_amd", "csrc", "mla_attend_mfma.hip")
+
+
+def attn_source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != attn_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
+    import torch
+
+    from head_latent_attention_10_amd import _lib
+    from head_latent_attention_10_amd.device import Decoder, DeviceInputs
+    from mla_inputs import CONFIGS, generate
+
+    cfg = CONFIGS[workload]
+    t0 = time.time()
+    inp = generate(cfg)
+    dev = DeviceInputs(inp)
+    dec = Decoder(dev, num_splits=num_splits)
+    pool_bytes = dev.c_kv.numel() * dev.c_kv.element_size() + dev.k_rope.numel() * dev.k_rope.element_size()
+    copies = max(2, math.ceil(768e6 / pool_bytes))
+    c_copies = [dev.c_kv] + [dev.c_kv.clone() for _ in range(copies - 1)]
+    r_copies = [dev.k_rope] + [dev.k_rope.clone() for _ in range(copies - 1)]
+    s_copies = [dev.c_kv_scale] * copies
+    if dev.c_kv_scale is not None:
+        s_copies = [dev.c_kv_scale] + [dev.c_kv_scale.clone() for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    print(f"[bench] {workload}: inputs ready in {time.time() - t0:.1f}s, "
+          f"{copies} cache copies of {pool_bytes / 1e6:.0f} MB", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    p = dec.p
+
+    def step(k, evb=None, eva=None):
+        i = k % copies
+        _lib.mla_decode_timed(p, dev.q, c_copies[i], s_copies[i], r_copies[i], dev.block_table,
+                              dev.seq_lens, dev.W_UK, dev.W_UV, dec.out, dec.workspace,
+                              dec.ws_bytes, stream, evb, eva)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(steps):
+        step(warmup + k, *evs[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    cache_bytes = inp.cache_bytes()
+    ms_per_step = total_ms / steps
+    return {
+        "workload": workload, "cfg": cfg, "batch": cfg.batch,
+        "total_tokens": int(inp.seq_lens.astype("int64").sum()),
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": cfg.batch / (ms_per_step * 1e-3),
+        "attn_ms": attn_avg,
+        "attn_ms_min": min(attn_ms),
+        "cache_bytes": cache_bytes,
+        "attn_gbps": cache_bytes / (attn_avg * 1e-3) / 1e9,
+        "step_cache_gbps": cache_bytes / (ms_per_step * 1e-3) / 1e9,
+        "splits": _lib.mla_decode_num_splits(p),
+        "copies": copies,
+        "inp": inp,
+    }
+
+
+def cpu_baseline(inp, seconds: float):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    whole heads of sequence 0 until about `seconds` of CPU time have passed,
+    extrapolated to the full step by the token x head count."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import oracle_from_inputs
+
+    cfg = inp.cfg
+    T0 = int(inp.seq_lens[0])
+    heads_done = 0
+    t_start = time.perf_counter()
+    while heads_done < cfg.heads and time.perf_counter() - t_start < seconds:
+        oracle_from_inputs(inp, batches=[0], heads=[heads_done])
+        heads_done += 1
+    elapsed = time.perf_counter() - t_start
+    work_done = T0 * heads_done
+    work_full = int(inp.seq_lens.astype(np.int64).sum()) * cfg.heads
+    t_full = elapsed * work_full / max(work_done, 1)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {
+        "value": cfg.batch / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"sequence 0 ({T0} tokens), {heads_done} of {cfg.heads} heads in "
+                   f"{elapsed:.1f} s, fp64 numpy oracle, extrapolated by tokens x heads "
+                   f"to the full step ({work_full} token-heads)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3_ragged_32k")
+    ap.add_argument("--also", default="dsv3_b8_32k,dsv3_b64_4k,transmla_llama2_7b,dsv3_fp8_16k",
+                    help="other workloads reported under 'extra' (comma list, may be empty)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the decode step on one GPU only; the multi-GPU path is a "
+              "design (batch or context-parallel sharding) and is not built. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    main_run = measure(args.workload, args.steps, args.warmup, args.num_splits)
+    extra = {}
+    for w in [w for w in args.also.split(",") if w]:
+        r = measure(w, max(10, args.steps // 2), max(3, args.warmup // 2), args.num_splits)
+        extra[w] = {"tokens_per_s": round(r["tokens_per_s"], 1),
+                    "ms_per_step": round(r["ms_per_step"], 4),
+                    "attn_kernel_ms": round(r["attn_ms"], 4),
+                    "attn_cache_GBps": round(r["attn_gbps"], 1),
+                    "attn_frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4)}
+        del r
+
+    cfg = main_run["cfg"]
+    traffic = measured_traffic(args.workload)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(main_run["attn_gbps"], 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(main_run["attn_gbps"] / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "kernel": "attend_mfma_kernel",
+        "algorithmic_bytes_per_launch": main_run["cache_bytes"],
+        "kernel_ms": round(main_run["attn_ms"], 4),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(main_run["inp"], args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(main_run["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_run["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": cfg.batch, "heads": cfg.heads,
+            "d_nope": cfg.d_nope, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "d_v": cfg.d_v,
+            "page_size": cfg.page_size, "cache_dtype": cfg.cache_dtype,
+            "seq_lens": (f"uniform [{cfg.seq_len_range[0]}, {cfg.seq_len_range[1]}], seed {cfg.seed}"
+                         if cfg.seq_len_range else f"{cfg.seq_len} each"),
+            "total_tokens": main_run["total_tokens"], "splits": main_run["splits"],
+            "cache_copies_rotated": main_run["copies"],
+        },
+        "latent_cache_GBps_step": round(main_run["step_cache_gbps"], 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

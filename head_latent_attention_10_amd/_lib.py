@@ -1,0 +1,203 @@
+"""ctypes binding of libmla_hip.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and takes the
+same arguments; tensors may be torch tensors (their data pointer is passed) or
+plain integer device addresses.  No arithmetic of the decode step happens in
+Python.  If the HIP library has not been built, loading raises instead of
+falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla_hip.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "e4m3": MLA_FP8_E4M3}
+
+
+class MlaDecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("d_nope", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32),
+        ("rope_dtype", ctypes.c_int32),
+        ("weight_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(MlaDecodeParams)
+
+_SIGNATURES = {
+    "mla_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "mla_last_error": (ctypes.c_char_p, []),
+    "mla_decode_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_decode_num_splits": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int32)]),
+    "mla_absorbed_dtype": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int32)]),
+    "mla_decode": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_decode_timed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+    "mla_absorb_q": (ctypes.c_int, [_PP, _P, _P, _P, _P]),
+    "mla_attend_latent": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_up_project": (ctypes.c_int, [_PP, _P, _P, _P, _P]),
+    "mla_gather_cache": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
+    "mla_split_begin": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+    "mla_split_owner": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m head_latent_attention_10_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, st: int):
+    if st != MLA_OK:
+        lib = load_library()
+        raise MlaError(st, fn, lib.mla_last_error().decode())
+
+
+def make_params(batch, num_heads, d_nope, d_rope, d_latent, d_v, page_size, max_blocks_per_seq,
+                num_blocks, q_dtype="bf16", cache_dtype="bf16", rope_dtype="bf16",
+                weight_dtype="bf16", out_dtype="bf16", sm_scale=0.0, num_splits=0):
+    code = lambda d: DTYPE_CODES[d] if isinstance(d, str) else int(d)
+    return MlaDecodeParams(batch, num_heads, d_nope, d_rope, d_latent, d_v, page_size,
+                           max_blocks_per_seq, num_blocks, code(q_dtype), code(cache_dtype),
+                           code(rope_dtype), code(weight_dtype), code(out_dtype), float(sm_scale),
+                           num_splits)
+
+
+def mla_status_string(status: int) -> str:
+    return load_library().mla_status_string(status).decode()
+
+
+def mla_last_error() -> str:
+    return load_library().mla_last_error().decode()
+
+
+def mla_decode_workspace_size(p: MlaDecodeParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_decode_workspace_size", load_library().mla_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode_num_splits(p: MlaDecodeParams) -> int:
+    n = ctypes.c_int32(0)
+    _check("mla_decode_num_splits", load_library().mla_decode_num_splits(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def mla_absorbed_dtype(p: MlaDecodeParams) -> int:
+    n = ctypes.c_int32(0)
+    _check("mla_absorbed_dtype", load_library().mla_absorbed_dtype(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK, W_UV, out,
+               workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("mla_decode", load_library().mla_decode(
+        ctypes.byref(p), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope), _ptr(block_table),
+        _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def mla_decode_timed(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK, W_UV, out,
+                     workspace, workspace_bytes, stream, ev_before, ev_after):
+    """ev_before / ev_after: torch.cuda.Event (created with enable_timing) or raw hipEvent_t."""
+    evb = ev_before.cuda_event if hasattr(ev_before, "cuda_event") else ev_before
+    eva = ev_after.cuda_event if hasattr(ev_after, "cuda_event") else ev_after
+    _check("mla_decode_timed", load_library().mla_decode_timed(
+        ctypes.byref(p), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope), _ptr(block_table),
+        _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(workspace), workspace_bytes,
+        _stream(stream), evb, eva))
+
+
+def mla_absorb_q(p, q, W_UK, q_lat, stream=None):
+    _check("mla_absorb_q", load_library().mla_absorb_q(
+        ctypes.byref(p), _ptr(q), _ptr(W_UK), _ptr(q_lat), _stream(stream)))
+
+
+def mla_attend_latent(p, q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens, o_lat,
+                      workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("mla_attend_latent", load_library().mla_attend_latent(
+        ctypes.byref(p), _ptr(q_lat), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope),
+        _ptr(block_table), _ptr(seq_lens), _ptr(o_lat), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def mla_up_project(p, o_lat, W_UV, out, stream=None):
+    _check("mla_up_project", load_library().mla_up_project(
+        ctypes.byref(p), _ptr(o_lat), _ptr(W_UV), _ptr(out), _stream(stream)))
+
+
+def mla_gather_cache(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens, max_tokens, c_out,
+                     scale_out, rope_out, stream=None):
+    _check("mla_gather_cache", load_library().mla_gather_cache(
+        ctypes.byref(p), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope), _ptr(block_table),
+        _ptr(seq_lens), int(max_tokens), _ptr(c_out), _ptr(scale_out), _ptr(rope_out),
+        _stream(stream)))
+
+
+def mla_split_begin(n_tiles: int, splits: int, g: int) -> int:
+    return load_library().mla_split_begin(n_tiles, splits, g)
+
+
+def mla_split_owner(n_tiles: int, splits: int, tile: int) -> int:
+    return load_library().mla_split_owner(n_tiles, splits, tile)

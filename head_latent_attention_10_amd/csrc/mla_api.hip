@@ -1,0 +1,324 @@
+// C ABI: host-side validation, workspace layout and launch sequencing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "mla_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status fail(mla_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_dtype(int32_t d, bool allow_fp8) {
+  return d == MLA_F32 || d == MLA_BF16 || (allow_fp8 && d == MLA_FP8_E4M3);
+}
+
+mla_status validate(const mla_decode_params* p) {
+  if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 1 || p->num_heads < 1 || p->d_nope < 1 || p->d_rope < 0 || p->d_latent < 1 ||
+      p->d_v < 1)
+    return fail(MLA_ERR_INVALID_ARG,
+                "shape out of range (batch=%d heads=%d d_nope=%d d_rope=%d d_latent=%d d_v=%d)",
+                p->batch, p->num_heads, p->d_nope, p->d_rope, p->d_latent, p->d_v);
+  if (p->page_size < 1 || p->page_size > 4096)
+    return fail(MLA_ERR_INVALID_ARG, "page_size %d outside [1, 4096]", p->page_size);
+  if (p->max_blocks_per_seq < 1 || p->num_blocks < 1)
+    return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq=%d num_blocks=%d must be >= 1",
+                p->max_blocks_per_seq, p->num_blocks);
+  if ((int64_t)p->max_blocks_per_seq * p->page_size > (int64_t)1 << 30)
+    return fail(MLA_ERR_INVALID_ARG, "table capacity above 2^30 tokens per sequence");
+  if (p->num_splits < 0 || p->num_splits > 65535)
+    return fail(MLA_ERR_INVALID_ARG, "num_splits %d outside [0, 65535]", p->num_splits);
+  if (!std::isfinite(p->sm_scale)) return fail(MLA_ERR_INVALID_ARG, "sm_scale not finite");
+  if (!is_dtype(p->q_dtype, false) || !is_dtype(p->cache_dtype, true) ||
+      !is_dtype(p->rope_dtype, false) || !is_dtype(p->weight_dtype, false) ||
+      !is_dtype(p->out_dtype, false))
+    return fail(MLA_ERR_INVALID_ARG, "unknown dtype code (q=%d cache=%d rope=%d weight=%d out=%d)",
+                p->q_dtype, p->cache_dtype, p->rope_dtype, p->weight_dtype, p->out_dtype);
+  if (p->d_nope > 1024 || p->d_rope > 1024 || p->d_v > 4096)
+    return fail(MLA_ERR_UNSUPPORTED, "d_nope <= 1024, d_rope <= 1024 and d_v <= 4096 required");
+  if (!mla::mfma_supported(*p) && p->d_latent > 1024)
+    return fail(MLA_ERR_UNSUPPORTED, "d_latent %d above 1024 outside the matrix-core shape",
+                p->d_latent);
+  return MLA_OK;
+}
+
+int32_t absorbed_dtype(const mla_decode_params& p) {
+  return p.cache_dtype == MLA_F32 ? MLA_F32 : MLA_BF16;
+}
+
+struct Layout {
+  size_t q_lat, cu_tiles, part_o, part_lse, o_lat, total;
+  int32_t splits, streams;
+  int64_t slots;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+mla_status resolve_splits(const mla_decode_params& p, int32_t* splits) {
+  if (p.num_splits > 0) {
+    *splits = p.num_splits;
+    return MLA_OK;
+  }
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiProcessorCount)");
+  *splits = cus > 0 ? cus : 1;
+  return MLA_OK;
+}
+
+mla_status layout(const mla_decode_params& p, Layout* L) {
+  mla_status st = resolve_splits(p, &L->splits);
+  if (st != MLA_OK) return st;
+  L->streams = mla::mfma_supported(p) ? mla::mfma_streams(p.num_heads) : 1;
+  L->slots = ((int64_t)L->splits + p.batch) * L->streams;
+  const size_t B = p.batch, h = p.num_heads, dc = p.d_latent, dr = p.d_rope;
+  size_t off = 0;
+  L->q_lat = off;
+  off = align256(off + B * h * (dc + dr) * mla::dtype_size(absorbed_dtype(p)));
+  L->cu_tiles = off;
+  off = align256(off + (B + 1) * sizeof(int32_t));
+  L->part_o = off;
+  off = align256(off + (size_t)L->slots * h * dc * sizeof(float));
+  L->part_lse = off;
+  off = align256(off + (size_t)L->slots * h * sizeof(float));
+  L->o_lat = off;
+  off = align256(off + B * h * dc * sizeof(float));
+  L->total = off;
+  return MLA_OK;
+}
+
+float resolved_scale(const mla_decode_params& p) {
+  return p.sm_scale > 0.f ? p.sm_scale : 1.0f / std::sqrt((float)(p.d_nope + p.d_rope));
+}
+
+mla_status check_cache_ptrs(const mla_decode_params* p, const void* c_kv, const float* c_kv_scale,
+                            const void* k_rope, const int32_t* block_table,
+                            const int32_t* seq_lens) {
+  if (!c_kv || !block_table || !seq_lens || (p->d_rope > 0 && !k_rope))
+    return fail(MLA_ERR_INVALID_ARG, "null cache, table or length pointer");
+  if ((p->cache_dtype == MLA_FP8_E4M3) != (c_kv_scale != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "c_kv_scale must be given exactly when the cache is fp8");
+  return MLA_OK;
+}
+
+mla_status check_workspace(const Layout& L, void* ws, size_t bytes) {
+  if (!ws) return fail(MLA_ERR_WORKSPACE, "workspace is NULL");
+  if (bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, %zu required", bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return MLA_OK;
+}
+
+mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat, const void* c_kv,
+                  const float* c_kv_scale, const void* k_rope, const int32_t* block_table,
+                  const int32_t* seq_lens, float* o_lat, char* ws, hipStream_t s,
+                  hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr) {
+  mla::AttnArgs a;
+  a.q_lat = q_lat;
+  a.c_kv = c_kv;
+  a.c_kv_scale = c_kv_scale;
+  a.k_rope = k_rope;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.cu_tiles = reinterpret_cast<int32_t*>(ws + L.cu_tiles);
+  a.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  a.B = p.batch;
+  a.h = p.num_heads;
+  a.d_c = p.d_latent;
+  a.d_r = p.d_rope;
+  a.P = p.page_size;
+  a.max_blocks = p.max_blocks_per_seq;
+  a.num_blocks = p.num_blocks;
+  a.splits = L.splits;
+  a.streams = L.streams;
+  a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
+
+  hipError_t e = mla::launch_plan(seq_lens, p.batch, p.max_blocks_per_seq, p.page_size,
+                                  reinterpret_cast<int32_t*>(ws + L.cu_tiles), s);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (mla::mfma_supported(p))
+    e = mla::launch_attend_mfma(a, p.cache_dtype, s);
+  else
+    e = mla::launch_attend_simt(a, p.cache_dtype, p.rope_dtype, absorbed_dtype(p), s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (ev_after && (e = hipEventRecord(ev_after, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mla::launch_combine(a, o_lat, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int32_t st) {
+  switch (st) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported combination";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  Layout L;
+  st = layout(*p, &L);
+  if (st != MLA_OK) return st;
+  *bytes = L.total;
+  return MLA_OK;
+}
+
+mla_status mla_decode_num_splits(const mla_decode_params* p, int32_t* splits) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!splits) return fail(MLA_ERR_INVALID_ARG, "splits is NULL");
+  return resolve_splits(*p, splits);
+}
+
+mla_status mla_absorbed_dtype(const mla_decode_params* p, int32_t* dtype) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!dtype) return fail(MLA_ERR_INVALID_ARG, "dtype is NULL");
+  *dtype = absorbed_dtype(*p);
+  return MLA_OK;
+}
+
+mla_status mla_absorb_q(const mla_decode_params* p, const void* q, const void* W_UK, void* q_lat,
+                        void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!q || !W_UK || !q_lat) return fail(MLA_ERR_INVALID_ARG, "null q, W_UK or q_lat");
+  hipError_t e = mla::launch_absorb(*p, q, W_UK, q_lat, absorbed_dtype(*p),
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "absorb launch");
+}
+
+mla_status mla_attend_latent(const mla_decode_params* p, const void* q_lat, const void* c_kv,
+                             const float* c_kv_scale, const void* k_rope,
+                             const int32_t* block_table, const int32_t* seq_lens, float* o_lat,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
+  if (st != MLA_OK) return st;
+  if (!q_lat || !o_lat) return fail(MLA_ERR_INVALID_ARG, "null q_lat or o_lat");
+  Layout L;
+  st = layout(*p, &L);
+  if (st != MLA_OK) return st;
+  st = check_workspace(L, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  return attend(*p, L, q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens, o_lat,
+                static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_up_project(const mla_decode_params* p, const float* o_lat, const void* W_UV,
+                          void* out, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!o_lat || !W_UV || !out) return fail(MLA_ERR_INVALID_ARG, "null o_lat, W_UV or out");
+  hipError_t e = mla::launch_up_project(*p, o_lat, W_UV, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
+}
+
+mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const void* c_kv,
+                            const float* c_kv_scale, const void* k_rope,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const void* W_UK, const void* W_UV, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream, void* ev_before,
+                            void* ev_after) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
+  if (st != MLA_OK) return st;
+  if (!q || !W_UK || !W_UV || !out) return fail(MLA_ERR_INVALID_ARG, "null q, W_UK, W_UV or out");
+  Layout L;
+  st = layout(*p, &L);
+  if (st != MLA_OK) return st;
+  st = check_workspace(L, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_absorb(*p, q, W_UK, ws + L.q_lat, absorbed_dtype(*p), s);
+  if (e != hipSuccess) return hip_fail(e, "absorb launch");
+  float* o_lat = reinterpret_cast<float*>(ws + L.o_lat);
+  st = attend(*p, L, ws + L.q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens, o_lat, ws, s,
+              static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after));
+  if (st != MLA_OK) return st;
+  e = mla::launch_up_project(*p, o_lat, W_UV, out, s);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
+}
+
+mla_status mla_decode(const mla_decode_params* p, const void* q, const void* c_kv,
+                      const float* c_kv_scale, const void* k_rope, const int32_t* block_table,
+                      const int32_t* seq_lens, const void* W_UK, const void* W_UV, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_timed(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK, W_UV, out,
+                          workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const float* c_kv_scale,
+                            const void* k_rope, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t max_tokens, void* c_out,
+                            float* scale_out, void* rope_out, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
+  if (st != MLA_OK) return st;
+  if (max_tokens < 0) return fail(MLA_ERR_INVALID_ARG, "max_tokens < 0");
+  if (!c_out || (p->d_rope > 0 && !rope_out) || (p->cache_dtype == MLA_FP8_E4M3 && !scale_out))
+    return fail(MLA_ERR_INVALID_ARG, "null output pointer");
+  hipError_t e = mla::launch_gather(*p, c_kv, c_kv_scale, k_rope, block_table, seq_lens,
+                                    max_tokens, c_out, scale_out, rope_out,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "gather launch");
+}
+
+int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g) {
+  if (splits < 1) return 0;
+  return mla::split_begin(n_tiles, splits, g);
+}
+
+int32_t mla_split_owner(int64_t n_tiles, int32_t splits, int64_t tile) {
+  if (n_tiles < 1 || splits < 1) return -1;
+  return mla::split_owner(n_tiles, splits, tile);
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Host-side launchers of the MLA decode kernels (one translation unit each).
+#pragma once
+
+#include "mla_common.hpp"
+
+namespace mla {
+
+// Prefix sums of ceil(T_b / kTile) over the batch -> cu_tiles[B + 1].
+hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32_t P,
+                       int32_t* cu_tiles, hipStream_t s);
+
+// q_lat[b,i,:d_c] = W_UK[i]^T q_nope[b,i,:]; q_lat[b,i,d_c:] = q_rope[b,i,:].
+hipError_t launch_absorb(const mla_decode_params& p, const void* q, const void* W_UK, void* q_lat,
+                         int32_t q_lat_dtype, hipStream_t s);
+
+// Generic (any shape, any storage type) split attention -> partials.
+hipError_t launch_attend_simt(const AttnArgs& a, int32_t cache_dtype, int32_t rope_dtype,
+                              int32_t q_lat_dtype, hipStream_t s);
+
+// Matrix-core split attention for d_c = 512, d_r = 64, h % 32 == 0, bf16 or fp8 latent,
+// bf16 rope and bf16 absorbed query.
+bool mfma_supported(const mla_decode_params& p);
+int32_t mfma_streams(int32_t heads);
+hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s);
+
+// Log-sum-exp merge of the token splits -> o_lat [B, h, d_c] fp32.
+hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s);
+
+// out[b,i,:] = W_UV[i] o_lat[b,i,:].
+hipError_t launch_up_project(const mla_decode_params& p, const float* o_lat, const void* W_UV,
+                             void* out, hipStream_t s);
+
+// Paged -> contiguous copy of the cache (storage bits).
+hipError_t launch_gather(const mla_decode_params& p, const void* c_kv, const float* c_kv_scale,
+                         const void* k_rope, const int32_t* block_table, const int32_t* seq_lens,
+                         int32_t max_tokens, void* c_out, float* scale_out, void* rope_out,
+                         hipStream_t s);
+
+inline int32_t dtype_size(int32_t dt) { return dt == MLA_F32 ? 4 : (dt == MLA_BF16 ? 2 : 1); }
+
+}  // namespace mla

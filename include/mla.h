@@ -1,0 +1,182 @@
+/*
+ * mla.h -- C ABI of the MLA decode library for MI355X (gfx950).
+ *
+ * One decode step of multi-head latent attention over a paged, compressed
+ * latent KV cache, run in absorbed form.  The operation is defined in
+ * "TPLA: Tensor Parallel Latent Attention for Efficient Disaggregated Prefill
+ * and Decode Inference", section 3.4 ("MLA Matrix Absorption": the key
+ * absorption of Eq. 5 and "The RoPE handling"):
+ *
+ *   q_lat[b,i,:]  = W_UK[i]^T q_nope[b,i,:]                       (absorb)
+ *   s[b,i,t]      = sm_scale * (q_lat[b,i,:] . c_KV[b,t,:]
+ *                               + q_rope[b,i,:] . k_rope[b,t,:])
+ *   p[b,i,:]      = softmax_t(s[b,i,:])
+ *   o_lat[b,i,:]  = sum_t p[b,i,t] c_KV[b,t,:]
+ *   out[b,i,:]    = W_UV[i] o_lat[b,i,:]                           (up-projection)
+ *
+ * which equals softmax((q_nope.(W_UK c) + q_rope.k_rope) * sm_scale) (W_UV c),
+ * the unabsorbed form, by associativity.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or retains them.  Scratch memory is the
+ *     caller's workspace.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream).  No entry point synchronises the host.
+ *   - Host-side validation runs before any launch; on error a negative
+ *     mla_status is returned, nothing is enqueued, and mla_last_error() gives
+ *     a message (thread-local).  Launch failures return MLA_ERR_HIP.
+ *   - Layouts are dense, row-major, innermost dimension last.  Indices are
+ *     0-based.  bf16 is IEEE binary32's top 16 bits; fp8 is OCP E4M3FN.
+ *   - The library is stateless and re-entrant; concurrent calls on different
+ *     streams need separate workspaces and outputs.
+ *
+ * Cache layout (the paged latent cache):
+ *   c_kv       [num_blocks, page_size, d_latent]   cache_dtype (bf16, fp8, f32)
+ *   c_kv_scale [num_blocks, page_size] fp32        per-token scale, fp8 only:
+ *              the latent row's value is scale * e4m3(byte)
+ *   k_rope     [num_blocks, page_size, d_rope]     rope_dtype, already rotated
+ *   block_table[batch, max_blocks_per_seq] int32   physical block of logical
+ *              block j of sequence b
+ *   seq_lens   [batch] int32                       cached tokens per sequence,
+ *              including the current one
+ *   Logical token t of sequence b lives in block block_table[b][t / page_size]
+ *   at slot t % page_size.  Table entries at or past ceil(T_b / page_size) are
+ *   never read, nor are slots at or past T_b.  Lengths are clamped on the
+ *   device to [0, max_blocks_per_seq * page_size] and block ids to
+ *   [0, num_blocks - 1], so malformed tables give wrong answers, not faults.
+ *   A sequence with T_b = 0 produces a zero output.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* bad shape, null pointer, inconsistent params */
+  MLA_ERR_UNSUPPORTED = -2, /* valid but not implemented combination        */
+  MLA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required      */
+  MLA_ERR_HIP = -4          /* a HIP runtime call or launch failed           */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
+
+typedef struct {
+  int32_t batch;              /* B  >= 1                                     */
+  int32_t num_heads;          /* h  >= 1                                     */
+  int32_t d_nope;             /* width of q_nope, rows of W_UK[i]            */
+  int32_t d_rope;             /* width of q_rope and k_rope (may be 0)       */
+  int32_t d_latent;           /* d_c, width of c_KV                          */
+  int32_t d_v;                /* rows of W_UV[i], width of out               */
+  int32_t page_size;          /* tokens per cache block, 1..4096             */
+  int32_t max_blocks_per_seq; /* block_table row stride                      */
+  int32_t num_blocks;         /* blocks in the pool                          */
+  int32_t q_dtype;            /* mla_dtype of q: F32 or BF16                 */
+  int32_t cache_dtype;        /* mla_dtype of c_kv: F32, BF16 or FP8_E4M3    */
+  int32_t rope_dtype;         /* mla_dtype of k_rope: F32 or BF16            */
+  int32_t weight_dtype;       /* mla_dtype of W_UK and W_UV: F32 or BF16     */
+  int32_t out_dtype;          /* mla_dtype of out: F32 or BF16               */
+  float sm_scale;             /* softmax scale; <= 0 means 1/sqrt(d_nope+d_rope) */
+  int32_t num_splits;         /* token-split work groups; 0 = one per compute unit */
+} mla_decode_params;
+
+/* Static description of a status code. */
+const char* mla_status_string(int32_t status);
+
+/* Message for the last error returned on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Bytes of workspace mla_decode and mla_attend_latent need for *p.  With
+ * num_splits == 0 the count depends on the current device's compute units
+ * (a HIP call); with num_splits > 0 no HIP call is made. */
+mla_status mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes);
+
+/* Number of token-split work groups the kernels use for *p (resolves
+ * num_splits == 0 against the current device). */
+mla_status mla_decode_num_splits(const mla_decode_params* p, int32_t* splits);
+
+/* Element type of the absorbed query that mla_absorb_q writes: MLA_F32 when
+ * cache_dtype is F32, else MLA_BF16 (the matrix-core operand type). */
+mla_status mla_absorbed_dtype(const mla_decode_params* p, int32_t* dtype);
+
+/* The whole decode step (absorb, attention over the paged latent cache with
+ * token splits and their log-sum-exp merge, W_UV up-projection).
+ *   q           [B, h, d_nope + d_rope] q_dtype; q_rope (last d_rope) pre-rotated
+ *   W_UK        [h, d_nope, d_latent]   weight_dtype
+ *   W_UV        [h, d_v, d_latent]      weight_dtype
+ *   out         [B, h, d_v]             out_dtype (written)
+ *   c_kv_scale  must be non-NULL iff cache_dtype is FP8_E4M3
+ *   workspace   >= mla_decode_workspace_size bytes, 256-byte aligned
+ * Cache arguments as described at the top of this header.  For a fixed
+ * split count the result is bitwise deterministic run to run. */
+mla_status mla_decode(const mla_decode_params* p, const void* q, const void* c_kv,
+                      const float* c_kv_scale, const void* k_rope,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const void* W_UK, const void* W_UV, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_decode that also records two caller-created hipEvent_t (may be NULL)
+ * on `stream` immediately before and after the split-attention kernel, so the
+ * caller can time that kernel alone (hipEventElapsedTime).  Same arguments,
+ * results and errors as mla_decode otherwise. */
+mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const void* c_kv,
+                            const float* c_kv_scale, const void* k_rope,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const void* W_UK, const void* W_UV, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream, void* ev_before,
+                            void* ev_after);
+
+/* Stage: query absorption ("MLA Matrix Absorption", Eq. 5).
+ *   q_lat [B, h, d_latent + d_rope] of mla_absorbed_dtype: the first d_latent
+ *   values are W_UK[i]^T q_nope[b,i,:] (fp32 accumulation, then rounded),
+ *   the last d_rope are q_rope copied. */
+mla_status mla_absorb_q(const mla_decode_params* p, const void* q, const void* W_UK,
+                        void* q_lat, void* stream);
+
+/* Stage: attention in the latent space over the paged cache, split along
+ * tokens, partial results merged by their log-sum-exp ("The RoPE handling"
+ * score, softmax, p . c_KV).
+ *   q_lat [B, h, d_latent + d_rope] as written by mla_absorb_q
+ *   o_lat [B, h, d_latent] fp32 (written)
+ *   workspace as for mla_decode. */
+mla_status mla_attend_latent(const mla_decode_params* p, const void* q_lat, const void* c_kv,
+                             const float* c_kv_scale, const void* k_rope,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             float* o_lat, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Stage: value up-projection, kept apart from W_O ("MLA Matrix Absorption":
+ * W_UV is in practice not folded into the output projection).
+ *   o_lat [B, h, d_latent] fp32;  out [B, h, d_v] out_dtype (written). */
+mla_status mla_up_project(const mla_decode_params* p, const float* o_lat, const void* W_UV,
+                          void* out, void* stream);
+
+/* Debug/test: copy the paged cache to contiguous per-sequence rows, bit for
+ * bit in the storage type.
+ *   c_out     [B, max_tokens, d_latent] cache_dtype
+ *   scale_out [B, max_tokens] fp32 (fp8 only; else may be NULL)
+ *   rope_out  [B, max_tokens, d_rope]   rope_dtype
+ * Rows at or past min(T_b, max_tokens) are zero-filled. */
+mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const float* c_kv_scale,
+                            const void* k_rope, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t max_tokens, void* c_out,
+                            float* scale_out, void* rope_out, void* stream);
+
+/* Host-side split arithmetic (no HIP call; used by the kernels' planner).
+ * The cache of all sequences is cut into 64-token tiles, numbered across
+ * sequences in order.  Split g of `splits` owns tiles
+ * [mla_split_begin(n, splits, g), mla_split_begin(n, splits, g + 1));
+ * mla_split_owner returns the split owning a tile. */
+int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g);
+int32_t mla_split_owner(int64_t n_tiles, int32_t splits, int64_t tile);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

@@ -31,7 +31,7 @@ class MLAConfig:
     q_dtype: str = "bf16"        # "f32" | "bf16"
     rope_dtype: str = "bf16"
     weight_dtype: str = "bf16"
-    out_dtype: str = "bf16"
+    out_dtype: str = "f32"       # the decode output; bf16 storage is also supported
     permuted: bool = True        # random physical block permutation
     seed: int = 1000
     spare_blocks: int = 3        # unused, NaN-poisoned pool blocks

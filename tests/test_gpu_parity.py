@@ -1,0 +1,249 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Small cases compare every output element; the full-size workloads compare a
+sample of (sequence, head) outputs that the oracle computes one by one.  The
+bar is max|gpu - oracle| <= tol * RMS(oracle output) with tol = 1e-5 for an
+fp32 cache, 2e-2 for bf16 and 6e-2 for an fp8 latent cache; integer work
+(paging) is compared bit for bit.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from head_latent_attention_10_amd import _lib
+from head_latent_attention_10_amd.device import Decoder, DeviceInputs, to_device_array
+from mla_inputs import CONFIGS, generate
+from mla_inputs.generate import repermute
+from oracle import decode_storage, oracle_from_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load_library()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, num_splits=0, repeats=1):
+    dev = DeviceInputs(inp)
+    dec = Decoder(dev, num_splits=num_splits)
+    outs = []
+    for _ in range(repeats):
+        dec()
+        torch.cuda.synchronize()
+        outs.append(dec.out_float().double().cpu().numpy())
+    return outs if repeats > 1 else outs[0]
+
+
+def check_close(inp, gpu, batches=None, heads=None, tol=None):
+    ref = oracle_from_inputs(inp, batches=batches, heads=heads)
+    mask = ~np.isnan(ref)
+    assert mask.any()
+    r = ref[mask]
+    g = gpu[mask]
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    rms = float(np.sqrt(np.mean(r * r)))
+    tol = TOL[inp.cfg.cache_dtype] if tol is None else tol
+    # a bf16 output carries its own rounding (half an ulp of the exact value) on top
+    allow = 0.5 * bf16_ulp(r) if inp.cfg.out_dtype == "bf16" else 0.0
+    excess = np.abs(g - r) - allow
+    err = float(np.max(excess))
+    _say(f"  {inp.cfg.name}: max(|err| - out rounding) = {err:.3e}, RMS = {rms:.3e}, "
+         f"ratio = {err / max(rms, 1e-30):.3e} (tol {tol})")
+    assert err <= tol * rms, (err, rms, err / rms)
+    return err / rms
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
+def small(name, **kw):
+    cfg = CONFIGS[name]
+    return cfg.replace(**kw)
+
+
+# ------------------------------------------------------------------ small, exhaustive
+
+SMALL_CASES = {
+    "tiny_fp32": (CONFIGS["tiny_fp32"], None),
+    "tiny_fp32_ragged_paged": (small("tiny_fp32", batch=4, page_size=16, permuted=True,
+                                     seq_len=None, seq_len_range=(1, 200)), None),
+    "llama2_ragged": (small("transmla_llama2_7b", batch=3, permuted=True), [1, 65, 300]),
+    "dsv3_ragged": (small("dsv3_b64_4k", batch=4), [64, 1, 129, 700]),
+    "dsv3_page16": (small("dsv3_b64_4k", batch=3, page_size=16), [17, 200, 64]),
+    "dsv3_page32": (small("dsv3_b64_4k", batch=2, page_size=32), [95, 33]),
+    "dsv3_page128": (small("dsv3_b64_4k", batch=2, page_size=128), [300, 127]),
+    "heads64": (small("dsv3_b64_4k", batch=2, heads=64), [200, 31]),
+    "heads256": (small("dsv3_b64_4k", batch=2, heads=256), [130, 64]),
+    "fp8_ragged": (small("dsv3_fp8_16k", batch=3), [5, 190, 64]),
+    "dsv3_bf16_out": (small("dsv3_b64_4k", batch=4, out_dtype="bf16"), [0, 1, 64, 333]),
+    "llama2_bf16_out": (small("transmla_llama2_7b", batch=2, out_dtype="bf16"), [700, 9]),
+    "odd_shape_bf16": (small("dsv3_b64_4k", batch=3, heads=3, d_nope=24, d_latent=48, d_rope=16,
+                             d_v=20, page_size=8), [1, 13, 40]),
+    "odd_shape_fp8": (small("dsv3_fp8_16k", batch=2, heads=5, d_nope=8, d_latent=40, d_rope=0,
+                            d_v=12, page_size=4), [3, 22]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL_CASES))
+def test_small_exhaustive(case):
+    cfg, lens = SMALL_CASES[case]
+    _say(f"case {case}: lens={lens}")
+    inp = generate(cfg, seq_lens=lens)
+    gpu = run_gpu(inp)
+    check_close(inp, gpu)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64, 1000])
+def test_split_counts_agree_with_oracle(splits):
+    cfg = small("dsv3_b64_4k", batch=3)
+    inp = generate(cfg, seq_lens=[400, 1, 257])
+    _say(f"splits={splits}")
+    check_close(inp, run_gpu(inp, num_splits=splits))
+
+
+def test_fp32_split_counts_agree_to_fp32_rounding():
+    cfg = small("tiny_fp32", batch=3, seq_len=None, seq_len_range=(1, 500), page_size=32,
+                permuted=True)
+    inp = generate(cfg, seq_lens=[500, 3, 64])
+    a = run_gpu(inp, num_splits=1)
+    b = run_gpu(inp, num_splits=17)
+    rms = np.sqrt(np.mean(a * a))
+    assert np.max(np.abs(a - b)) <= 1e-6 * rms
+
+
+def test_empty_and_single_token_sequences():
+    cfg = small("dsv3_b64_4k", batch=4)
+    inp = generate(cfg, seq_lens=[0, 1, 0, 64])
+    gpu = run_gpu(inp, num_splits=5)
+    assert np.all(gpu[0] == 0) and np.all(gpu[2] == 0)
+    check_close(inp, gpu, batches=[1, 3])
+
+
+def test_all_sequences_empty():
+    inp = generate(small("dsv3_b64_4k", batch=2), seq_lens=[0, 0])
+    assert np.all(run_gpu(inp) == 0)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_bitwise_deterministic():
+    inp = generate(small("dsv3_b64_4k", batch=2), seq_lens=[1000, 333])
+    a, b, c = run_gpu(inp, repeats=3)
+    assert np.array_equal(a, b) and np.array_equal(b, c)
+
+
+@pytest.mark.parametrize("name", ["dsv3_b64_4k", "dsv3_fp8_16k", "tiny_fp32"])
+def test_block_permutation_invariance_bitwise(name):
+    cfg = small(name, batch=3, permuted=True, seq_len=None, seq_len_range=(1, 400))
+    inp = generate(cfg, seq_lens=[400, 77, 129])
+    other = repermute(inp, seed=5)
+    a = run_gpu(inp, num_splits=9)
+    b = run_gpu(other, num_splits=9)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["dsv3_ragged_32k", "dsv3_fp8_16k", "tiny_fp32"])
+def test_gather_is_bit_exact(name):
+    cfg = small(name, batch=3, page_size=16 if name != "tiny_fp32" else 8, seq_len=None,
+                seq_len_range=(1, 300))
+    inp = generate(cfg, seq_lens=[300, 1, 50])
+    dev = DeviceInputs(inp)
+    p = dev.params()
+    Tm = 320
+    itm = {"f32": 4, "bf16": 2, "e4m3": 1}
+    c_out = torch.full((cfg.batch, Tm, cfg.d_latent * itm[cfg.cache_dtype]), 0xAB, dtype=torch.uint8, device="cuda")
+    r_out = torch.full((cfg.batch, Tm, cfg.d_rope * itm[cfg.rope_dtype]), 0xCD, dtype=torch.uint8, device="cuda")
+    s_out = torch.full((cfg.batch, Tm), -1.0, dtype=torch.float32, device="cuda") if cfg.cache_dtype == "e4m3" else None
+    _lib.mla_gather_cache(p, dev.c_kv, dev.c_kv_scale, dev.k_rope, dev.block_table, dev.seq_lens,
+                          Tm, c_out, s_out, r_out)
+    torch.cuda.synchronize()
+    c_host = c_out.cpu().numpy()
+    r_host = r_out.cpu().numpy()
+    P = cfg.page_size
+    for b, T in enumerate(inp.seq_lens):
+        want_c = np.zeros((Tm, c_host.shape[2]), np.uint8)
+        want_r = np.zeros((Tm, r_host.shape[2]), np.uint8)
+        for t in range(int(T)):
+            blk = inp.block_table[b, t // P]
+            want_c[t] = inp.c_kv[blk, t % P].view(np.uint8)
+            want_r[t] = inp.k_rope[blk, t % P].view(np.uint8)
+        assert np.array_equal(c_host[b], want_c)
+        assert np.array_equal(r_host[b], want_r)
+        if s_out is not None:
+            s_host = s_out.cpu().numpy()
+            want_s = np.zeros(Tm, np.float32)
+            for t in range(int(T)):
+                want_s[t] = inp.c_kv_scale[inp.block_table[b, t // P], t % P]
+            assert np.array_equal(s_host[b], want_s)
+
+
+def test_stage_entry_points_compose_to_decode():
+    inp = generate(small("dsv3_b64_4k", batch=2), seq_lens=[500, 70])
+    dev = DeviceInputs(inp)
+    dec = Decoder(dev, num_splits=11)
+    dec()
+    p = dec.p
+    cfg = inp.cfg
+    qlat = torch.empty((cfg.batch, cfg.heads, cfg.d_latent + cfg.d_rope), dtype=torch.int16, device="cuda")
+    assert _lib.mla_absorbed_dtype(p) == _lib.MLA_BF16
+    _lib.mla_absorb_q(p, dev.q, dev.W_UK, qlat)
+    olat = torch.empty((cfg.batch, cfg.heads, cfg.d_latent), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dec.ws_bytes, dtype=torch.uint8, device="cuda")
+    _lib.mla_attend_latent(p, qlat, dev.c_kv, dev.c_kv_scale, dev.k_rope, dev.block_table,
+                           dev.seq_lens, olat, ws)
+    out = torch.empty_like(dec.out)
+    _lib.mla_up_project(p, olat, dev.W_UV, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dec.out)
+    # the absorbed query's rope half is q_rope copied exactly
+    q_rope = inp.q[:, :, cfg.d_nope:]
+    assert np.array_equal(qlat.cpu().numpy()[:, :, cfg.d_latent:].view(np.uint16), q_rope)
+
+
+# ------------------------------------------------------------------ full size, sampled
+
+FULL = ["tiny_fp32", "transmla_llama2_7b", "dsv3_b64_4k", "dsv3_ragged_32k", "dsv3_fp8_16k",
+        "dsv3_b8_32k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    _say(f"full-size {name}: generating")
+    inp = generate(cfg)
+    _say(f"  tokens={int(inp.seq_lens.sum())} running GPU")
+    gpu = run_gpu(inp)
+    assert np.all(np.isfinite(gpu)), "NaN-poisoned slots leaked into the output"
+    rng = np.random.default_rng(7)
+    if cfg.batch * cfg.heads <= 16:
+        check_close(inp, gpu)
+        return
+    pairs = {(int(rng.integers(cfg.batch)), int(rng.integers(cfg.heads))) for _ in range(6)}
+    pairs |= {(cfg.batch - 1, cfg.heads - 1), (0, 0)}
+    # the oracle computes one (sequence, head) at a time; keep only those entries
+    ref = np.full(gpu.shape, np.nan)
+    for b, h in sorted(pairs):
+        ref[b, h] = oracle_from_inputs(inp, batches=[b], heads=[h])[b, h]
+    mask = ~np.isnan(ref)
+    r, g = ref[mask], gpu[mask]
+    rms = float(np.sqrt(np.mean(r * r)))
+    allow = 0.5 * bf16_ulp(r) if cfg.out_dtype == "bf16" else 0.0
+    err = float(np.max(np.abs(g - r) - allow))
+    _say(f"  sampled {len(pairs)} (b,h): max|err| = {err:.3e}, RMS = {rms:.3e}, ratio {err / rms:.3e}")
+    assert err <= TOL[cfg.cache_dtype] * rms
