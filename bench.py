@@ -87,6 +87,9 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
+    for a, b in evs:            # torch creates the HIP events on first record
+        a.record(stream)
+        b.record(stream)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
