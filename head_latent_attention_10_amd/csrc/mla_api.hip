@@ -72,17 +72,23 @@ struct Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Token splits.  The matrix-core kernel serves a split's heads with HG work
+// groups that must share an XCD, which needs the split count to be a multiple
+// of 8 when HG > 1; by default one work group runs per compute unit.
 mla_status resolve_splits(const mla_decode_params& p, int32_t* splits) {
-  if (p.num_splits > 0) {
-    *splits = p.num_splits;
-    return MLA_OK;
+  const int32_t hg = mla::mfma_supported(p) ? mla::mfma_head_groups(p.num_heads) : 1;
+  int32_t n = p.num_splits;
+  if (n <= 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiProcessorCount)");
+    n = cus / hg;
   }
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiProcessorCount)");
-  *splits = cus > 0 ? cus : 1;
+  if (n < 1) n = 1;
+  if (hg > 1) n = (n + 7) / 8 * 8;
+  *splits = n;
   return MLA_OK;
 }
 

@@ -3,35 +3,54 @@
 // Shape: d_c = 512 latent values + d_r = 64 rope values per cached token,
 // heads a multiple of 32, bf16 latent/rope rows, bf16 absorbed query.
 //
-// Work decomposition.  Work group = (token split g, block of up to 128 heads).
-// Split g owns a contiguous run of 64-token tiles of the concatenated
-// sequences ("split plan" in mla_common.hpp); every tile is read from HBM
-// once and staged in LDS, where all heads of the work group use it.  A wave
-// owns 32 heads and, per 32-token sub-tile, computes
-//   S^T[t, i] = sum_d KV[t, d] Q[i, d]        (MFMA 32x32x16: M = tokens,
-//                                              N = heads, K = 576)
-//   online softmax over t (one lane = one head: in-lane reductions plus one
-//                          exchange with the lane 32 away)
-//   O^T[d, i] += sum_t C[t, d] P[i, t]        (MFMA: M = latent rows, N = heads,
+// Work decomposition.  A token split g owns a contiguous run of 64-token tiles
+// of the concatenated sequences ("split plan" in mla_common.hpp).  Its heads
+// are served by HG work groups of 32*HB heads each (HB = 2 for 64 heads, 1 for
+// 32); the HG groups of one split get workgroup ids that differ by a multiple
+// of 8 and are dispatched together, so they run on the same XCD and the
+// second read of every tile is served by that XCD's L2.
+//
+// Inside a work group the waves specialise:
+//  * 2*HB score waves.  Wave (hb, kh) holds the absorbed query of 32 heads for
+//    half of the 576-wide key (kh = 0: latent 0..287; kh = 1: latent 288..511
+//    and the 64 rope values) in registers and computes, for each 32-token step,
+//      S^T[t, i] = sum_d KV[t, d] Q[i, d]      (MFMA 32x32x16 bf16, M = tokens,
+//                                              N = heads, K = its 288 values)
+//    The kh = 1 wave hands its partial scores to its partner through LDS; the
+//    partner adds them, runs the online softmax (one lane = one head) and
+//    publishes the bf16 weights P, the per-head rescale factors and, at the
+//    end of a sequence segment, 1/l and the log-sum-exp.
+//  * 4 (HB = 2) or 2 (HB = 1) value waves.  Each owns a slice of 128 (or 256)
+//    latent rows of the output for all heads of the group and computes
+//      O^T[d, i] += sum_t C[t, d] P[i, t]      (M = latent rows, N = heads,
 //                                              K = tokens)
-// The heads that share one latent row sit on the MFMA's N dimension, so each
-// row is fetched once per 32 heads.  The softmax weights go from the score
-// accumulator straight into the PV operand: the K order inside each 16-token
-// step is permuted (slot i of lane group g is token 8*(i/4) + 4*g + i%4) so
-// that it matches the accumulator layout, and the latent tile is read in the
-// same permuted order with the gfx950 transposing LDS read.
+//    one step behind the score waves.  The latent tile is read with the
+//    transposing LDS read; each such read feeds HB MFMAs.  The weights are in
+//    a permuted token order (slot i of lane group g is token 8*(i/4) + 4*g +
+//    i%4 of the 16-token k-step) that matches the score accumulator layout,
+//    and the latent tile is read in the same order.
 //
-// LDS ring.  Two stages of one 64-token tile: 64 latent rows of 1 KiB and 64
-// rope rows of 128 B.  Rows are written by direct global->LDS 16-byte loads
-// (one instruction per latent row, eight rope rows per instruction) with the
-// 16-byte chunk index XOR-swizzled by the row so the MFMA operand reads are
-// spread over the banks.  The loads of tile i+1 are in flight while tile i is
-// computed.
+// LDS ring.  Four stages of one 32-token step: 32 latent rows of 1 KiB and 32
+// rope rows of 128 B, written by direct global->LDS 16-byte loads (one
+// instruction per latent row, eight rope rows per instruction) two steps
+// ahead of use.  The 16-byte chunk index is XOR-swizzled with a permutation
+// of the row's low four bits, which keeps both the row reads of the score
+// product and the 4-row transposing reads of the value product free of bank
+// conflicts.
 //
-// Softmax rescaling is lazy: the running maximum is only raised when a tile's
-// maximum exceeds it by more than 2^8 in weight, so the 256-register
-// accumulator is rarely rescaled; weights then stay below 2^8, well inside
-// bf16 and fp32 range, and the final normalisation uses the same reference.
+// Step i (three work-group barriers):
+//   wait for step i's loads; barrier
+//   issue loads of step i+2 | score waves: partial S(i) | value waves: O += P(i-1) C(i-1)
+//   barrier
+//   score wave kh = 0: merge partial scores, softmax, publish P(i)
+//   barrier
+//
+// Softmax rescaling is lazy: after the first four steps of a sequence segment
+// (which track the exact maximum, so an early dominant token gets weight
+// exactly 1), the running maximum is only raised when a step's maximum
+// exceeds it by more than 2^8 in weight, so the output accumulator is rarely
+// rescaled; weights stay below 2^8.  The normaliser is the sum of the
+// bf16-rounded weights that the MFMA consumes.
 #include "mla_kernels.hpp"
 
 namespace mla {
@@ -39,273 +58,426 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_t;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kDc = 512, kDr = 64;
-constexpr int kKsC = kDc / 16;          // 32 score k-steps over the latent
-constexpr int kKs = (kDc + kDr) / 16;   // 36 score k-steps in all
-constexpr int kMd = kDc / 32;           // 16 output row blocks
-constexpr int kCRow = kDc * 2;          // 1024 bytes per latent row
-constexpr int kRRow = kDr * 2;          // 128 bytes per rope row
-constexpr int kStageC = kTile * kCRow;  // 65536
-constexpr int kStage = kStageC + kTile * kRRow;  // 73728
-constexpr float kLazy = 8.0f;           // log2 of the largest unnormalised weight
-constexpr int kQkDepth = 4;             // score operand reads in flight
-constexpr int kPvDepth = 4;             // value operand reads in flight
+constexpr int kStep = 32;                         // tokens per pipeline step
+constexpr int kCRow = kDc * 2;                    // 1024 bytes per latent row
+constexpr int kRRow = kDr * 2;                    // 128 bytes per rope row
+constexpr int kStageC = kStep * kCRow;            // 32768
+constexpr int kStage = kStageC + kStep * kRRow;   // 36864
+constexpr int kStages = 4;
+constexpr int kRing = kStages * kStage;           // 147456
+constexpr int kLoadsPerStep = kStep + kStep / 8;  // 32 latent rows + 4 rope groups
+constexpr int kKsHalf = 18;                       // score k-steps per score wave
+constexpr int kXBytes = 64 * 64;                  // one wave's partial scores
+constexpr int kPBytes = 2 * 64 * 16;              // weights of one head block, two k-steps
+constexpr float kLazy = 8.0f;                     // log2 of the largest unnormalised weight
+constexpr int kExactSteps = 4;                    // steps per segment with an exact maximum
 
-__device__ inline int swz_c(int row) { return row & 15; }
+template <int HB>
+struct Shape {
+  static constexpr int NQ = 2 * HB;             // score waves
+  static constexpr int NP = HB == 2 ? 4 : 2;    // value waves
+  static constexpr int NW = NQ + NP;
+  static constexpr int MDP = kDc / 32 / NP;     // 32-row output blocks per value wave
+  static constexpr int LDS = kRing + HB * (kXBytes + kPBytes) + HB * 32 * 4 * 2 + 16;
+};
 
-// fp32 value of the round-to-nearest-even bf16 of a finite x.
+// Chunk swizzles: row bits (b3 b2 b1 b0) -> chunk bits (b2 b1 b0 b3) for latent
+// rows; rope rows share 256-byte bank lines in pairs.
+__device__ inline int swz_c(int r) { return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1); }
+__device__ inline int swz_r(int r) { return (r >> 1) & 7; }
+
 __device__ inline float round_to_bf16(float x) {
   uint32_t u = __float_as_uint(x);
   u += 0x7fffu + ((u >> 16) & 1u);
   return __uint_as_float(u & 0xffff0000u);
 }
-__device__ inline int swz_r(int row) { return (row >> 1) & 7; }
 
-// Issue the direct-to-LDS loads of one tile (tokens t0.. of sequence b, T tokens
-// in all; t0 is a multiple of 64).  Rows past the end repeat the last valid
-// token so every load reads finite data; those rows are masked in the softmax.
-// `wave` must be wave-uniform so the block-table lookups are scalar loads and
-// never make the wave wait on the vector-memory counter.
-template <int NW>
-__device__ inline void issue_tile(const AttnArgs& a, lds_t* stage, int32_t b, int32_t t0,
-                                  int32_t T, int wave, int lane) {
-  const char* ckv = static_cast<const char*>(a.c_kv);
-  const char* krp = static_cast<const char*>(a.k_rope);
-  const int32_t rmax = T - 1 - t0;
-  const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks;
-  if (a.P % kTile == 0) {
-    // the whole tile lies in one block: one table lookup
-    int32_t blk = trow[t0 / a.P];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-    const int64_t base = (int64_t)blk * a.P + (t0 % a.P);
-#pragma unroll
-    for (int r0 = 0; r0 < kTile; r0 += NW) {
-      const int r = r0 + wave;
-      const char* src = ckv + (base + min(r, rmax)) * kCRow + ((lane ^ swz_c(r)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)(stage + r * kCRow), 16, 0, 0);
-    }
-#pragma unroll
-    for (int j0 = 0; j0 < 8; j0 += NW) {
-      const int j = j0 + wave;
-      const int r = 8 * j + (lane >> 3);
-      const char* src = krp + (base + min(r, rmax)) * kRRow + (((lane & 7) ^ swz_r(r)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)(stage + kStageC + j * 1024), 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int r0 = 0; r0 < kTile; r0 += NW) {
-      const int r = r0 + wave;
-      const int64_t slot = phys_slot(a.block_table, b, t0 + min(r, rmax), a.P, a.max_blocks, a.num_blocks);
-      const char* src = ckv + slot * kCRow + ((lane ^ swz_c(r)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)(stage + r * kCRow), 16, 0, 0);
-    }
-#pragma unroll
-    for (int j0 = 0; j0 < 8; j0 += NW) {
-      const int j = j0 + wave;
-      const int r = 8 * j + (lane >> 3);
-      const int64_t slot = phys_slot(a.block_table, b, t0 + min(r, rmax), a.P, a.max_blocks, a.num_blocks);
-      const char* src = krp + slot * kRRow + (((lane & 7) ^ swz_r(r)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)(stage + kStageC + j * 1024), 16, 0, 0);
-    }
-  }
-}
-
-template <int NW>
-constexpr int loads_per_tile() { return kTile / NW + (8 + NW - 1) / NW; }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-struct SoftmaxState {
-  float m;  // running reference maximum, log2 units
-  float l;  // lane-partial sum of weights
+// Walks the 32-token steps of a split's tiles in order; a tile's second half
+// is skipped when it holds no token of its sequence.
+struct StepIter {
+  int32_t t, t_end, half, b, T, first;  // first = first tile of sequence b
+  bool valid;
+
+  __device__ void init(const AttnArgs& a, int32_t t_begin, int32_t t_stop) {
+    t = t_begin;
+    t_end = t_stop;
+    half = 0;
+    b = 0;
+    while (a.cu_tiles[b + 1] <= t) b++;
+    T = seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
+    first = a.cu_tiles[b];
+    valid = t < t_end;
+  }
+  __device__ int32_t t0() const { return (t - first) * kTile + half * kStep; }
+  __device__ int32_t nvalid() const { return min(kStep, T - t0()); }
+  __device__ bool has_second_half() const { return (t - first) * kTile + kStep < T; }
+  // last step of its sequence within this split
+  __device__ bool seg_last(const AttnArgs& a) const {
+    const bool last_of_tile = half == 1 || !has_second_half();
+    return last_of_tile && (t + 1 == t_end || a.cu_tiles[b + 1] <= t + 1);
+  }
+  __device__ void advance(const AttnArgs& a) {
+    if (half == 0 && has_second_half()) {
+      half = 1;
+      return;
+    }
+    half = 0;
+    t++;
+    valid = t < t_end;
+    if (valid && a.cu_tiles[b + 1] <= t) {
+      while (a.cu_tiles[b + 1] <= t) b++;
+      T = seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
+      first = a.cu_tiles[b];
+    }
+  }
 };
 
-// HB = 32-head blocks per work group, TS = token streams (waves splitting the
-// two 32-token halves of each tile, each with its own partial).
-template <int HB, int TS>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * HB * TS, 64 * HB * TS),
-                          amdgpu_waves_per_eu(1, 1)))
+// Direct-to-LDS loads of one step.  Rows past the end repeat the last valid
+// token (finite data; masked in the softmax).  `wave` is wave-uniform, so the
+// block-table lookups are scalar loads.
+template <int NW>
+__device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const StepIter& it, int wave,
+                                  int lane) {
+  const char* ckv = static_cast<const char*>(a.c_kv);
+  const char* krp = static_cast<const char*>(a.k_rope);
+  const int32_t t0 = it.t0();
+  const int32_t rmax = it.T - 1 - t0;
+  const int32_t* trow = a.block_table + (int64_t)it.b * a.max_blocks;
+  const bool one_block = (a.P % kStep) == 0;  // the step lies inside one block
+  int64_t base = 0;
+  if (one_block) {
+    int32_t blk = trow[t0 / a.P];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    base = (int64_t)blk * a.P + (t0 % a.P);
+  }
+  for (int k = wave; k < kLoadsPerStep; k += NW) {
+    if (k < kStep) {
+      const int r = k;
+      const int64_t slot = one_block ? base + min(r, rmax)
+                                     : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
+                                                 a.max_blocks, a.num_blocks);
+      const char* src = ckv + slot * kCRow + ((lane ^ swz_c(r)) << 4);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + r * kCRow), 16, 0, 0);
+    } else {
+      const int j = k - kStep;
+      const int r = 8 * j + (lane >> 3);
+      const int64_t slot = one_block ? base + min(r, rmax)
+                                     : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
+                                                 a.max_blocks, a.num_blocks);
+      const char* src = krp + slot * kRRow + (((lane & 7) ^ swz_r(r)) << 4);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + kStageC + j * 1024), 16, 0, 0);
+    }
+  }
+}
+
+template <int NW>
+__device__ constexpr int loads_of_wave(int wave) { return (kLoadsPerStep - wave + NW - 1) / NW; }
+
+// The load schedule every wave keeps identically.
+template <int NW>
+struct Loader {
+  StepIter next;       // next step to load
+  int32_t loaded;      // steps issued so far
+  bool newer_issued;   // the batch after the awaited one was issued
+
+  __device__ void start(const AttnArgs& a, lds_t* ring, int32_t tb, int32_t te, int wave,
+                        int lane) {
+    next.init(a, tb, te);
+    loaded = 0;
+    for (int s = 0; s < 2 && next.valid; s++) {
+      issue_step<NW>(a, ring + (loaded % kStages) * kStage, next, wave, lane);
+      next.advance(a);
+      loaded++;
+    }
+    newer_issued = loaded == 2;
+  }
+  // Start of step i: wait for this wave's loads of step i (only the newer batch
+  // i+1 may stay in flight), barrier, then issue step i+2.
+  __device__ void begin_step(const AttnArgs& a, lds_t* ring, int wave, int lane) {
+    if (!newer_issued)
+      wait_vmcnt<0>();
+    else if (loads_of_wave<NW>(wave) == loads_of_wave<NW>(0))
+      wait_vmcnt<loads_of_wave<NW>(0)>();
+    else
+      wait_vmcnt<loads_of_wave<NW>(NW - 1)>();
+    __syncthreads();
+    if (next.valid) {
+      issue_step<NW>(a, ring + (loaded % kStages) * kStage, next, wave, lane);
+      next.advance(a);
+      loaded++;
+      newer_issued = true;
+    } else {
+      newer_issued = false;
+    }
+  }
+};
+
+template <int HB>
+__global__ __attribute__((amdgpu_flat_work_group_size(Shape<HB>::NW * 64, Shape<HB>::NW * 64)))
 void attend_mfma_kernel(AttnArgs a) {
-  constexpr int NW = HB * TS;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
-  lds_t* lds = (lds_t*)(lds_raw);
+  using S = Shape<HB>;
+  constexpr int NW = S::NW;
+  __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
+  lds_t* ring = (lds_t*)smem;
+  lds_t* xbuf = ring + kRing;                       // [HB][64 lanes][16 floats]
+  lds_t* pbuf = xbuf + HB * kXBytes;                // [HB][2 k-steps][64 lanes][16 B]
+  float* s_alpha = (float*)(smem + kRing + HB * (kXBytes + kPBytes));  // [HB][32]
+  float* s_invl = s_alpha + HB * 32;                // [HB][32]
+  int* s_flag = (int*)(s_invl + HB * 32);           // [HB]
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int hb = wave % HB, ts = wave / HB;
-  const int g32 = lane >> 5;                       // lane group within the MFMA
-  const int32_t head = blockIdx.y * (32 * HB) + hb * 32 + (lane & 31);
-  const int32_t g = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g32 = lane >> 5;
 
+  // workgroup id -> (split, head group); the HG groups of a split share an XCD
+  const int32_t HG = a.h / (32 * HB);
+  int32_t g, hg;
+  if (HG > 1) {
+    const int32_t L = blockIdx.x, span = 8 * HG;
+    hg = (L % span) / 8;
+    g = (L / span) * 8 + (L % 8);
+  } else {
+    hg = 0;
+    g = blockIdx.x;
+  }
+  if (g >= a.splits) return;
   const int32_t n_total = a.cu_tiles[a.B];
   if (n_total == 0) return;
   const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);
   const int32_t t_end = (int32_t)split_begin(n_total, a.splits, g + 1);
   if (t_begin >= t_end) return;
 
-  int32_t b = 0;
-  while (a.cu_tiles[b + 1] <= t_begin) b++;
-  int32_t T = seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
-  int32_t first = a.cu_tiles[b];
-
-  issue_tile<NW>(a, lds, b, (t_begin - first) * kTile, T, wave, lane);
-
-  bf16x8 qf[kKs];
-  auto load_q = [&](int32_t bb) {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-        static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc + kDr));
-#pragma unroll
-    for (int ks = 0; ks < kKs; ks++) qf[ks] = qp[2 * ks + g32];
-  };
-  load_q(b);
-
-  f32x16 o[kMd];
-#pragma unroll
-  for (int md = 0; md < kMd; md++) o[md] = f32x16{};
-  SoftmaxState st{-INFINITY, 0.f};
+  Loader<NW> ld;
+  ld.start(a, ring, t_begin, t_end, wave, lane);
+  StepIter cur;
+  cur.init(a, t_begin, t_end);
   const float sm = a.sm_scale_log2;
 
-  for (int32_t tile = t_begin; tile < t_end; tile++) {
-    lds_t* cur = lds + ((tile - t_begin) & 1) * kStage;
-    lds_t* nxt = lds + (((tile - t_begin) & 1) ^ 1) * kStage;
-    int32_t b_next = b;
-    const bool more = tile + 1 < t_end;
-    if (more) {
-      while (a.cu_tiles[b_next + 1] <= tile + 1) b_next++;
-      const int32_t T_next = b_next == b ? T : seq_len_clamped(a.seq_lens, b_next, a.max_blocks, a.P);
-      issue_tile<NW>(a, nxt, b_next, (tile + 1 - a.cu_tiles[b_next]) * kTile, T_next, wave, lane);
-      wait_vmcnt<loads_per_tile<NW>()>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();
-
-    const int32_t nvalid = min(kTile, T - (tile - first) * kTile);
+  if (wave < S::NQ) {
+    // ================================================================ score waves
+    const int hb = wave >> 1, kh = wave & 1;
+    const int32_t head = hg * 32 * HB + hb * 32 + (lane & 31);
+    bf16x8 qf[kKsHalf];
+    auto load_q = [&](int32_t bb) {
+      const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+          static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc + kDr));
 #pragma unroll
-    for (int sub = 0; sub < 2; sub++) {
-      if (TS == 2 && sub != ts) continue;
-      // ---- scores S^T[t, i] for the 32 tokens of this sub-tile
+      for (int k = 0; k < kKsHalf; k++) qf[k] = qp[2 * (kh * kKsHalf + k) + g32];
+    };
+    load_q(cur.b);
+    float m_run = -INFINITY, l_run = 0.f;
+    int32_t seg_step = 0;  // steps of the current segment seen so far
+    lds_t* xb = xbuf + hb * kXBytes + lane * 64;
+    lds_t* pb = pbuf + hb * kPBytes + lane * 16;
+    // n steps of scores plus one final step in which only the value waves work
+    for (int32_t i = 0;; i++) {
+      ld.begin_step(a, ring, wave, lane);
+      lds_t* st = ring + (i % kStages) * kStage;
       f32x16 s = f32x16{};
-      const int row = 32 * sub + (lane & 31);
-      auto ld_a = [&](int ks) -> bf16x8 {
-        const int chunk = 2 * (ks < kKsC ? ks : ks - kKsC) + g32;
-        const lds_t* p = ks < kKsC ? cur + row * kCRow + ((chunk ^ swz_c(row)) << 4)
-                                   : cur + kStageC + row * kRRow + ((chunk ^ swz_r(row)) << 4);
-        return *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(p);
-      };
-      bf16x8 av[kQkDepth];
+      if (cur.valid) {
+        const int row = lane & 31;
+        auto ld_a = [&](int k) -> bf16x8 {
+          const int ks = kh * kKsHalf + k;
+          const lds_t* p = ks < 32
+              ? st + row * kCRow + (((2 * ks + g32) ^ swz_c(row)) << 4)
+              : st + kStageC + row * kRRow + (((2 * (ks - 32) + g32) ^ swz_r(row)) << 4);
+          return *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(p);
+        };
+        constexpr int D = 4;
+        bf16x8 av[D];
 #pragma unroll
-      for (int k = 0; k < kQkDepth; k++) av[k] = ld_a(k);
+        for (int k = 0; k < D; k++) av[k] = ld_a(k);
 #pragma unroll
-      for (int ks = 0; ks < kKs; ks++) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks % kQkDepth], qf[ks], s, 0, 0, 0);
-        if (ks + kQkDepth < kKs) av[ks % kQkDepth] = ld_a(ks + kQkDepth);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // ---- online softmax (one lane = one head; tokens split over g32)
-      float sv[16];
-      float mt = -INFINITY;
+        for (int k = 0; k < kKsHalf; k++) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k % D], qf[k], s, 0, 0, 0);
+          if (k + D < kKsHalf) av[k % D] = ld_a(k + D);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kh == 1) {
 #pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const int tok = 32 * sub + 8 * (j >> 2) + 4 * g32 + (j & 3);
-        sv[j] = tok < nvalid ? s[j] * sm : -INFINITY;
-        mt = fmaxf(mt, sv[j]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const bool need = mt > st.m + kLazy;
-      if (__any(need)) {
-        const float m_new = fmaxf(st.m, mt);
-        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-#pragma unroll
-        for (int md = 0; md < kMd; md++) o[md] *= alpha;
-        st.l *= alpha;
-        st.m = m_new;
-      }
-      const float mref = st.m == -INFINITY ? 0.f : st.m;
-      // Weights to bf16 with whole-vector conversions only: element-wise
-      // writes into bf16 vectors are not lowered correctly by this compiler.
-      f32x8 pw[2];
-      float lsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const float pj = __builtin_amdgcn_exp2f(sv[j] - mref);
-        pw[j >> 3][j & 7] = pj;
-        lsum += round_to_bf16(pj);   // normalise by the weights the MFMA actually uses
-      }
-      const bf16x8 pf[2] = {__builtin_convertvector(pw[0], bf16x8),
-                            __builtin_convertvector(pw[1], bf16x8)};
-      st.l += lsum;
-      // ---- O^T[d, i] += C[t, d] P[i, t]
-      const int j16 = lane & 15, grp = lane >> 4;
-      const int e = j16 >> 2, qd = j16 & 3;
-      // A operand of (md, half): latent rows d, the 8 permuted tokens of the step
-      auto ld_c = [&](int md, int half) -> bf16x8 {
-        const int dd = 32 * md + 16 * (grp & 1) + 4 * qd;
-        const int chunk = dd >> 3, hoff = (dd & 7) * 2;
-        const int r0 = 32 * sub + 16 * half + 4 * g32 + e;
-        const int r1 = r0 + 8;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-            cur + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-            cur + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
-        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, cat);
-      };
-      bf16x8 cv[kPvDepth];
-#pragma unroll
-      for (int k = 0; k < kPvDepth; k++) cv[k] = ld_c(k >> 1, k & 1);
-#pragma unroll
-      for (int step = 0; step < 2 * kMd; step++) {
-        const int md = step >> 1, half = step & 1;
-        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[step % kPvDepth], pf[half], o[md], 0, 0, 0);
-        const int nx = step + kPvDepth;
-        if (nx < 2 * kMd) cv[step % kPvDepth] = ld_c(nx >> 1, nx & 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // ---- end of a sequence segment: write the normalised partial
-    if (!more || b_next != b) {
-      const float ltot = st.l + __shfl_xor(st.l, 32);
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      const int64_t slot = (int64_t)(g + b) * TS + ts;
-      float* dst = a.part_o + (slot * a.h + head) * kDc;
-#pragma unroll
-      for (int md = 0; md < kMd; md++) {
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          f32x4 v = {o[md][4 * jj] * inv, o[md][4 * jj + 1] * inv, o[md][4 * jj + 2] * inv,
-                     o[md][4 * jj + 3] * inv};
-          *reinterpret_cast<f32x4*>(dst + 32 * md + 8 * jj + 4 * g32) = v;
+          for (int q = 0; q < 4; q++)
+            *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 16 * q) =
+                f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
         }
       }
-      if (g32 == 0)
-        a.part_lse[slot * a.h + head] =
-            ltot > 0.f ? (st.m + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
-      if (more) {
-        b = b_next;
-        T = seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
-        first = a.cu_tiles[b];
-        load_q(b);
+      __syncthreads();
+      if (cur.valid && kh == 0) {
 #pragma unroll
-        for (int md = 0; md < kMd; md++) o[md] = f32x16{};
-        st = SoftmaxState{-INFINITY, 0.f};
+        for (int q = 0; q < 4; q++) {
+          const f32x4 o = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 16 * q);
+          s[4 * q] += o[0];
+          s[4 * q + 1] += o[1];
+          s[4 * q + 2] += o[2];
+          s[4 * q + 3] += o[3];
+        }
+        const int32_t nv = cur.nvalid();
+        float sv[16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int tok = 8 * (j >> 2) + 4 * g32 + (j & 3);
+          sv[j] = tok < nv ? s[j] * sm : -INFINITY;
+          mt = fmaxf(mt, sv[j]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // exact running maximum for the first steps of a segment (the largest
+        // weight is then exactly 1 in bf16), lazy afterwards
+        const float thr = seg_step < kExactSteps ? 0.f : kLazy;
+        const bool any = __any(mt > m_run + thr);
+        float alpha = 1.f;
+        if (any) {
+          const float m_new = fmaxf(m_run, mt);
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float mref = m_run == -INFINITY ? 0.f : m_run;
+        f32x8 pw[2];
+        float lsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const float pj = __builtin_amdgcn_exp2f(sv[j] - mref);
+          pw[j >> 3][j & 7] = pj;
+          lsum += round_to_bf16(pj);
+        }
+        l_run += lsum;
+        seg_step++;
+        // publish the weights in the value product's operand layout (whole-vector
+        // conversions only: element-wise bf16 vector writes are not lowered correctly)
+        *reinterpret_cast<bf16x8 __attribute__((address_space(3)))*>(pb) =
+            __builtin_convertvector(pw[0], bf16x8);
+        *reinterpret_cast<bf16x8 __attribute__((address_space(3)))*>(pb + 64 * 16) =
+            __builtin_convertvector(pw[1], bf16x8);
+        if (g32 == 0) s_alpha[hb * 32 + lane] = alpha;
+        if (lane == 0) s_flag[hb] = any ? 1 : 0;
+        if (cur.seg_last(a)) {
+          const float ltot = l_run + __shfl_xor(l_run, 32);
+          if (g32 == 0) {
+            s_invl[hb * 32 + lane] = ltot > 0.f ? 1.f / ltot : 0.f;
+            const int64_t slot = (int64_t)(g + cur.b);
+            a.part_lse[slot * a.h + head] =
+                ltot > 0.f ? (m_run + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+          }
+        }
+      }
+      __syncthreads();
+      if (!cur.valid) break;  // that was the value waves' final step
+      const bool was_last = cur.seg_last(a);
+      cur.advance(a);
+      if (cur.valid && was_last) {
+        load_q(cur.b);
+        m_run = -INFINITY;
+        l_run = 0.f;
+        seg_step = 0;
       }
     }
-    __syncthreads();
+  } else {
+    // ================================================================ value waves
+    constexpr int MDP = S::MDP;
+    const int pw_id = wave - S::NQ;
+    const int j16 = lane & 15, grp = lane >> 4, e = j16 >> 2, qd = j16 & 3;
+    f32x16 o[MDP][HB];
+#pragma unroll
+    for (int md = 0; md < MDP; md++)
+#pragma unroll
+      for (int hb = 0; hb < HB; hb++) o[md][hb] = f32x16{};
+    StepIter prev = cur;  // the step whose weights are consumed in this iteration
+    bool prev_valid = false;
+    for (int32_t i = 0;; i++) {
+      if (!cur.valid && !prev_valid) break;
+      ld.begin_step(a, ring, wave, lane);
+      if (prev_valid) {
+        lds_t* st = ring + ((i - 1) % kStages) * kStage;
+        // rescale by the factors published with the step being consumed
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++) {
+          if (s_flag[hb]) {
+            const float al = s_alpha[hb * 32 + (lane & 31)];
+#pragma unroll
+            for (int md = 0; md < MDP; md++) o[md][hb] *= al;
+          }
+        }
+        bf16x8 pf[HB][2];
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+          for (int kk = 0; kk < 2; kk++)
+            pf[hb][kk] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+                pbuf + hb * kPBytes + (kk * 64 + lane) * 16);
+        auto ld_c = [&](int md, int kk) -> bf16x8 {
+          const int dd = 32 * (pw_id * MDP + md) + 16 * (grp & 1) + 4 * qd;
+          const int chunk = dd >> 3, hoff = (dd & 7) * 2;
+          const int r0 = 16 * kk + 4 * g32 + e;
+          const int r1 = r0 + 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+                  st + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+                  st + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
+          const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          return __builtin_bit_cast(bf16x8, cat);
+        };
+        constexpr int NSTEP = 2 * MDP;
+        constexpr int D = 4;
+        bf16x8 cv[D];
+#pragma unroll
+        for (int k = 0; k < D; k++) cv[k] = ld_c(k >> 1, k & 1);
+#pragma unroll
+        for (int s = 0; s < NSTEP; s++) {
+          const int md = s >> 1, kk = s & 1;
+#pragma unroll
+          for (int hb = 0; hb < HB; hb++)
+            o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[s % D], pf[hb][kk], o[md][hb], 0, 0, 0);
+          if (s + D < NSTEP) cv[s % D] = ld_c((s + D) >> 1, (s + D) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (prev.seg_last(a)) {
+          const int64_t slot = (int64_t)(g + prev.b);
+#pragma unroll
+          for (int hb = 0; hb < HB; hb++) {
+            const int32_t head = hg * 32 * HB + hb * 32 + (lane & 31);
+            const float inv = s_invl[hb * 32 + (lane & 31)];
+            float* dst = a.part_o + (slot * a.h + head) * kDc + 32 * pw_id * MDP;
+#pragma unroll
+            for (int md = 0; md < MDP; md++) {
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++) {
+                const f32x4 v = {o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
+                                 o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv};
+                *reinterpret_cast<f32x4*>(dst + 32 * md + 8 * jj + 4 * g32) = v;
+              }
+              o[md][hb] = f32x16{};
+            }
+          }
+        }
+      }
+      __syncthreads();
+      __syncthreads();
+      prev = cur;
+      prev_valid = cur.valid;
+      if (cur.valid) cur.advance(a);
+    }
   }
 }
+
+// heads served by one work group
+int32_t heads_per_group(int32_t heads) { return heads % 64 == 0 ? 64 : 32; }
 
 }  // namespace
 
@@ -314,17 +486,20 @@ bool mfma_supported(const mla_decode_params& p) {
          p.d_rope == kDr && p.num_heads % 32 == 0;
 }
 
-int32_t mfma_streams(int32_t heads) { return (heads % 128 == 0) ? 1 : 2; }
+int32_t mfma_streams(int32_t) { return 1; }
+
+int32_t mfma_head_groups(int32_t heads) { return heads / heads_per_group(heads); }
 
 hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s) {
   if (cache_dtype != MLA_BF16 || a.d_c != kDc || a.d_r != kDr || a.h % 32) return hipErrorInvalidValue;
-  if (a.h % 128 == 0) {
-    hipLaunchKernelGGL((attend_mfma_kernel<4, 1>), dim3(a.splits, a.h / 128), dim3(256), 0, s, a);
-  } else if (a.h % 64 == 0) {
-    hipLaunchKernelGGL((attend_mfma_kernel<2, 2>), dim3(a.splits, a.h / 64), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((attend_mfma_kernel<1, 2>), dim3(a.splits, a.h / 32), dim3(128), 0, s, a);
-  }
+  const int32_t hpg = heads_per_group(a.h);
+  const int32_t HG = a.h / hpg;
+  if (HG > 1 && a.splits % 8) return hipErrorInvalidValue;  // XCD pairing uses whole groups of 8
+  const dim3 grid(a.splits * HG);
+  if (hpg == 64)
+    hipLaunchKernelGGL((attend_mfma_kernel<2>), grid, dim3(Shape<2>::NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_mfma_kernel<1>), grid, dim3(Shape<1>::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

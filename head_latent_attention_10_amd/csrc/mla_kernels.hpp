@@ -21,6 +21,9 @@ hipError_t launch_attend_simt(const AttnArgs& a, int32_t cache_dtype, int32_t ro
 // bf16 rope and bf16 absorbed query.
 bool mfma_supported(const mla_decode_params& p);
 int32_t mfma_streams(int32_t heads);
+// Work groups that share one token split (head groups of 64 or 32 heads); with
+// more than one, the split count must be a multiple of 8 (XCD pairing).
+int32_t mfma_head_groups(int32_t heads);
 hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s);
 
 // Log-sum-exp merge of the token splits -> o_lat [B, h, d_c] fp32.
