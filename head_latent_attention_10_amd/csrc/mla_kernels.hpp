@@ -26,6 +26,14 @@ int32_t mfma_streams(int32_t heads);
 int32_t mfma_head_groups(int32_t heads);
 hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s);
 
+// Matrix-core absorb / up-projection for bf16 q and weights, d_c = 512
+// (d_nope <= 128, multiple of 16; d_v multiple of 32).
+bool proj_mfma_supported(const mla_decode_params& p);
+hipError_t launch_absorb_mfma(const mla_decode_params& p, const void* q, const void* W_UK,
+                              void* q_lat, int32_t q_lat_dtype, hipStream_t s);
+hipError_t launch_up_project_mfma(const mla_decode_params& p, const float* o_lat,
+                                  const void* W_UV, void* out, hipStream_t s);
+
 // Log-sum-exp merge of the token splits -> o_lat [B, h, d_c] fp32.
 hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s);
 
