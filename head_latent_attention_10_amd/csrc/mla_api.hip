@@ -155,6 +155,7 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.d_c = p.d_latent;
   a.d_r = p.d_rope;
   a.P = p.page_size;
+  a.log2P = (p.page_size & (p.page_size - 1)) == 0 ? __builtin_ctz(p.page_size) : -1;
   a.max_blocks = p.max_blocks_per_seq;
   a.num_blocks = p.num_blocks;
   a.splits = L.splits;

@@ -39,10 +39,12 @@
 // conflicts.
 //
 // Step i (three work-group barriers):
-//   wait for step i's loads; barrier
-//   issue loads of step i+2 | score waves: partial S(i) | value waves: O += P(i-1) C(i-1)
+//   score waves kh = 1 wait for their loads of step i; barrier
+//   score waves: partial S(i) | value waves: read P(i-1) and the rescale
+//   factors, first row blocks of O += C(i-1) P(i-1)
 //   barrier
-//   score wave kh = 0: merge partial scores, softmax, publish P(i)
+//   score waves kh = 0: merge partial scores, softmax, publish P(i) |
+//   kh = 1: issue the loads of step i+2 | value waves: remaining row blocks
 //   barrier
 //
 // Softmax rescaling is lazy: after the first four steps of a sequence segment
@@ -53,6 +55,8 @@
 // bf16-rounded weights that the MFMA consumes.
 #include "mla_kernels.hpp"
 
+#include <type_traits>
+
 namespace mla {
 namespace {
 
@@ -60,8 +64,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -86,7 +93,12 @@ struct Shape {
   static constexpr int NP = HB == 2 ? 4 : 2;    // value waves
   static constexpr int NW = NQ + NP;
   static constexpr int MDP = kDc / 32 / NP;     // 32-row output blocks per value wave
-  static constexpr int LDS = kRing + HB * (kXBytes + kPBytes) + HB * 32 * 4 * 2 + 16;
+#ifndef MLA_MDA
+  static constexpr int MDA = MDP / 4;           // of which computed before the softmax barrier
+#else
+  static constexpr int MDA = MLA_MDA;
+#endif
+  static constexpr int LDS = kRing + HB * (kXBytes + kPBytes) + HB * 32 * 4 * 2 + 16 + HB * 16;
 };
 
 // Chunk swizzles: row bits (b3 b2 b1 b0) -> chunk bits (b2 b1 b0 b3) for latent
@@ -94,41 +106,92 @@ struct Shape {
 __device__ inline int swz_c(int r) { return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1); }
 __device__ inline int swz_r(int r) { return (r >> 1) & 7; }
 
-__device__ inline float round_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xffff0000u);
+
+// Work-group barrier that only waits for this wave's LDS traffic.  Unlike
+// __syncthreads() it does not drain the vector-memory counter, so the
+// direct-to-LDS loads of later steps stay in flight across it; each batch of
+// those loads is awaited explicitly by the waves that issued it before the
+// barrier that starts the step using it.
+__device__ inline void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane direct global->LDS load (lane l writes lds + 16 l).
+// Issued from inline assembly so that the compiler does not track it: the
+// compiler cannot tell which ring stage a load targets, and for a load it
+// tracks it waits for completion (vmcnt(0)) before the issuing wave's next
+// LDS read of the ring, which would serialise the two-step prefetch.  Every
+// stage is instead awaited explicitly (wait_vmcnt in the issuing waves, then a
+// work-group barrier) before any wave reads it.  The load has no register
+// results, so nothing the compiler allocates is written behind its back; M0 is
+// a reserved register that the compiler sets before each of its own uses.
+__device__ inline void dma16(const void* g, lds_t* l) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)l;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+               : "memory");
+}
+
+// The same load with a wave-uniform 64-bit base and a 32-bit per-lane offset.
+__device__ inline void dma16s(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(m0)
+               : "memory");
+}
+
+// Work-group barrier for a wave that has no LDS writes to publish: it does
+// not wait for its own outstanding LDS or scalar-memory operations, so a
+// scalar load issued before it stays in flight.
+__device__ inline void wg_barrier_nowait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 4-byte direct global->LDS load per active lane (lane l writes l + 4 l).
+__device__ inline void dma4(const void* g, lds_t* l) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)l;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0)
+               : "memory");
 }
 
 template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");  // LDS written by the awaited loads is read after this
 }
 
 // Walks the 32-token steps of a split's tiles in order; a tile's second half
 // is skipped when it holds no token of its sequence.
 struct StepIter {
-  int32_t t, t_end, half, b, T, first;  // first = first tile of sequence b
+  int32_t t, t_end, half, b, T, first, next_first;  // first/next_first: tile range of sequence b
   bool valid;
 
+  __device__ void load_seq(const AttnArgs& a) {
+    const int32_t tl = load_ro(a.seq_lens, b), cap = a.max_blocks * a.P;
+    T = tl < 0 ? 0 : (tl > cap ? cap : tl);
+    first = load_ro(a.cu_tiles, b);
+    next_first = load_ro(a.cu_tiles, b + 1);
+  }
   __device__ void init(const AttnArgs& a, int32_t t_begin, int32_t t_stop) {
     t = t_begin;
     t_end = t_stop;
     half = 0;
     b = 0;
-    while (a.cu_tiles[b + 1] <= t) b++;
-    T = seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
-    first = a.cu_tiles[b];
+    while (load_ro(a.cu_tiles, b + 1) <= t) b++;
+    load_seq(a);
     valid = t < t_end;
   }
   __device__ int32_t t0() const { return (t - first) * kTile + half * kStep; }
   __device__ int32_t nvalid() const { return min(kStep, T - t0()); }
   __device__ bool has_second_half() const { return (t - first) * kTile + kStep < T; }
   // last step of its sequence within this split
-  __device__ bool seg_last(const AttnArgs& a) const {
+  __device__ bool seg_last() const {
     const bool last_of_tile = half == 1 || !has_second_half();
-    return last_of_tile && (t + 1 == t_end || a.cu_tiles[b + 1] <= t + 1);
+    return last_of_tile && (t + 1 == t_end || next_first <= t + 1);
   }
   __device__ void advance(const AttnArgs& a) {
     if (half == 0 && has_second_half()) {
@@ -138,87 +201,133 @@ struct StepIter {
     half = 0;
     t++;
     valid = t < t_end;
-    if (valid && a.cu_tiles[b + 1] <= t) {
-      while (a.cu_tiles[b + 1] <= t) b++;
-      T = seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
-      first = a.cu_tiles[b];
+    if (valid && next_first <= t) {
+      while (load_ro(a.cu_tiles, b + 1) <= t) b++;
+      load_seq(a);
     }
   }
 };
 
-// Direct-to-LDS loads of one step.  Rows past the end repeat the last valid
-// token (finite data; masked in the softmax).  `wave` is wave-uniform, so the
-// block-table lookups are scalar loads.
-template <int NW>
-__device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const StepIter& it, int wave,
-                                  int lane) {
-  const char* ckv = static_cast<const char*>(a.c_kv);
-  const char* krp = static_cast<const char*>(a.k_rope);
+// Physical slot of the first token of a step, when the whole step lies in one
+// block (page size a multiple of 32), else -1.  step_entry is the index of the
+// block-table entry that holds the step's block.
+__device__ inline int64_t step_entry(const AttnArgs& a, const StepIter& it) {
+  const int32_t t0 = it.t0();
+  const int32_t pg = a.log2P >= 0 ? t0 >> a.log2P : t0 / a.P;
+  return (int64_t)it.b * a.max_blocks + pg;
+}
+__device__ inline int64_t step_base(const AttnArgs& a, const StepIter& it, int32_t blk) {
+  if (a.P % kStep) return -1;
+  const int32_t t0 = it.t0();
+  const int32_t off = a.log2P >= 0 ? t0 & (a.P - 1) : t0 % a.P;
+  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+  return (int64_t)blk * a.P + off;
+}
+
+// Direct-to-LDS loads of one step, issued by the NL value waves: wave lw
+// loads latent rows lw, lw + NL, ... and rope groups lw, lw + NL, ...
+// (kLoadsPerStep / NL loads per wave on every path).  A full step inside one
+// block takes straight-line code: one scalar base per step, one offset per
+// row.  Otherwise rows past the end repeat the last valid token (finite data,
+// masked in the softmax) and every lane looks up its own block.
+template <int NL>
+__device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const StepIter& it,
+                                  int64_t base, int lw, int lane) {
+  static_assert(kStep % NL == 0 && (kStep / 8) % NL == 0, "uniform row assignment");
   const int32_t t0 = it.t0();
   const int32_t rmax = it.T - 1 - t0;
-  const int32_t* trow = a.block_table + (int64_t)it.b * a.max_blocks;
-  const bool one_block = (a.P % kStep) == 0;  // the step lies inside one block
-  int64_t base = 0;
-  if (one_block) {
-    int32_t blk = trow[t0 / a.P];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-    base = (int64_t)blk * a.P + (t0 % a.P);
-  }
-  for (int k = wave; k < kLoadsPerStep; k += NW) {
-    if (k < kStep) {
-      const int r = k;
-      const int64_t slot = one_block ? base + min(r, rmax)
-                                     : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
-                                                 a.max_blocks, a.num_blocks);
-      const char* src = ckv + slot * kCRow + ((lane ^ swz_c(r)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + r * kCRow), 16, 0, 0);
-    } else {
-      const int j = k - kStep;
-      const int r = 8 * j + (lane >> 3);
-      const int64_t slot = one_block ? base + min(r, rmax)
-                                     : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
-                                                 a.max_blocks, a.num_blocks);
-      const char* src = krp + slot * kRRow + (((lane & 7) ^ swz_r(r)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + kStageC + j * 1024), 16, 0, 0);
+  const uint32_t st = (uint32_t)(uintptr_t)stage;
+  if (base >= 0 && rmax >= kStep - 1) {
+    const char* cb = static_cast<const char*>(a.c_kv) + base * kCRow;
+    const char* rb = static_cast<const char*>(a.k_rope) + base * kRRow;
+    const uint32_t l16 = (uint32_t)lane << 4;
+#pragma unroll
+    for (int m = 0; m < kStep / NL; m++) {
+      const int r = lw + NL * m;
+      dma16s(cb, (l16 ^ ((uint32_t)swz_c(r) << 4)) + (uint32_t)(r * kCRow), st + r * kCRow);
     }
+#pragma unroll
+    for (int m = 0; m < kStep / 8 / NL; m++) {
+      const int j = lw + NL * m;
+      const int r = 8 * j + (lane >> 3);
+      dma16s(rb, (uint32_t)(r * kRRow + (((lane & 7) ^ swz_r(r)) << 4)), st + kStageC + j * 1024);
+    }
+    return;
+  }
+  const char* ckv = static_cast<const char*>(a.c_kv);
+  const char* krp = static_cast<const char*>(a.k_rope);
+#pragma unroll
+  for (int m = 0; m < kStep / NL; m++) {
+    const int r = lw + NL * m;
+    const int64_t slot = base >= 0 ? base + min(r, rmax)
+                                   : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
+                                               a.max_blocks, a.num_blocks);
+    dma16(ckv + slot * kCRow + ((lane ^ swz_c(r)) << 4), stage + r * kCRow);
+  }
+#pragma unroll
+  for (int m = 0; m < kStep / 8 / NL; m++) {
+    const int j = lw + NL * m;
+    const int r = 8 * j + (lane >> 3);
+    const int64_t slot = base >= 0 ? base + min(r, rmax)
+                                   : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
+                                               a.max_blocks, a.num_blocks);
+    dma16(krp + slot * kRRow + (((lane & 7) ^ swz_r(r)) << 4), stage + kStageC + j * 1024);
   }
 }
 
-template <int NW>
-__device__ constexpr int loads_of_wave(int wave) { return (kLoadsPerStep - wave + NW - 1) / NW; }
-
-// The load schedule every wave keeps identically.
-template <int NW>
+// The load schedule of one of the NL loader waves (lane group lw).  A batch is
+// the block-table entry of the following step (one 4-byte direct load by lane
+// 0 into the wave's entry ring) followed by the wave's kLoadsPerStep / NL
+// loads of the step itself, so every batch is kPerBatch operations and the
+// table read never waits on the scalar path.
+template <int NL>
 struct Loader {
+  static_assert(kLoadsPerStep % NL == 0, "equal load counts per wave");
+  static constexpr int kPerWave = kLoadsPerStep / NL;
+  static constexpr int kPerBatch = kPerWave + 1;
   StepIter next;       // next step to load
+  int32_t first_blk;   // table entry of the first step (read directly)
   int32_t loaded;      // steps issued so far
   bool newer_issued;   // the batch after the awaited one was issued
+  int32_t* ent;        // this wave's entry ring in LDS (4 slots)
 
-  __device__ void start(const AttnArgs& a, lds_t* ring, int32_t tb, int32_t te, int wave,
-                        int lane) {
-    next.init(a, tb, te);
-    loaded = 0;
-    for (int s = 0; s < 2 && next.valid; s++) {
-      issue_step<NW>(a, ring + (loaded % kStages) * kStage, next, wave, lane);
-      next.advance(a);
-      loaded++;
+  __device__ void issue_next(const AttnArgs& a, lds_t* ring, int lw, int lane) {
+    int32_t blk = first_blk;
+    if (loaded > 0) {
+      // the entry came with the previous batch; only the latest batch (this
+      // step's predecessor) may still be in flight
+      wait_vmcnt<kPerWave>();
+      blk = __builtin_amdgcn_readfirstlane(ent[loaded & 3]);
     }
+    const int64_t base = step_base(a, next, blk);
+    StepIter after = next;
+    after.advance(a);
+    const int32_t* src = a.block_table + (after.valid ? step_entry(a, after) : 0);
+    if (lane == 0) dma4(src, (lds_t*)(ent + ((loaded + 1) & 3)));
+    issue_step<NL>(a, ring + (loaded % kStages) * kStage, next, base, lw, lane);
+    next = after;
+    loaded++;
+  }
+  __device__ void start(const AttnArgs& a, lds_t* ring, int32_t* ent_ring, int32_t tb, int32_t te,
+                        int lw, int lane) {
+    ent = ent_ring;
+    next.init(a, tb, te);
+    first_blk = next.valid ? load_ro(a.block_table, step_entry(a, next)) : 0;
+    loaded = 0;
+    for (int s = 0; s < 2 && next.valid; s++) issue_next(a, ring, lw, lane);
     newer_issued = loaded == 2;
   }
-  // Start of step i: wait for this wave's loads of step i (only the newer batch
-  // i+1 may stay in flight), barrier, then issue step i+2.
-  __device__ void begin_step(const AttnArgs& a, lds_t* ring, int wave, int lane) {
-    if (!newer_issued)
-      wait_vmcnt<0>();
-    else if (loads_of_wave<NW>(wave) == loads_of_wave<NW>(0))
-      wait_vmcnt<loads_of_wave<NW>(0)>();
+  // Wait for this wave's loads of step i (only batch i+1 may stay in flight).
+  __device__ void wait_current() {
+    if (newer_issued)
+      wait_vmcnt<kPerBatch>();
     else
-      wait_vmcnt<loads_of_wave<NW>(NW - 1)>();
-    __syncthreads();
+      wait_vmcnt<0>();
+  }
+  // After the step barrier: issue step i+2.
+  __device__ void issue_ahead(const AttnArgs& a, lds_t* ring, int lw, int lane) {
     if (next.valid) {
-      issue_step<NW>(a, ring + (loaded % kStages) * kStage, next, wave, lane);
-      next.advance(a);
-      loaded++;
+      issue_next(a, ring, lw, lane);
       newer_issued = true;
     } else {
       newer_issued = false;
@@ -230,14 +339,14 @@ template <int HB>
 __global__ __attribute__((amdgpu_flat_work_group_size(Shape<HB>::NW * 64, Shape<HB>::NW * 64)))
 void attend_mfma_kernel(AttnArgs a) {
   using S = Shape<HB>;
-  constexpr int NW = S::NW;
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
   lds_t* ring = (lds_t*)smem;
   lds_t* xbuf = ring + kRing;                       // [HB][64 lanes][16 floats]
   lds_t* pbuf = xbuf + HB * kXBytes;                // [HB][2 k-steps][64 lanes][16 B]
   float* s_alpha = (float*)(smem + kRing + HB * (kXBytes + kPBytes));  // [HB][32]
   float* s_invl = s_alpha + HB * 32;                // [HB][32]
-  int* s_flag = (int*)(s_invl + HB * 32);           // [HB]
+  int* s_flag = (int*)(s_invl + HB * 32);           // [HB] (padded to 4)
+  int32_t* s_ent = (int32_t*)(s_flag + 4);          // [HB][4] block-table entries in flight
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -256,14 +365,12 @@ void attend_mfma_kernel(AttnArgs a) {
     g = blockIdx.x;
   }
   if (g >= a.splits) return;
-  const int32_t n_total = a.cu_tiles[a.B];
+  const int32_t n_total = load_ro(a.cu_tiles, a.B);
   if (n_total == 0) return;
   const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);
   const int32_t t_end = (int32_t)split_begin(n_total, a.splits, g + 1);
   if (t_begin >= t_end) return;
 
-  Loader<NW> ld;
-  ld.start(a, ring, t_begin, t_end, wave, lane);
   StepIter cur;
   cur.init(a, t_begin, t_end);
   const float sm = a.sm_scale_log2;
@@ -278,15 +385,27 @@ void attend_mfma_kernel(AttnArgs a) {
           static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc + kDr));
 #pragma unroll
       for (int k = 0; k < kKsHalf; k++) qf[k] = qp[2 * (kh * kKsHalf + k) + g32];
+      // wait here, once per segment: otherwise the compiler, unable to tell
+      // whether a segment started, waits for these loads in every step, and
+      // the hardware counter it waits on also counts the loader's tile loads
+      wait_vmcnt<0>();
     };
     load_q(cur.b);
     float m_run = -INFINITY, l_run = 0.f;
     int32_t seg_step = 0;  // steps of the current segment seen so far
     lds_t* xb = xbuf + hb * kXBytes + lane * 64;
     lds_t* pb = pbuf + hb * kPBytes + lane * 16;
+    // the kh = 1 waves issue the loads: HB loader waves of kLoadsPerStep / HB
+    Loader<HB> ld;
+    if (kh == 1) ld.start(a, ring, s_ent + 4 * hb, t_begin, t_end, hb, lane);
     // n steps of scores plus one final step in which only the value waves work
     for (int32_t i = 0;; i++) {
-      ld.begin_step(a, ring, wave, lane);
+      if (kh == 1) {
+        ld.wait_current();
+        wg_barrier_nowait();  // step i's tile is in LDS
+      } else {
+        wg_barrier();
+      }
       lds_t* st = ring + (i % kStages) * kStage;
       f32x16 s = f32x16{};
       if (cur.valid) {
@@ -315,8 +434,12 @@ void attend_mfma_kernel(AttnArgs a) {
                 f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
         }
       }
-      __syncthreads();
-      if (cur.valid && kh == 0) {
+      wg_barrier();
+      if (kh == 1) {
+        // loads of step i+2, into the stage last read in step i-2, issued
+        // while the partner wave runs the softmax
+        ld.issue_ahead(a, ring, hb, lane);
+      } else if (cur.valid) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           const f32x4 o = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 16 * q);
@@ -325,16 +448,24 @@ void attend_mfma_kernel(AttnArgs a) {
           s[4 * q + 2] += o[2];
           s[4 * q + 3] += o[3];
         }
+        // mask the tokens past the end (only the last step of a sequence)
         const int32_t nv = cur.nvalid();
-        float sv[16];
-        float mt = -INFINITY;
+        if (nv < kStep) {
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const int tok = 8 * (j >> 2) + 4 * g32 + (j & 3);
-          sv[j] = tok < nv ? s[j] * sm : -INFINITY;
-          mt = fmaxf(mt, sv[j]);
+          for (int j = 0; j < 16; j++)
+            if (8 * (j >> 2) + 4 * g32 + (j & 3) >= nv) s[j] = -INFINITY;
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // step maximum per head: over the lane's 16 tokens, then across the
+        // two lane halves that hold the same head (the scale is positive)
+        float mx = s[0];
+#pragma unroll
+        for (int j = 1; j < 16; j++) mx = fmaxf(mx, s[j]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mt = mx * sm;
         // exact running maximum for the first steps of a segment (the largest
         // weight is then exactly 1 in bf16), lazy afterwards
         const float thr = seg_step < kExactSteps ? 0.f : kLazy;
@@ -347,25 +478,29 @@ void attend_mfma_kernel(AttnArgs a) {
           m_run = m_new;
         }
         const float mref = m_run == -INFINITY ? 0.f : m_run;
-        f32x8 pw[2];
+        // weights as bf16 pairs (one pair per conversion: extracting elements
+        // from a wider bf16 vector is not lowered correctly); the normaliser
+        // sums exactly the bf16 weights the value product consumes
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+        uint32_t pk[8];
         float lsum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const float pj = __builtin_amdgcn_exp2f(sv[j] - mref);
-          pw[j >> 3][j & 7] = pj;
-          lsum += round_to_bf16(pj);
+        for (int q = 0; q < 8; q++) {
+          const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q], sm, -mref)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + 1], sm, -mref))};
+          const bf16x2 pr = __builtin_convertvector(e, bf16x2);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          pk[q] = __builtin_bit_cast(uint32_t, pr);
         }
         l_run += lsum;
+        // publish the weights in the value product's operand layout
+        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb + 64 * 16) =
+            u32x4{pk[4], pk[5], pk[6], pk[7]};
         seg_step++;
-        // publish the weights in the value product's operand layout (whole-vector
-        // conversions only: element-wise bf16 vector writes are not lowered correctly)
-        *reinterpret_cast<bf16x8 __attribute__((address_space(3)))*>(pb) =
-            __builtin_convertvector(pw[0], bf16x8);
-        *reinterpret_cast<bf16x8 __attribute__((address_space(3)))*>(pb + 64 * 16) =
-            __builtin_convertvector(pw[1], bf16x8);
         if (g32 == 0) s_alpha[hb * 32 + lane] = alpha;
         if (lane == 0) s_flag[hb] = any ? 1 : 0;
-        if (cur.seg_last(a)) {
+        if (cur.seg_last()) {
           const float ltot = l_run + __shfl_xor(l_run, 32);
           if (g32 == 0) {
             s_invl[hb * 32 + lane] = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -375,9 +510,12 @@ void attend_mfma_kernel(AttnArgs a) {
           }
         }
       }
-      __syncthreads();
+      if (kh == 1)
+        wg_barrier_nowait();
+      else
+        wg_barrier();
       if (!cur.valid) break;  // that was the value waves' final step
-      const bool was_last = cur.seg_last(a);
+      const bool was_last = cur.seg_last();
       cur.advance(a);
       if (cur.valid && was_last) {
         load_q(cur.b);
@@ -389,6 +527,7 @@ void attend_mfma_kernel(AttnArgs a) {
   } else {
     // ================================================================ value waves
     constexpr int MDP = S::MDP;
+    constexpr int kMdFirst = S::MDA;  // row blocks computed before the softmax barrier
     const int pw_id = wave - S::NQ;
     const int j16 = lane & 15, grp = lane >> 4, e = j16 >> 2, qd = j16 & 3;
     f32x16 o[MDP][HB];
@@ -400,10 +539,48 @@ void attend_mfma_kernel(AttnArgs a) {
     bool prev_valid = false;
     for (int32_t i = 0;; i++) {
       if (!cur.valid && !prev_valid) break;
-      ld.begin_step(a, ring, wave, lane);
+      wg_barrier();
+      lds_t* st = ring + ((i + kStages - 1) % kStages) * kStage;
+      const bool last = prev_valid && prev.seg_last();
+      bf16x8 pf[HB][2];
+      float inv[HB];
+      auto ld_c = [&](int md, int kk) -> bf16x8 {
+        const int dd = 32 * (pw_id * MDP + md) + 16 * (grp & 1) + 4 * qd;
+        const int chunk = dd >> 3, hoff = (dd & 7) * 2;
+        const int r0 = 16 * kk + 4 * g32 + e;
+        const int r1 = r0 + 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+                st + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+                st + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
+        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, cat);
+      };
+      // O[md] += C(i-1) P(i-1) for the 32-row blocks md0 <= md < md1
+      auto products = [&](auto md0_c, auto md1_c) {
+        constexpr int md0 = decltype(md0_c)::value, md1 = decltype(md1_c)::value;
+        if constexpr (md1 > md0) {
+        constexpr int NSTEP = 2 * (md1 - md0);
+        constexpr int D = NSTEP < 4 ? NSTEP : 4;
+        bf16x8 cv[D];
+#pragma unroll
+        for (int k = 0; k < D; k++) cv[k] = ld_c(md0 + (k >> 1), k & 1);
+#pragma unroll
+        for (int s = 0; s < NSTEP; s++) {
+          const int md = md0 + (s >> 1), kk = s & 1;
+#pragma unroll
+          for (int hb = 0; hb < HB; hb++)
+            o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[s % D], pf[hb][kk], o[md][hb], 0, 0, 0);
+          if (s + D < NSTEP) cv[s % D] = ld_c(md0 + ((s + D) >> 1), (s + D) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        }
+      };
       if (prev_valid) {
-        lds_t* st = ring + ((i - 1) % kStages) * kStage;
-        // rescale by the factors published with the step being consumed
+        // everything published with the step being consumed is read now: the
+        // score waves overwrite it after the next barrier
 #pragma unroll
         for (int hb = 0; hb < HB; hb++) {
           if (s_flag[hb]) {
@@ -411,55 +588,29 @@ void attend_mfma_kernel(AttnArgs a) {
 #pragma unroll
             for (int md = 0; md < MDP; md++) o[md][hb] *= al;
           }
-        }
-        bf16x8 pf[HB][2];
-#pragma unroll
-        for (int hb = 0; hb < HB; hb++)
+          inv[hb] = last ? s_invl[hb * 32 + (lane & 31)] : 0.f;
 #pragma unroll
           for (int kk = 0; kk < 2; kk++)
             pf[hb][kk] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
                 pbuf + hb * kPBytes + (kk * 64 + lane) * 16);
-        auto ld_c = [&](int md, int kk) -> bf16x8 {
-          const int dd = 32 * (pw_id * MDP + md) + 16 * (grp & 1) + 4 * qd;
-          const int chunk = dd >> 3, hoff = (dd & 7) * 2;
-          const int r0 = 16 * kk + 4 * g32 + e;
-          const int r1 = r0 + 8;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-                  st + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-                  st + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
-          const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          return __builtin_bit_cast(bf16x8, cat);
-        };
-        constexpr int NSTEP = 2 * MDP;
-        constexpr int D = 4;
-        bf16x8 cv[D];
-#pragma unroll
-        for (int k = 0; k < D; k++) cv[k] = ld_c(k >> 1, k & 1);
-#pragma unroll
-        for (int s = 0; s < NSTEP; s++) {
-          const int md = s >> 1, kk = s & 1;
-#pragma unroll
-          for (int hb = 0; hb < HB; hb++)
-            o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[s % D], pf[hb][kk], o[md][hb], 0, 0, 0);
-          if (s + D < NSTEP) cv[s % D] = ld_c((s + D) >> 1, (s + D) & 1);
-          __builtin_amdgcn_sched_barrier(0);
         }
-        if (prev.seg_last(a)) {
+        products(std::integral_constant<int, 0>{}, std::integral_constant<int, kMdFirst>{});
+      }
+      wg_barrier();
+      if (prev_valid) {
+        products(std::integral_constant<int, kMdFirst>{}, std::integral_constant<int, MDP>{});
+        if (last) {
           const int64_t slot = (int64_t)(g + prev.b);
 #pragma unroll
           for (int hb = 0; hb < HB; hb++) {
             const int32_t head = hg * 32 * HB + hb * 32 + (lane & 31);
-            const float inv = s_invl[hb * 32 + (lane & 31)];
             float* dst = a.part_o + (slot * a.h + head) * kDc + 32 * pw_id * MDP;
 #pragma unroll
             for (int md = 0; md < MDP; md++) {
 #pragma unroll
               for (int jj = 0; jj < 4; jj++) {
-                const f32x4 v = {o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
-                                 o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv};
+                const f32x4 v = {o[md][hb][4 * jj] * inv[hb], o[md][hb][4 * jj + 1] * inv[hb],
+                                 o[md][hb][4 * jj + 2] * inv[hb], o[md][hb][4 * jj + 3] * inv[hb]};
                 *reinterpret_cast<f32x4*>(dst + 32 * md + 8 * jj + 4 * g32) = v;
               }
               o[md][hb] = f32x16{};
@@ -467,8 +618,7 @@ void attend_mfma_kernel(AttnArgs a) {
           }
         }
       }
-      __syncthreads();
-      __syncthreads();
+      wg_barrier();
       prev = cur;
       prev_valid = cur.valid;
       if (cur.valid) cur.advance(a);

@@ -32,10 +32,19 @@ struct AttnArgs {
   float* part_o;             // [slots, h, d_c]
   float* part_lse;           // [slots, h]
   int32_t B, h, d_c, d_r, P, max_blocks, num_blocks;
+  int32_t log2P;             // log2(P) when P is a power of two, else -1
   int32_t splits;            // work groups along tokens (gridDim.x)
   int32_t streams;           // partial slots per (split, sequence)
   float sm_scale_log2;       // sm_scale * log2(e)
 };
+
+// Read of a table that no kernel of the launch writes (sequence lengths, block
+// table, tile prefix sums).  The constant address space lets the compiler use
+// scalar loads for wave-uniform indices, whose waits do not depend on the
+// vector-memory traffic in flight.
+__device__ inline int32_t load_ro(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
 
 // Tokens of sequence b, clamped to what its table row can address.
 __device__ inline int32_t seq_len_clamped(const int32_t* seq_lens, int32_t b, int32_t max_blocks,
