@@ -21,7 +21,7 @@ SOURCES = ["mla_api.hip", "mla_small_kernels.hip", "mla_attend_simt.hip", "mla_a
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc",
+    "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc",
     # never let the compiler form packed-fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",

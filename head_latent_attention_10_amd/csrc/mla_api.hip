@@ -32,6 +32,8 @@ bool is_dtype(int32_t d, bool allow_fp8) {
 
 mla_status validate(const mla_decode_params* p) {
   if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch > mla::kPlanMaxBatch)
+    return fail(MLA_ERR_UNSUPPORTED, "batch %d above %d", p->batch, mla::kPlanMaxBatch);
   if (p->batch < 1 || p->num_heads < 1 || p->d_nope < 1 || p->d_rope < 0 || p->d_latent < 1 ||
       p->d_v < 1)
     return fail(MLA_ERR_INVALID_ARG,
@@ -65,7 +67,7 @@ int32_t absorbed_dtype(const mla_decode_params& p) {
 }
 
 struct Layout {
-  size_t q_lat, cu_tiles, part_o, part_lse, o_lat, total;
+  size_t q_lat, cu_tiles, tiles, part_o, part_lse, o_lat, total;
   int32_t splits, streams;
   int64_t slots;
 };
@@ -103,6 +105,10 @@ mla_status layout(const mla_decode_params& p, Layout* L) {
   off = align256(off + B * h * (dc + dr) * mla::dtype_size(absorbed_dtype(p)));
   L->cu_tiles = off;
   off = align256(off + (B + 1) * sizeof(int32_t));
+  L->tiles = off;
+  const size_t tiles_per_seq =
+      ((size_t)p.max_blocks_per_seq * p.page_size + mla::kTile - 1) / mla::kTile;
+  off = align256(off + B * tiles_per_seq * 4 * sizeof(int32_t));
   L->part_o = off;
   off = align256(off + (size_t)L->slots * h * dc * sizeof(float));
   L->part_lse = off;
@@ -148,6 +154,7 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.cu_tiles = reinterpret_cast<int32_t*>(ws + L.cu_tiles);
+  a.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   a.part_o = reinterpret_cast<float*>(ws + L.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
   a.B = p.batch;
@@ -162,8 +169,10 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.streams = L.streams;
   a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
 
-  hipError_t e = mla::launch_plan(seq_lens, p.batch, p.max_blocks_per_seq, p.page_size,
-                                  reinterpret_cast<int32_t*>(ws + L.cu_tiles), s);
+  hipError_t e = mla::launch_plan(seq_lens, block_table, p.batch, p.max_blocks_per_seq,
+                                  p.page_size, p.num_blocks,
+                                  reinterpret_cast<int32_t*>(ws + L.cu_tiles),
+                                  reinterpret_cast<int32_t*>(ws + L.tiles), s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (mla::mfma_supported(p))

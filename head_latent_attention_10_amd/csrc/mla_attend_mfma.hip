@@ -3,23 +3,31 @@
 // Shape: d_c = 512 latent values + d_r = 64 rope values per cached token,
 // heads a multiple of 32, bf16 latent/rope rows, bf16 absorbed query.
 //
-// Work decomposition.  A token split g owns a contiguous run of 64-token tiles
-// of the concatenated sequences ("split plan" in mla_common.hpp).  Its heads
-// are served by HG work groups of 32*HB heads each (HB = 2 for 64 heads, 1 for
-// 32); the HG groups of one split get workgroup ids that differ by a multiple
-// of 8 and are dispatched together, so they run on the same XCD and the
-// second read of every tile is served by that XCD's L2.
+// Work decomposition.  A token split g owns a contiguous run of 32-token tiles
+// of the concatenated sequences ("split plan" in mla_common.hpp); one tile is
+// one pipeline step.  Its heads are served by HG work groups of 32*HB heads
+// each (HB = 2 for 64 heads, 1 for 32); the HG groups of one split get
+// workgroup ids that differ by a multiple of 8 and are dispatched together, so
+// they run on the same XCD and the second read of every tile is served by that
+// XCD's L2.
+//
+// Every step is described by the tile descriptor the planning kernel wrote
+// (page, sequence, first token, valid tokens, last-of-sequence flag).  The
+// descriptors of a split are contiguous; they are brought into a two-buffer
+// LDS window of 64 tiles by direct global->LDS loads, so the per-step
+// bookkeeping of every wave is one LDS read.
 //
 // Inside a work group the waves specialise:
 //  * 2*HB score waves.  Wave (hb, kh) holds the absorbed query of 32 heads for
 //    half of the 576-wide key (kh = 0: latent 0..287; kh = 1: latent 288..511
-//    and the 64 rope values) in registers and computes, for each 32-token step,
+//    and the 64 rope values) in registers and computes, for each step,
 //      S^T[t, i] = sum_d KV[t, d] Q[i, d]      (MFMA 32x32x16 bf16, M = tokens,
 //                                              N = heads, K = its 288 values)
 //    The kh = 1 wave hands its partial scores to its partner through LDS; the
 //    partner adds them, runs the online softmax (one lane = one head) and
 //    publishes the bf16 weights P, the per-head rescale factors and, at the
-//    end of a sequence segment, 1/l and the log-sum-exp.
+//    end of a sequence segment, 1/l and the log-sum-exp.  The kh = 1 waves
+//    issue the tile loads meanwhile (below).
 //  * 4 (HB = 2) or 2 (HB = 1) value waves.  Each owns a slice of 128 (or 256)
 //    latent rows of the output for all heads of the group and computes
 //      O^T[d, i] += sum_t C[t, d] P[i, t]      (M = latent rows, N = heads,
@@ -30,13 +38,12 @@
 //    i%4 of the 16-token k-step) that matches the score accumulator layout,
 //    and the latent tile is read in the same order.
 //
-// LDS ring.  Four stages of one 32-token step: 32 latent rows of 1 KiB and 32
-// rope rows of 128 B, written by direct global->LDS 16-byte loads (one
-// instruction per latent row, eight rope rows per instruction) two steps
-// ahead of use.  The 16-byte chunk index is XOR-swizzled with a permutation
-// of the row's low four bits, which keeps both the row reads of the score
-// product and the 4-row transposing reads of the value product free of bank
-// conflicts.
+// LDS ring.  Four stages of one step: 32 latent rows of 1 KiB and 32 rope
+// rows of 128 B, written by direct global->LDS 16-byte loads (one instruction
+// per latent row, eight rope rows per instruction) two steps ahead of use.
+// The 16-byte chunk index is XOR-swizzled with a permutation of the row's low
+// four bits, which keeps both the row reads of the score product and the
+// 4-row transposing reads of the value product free of bank conflicts.
 //
 // Step i (three work-group barriers):
 //   score waves kh = 1 wait for their loads of step i; barrier
@@ -69,11 +76,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kDc = 512, kDr = 64;
-constexpr int kStep = 32;                         // tokens per pipeline step
+constexpr int kStep = kTile;                      // tokens per pipeline step
 constexpr int kCRow = kDc * 2;                    // 1024 bytes per latent row
 constexpr int kRRow = kDr * 2;                    // 128 bytes per rope row
 constexpr int kStageC = kStep * kCRow;            // 32768
@@ -86,6 +93,9 @@ constexpr int kXBytes = 64 * 64;                  // one wave's partial scores
 constexpr int kPBytes = 2 * 64 * 16;              // weights of one head block, two k-steps
 constexpr float kLazy = 8.0f;                     // log2 of the largest unnormalised weight
 constexpr int kExactSteps = 4;                    // steps per segment with an exact maximum
+constexpr int kWin = 64;                          // tile descriptors per window buffer
+constexpr int kWinBytes = 2 * kWin * 16;          // two window buffers
+static_assert(kStep == 32, "the score and value products are laid out for 32-token steps");
 
 template <int HB>
 struct Shape {
@@ -98,14 +108,13 @@ struct Shape {
 #else
   static constexpr int MDA = MLA_MDA;
 #endif
-  static constexpr int LDS = kRing + HB * (kXBytes + kPBytes) + HB * 32 * 4 * 2 + 16 + HB * 16;
+  static constexpr int LDS = kRing + kWinBytes + HB * (kXBytes + kPBytes) + HB * 32 * 4 * 2 + 16;
 };
 
 // Chunk swizzles: row bits (b3 b2 b1 b0) -> chunk bits (b2 b1 b0 b3) for latent
 // rows; rope rows share 256-byte bank lines in pairs.
 __device__ inline int swz_c(int r) { return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1); }
 __device__ inline int swz_r(int r) { return (r >> 1) & 7; }
-
 
 // Work-group barrier that only waits for this wave's LDS traffic.  Unlike
 // __syncthreads() it does not drain the vector-memory counter, so the
@@ -115,6 +124,14 @@ __device__ inline int swz_r(int r) { return (r >> 1) & 7; }
 __device__ inline void wg_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Work-group barrier for a wave that has no LDS writes to publish: it does
+// not wait for its own outstanding LDS or scalar-memory operations.
+__device__ inline void wg_barrier_nowait() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -141,22 +158,6 @@ __device__ inline void dma16s(const void* sbase, uint32_t voff, uint32_t m0) {
                : "memory");
 }
 
-// Work-group barrier for a wave that has no LDS writes to publish: it does
-// not wait for its own outstanding LDS or scalar-memory operations, so a
-// scalar load issued before it stays in flight.
-__device__ inline void wg_barrier_nowait() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One 4-byte direct global->LDS load per active lane (lane l writes l + 4 l).
-__device__ inline void dma4(const void* g, lds_t* l) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)l;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0)
-               : "memory");
-}
-
 template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -164,80 +165,50 @@ __device__ inline void wait_vmcnt() {
   asm volatile("" ::: "memory");  // LDS written by the awaited loads is read after this
 }
 
-// Walks the 32-token steps of a split's tiles in order; a tile's second half
-// is skipped when it holds no token of its sequence.
-struct StepIter {
-  int32_t t, t_end, half, b, T, first, next_first;  // first/next_first: tile range of sequence b
-  bool valid;
-
-  __device__ void load_seq(const AttnArgs& a) {
-    const int32_t tl = load_ro(a.seq_lens, b), cap = a.max_blocks * a.P;
-    T = tl < 0 ? 0 : (tl > cap ? cap : tl);
-    first = load_ro(a.cu_tiles, b);
-    next_first = load_ro(a.cu_tiles, b + 1);
-  }
-  __device__ void init(const AttnArgs& a, int32_t t_begin, int32_t t_stop) {
-    t = t_begin;
-    t_end = t_stop;
-    half = 0;
-    b = 0;
-    while (load_ro(a.cu_tiles, b + 1) <= t) b++;
-    load_seq(a);
-    valid = t < t_end;
-  }
-  __device__ int32_t t0() const { return (t - first) * kTile + half * kStep; }
-  __device__ int32_t nvalid() const { return min(kStep, T - t0()); }
-  __device__ bool has_second_half() const { return (t - first) * kTile + kStep < T; }
-  // last step of its sequence within this split
-  __device__ bool seg_last() const {
-    const bool last_of_tile = half == 1 || !has_second_half();
-    return last_of_tile && (t + 1 == t_end || next_first <= t + 1);
-  }
-  __device__ void advance(const AttnArgs& a) {
-    if (half == 0 && has_second_half()) {
-      half = 1;
-      return;
-    }
-    half = 0;
-    t++;
-    valid = t < t_end;
-    if (valid && next_first <= t) {
-      while (load_ro(a.cu_tiles, b + 1) <= t) b++;
-      load_seq(a);
-    }
-  }
+// ------------------------------------------------------------------ tiles
+// A step's descriptor, read from the LDS window (wave-uniform).
+struct Tile {
+  int32_t blk, b, t0, nv, off;
+  bool last;  // last tile of its sequence
 };
 
-// Physical slot of the first token of a step, when the whole step lies in one
-// block (page size a multiple of 32), else -1.  step_entry is the index of the
-// block-table entry that holds the step's block.
-__device__ inline int64_t step_entry(const AttnArgs& a, const StepIter& it) {
-  const int32_t t0 = it.t0();
-  const int32_t pg = a.log2P >= 0 ? t0 >> a.log2P : t0 / a.P;
-  return (int64_t)it.b * a.max_blocks + pg;
-}
-__device__ inline int64_t step_base(const AttnArgs& a, const StepIter& it, int32_t blk) {
-  if (a.P % kStep) return -1;
-  const int32_t t0 = it.t0();
-  const int32_t off = a.log2P >= 0 ? t0 & (a.P - 1) : t0 % a.P;
-  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-  return (int64_t)blk * a.P + off;
+__device__ inline Tile read_tile(const lds_t* win, int32_t local) {
+  const i32x4 v = *reinterpret_cast<const i32x4 __attribute__((address_space(3)))*>(
+      win + (((local / kWin) & 1) * kWin + (local % kWin)) * 16);
+  Tile t;
+  t.blk = __builtin_amdgcn_readfirstlane(v[0]);
+  t.b = __builtin_amdgcn_readfirstlane(v[1]);
+  t.t0 = __builtin_amdgcn_readfirstlane(v[2]);
+  const int32_t w = __builtin_amdgcn_readfirstlane(v[3]);
+  t.nv = w & 63;
+  t.last = (w >> 6) & 1;
+  t.off = w >> 7;
+  return t;
 }
 
-// Direct-to-LDS loads of one step, issued by the NL value waves: wave lw
+// Descriptors of tiles [t_begin + kWin w, +kWin) of the split ending at t_end
+// into window buffer w % 2 (one direct load, lane l = tile l).
+__device__ inline void load_window(const AttnArgs& a, lds_t* win, int32_t t_begin, int32_t t_end,
+                                   int32_t w, int lane) {
+  const int32_t first = t_begin + kWin * w;
+  if (first + lane < t_end)
+    dma16(a.tiles + 4 * (int64_t)(first + lane), win + (w & 1) * kWin * 16);
+}
+
+// Direct-to-LDS loads of one step, issued by the NL loader waves: wave lw
 // loads latent rows lw, lw + NL, ... and rope groups lw, lw + NL, ...
 // (kLoadsPerStep / NL loads per wave on every path).  A full step inside one
-// block takes straight-line code: one scalar base per step, one offset per
+// page takes straight-line code: one scalar base per step, one offset per
 // row.  Otherwise rows past the end repeat the last valid token (finite data,
-// masked in the softmax) and every lane looks up its own block.
+// masked in the softmax) and, when a step can span pages, every lane looks up
+// its own block.
 template <int NL>
-__device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const StepIter& it,
-                                  int64_t base, int lw, int lane) {
+__device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d, int lw,
+                                  int lane) {
   static_assert(kStep % NL == 0 && (kStep / 8) % NL == 0, "uniform row assignment");
-  const int32_t t0 = it.t0();
-  const int32_t rmax = it.T - 1 - t0;
   const uint32_t st = (uint32_t)(uintptr_t)stage;
-  if (base >= 0 && rmax >= kStep - 1) {
+  const int64_t base = (int64_t)d.blk * a.P + d.off;
+  if (d.blk >= 0 && d.nv == kStep) {
     const char* cb = static_cast<const char*>(a.c_kv) + base * kCRow;
     const char* rb = static_cast<const char*>(a.k_rope) + base * kRRow;
     const uint32_t l16 = (uint32_t)lane << 4;
@@ -256,78 +227,68 @@ __device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const StepIte
   }
   const char* ckv = static_cast<const char*>(a.c_kv);
   const char* krp = static_cast<const char*>(a.k_rope);
+  const int32_t rmax = d.nv - 1;
 #pragma unroll
   for (int m = 0; m < kStep / NL; m++) {
     const int r = lw + NL * m;
-    const int64_t slot = base >= 0 ? base + min(r, rmax)
-                                   : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
-                                               a.max_blocks, a.num_blocks);
+    const int64_t slot = d.blk >= 0 ? base + min(r, rmax)
+                                    : phys_slot(a.block_table, d.b, d.t0 + min(r, rmax), a.P,
+                                                a.max_blocks, a.num_blocks);
     dma16(ckv + slot * kCRow + ((lane ^ swz_c(r)) << 4), stage + r * kCRow);
   }
 #pragma unroll
   for (int m = 0; m < kStep / 8 / NL; m++) {
     const int j = lw + NL * m;
     const int r = 8 * j + (lane >> 3);
-    const int64_t slot = base >= 0 ? base + min(r, rmax)
-                                   : phys_slot(a.block_table, it.b, t0 + min(r, rmax), a.P,
-                                               a.max_blocks, a.num_blocks);
+    const int64_t slot = d.blk >= 0 ? base + min(r, rmax)
+                                    : phys_slot(a.block_table, d.b, d.t0 + min(r, rmax), a.P,
+                                                a.max_blocks, a.num_blocks);
     dma16(krp + slot * kRRow + (((lane & 7) ^ swz_r(r)) << 4), stage + kStageC + j * 1024);
   }
 }
 
-// The load schedule of one of the NL loader waves (lane group lw).  A batch is
-// the block-table entry of the following step (one 4-byte direct load by lane
-// 0 into the wave's entry ring) followed by the wave's kLoadsPerStep / NL
-// loads of the step itself, so every batch is kPerBatch operations and the
-// table read never waits on the scalar path.
+// The load schedule of one of the NL loader waves (lane group lw).  Loader 0
+// also refills the descriptor window: window w + 1 goes into the buffer of
+// window w - 1 together with the loads of step kWin w + 4, when every wave has
+// moved past window w - 1 (the value waves, the furthest behind, are then at
+// step kWin w + 1).  It is complete before step kWin w + 4 starts, long before
+// its first use.
 template <int NL>
 struct Loader {
   static_assert(kLoadsPerStep % NL == 0, "equal load counts per wave");
   static constexpr int kPerWave = kLoadsPerStep / NL;
-  static constexpr int kPerBatch = kPerWave + 1;
-  StepIter next;       // next step to load
-  int32_t first_blk;   // table entry of the first step (read directly)
-  int32_t loaded;      // steps issued so far
+  int32_t next;        // split-local index of the next step to load
+  int32_t n;           // steps of the split
   bool newer_issued;   // the batch after the awaited one was issued
-  int32_t* ent;        // this wave's entry ring in LDS (4 slots)
 
-  __device__ void issue_next(const AttnArgs& a, lds_t* ring, int lw, int lane) {
-    int32_t blk = first_blk;
-    if (loaded > 0) {
-      // the entry came with the previous batch; only the latest batch (this
-      // step's predecessor) may still be in flight
-      wait_vmcnt<kPerWave>();
-      blk = __builtin_amdgcn_readfirstlane(ent[loaded & 3]);
-    }
-    const int64_t base = step_base(a, next, blk);
-    StepIter after = next;
-    after.advance(a);
-    const int32_t* src = a.block_table + (after.valid ? step_entry(a, after) : 0);
-    if (lane == 0) dma4(src, (lds_t*)(ent + ((loaded + 1) & 3)));
-    issue_step<NL>(a, ring + (loaded % kStages) * kStage, next, base, lw, lane);
-    next = after;
-    loaded++;
+  __device__ void issue_next(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
+                             int lane) {
+    if (lw == 0 && next >= kWin + 4 && next % kWin == 4 && next + kWin - 4 < n)
+      load_window(a, win, t_begin, t_begin + n, next / kWin + 1, lane);
+    const Tile d = read_tile(win, next);
+    issue_step<NL>(a, ring + (next % kStages) * kStage, d, lw, lane);
+    next++;
   }
-  __device__ void start(const AttnArgs& a, lds_t* ring, int32_t* ent_ring, int32_t tb, int32_t te,
+  __device__ void start(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int32_t steps,
                         int lw, int lane) {
-    ent = ent_ring;
-    next.init(a, tb, te);
-    first_blk = next.valid ? load_ro(a.block_table, step_entry(a, next)) : 0;
-    loaded = 0;
-    for (int s = 0; s < 2 && next.valid; s++) issue_next(a, ring, lw, lane);
-    newer_issued = loaded == 2;
+    next = 0;
+    n = steps;
+    for (int s = 0; s < 2 && next < n; s++) issue_next(a, ring, win, t_begin, lw, lane);
+    newer_issued = next == 2;
   }
-  // Wait for this wave's loads of step i (only batch i+1 may stay in flight).
+  // Wait for this wave's loads of step i (only batch i+1 may stay in flight;
+  // an extra window load in that batch only makes the wait longer).
   __device__ void wait_current() {
     if (newer_issued)
-      wait_vmcnt<kPerBatch>();
+      wait_vmcnt<kPerWave>();
     else
       wait_vmcnt<0>();
   }
-  // After the step barrier: issue step i+2.
-  __device__ void issue_ahead(const AttnArgs& a, lds_t* ring, int lw, int lane) {
-    if (next.valid) {
-      issue_next(a, ring, lw, lane);
+  // During the softmax of step i: issue step i+2.
+  __device__ void issue_ahead(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
+                              int lane) {
+    if (next < n) {
+      issue_next(a, ring, win, t_begin, lw, lane);
       newer_issued = true;
     } else {
       newer_issued = false;
@@ -341,12 +302,12 @@ void attend_mfma_kernel(AttnArgs a) {
   using S = Shape<HB>;
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
   lds_t* ring = (lds_t*)smem;
-  lds_t* xbuf = ring + kRing;                       // [HB][64 lanes][16 floats]
+  lds_t* win = ring + kRing;                        // [2][kWin] tile descriptors
+  lds_t* xbuf = win + kWinBytes;                    // [HB][64 lanes][16 floats]
   lds_t* pbuf = xbuf + HB * kXBytes;                // [HB][2 k-steps][64 lanes][16 B]
-  float* s_alpha = (float*)(smem + kRing + HB * (kXBytes + kPBytes));  // [HB][32]
+  float* s_alpha = (float*)(smem + kRing + kWinBytes + HB * (kXBytes + kPBytes));  // [HB][32]
   float* s_invl = s_alpha + HB * 32;                // [HB][32]
-  int* s_flag = (int*)(s_invl + HB * 32);           // [HB] (padded to 4)
-  int32_t* s_ent = (int32_t*)(s_flag + 4);          // [HB][4] block-table entries in flight
+  int* s_flag = (int*)(s_invl + HB * 32);           // [HB]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -370,9 +331,15 @@ void attend_mfma_kernel(AttnArgs a) {
   const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);
   const int32_t t_end = (int32_t)split_begin(n_total, a.splits, g + 1);
   if (t_begin >= t_end) return;
+  const int32_t n = t_end - t_begin;  // steps of this split
 
-  StepIter cur;
-  cur.init(a, t_begin, t_end);
+  // descriptor windows 0 and 1, visible to every wave after the barrier
+  if (wave == 1) {
+    load_window(a, win, t_begin, t_end, 0, lane);
+    if (n > kWin) load_window(a, win, t_begin, t_end, 1, lane);
+    wait_vmcnt<0>();
+  }
+  wg_barrier();
   const float sm = a.sm_scale_log2;
 
   if (wave < S::NQ) {
@@ -390,6 +357,7 @@ void attend_mfma_kernel(AttnArgs a) {
       // the hardware counter it waits on also counts the loader's tile loads
       wait_vmcnt<0>();
     };
+    Tile cur = read_tile(win, 0);
     load_q(cur.b);
     float m_run = -INFINITY, l_run = 0.f;
     int32_t seg_step = 0;  // steps of the current segment seen so far
@@ -397,9 +365,11 @@ void attend_mfma_kernel(AttnArgs a) {
     lds_t* pb = pbuf + hb * kPBytes + lane * 16;
     // the kh = 1 waves issue the loads: HB loader waves of kLoadsPerStep / HB
     Loader<HB> ld;
-    if (kh == 1) ld.start(a, ring, s_ent + 4 * hb, t_begin, t_end, hb, lane);
+    if (kh == 1) ld.start(a, ring, win, t_begin, n, hb, lane);
     // n steps of scores plus one final step in which only the value waves work
     for (int32_t i = 0;; i++) {
+      const bool valid = i < n;
+      const bool seg_last = valid && (cur.last || i + 1 == n);
       if (kh == 1) {
         ld.wait_current();
         wg_barrier_nowait();  // step i's tile is in LDS
@@ -408,7 +378,7 @@ void attend_mfma_kernel(AttnArgs a) {
       }
       lds_t* st = ring + (i % kStages) * kStage;
       f32x16 s = f32x16{};
-      if (cur.valid) {
+      if (valid) {
         const int row = lane & 31;
         auto ld_a = [&](int k) -> bf16x8 {
           const int ks = kh * kKsHalf + k;
@@ -438,8 +408,8 @@ void attend_mfma_kernel(AttnArgs a) {
       if (kh == 1) {
         // loads of step i+2, into the stage last read in step i-2, issued
         // while the partner wave runs the softmax
-        ld.issue_ahead(a, ring, hb, lane);
-      } else if (cur.valid) {
+        ld.issue_ahead(a, ring, win, t_begin, hb, lane);
+      } else if (valid) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           const f32x4 o = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 16 * q);
@@ -449,7 +419,7 @@ void attend_mfma_kernel(AttnArgs a) {
           s[4 * q + 3] += o[3];
         }
         // mask the tokens past the end (only the last step of a sequence)
-        const int32_t nv = cur.nvalid();
+        const int32_t nv = cur.nv;
         if (nv < kStep) {
 #pragma unroll
           for (int j = 0; j < 16; j++)
@@ -500,7 +470,7 @@ void attend_mfma_kernel(AttnArgs a) {
         seg_step++;
         if (g32 == 0) s_alpha[hb * 32 + lane] = alpha;
         if (lane == 0) s_flag[hb] = any ? 1 : 0;
-        if (cur.seg_last()) {
+        if (seg_last) {
           const float ltot = l_run + __shfl_xor(l_run, 32);
           if (g32 == 0) {
             s_invl[hb * 32 + lane] = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -514,14 +484,15 @@ void attend_mfma_kernel(AttnArgs a) {
         wg_barrier_nowait();
       else
         wg_barrier();
-      if (!cur.valid) break;  // that was the value waves' final step
-      const bool was_last = cur.seg_last();
-      cur.advance(a);
-      if (cur.valid && was_last) {
-        load_q(cur.b);
-        m_run = -INFINITY;
-        l_run = 0.f;
-        seg_step = 0;
+      if (!valid) break;  // that was the value waves' final step
+      if (i + 1 < n) {
+        cur = read_tile(win, i + 1);
+        if (seg_last) {
+          load_q(cur.b);
+          m_run = -INFINITY;
+          l_run = 0.f;
+          seg_step = 0;
+        }
       }
     }
   } else {
@@ -535,13 +506,14 @@ void attend_mfma_kernel(AttnArgs a) {
     for (int md = 0; md < MDP; md++)
 #pragma unroll
       for (int hb = 0; hb < HB; hb++) o[md][hb] = f32x16{};
-    StepIter prev = cur;  // the step whose weights are consumed in this iteration
-    bool prev_valid = false;
-    for (int32_t i = 0;; i++) {
-      if (!cur.valid && !prev_valid) break;
+    // iteration i consumes the weights of step i - 1
+    for (int32_t i = 0; i <= n; i++) {
       wg_barrier();
       lds_t* st = ring + ((i + kStages - 1) % kStages) * kStage;
-      const bool last = prev_valid && prev.seg_last();
+      const bool have = i > 0;
+      Tile prev{};
+      if (have) prev = read_tile(win, i - 1);
+      const bool last = have && (prev.last || i == n);
       bf16x8 pf[HB][2];
       float inv[HB];
       auto ld_c = [&](int md, int kk) -> bf16x8 {
@@ -562,23 +534,23 @@ void attend_mfma_kernel(AttnArgs a) {
       auto products = [&](auto md0_c, auto md1_c) {
         constexpr int md0 = decltype(md0_c)::value, md1 = decltype(md1_c)::value;
         if constexpr (md1 > md0) {
-        constexpr int NSTEP = 2 * (md1 - md0);
-        constexpr int D = NSTEP < 4 ? NSTEP : 4;
-        bf16x8 cv[D];
+          constexpr int NSTEP = 2 * (md1 - md0);
+          constexpr int D = NSTEP < 4 ? NSTEP : 4;
+          bf16x8 cv[D];
 #pragma unroll
-        for (int k = 0; k < D; k++) cv[k] = ld_c(md0 + (k >> 1), k & 1);
+          for (int k = 0; k < D; k++) cv[k] = ld_c(md0 + (k >> 1), k & 1);
 #pragma unroll
-        for (int s = 0; s < NSTEP; s++) {
-          const int md = md0 + (s >> 1), kk = s & 1;
+          for (int s = 0; s < NSTEP; s++) {
+            const int md = md0 + (s >> 1), kk = s & 1;
 #pragma unroll
-          for (int hb = 0; hb < HB; hb++)
-            o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[s % D], pf[hb][kk], o[md][hb], 0, 0, 0);
-          if (s + D < NSTEP) cv[s % D] = ld_c(md0 + ((s + D) >> 1), (s + D) & 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int hb = 0; hb < HB; hb++)
+              o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[s % D], pf[hb][kk], o[md][hb], 0, 0, 0);
+            if (s + D < NSTEP) cv[s % D] = ld_c(md0 + ((s + D) >> 1), (s + D) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       };
-      if (prev_valid) {
+      if (have) {
         // everything published with the step being consumed is read now: the
         // score waves overwrite it after the next barrier
 #pragma unroll
@@ -597,7 +569,7 @@ void attend_mfma_kernel(AttnArgs a) {
         products(std::integral_constant<int, 0>{}, std::integral_constant<int, kMdFirst>{});
       }
       wg_barrier();
-      if (prev_valid) {
+      if (have) {
         products(std::integral_constant<int, kMdFirst>{}, std::integral_constant<int, MDP>{});
         if (last) {
           const int64_t slot = (int64_t)(g + prev.b);
@@ -619,9 +591,6 @@ void attend_mfma_kernel(AttnArgs a) {
         }
       }
       wg_barrier();
-      prev = cur;
-      prev_valid = cur.valid;
-      if (cur.valid) cur.advance(a);
     }
   }
 }

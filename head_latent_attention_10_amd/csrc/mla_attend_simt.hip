@@ -72,8 +72,9 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
     }
     __syncthreads();
     // tile max and weights
+    static_assert(kTile <= 64, "one wave reduces a tile");
     if (wave == 0) {
-      float v = ps[lane];
+      float v = lane < kTile ? ps[lane] : -INFINITY;
       for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
       if (lane == 0) bcast = v;
     }
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
     if (tid < kTile) ps[tid] = (tid < nvalid) ? expf(ps[tid] - m_new) : 0.f;
     __syncthreads();
     if (wave == 0) {
-      float v = ps[lane];
+      float v = lane < kTile ? ps[lane] : 0.f;
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
       if (lane == 0) red[0] = v;
     }

@@ -8,7 +8,22 @@
 
 namespace mla {
 
-constexpr int kTile = 64;  // tokens per planning tile (one page at page_size 64)
+constexpr int kTile = 32;  // tokens per planning tile (one step of the attention kernels)
+
+// Planning limit: the planning kernel keeps the tile prefix sums in LDS.
+constexpr int kPlanMaxBatch = 16384;
+
+// Per-tile descriptor written by the planning kernel, tiles numbered across
+// the sequences in order (four int32):
+//   x: block id of the page holding the whole tile (clamped to the pool), or
+//      -1 when a tile can span pages (page size not a multiple of kTile)
+//   y: sequence b
+//   z: first token t0 of the tile within the sequence
+//   w: valid tokens nv (1..kTile) | last tile of the sequence << 6 |
+//      offset of t0 within its page << 7
+__host__ __device__ inline int32_t tile_word(int32_t nv, bool last, int32_t off) {
+  return nv | ((int32_t)last << 6) | (off << 7);
+}
 
 // ---------------------------------------------------------------- split plan
 // Tiles of all sequences are numbered in order; split g owns a contiguous run.
@@ -29,6 +44,7 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* cu_tiles;   // [B + 1] prefix sums of ceil(T_b / kTile) (workspace)
+  const int32_t* tiles;      // [n_tiles][4] tile descriptors (workspace)
   float* part_o;             // [slots, h, d_c]
   float* part_lse;           // [slots, h]
   int32_t B, h, d_c, d_r, P, max_blocks, num_blocks;

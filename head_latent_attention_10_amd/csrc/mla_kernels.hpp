@@ -5,9 +5,11 @@
 
 namespace mla {
 
-// Prefix sums of ceil(T_b / kTile) over the batch -> cu_tiles[B + 1].
-hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32_t P,
-                       int32_t* cu_tiles, hipStream_t s);
+// Prefix sums of ceil(T_b / kTile) over the batch -> cu_tiles[B + 1], and the
+// descriptor of every tile -> tiles[n][4] (B <= kPlanMaxBatch).
+hipError_t launch_plan(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
+                       int32_t max_blocks, int32_t P, int32_t num_blocks, int32_t* cu_tiles,
+                       int32_t* tiles, hipStream_t s);
 
 // q_lat[b,i,:d_c] = W_UK[i]^T q_nope[b,i,:]; q_lat[b,i,d_c:] = q_rope[b,i,:].
 hipError_t launch_absorb(const mla_decode_params& p, const void* q, const void* W_UK, void* q_lat,

@@ -4,11 +4,17 @@
 namespace mla {
 
 // ------------------------------------------------------------------ planner
-// One work group scans the batch: cu_tiles[b] = sum_{j<b} ceil(T_j / kTile).
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ seq_lens, int32_t B,
-                                                     int32_t max_blocks, int32_t P,
-                                                     int32_t* __restrict__ cu_tiles) {
+// One work group scans the batch, cu_tiles[b] = sum_{j<b} ceil(T_j / kTile),
+// then writes the descriptor of every tile (one thread per tile).
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ seq_lens,
+                                                     const int32_t* __restrict__ block_table,
+                                                     int32_t B, int32_t max_blocks, int32_t P,
+                                                     int32_t num_blocks,
+                                                     int32_t* __restrict__ cu_tiles,
+                                                     int32_t* __restrict__ tiles) {
   __shared__ int32_t buf[1024];
+  __shared__ int32_t cu_s[kPlanMaxBatch + 1];
+  __shared__ int32_t len_s[kPlanMaxBatch];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
   if (tid == 0) carry = 0;
@@ -16,7 +22,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   for (int32_t base = 0; base < B; base += 1024) {
     int32_t b = base + tid;
     int32_t n = 0;
-    if (b < B) n = (seq_len_clamped(seq_lens, b, max_blocks, P) + kTile - 1) / kTile;
+    if (b < B) {
+      const int32_t T = seq_len_clamped(seq_lens, b, max_blocks, P);
+      len_s[b] = T;
+      n = (T + kTile - 1) / kTile;
+    }
     buf[tid] = n;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
@@ -25,17 +35,49 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       buf[tid] += v;
       __syncthreads();
     }
-    if (b < B) cu_tiles[b + 1] = carry + buf[tid];
+    if (b < B) {
+      cu_s[b + 1] = carry + buf[tid];
+      cu_tiles[b + 1] = carry + buf[tid];
+    }
     __syncthreads();
     if (tid == 1023) carry += buf[1023];
     __syncthreads();
   }
-  if (tid == 0) cu_tiles[0] = 0;
+  if (tid == 0) {
+    cu_tiles[0] = 0;
+    cu_s[0] = 0;
+  }
+  __syncthreads();
+  // descriptors: tile t belongs to the last sequence b with cu_s[b] <= t
+  // (sequences without tiles share their start with the next one)
+  const int32_t n_total = cu_s[B];
+  const bool one_page = P % kTile == 0;
+#pragma unroll 4
+  for (int32_t t = tid; t < n_total; t += 1024) {
+    int32_t lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (cu_s[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int32_t b = lo, T = len_s[b];
+    const int32_t t0 = (t - cu_s[b]) * kTile;
+    const int32_t nv = min(kTile, T - t0);
+    int32_t blk = -1, off = 0;
+    if (one_page) {
+      const int32_t raw = block_table[(int64_t)b * max_blocks + t0 / P];
+      blk = raw < 0 ? 0 : (raw >= num_blocks ? num_blocks - 1 : raw);
+      off = t0 % P;
+    }
+    reinterpret_cast<int4*>(tiles)[t] = make_int4(blk, b, t0, tile_word(nv, t0 + kTile >= T, off));
+  }
 }
 
-hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32_t P,
-                       int32_t* cu_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, seq_lens, B, max_blocks, P, cu_tiles);
+hipError_t launch_plan(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
+                       int32_t max_blocks, int32_t P, int32_t num_blocks, int32_t* cu_tiles,
+                       int32_t* tiles, hipStream_t s) {
+  if (B > kPlanMaxBatch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, seq_lens, block_table, B, max_blocks,
+                     P, num_blocks, cu_tiles, tiles);
   return hipGetLastError();
 }
 

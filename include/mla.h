@@ -68,7 +68,7 @@ typedef enum {
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
 
 typedef struct {
-  int32_t batch;              /* B  >= 1                                     */
+  int32_t batch;              /* B, 1..16384                                 */
   int32_t num_heads;          /* h  >= 1                                     */
   int32_t d_nope;             /* width of q_nope, rows of W_UK[i]            */
   int32_t d_rope;             /* width of q_rope and k_rope (may be 0)       */
@@ -169,7 +169,7 @@ mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const 
                             float* scale_out, void* rope_out, void* stream);
 
 /* Host-side split arithmetic (no HIP call; used by the kernels' planner).
- * The cache of all sequences is cut into 64-token tiles, numbered across
+ * The cache of all sequences is cut into 32-token tiles, numbered across
  * sequences in order.  Split g of `splits` owns tiles
  * [mla_split_begin(n, splits, g), mla_split_begin(n, splits, g + 1));
  * mla_split_owner returns the split owning a tile. */

@@ -47,16 +47,19 @@ def _params(**kw):
 
 def test_workspace_size_without_device():
     n = _lib.mla_decode_workspace_size(_params())
-    # q_lat + cu_tiles + partials ((8 + 2) slots) + lse + o_lat, each 256-aligned
+    # q_lat + cu_tiles + tile descriptors (B * ceil(2 blocks * 64 / 32) of 16 B)
+    # + partials ((8 + 2) slots) + lse + o_lat, each 256-aligned
     B, h, dc, dr = 2, 4, 32, 8
     expect = 0
-    for size in (B * h * (dc + dr) * 4, (B + 1) * 4, 10 * h * dc * 4, 10 * h * 4, B * h * dc * 4):
+    for size in (B * h * (dc + dr) * 4, (B + 1) * 4, B * 4 * 16, 10 * h * dc * 4, 10 * h * 4,
+                 B * h * dc * 4):
         expect += (size + 255) // 256 * 256
     assert n == expect
 
 
 @pytest.mark.parametrize("bad,status", [
     (dict(batch=0), _lib.MLA_ERR_INVALID_ARG),
+    (dict(batch=16385), _lib.MLA_ERR_UNSUPPORTED),
     (dict(num_heads=-1), _lib.MLA_ERR_INVALID_ARG),
     (dict(page_size=0), _lib.MLA_ERR_INVALID_ARG),
     (dict(page_size=5000), _lib.MLA_ERR_INVALID_ARG),
