@@ -120,32 +120,92 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
 
 def cpu_baseline(inp, seconds: float):
     """The oracle as it stands, on a bounded sample of the same workload:
-    whole heads of sequence 0 until about `seconds` of CPU time have passed,
-    extrapolated to the full step by the token x head count."""
+    (sequence, group of up to 32 heads) calls in order until about `seconds` of CPU time
+    have passed, extrapolated to the full step by the token x head count."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import oracle_from_inputs
 
     cfg = inp.cfg
-    T0 = int(inp.seq_lens[0])
-    heads_done = 0
+    lens = inp.seq_lens.astype(np.int64)
+    chunk = min(cfg.heads, 32)
+    pairs, work_done, passes = 0, 0, 0
     t_start = time.perf_counter()
-    while heads_done < cfg.heads and time.perf_counter() - t_start < seconds:
-        oracle_from_inputs(inp, batches=[0], heads=[heads_done])
-        heads_done += 1
+    while time.perf_counter() - t_start < seconds:     # repeat whole steps if one is short
+        for b in range(cfg.batch):
+            for i0 in range(0, cfg.heads, chunk):
+                if time.perf_counter() - t_start >= seconds:
+                    break
+                heads = list(range(i0, min(i0 + chunk, cfg.heads)))
+                oracle_from_inputs(inp, batches=[b], heads=heads)
+                pairs += len(heads)
+                work_done += int(lens[b]) * len(heads)
+        passes += 1
     elapsed = time.perf_counter() - t_start
-    work_done = T0 * heads_done
-    work_full = int(inp.seq_lens.astype(np.int64).sum()) * cfg.heads
+    work_full = int(lens.sum()) * cfg.heads
     t_full = elapsed * work_full / max(work_done, 1)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     return {
         "value": cfg.batch / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-        "sample": (f"sequence 0 ({T0} tokens), {heads_done} of {cfg.heads} heads in "
-                   f"{elapsed:.1f} s, fp64 numpy oracle, extrapolated by tokens x heads "
-                   f"to the full step ({work_full} token-heads)"),
+        "sample": (f"{pairs} (sequence, head) pairs in order over {passes} pass(es) of the "
+                   f"step ({work_done} token-heads; one step is {work_full}) in {elapsed:.1f} s, "
+                   f"fp64 numpy oracle, scaled by token-heads to one step"),
     }
+
+
+def _counter_rows(directory: str):
+    """(dispatch id, kernel name, counter name, value) rows of a rocprofv3
+    csv counter collection found under `directory`."""
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                             float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no counter collection under {directory}")
+    return rows
+
+
+def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: int, commands):
+    """HBM bytes per attention launch from two rocprofv3 --pmc runs of
+    `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB
+    per dispatch).  Each counter is scaled by what it reads for the plain copy
+    of copy_mb MiB in the same run (the largest copy dispatch)."""
+    import statistics
+
+    out = {}
+    for name, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(directory) if r[2] == name]
+        attn = [v for _, k, _, v in rows if "attend_mfma_kernel" in k]
+        copies = [(v, d) for d, k, _, v in rows if "copyBuffer" in k]
+        if not attn or not copies:
+            raise SystemExit(f"{name}: attention or copy dispatches missing")
+        copy_kib = max(copies)[0]
+        factor = copy_mb * 1024.0 / copy_kib
+        out[name] = {"attention_kib_median": statistics.median(attn), "dispatches": len(attn),
+                     "copy_kib": copy_kib, "factor": factor,
+                     "bytes_per_launch": statistics.median(attn) * 1024.0 * factor}
+    rec = {
+        "workload": workload,
+        "kernel": "attend_mfma_kernel",
+        "kernel_source_sha256_16": attn_source_hash(),
+        "copy_calibration_mib": copy_mb,
+        "fetch": out["FETCH_SIZE"],
+        "write": out["WRITE_SIZE"],
+        "hbm_bytes_per_launch": round(out["FETCH_SIZE"]["bytes_per_launch"] +
+                                      out["WRITE_SIZE"]["bytes_per_launch"]),
+        "commands": commands,
+    }
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def main():
@@ -159,7 +219,20 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after the measurement, copy this many MiB once (a plain copy of known "
+                         "size for scaling rocprofv3 byte counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/attend_<workload>_traffic.json from two rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE) of this script; no GPU needed")
+    ap.add_argument("--profile-command", action="append", default=[],
+                    help="command line recorded with --summarize-traffic (repeatable)")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args.workload, args.summarize_traffic[0], args.summarize_traffic[1],
+                          args.calibrate_copy_mb, args.profile_command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -183,6 +256,15 @@ def main():
                     "attn_cache_GBps": round(r["attn_gbps"], 1),
                     "attn_frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4)}
         del r
+
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = main_run["cfg"]
     traffic = measured_traffic(args.workload)
