@@ -32,8 +32,6 @@ bool is_dtype(int32_t d, bool allow_fp8) {
 
 mla_status validate(const mla_decode_params* p) {
   if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
-  if (p->batch > mla::kPlanMaxBatch)
-    return fail(MLA_ERR_UNSUPPORTED, "batch %d above %d", p->batch, mla::kPlanMaxBatch);
   if (p->batch < 1 || p->num_heads < 1 || p->d_nope < 1 || p->d_rope < 0 || p->d_latent < 1 ||
       p->d_v < 1)
     return fail(MLA_ERR_INVALID_ARG,
@@ -46,6 +44,10 @@ mla_status validate(const mla_decode_params* p) {
                 p->max_blocks_per_seq, p->num_blocks);
   if ((int64_t)p->max_blocks_per_seq * p->page_size > (int64_t)1 << 30)
     return fail(MLA_ERR_INVALID_ARG, "table capacity above 2^30 tokens per sequence");
+  if ((int64_t)p->batch * (((int64_t)p->max_blocks_per_seq * p->page_size + mla::kTile - 1) /
+                           mla::kTile) >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "batch x table capacity above 2^31 tiles of %d tokens",
+                mla::kTile);
   if (p->num_splits < 0 || p->num_splits > 65535)
     return fail(MLA_ERR_INVALID_ARG, "num_splits %d outside [0, 65535]", p->num_splits);
   if (!std::isfinite(p->sm_scale)) return fail(MLA_ERR_INVALID_ARG, "sm_scale not finite");
@@ -145,7 +147,8 @@ mla_status check_workspace(const Layout& L, void* ws, size_t bytes) {
 mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat, const void* c_kv,
                   const float* c_kv_scale, const void* k_rope, const int32_t* block_table,
                   const int32_t* seq_lens, float* o_lat, char* ws, hipStream_t s,
-                  hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr) {
+                  bool planned = false, hipEvent_t ev_before = nullptr,
+                  hipEvent_t ev_after = nullptr) {
   mla::AttnArgs a;
   a.q_lat = q_lat;
   a.c_kv = c_kv;
@@ -167,13 +170,16 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.num_blocks = p.num_blocks;
   a.splits = L.splits;
   a.streams = L.streams;
+  a.frag_layout = mla::mfma_supported(p) ? 1 : 0;
   a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
 
-  hipError_t e = mla::launch_plan(seq_lens, block_table, p.batch, p.max_blocks_per_seq,
-                                  p.page_size, p.num_blocks,
-                                  reinterpret_cast<int32_t*>(ws + L.cu_tiles),
-                                  reinterpret_cast<int32_t*>(ws + L.tiles), s);
-  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  hipError_t e = hipSuccess;
+  if (!planned) {
+    e = mla::launch_plan(seq_lens, block_table, p.batch, p.max_blocks_per_seq, p.page_size,
+                         p.num_blocks, reinterpret_cast<int32_t*>(ws + L.cu_tiles),
+                         reinterpret_cast<int32_t*>(ws + L.tiles), s);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+  }
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (mla::mfma_supported(p))
     e = mla::launch_attend_mfma(a, p.cache_dtype, s);
@@ -238,7 +244,7 @@ mla_status mla_absorb_q(const mla_decode_params* p, const void* q, const void* W
   mla_status st = validate(p);
   if (st != MLA_OK) return st;
   if (!q || !W_UK || !q_lat) return fail(MLA_ERR_INVALID_ARG, "null q, W_UK or q_lat");
-  hipError_t e = mla::launch_absorb(*p, q, W_UK, q_lat, absorbed_dtype(*p),
+  hipError_t e = mla::launch_absorb(*p, q, W_UK, q_lat, absorbed_dtype(*p), nullptr, nullptr,
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "absorb launch");
 }
@@ -291,11 +297,15 @@ mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const voi
   if (st != MLA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = mla::launch_absorb(*p, q, W_UK, ws + L.q_lat, absorbed_dtype(*p), s);
+  const mla::PlanRequest plan{seq_lens, block_table, reinterpret_cast<int32_t*>(ws + L.cu_tiles),
+                              reinterpret_cast<int32_t*>(ws + L.tiles)};
+  bool planned = false;
+  hipError_t e =
+      mla::launch_absorb(*p, q, W_UK, ws + L.q_lat, absorbed_dtype(*p), &plan, &planned, s);
   if (e != hipSuccess) return hip_fail(e, "absorb launch");
   float* o_lat = reinterpret_cast<float*>(ws + L.o_lat);
   st = attend(*p, L, ws + L.q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens, o_lat, ws, s,
-              static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after));
+              planned, static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after));
   if (st != MLA_OK) return st;
   e = mla::launch_up_project(*p, o_lat, W_UV, out, s);
   return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");

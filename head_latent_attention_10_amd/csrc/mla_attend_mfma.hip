@@ -575,15 +575,16 @@ void attend_mfma_kernel(AttnArgs a) {
           const int64_t slot = (int64_t)(g + prev.b);
 #pragma unroll
           for (int hb = 0; hb < HB; hb++) {
-            const int32_t head = hg * 32 * HB + hb * 32 + (lane & 31);
-            float* dst = a.part_o + (slot * a.h + head) * kDc + 32 * pw_id * MDP;
+            // fragment-major partial: one store instruction writes 1 KiB contiguous
+            float* dst = a.part_o + slot * a.h * kDc +
+                         frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
 #pragma unroll
             for (int md = 0; md < MDP; md++) {
 #pragma unroll
               for (int jj = 0; jj < 4; jj++) {
                 const f32x4 v = {o[md][hb][4 * jj] * inv[hb], o[md][hb][4 * jj + 1] * inv[hb],
                                  o[md][hb][4 * jj + 2] * inv[hb], o[md][hb][4 * jj + 3] * inv[hb]};
-                *reinterpret_cast<f32x4*>(dst + 32 * md + 8 * jj + 4 * g32) = v;
+                *reinterpret_cast<f32x4*>(dst + (md * 4 + jj) * 256) = v;
               }
               o[md][hb] = f32x16{};
             }

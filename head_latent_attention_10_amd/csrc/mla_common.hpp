@@ -10,8 +10,9 @@ namespace mla {
 
 constexpr int kTile = 32;  // tokens per planning tile (one step of the attention kernels)
 
-// Planning limit: the planning kernel keeps the tile prefix sums in LDS.
-constexpr int kPlanMaxBatch = 16384;
+// Planning: kPlanGroups work groups of kPlanThreads threads (see plan_block).
+constexpr int kPlanThreads = 256;
+constexpr int kPlanGroups = 8;
 
 // Per-tile descriptor written by the planning kernel, tiles numbered across
 // the sequences in order (four int32):
@@ -23,6 +24,16 @@ constexpr int kPlanMaxBatch = 16384;
 //      offset of t0 within its page << 7
 __host__ __device__ inline int32_t tile_word(int32_t nv, bool last, int32_t off) {
   return nv | ((int32_t)last << 6) | (off << 7);
+}
+
+// Fragment-major layout of one slot's partial output, used by the matrix-core
+// kernel (512 latent values, heads a multiple of 32): the slot's [h, 512] fp32
+// block is stored as [h/32][16][4][64][4] = (head block, 32-value latent block
+// mdg, 8-value group jj, lane, 4 values), where lane = 32*g + r holds head
+// 32*hblk + r and latent values 32*mdg + 8*jj + 4*g + (0..3).  This is the
+// matrix-core accumulator layout, so each 64-lane store covers 1 KiB.
+__host__ __device__ inline int64_t frag_offset(int32_t hblk, int32_t mdg, int32_t jj, int32_t lane) {
+  return (((int64_t)hblk * 16 + mdg) * 4 + jj) * 256 + lane * 4;
 }
 
 // ---------------------------------------------------------------- split plan
@@ -51,6 +62,7 @@ struct AttnArgs {
   int32_t log2P;             // log2(P) when P is a power of two, else -1
   int32_t splits;            // work groups along tokens (gridDim.x)
   int32_t streams;           // partial slots per (split, sequence)
+  int32_t frag_layout;       // part_o in fragment-major layout (frag_offset), else row-major
   float sm_scale_log2;       // sm_scale * log2(e)
 };
 
@@ -76,6 +88,77 @@ __device__ inline int64_t phys_slot(const int32_t* block_table, int32_t b, int32
   int32_t blk = block_table[(int64_t)b * max_blocks + t / P];
   blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
   return (int64_t)blk * P + (t % P);
+}
+
+// ---------------------------------------------------------------- planner
+// LDS of one planning work group.
+struct PlanShared {
+  int32_t scan[kPlanThreads];
+  int32_t cu[kPlanThreads + 1];  // tile prefix sums of the current chunk of sequences
+  int32_t len[kPlanThreads];
+};
+
+// Work group `wg` of `nwg` (kPlanThreads threads each) of the planner.  The
+// sequences are taken in chunks of kPlanThreads; every planning group scans
+// each chunk (cu_tiles[b] = sum_{j<b} ceil(T_j / kTile), written by group 0),
+// and the groups share out the chunk's tiles, writing one descriptor per tile
+// (tile_word).  The tile's page is resolved here when no tile can span two
+// pages (P a multiple of kTile).
+__device__ inline void plan_block(const int32_t* __restrict__ seq_lens,
+                                  const int32_t* __restrict__ block_table, int32_t B,
+                                  int32_t max_blocks, int32_t P, int32_t num_blocks,
+                                  int32_t* __restrict__ cu_tiles, int32_t* __restrict__ tiles,
+                                  int32_t wg, int32_t nwg, PlanShared& sh) {
+  const int tid = threadIdx.x;
+  const bool one_page = P % kTile == 0;
+  int32_t carry = 0;
+  if (wg == 0 && tid == 0) cu_tiles[0] = 0;
+  for (int32_t base = 0; base < B; base += kPlanThreads) {
+    const int32_t cnt = min(kPlanThreads, B - base);
+    const int32_t b = base + tid;
+    int32_t n = 0;
+    if (tid < cnt) {
+      const int32_t T = seq_len_clamped(seq_lens, b, max_blocks, P);
+      sh.len[tid] = T;
+      n = (T + kTile - 1) / kTile;
+    }
+    sh.scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int32_t v = tid >= off ? sh.scan[tid - off] : 0;
+      __syncthreads();
+      sh.scan[tid] += v;
+      __syncthreads();
+    }
+    sh.cu[tid + 1] = carry + sh.scan[tid];
+    if (tid == 0) sh.cu[0] = carry;
+    if (wg == 0 && tid < cnt) cu_tiles[b + 1] = carry + sh.scan[tid];
+    __syncthreads();
+    // tile t of this chunk belongs to the last local sequence j with cu[j] <= t
+    // (sequences without tiles share their start with the next one)
+    const int32_t t_end = sh.cu[cnt];
+#pragma unroll 4
+    for (int32_t t = sh.cu[0] + wg * kPlanThreads + tid; t < t_end; t += nwg * kPlanThreads) {
+      int32_t lo = 0, hi = cnt - 1;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (sh.cu[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int32_t T = sh.len[lo];
+      const int32_t t0 = (t - sh.cu[lo]) * kTile;
+      const int32_t nv = min(kTile, T - t0);
+      int32_t blk = -1, off = 0;
+      if (one_page) {
+        const int32_t raw = block_table[(int64_t)(base + lo) * max_blocks + t0 / P];
+        blk = raw < 0 ? 0 : (raw >= num_blocks ? num_blocks - 1 : raw);
+        off = t0 % P;
+      }
+      reinterpret_cast<int4*>(tiles)[t] =
+          make_int4(blk, base + lo, t0, tile_word(nv, t0 + kTile >= T, off));
+    }
+    carry = t_end;
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- storage types

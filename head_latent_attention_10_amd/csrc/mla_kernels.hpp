@@ -6,14 +6,25 @@
 namespace mla {
 
 // Prefix sums of ceil(T_b / kTile) over the batch -> cu_tiles[B + 1], and the
-// descriptor of every tile -> tiles[n][4] (B <= kPlanMaxBatch).
+// descriptor of every tile -> tiles[n][4].
 hipError_t launch_plan(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
                        int32_t max_blocks, int32_t P, int32_t num_blocks, int32_t* cu_tiles,
                        int32_t* tiles, hipStream_t s);
 
+// Where the split planner writes when it shares the absorption's launch.
+struct PlanRequest {
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t* cu_tiles;
+  int32_t* tiles;
+};
+
 // q_lat[b,i,:d_c] = W_UK[i]^T q_nope[b,i,:]; q_lat[b,i,d_c:] = q_rope[b,i,:].
+// With plan != null the matrix-core absorption also runs the split planner in
+// the same launch and sets *planned; otherwise the caller launches the plan.
 hipError_t launch_absorb(const mla_decode_params& p, const void* q, const void* W_UK, void* q_lat,
-                         int32_t q_lat_dtype, hipStream_t s);
+                         int32_t q_lat_dtype, const PlanRequest* plan, bool* planned,
+                         hipStream_t s);
 
 // Generic (any shape, any storage type) split attention -> partials.
 hipError_t launch_attend_simt(const AttnArgs& a, int32_t cache_dtype, int32_t rope_dtype,
@@ -31,8 +42,10 @@ hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_
 // Matrix-core absorb / up-projection for bf16 q and weights, d_c = 512
 // (d_nope <= 128, multiple of 16; d_v multiple of 32).
 bool proj_mfma_supported(const mla_decode_params& p);
+// With plan != null the launch also runs the planner (as launch_plan would).
 hipError_t launch_absorb_mfma(const mla_decode_params& p, const void* q, const void* W_UK,
-                              void* q_lat, int32_t q_lat_dtype, hipStream_t s);
+                              void* q_lat, int32_t q_lat_dtype, const PlanRequest* plan,
+                              hipStream_t s);
 hipError_t launch_up_project_mfma(const mla_decode_params& p, const float* o_lat,
                                   const void* W_UV, void* out, hipStream_t s);
 

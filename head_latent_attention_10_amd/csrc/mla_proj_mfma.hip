@@ -15,40 +15,76 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_t;
 
 constexpr int kLat = 512;             // latent width of the fast path
 constexpr int kUpKs = kLat / 16;      // k-steps of the up-projection
 
 // ------------------------------------------------------------------ up-projection
-// Work group = one wave = (head, 32 rows of W_UV).  The wave keeps its 32 W_UV
-// rows (32 KiB) in registers as the MFMA B operand and sweeps the sequences in
-// blocks of 32.  o_lat is fp32; it is split into a bf16 high part and a bf16
-// remainder, multiplied separately and summed in fp32, which keeps about 16
-// significant bits of o_lat in the product.
+// Work group = (head, 64 rows of W_UV), two waves of 32 rows.  Each wave keeps
+// its 32 W_UV rows (32 KiB) in registers as the MFMA B operand.  The o_lat
+// rows of 32 sequences at a time are staged in LDS, split into a bf16 high
+// part and a bf16 remainder (16-byte chunks XOR-swizzled by the row); both
+// are multiplied and the products summed in fp32, which keeps about 16
+// significant bits of o_lat.  All global loads of a stage are issued before
+// the first is waited for.
+constexpr int kUpWaves = 2;
+constexpr int kUpStage = 32 * kLat / 4 / (64 * kUpWaves);  // float4 loads per thread per stage
+
+__device__ inline int up_swz(int row) { return row & 15; }
+
 template <int OT>
-__global__ __launch_bounds__(64) void up_project_mfma_kernel(const float* __restrict__ o_lat,
-                                                             const uint16_t* __restrict__ W_UV,
-                                                             void* __restrict__ out, int32_t B,
-                                                             int32_t h, int32_t d_v) {
+__global__ __launch_bounds__(64 * kUpWaves) void up_project_mfma_kernel(
+    const float* __restrict__ o_lat, const uint16_t* __restrict__ W_UV, void* __restrict__ out,
+    int32_t B, int32_t h, int32_t d_v) {
+  __shared__ __attribute__((aligned(16))) char os[2][32 * kLat * 2];  // high, low parts
   const int32_t head = blockIdx.x;
-  const int32_t v0 = blockIdx.y * 32;
-  const int lane = threadIdx.x, g = lane >> 5, r = lane & 31;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+  const int32_t v0 = (blockIdx.y * kUpWaves + wave) * 32;
+  const bool live_w = v0 < d_v;
   bf16x8 wf[kUpKs];
-  const uint16_t* wrow = W_UV + ((int64_t)head * d_v + v0 + r) * kLat + 8 * g;
+  {
+    const uint16_t* wrow = W_UV + ((int64_t)head * d_v + (live_w ? v0 : 0) + r) * kLat + 8 * g;
 #pragma unroll
-  for (int ks = 0; ks < kUpKs; ks++) wf[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
+    for (int ks = 0; ks < kUpKs; ks++) wf[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
+  }
   for (int32_t b0 = 0; b0 < B; b0 += 32) {
-    const int32_t b = b0 + r;
-    const bool live = b < B;
-    const float* orow = o_lat + ((int64_t)(live ? b : 0) * h + head) * kLat + 8 * g;
+    if (b0 > 0) __syncthreads();  // the previous stage has been read
+    float4 x[kUpStage];
+#pragma unroll
+    for (int i = 0; i < kUpStage; i++) {
+      const int idx = tid + 64 * kUpWaves * i, row = idx >> 7, c4 = idx & 127;
+      const int32_t b = b0 + row;
+      x[i] = b < B ? *reinterpret_cast<const float4*>(o_lat + ((int64_t)b * h + head) * kLat + 4 * c4)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < kUpStage; i++) {
+      const int idx = tid + 64 * kUpWaves * i, row = idx >> 7, c4 = idx & 127;
+      const f32x4 v = {x[i].x, x[i].y, x[i].z, x[i].w};
+      const f32x2 v01 = {v[0], v[1]}, v23 = {v[2], v[3]};
+      const bf16x2 h01 = __builtin_convertvector(v01, bf16x2);
+      const bf16x2 h23 = __builtin_convertvector(v23, bf16x2);
+      const bf16x2 l01 = __builtin_convertvector(v01 - __builtin_convertvector(h01, f32x2), bf16x2);
+      const bf16x2 l23 = __builtin_convertvector(v23 - __builtin_convertvector(h23, f32x2), bf16x2);
+      const int off = row * 1024 + (((c4 >> 1) ^ up_swz(row)) << 4) + (c4 & 1) * 8;
+      const u32x2 hv = {__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+      const u32x2 lv = {__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+      *reinterpret_cast<u32x2*>(os[0] + off) = hv;
+      *reinterpret_cast<u32x2*>(os[1] + off) = lv;
+    }
+    __syncthreads();
+    if (!live_w) continue;
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kUpKs; ks++) {
-      f32x8 x = *reinterpret_cast<const f32x8*>(orow + 16 * ks);
-      if (!live) x = f32x8{};
-      const bf16x8 hi = __builtin_convertvector(x, bf16x8);
-      const bf16x8 lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), bf16x8);
+      const int off = r * 1024 + (((2 * ks + g) ^ up_swz(r)) << 4);
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(os[0] + off);
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(os[1] + off);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[ks], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[ks], acc, 0, 0, 0);
     }
@@ -65,59 +101,127 @@ __global__ __launch_bounds__(64) void up_project_mfma_kernel(const float* __rest
 // Work group = (head, 128 latent columns), four waves of 32 columns each.  The
 // W_UK rows of the group (d_nope x 128 bf16) are staged in LDS with the
 // 16-byte chunk index XOR-swizzled by the row; the MFMA B operand (8
-// consecutive rows n of one column) comes from the transposing LDS read.
+// consecutive rows n of one column) comes from the transposing LDS read.  All
+// global loads of a work group are issued before the first is waited for.
+//
+// The first kPlanGroups work groups of the launch run the split planner
+// instead (plan_block), which needs no result of the absorption, so that the
+// two latency-bound steps share one launch.
 constexpr int kAbsCols = 128;
+constexpr int kAbsColGroups = kLat / kAbsCols;
 constexpr int kAbsMaxN = 128;         // d_nope of the fast path (LDS 32 KiB)
+constexpr int kAbsStage = kAbsMaxN * 16 / 256;  // 16-byte staging loads per thread
+constexpr int kAbsKs = kAbsMaxN / 16;           // MFMA k-steps
 
 __device__ inline int abs_swz(int row) { return row & 15; }
+
+struct PlanArgs {
+  int32_t groups;  // planning work groups at the start of the launch (0: none)
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t max_blocks, P, num_blocks;
+  int32_t* cu_tiles;
+  int32_t* tiles;
+};
 
 template <int OT>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ W_UK,
                                                           void* __restrict__ q_lat, int32_t B,
-                                                          int32_t h, int32_t d_n, int32_t d_r) {
+                                                          int32_t h, int32_t d_n, int32_t d_r,
+                                                          PlanArgs pl) {
   __shared__ __attribute__((aligned(16))) char ws[kAbsMaxN * kAbsCols * 2];
-  const int32_t head = blockIdx.x;
-  const int32_t c0 = blockIdx.y * kAbsCols;
+  static_assert(sizeof(PlanShared) <= sizeof(ws), "planner LDS");
+  if ((int32_t)blockIdx.x < pl.groups) {
+    plan_block(pl.seq_lens, pl.block_table, B, pl.max_blocks, pl.P, pl.num_blocks, pl.cu_tiles,
+               pl.tiles, blockIdx.x, pl.groups, *reinterpret_cast<PlanShared*>(ws));
+    return;
+  }
+  const int32_t id = blockIdx.x - pl.groups;
+  const int32_t head = id / kAbsColGroups;
+  const int32_t cgrp = id % kAbsColGroups;
+  const int32_t c0 = cgrp * kAbsCols;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int32_t dq = d_n + d_r, dl = kLat + d_r;
+  const int g = lane >> 5, r = lane & 31;
+  const int nks = d_n / 16;
   // stage W_UK[head][0:d_n][c0:c0+128]: rows of 256 B, 16 chunks of 16 B
-  for (int idx = tid; idx < d_n * 16; idx += 256) {
-    const int row = idx >> 4, ch = idx & 15;
-    const uint4 v = *reinterpret_cast<const uint4*>(W_UK + ((int64_t)head * d_n + row) * kLat + c0 + 8 * ch);
-    *reinterpret_cast<uint4*>(ws + row * 256 + ((ch ^ abs_swz(row)) << 4)) = v;
+  // (loads are unconditional, from clamped addresses, so that none waits on a branch)
+  uint4 wv[kAbsStage];
+#pragma unroll
+  for (int i = 0; i < kAbsStage; i++) {
+    const int idx = tid + 256 * i, row = min(idx >> 4, d_n - 1), ch = idx & 15;
+    wv[i] = *reinterpret_cast<const uint4*>(W_UK + ((int64_t)head * d_n + row) * kLat + c0 + 8 * ch);
+  }
+  // q_nope fragments of a block of 32 sequences (rows past B are zeroed where
+  // they are used)
+  bf16x8 qa[kAbsKs];
+  auto load_q = [&](int32_t b0) {
+    const int32_t b = b0 + r;
+    const uint16_t* qrow = q + ((int64_t)(b < B ? b : 0) * h + head) * dq + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kAbsKs; ks++)
+      qa[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * min(ks, nks - 1));
+  };
+  load_q(0);
+  // rows past d_n repeat row d_n - 1 (same value, same place)
+#pragma unroll
+  for (int i = 0; i < kAbsStage; i++) {
+    const int idx = tid + 256 * i, row = min(idx >> 4, d_n - 1), ch = idx & 15;
+    *reinterpret_cast<uint4*>(ws + row * 256 + ((ch ^ abs_swz(row)) << 4)) = wv[i];
   }
   // the rope part of the absorbed query is q_rope copied (once per head)
-  if (blockIdx.y == 0) {
-    for (int32_t i = tid; i < B * d_r; i += 256) {
-      const int32_t b = i / d_r, k = i % d_r;
-      store_elem<OT>(q_lat, ((int64_t)b * h + head) * dl + kLat + k,
-                     load_elem<MLA_BF16>(q, ((int64_t)b * h + head) * dq + d_n + k));
+  if (cgrp == 0 && OT == MLA_BF16 && d_r % 8 == 0) {
+    const int32_t per = d_r / 8;  // 16-byte pieces per row
+    for (int32_t i = tid; i < B * per; i += 256) {
+      const int32_t b = i / per, k = 8 * (i % per);
+      const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * h + head) * dq + d_n + k);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(q_lat) + ((int64_t)b * h + head) * dl +
+                                kLat + k) = v;
+    }
+  } else if (cgrp == 0) {
+    for (int32_t i0 = 0; i0 < B * d_r; i0 += 4 * 256) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int32_t i = i0 + u * 256 + tid;
+        if (i < B * d_r)
+          v[u] = load_elem<MLA_BF16>(q, ((int64_t)(i / d_r) * h + head) * dq + d_n + i % d_r);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int32_t i = i0 + u * 256 + tid;
+        if (i < B * d_r)
+          store_elem<OT>(q_lat, ((int64_t)(i / d_r) * h + head) * dl + kLat + i % d_r, v[u]);
+      }
     }
   }
   __syncthreads();
-  const int g = lane >> 5, r = lane & 31;
   const int j16 = lane & 15, grp = lane >> 4, e = j16 >> 2, qd = j16 & 3;
   const int cw = 32 * wave;                      // this wave's columns within the group
   const int col_in = cw + 16 * (grp & 1) + 4 * qd;
   const int chunk = col_in >> 3, hoff = (col_in & 7) * 2;
-  const int nks = d_n / 16;
-  for (int32_t b0 = 0; b0 < B; b0 += 32) {
-    const int32_t b = b0 + r;
-    const bool live = b < B;
-    const uint16_t* qrow = q + ((int64_t)(live ? b : 0) * h + head) * dq + 8 * g;
-    f32x16 acc = f32x16{};
-    for (int ks = 0; ks < nks; ks++) {
-      bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-      if (!live) a = __builtin_bit_cast(bf16x8, i16x8{});
+  bf16x8 bw[kAbsKs];
+#pragma unroll
+  for (int ks = 0; ks < kAbsKs; ks++) {
+    if (ks < nks) {
       const int row0 = 16 * ks + 8 * g + e, row1 = row0 + 4;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
           (lds_t*)ws + row0 * 256 + ((chunk ^ abs_swz(row0)) << 4) + hoff));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
           (lds_t*)ws + row1 * 256 + ((chunk ^ abs_swz(row1)) << 4) + hoff));
-      const bf16x8 bw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw, acc, 0, 0, 0);
+      bw[ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+  }
+  for (int32_t b0 = 0; b0 < B; b0 += 32) {
+    if (b0 > 0) load_q(b0);
+    const bool live = b0 + r < B;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kAbsKs; ks++)
+      if (ks < nks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            live ? qa[ks] : __builtin_bit_cast(bf16x8, i16x8{}), bw[ks], acc, 0, 0, 0);
     // D[m = sequence][n = column]: lane holds column c0 + cw + r
 #pragma unroll
     for (int j = 0; j < 16; j++) {
@@ -135,27 +239,31 @@ bool proj_mfma_supported(const mla_decode_params& p) {
 }
 
 hipError_t launch_absorb_mfma(const mla_decode_params& p, const void* q, const void* W_UK,
-                              void* q_lat, int32_t ot, hipStream_t s) {
-  const dim3 grid(p.num_heads, kLat / kAbsCols);
+                              void* q_lat, int32_t ot, const PlanRequest* plan, hipStream_t s) {
+  PlanArgs pl{};
+  if (plan)
+    pl = PlanArgs{kPlanGroups, plan->seq_lens, plan->block_table, p.max_blocks_per_seq,
+                  p.page_size, p.num_blocks, plan->cu_tiles, plan->tiles};
+  const dim3 grid(p.num_heads * kAbsColGroups + pl.groups);
   if (ot == MLA_BF16)
     hipLaunchKernelGGL((absorb_mfma_kernel<MLA_BF16>), grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(W_UK), q_lat,
-                       p.batch, p.num_heads, p.d_nope, p.d_rope);
+                       p.batch, p.num_heads, p.d_nope, p.d_rope, pl);
   else
     hipLaunchKernelGGL((absorb_mfma_kernel<MLA_F32>), grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(W_UK), q_lat,
-                       p.batch, p.num_heads, p.d_nope, p.d_rope);
+                       p.batch, p.num_heads, p.d_nope, p.d_rope, pl);
   return hipGetLastError();
 }
 
 hipError_t launch_up_project_mfma(const mla_decode_params& p, const float* o_lat,
                                   const void* W_UV, void* out, hipStream_t s) {
-  const dim3 grid(p.num_heads, p.d_v / 32);
+  const dim3 grid(p.num_heads, (p.d_v + 32 * kUpWaves - 1) / (32 * kUpWaves));
   if (p.out_dtype == MLA_BF16)
-    hipLaunchKernelGGL((up_project_mfma_kernel<MLA_BF16>), grid, dim3(64), 0, s, o_lat,
+    hipLaunchKernelGGL((up_project_mfma_kernel<MLA_BF16>), grid, dim3(64 * kUpWaves), 0, s, o_lat,
                        static_cast<const uint16_t*>(W_UV), out, p.batch, p.num_heads, p.d_v);
   else
-    hipLaunchKernelGGL((up_project_mfma_kernel<MLA_F32>), grid, dim3(64), 0, s, o_lat,
+    hipLaunchKernelGGL((up_project_mfma_kernel<MLA_F32>), grid, dim3(64 * kUpWaves), 0, s, o_lat,
                        static_cast<const uint16_t*>(W_UV), out, p.batch, p.num_heads, p.d_v);
   return hipGetLastError();
 }

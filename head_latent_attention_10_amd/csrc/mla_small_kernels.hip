@@ -4,80 +4,23 @@
 namespace mla {
 
 // ------------------------------------------------------------------ planner
-// One work group scans the batch, cu_tiles[b] = sum_{j<b} ceil(T_j / kTile),
-// then writes the descriptor of every tile (one thread per tile).
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ seq_lens,
-                                                     const int32_t* __restrict__ block_table,
-                                                     int32_t B, int32_t max_blocks, int32_t P,
-                                                     int32_t num_blocks,
-                                                     int32_t* __restrict__ cu_tiles,
-                                                     int32_t* __restrict__ tiles) {
-  __shared__ int32_t buf[1024];
-  __shared__ int32_t cu_s[kPlanMaxBatch + 1];
-  __shared__ int32_t len_s[kPlanMaxBatch];
-  __shared__ int32_t carry;
-  const int tid = threadIdx.x;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int32_t base = 0; base < B; base += 1024) {
-    int32_t b = base + tid;
-    int32_t n = 0;
-    if (b < B) {
-      const int32_t T = seq_len_clamped(seq_lens, b, max_blocks, P);
-      len_s[b] = T;
-      n = (T + kTile - 1) / kTile;
-    }
-    buf[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-      int32_t v = tid >= off ? buf[tid - off] : 0;
-      __syncthreads();
-      buf[tid] += v;
-      __syncthreads();
-    }
-    if (b < B) {
-      cu_s[b + 1] = carry + buf[tid];
-      cu_tiles[b + 1] = carry + buf[tid];
-    }
-    __syncthreads();
-    if (tid == 1023) carry += buf[1023];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    cu_tiles[0] = 0;
-    cu_s[0] = 0;
-  }
-  __syncthreads();
-  // descriptors: tile t belongs to the last sequence b with cu_s[b] <= t
-  // (sequences without tiles share their start with the next one)
-  const int32_t n_total = cu_s[B];
-  const bool one_page = P % kTile == 0;
-#pragma unroll 4
-  for (int32_t t = tid; t < n_total; t += 1024) {
-    int32_t lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (cu_s[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int32_t b = lo, T = len_s[b];
-    const int32_t t0 = (t - cu_s[b]) * kTile;
-    const int32_t nv = min(kTile, T - t0);
-    int32_t blk = -1, off = 0;
-    if (one_page) {
-      const int32_t raw = block_table[(int64_t)b * max_blocks + t0 / P];
-      blk = raw < 0 ? 0 : (raw >= num_blocks ? num_blocks - 1 : raw);
-      off = t0 % P;
-    }
-    reinterpret_cast<int4*>(tiles)[t] = make_int4(blk, b, t0, tile_word(nv, t0 + kTile >= T, off));
-  }
+// kPlanGroups work groups running plan_block.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seq_lens,
+                                                             const int32_t* __restrict__ block_table,
+                                                             int32_t B, int32_t max_blocks, int32_t P,
+                                                             int32_t num_blocks,
+                                                             int32_t* __restrict__ cu_tiles,
+                                                             int32_t* __restrict__ tiles) {
+  __shared__ PlanShared sh;
+  plan_block(seq_lens, block_table, B, max_blocks, P, num_blocks, cu_tiles, tiles, blockIdx.x,
+             gridDim.x, sh);
 }
 
 hipError_t launch_plan(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
                        int32_t max_blocks, int32_t P, int32_t num_blocks, int32_t* cu_tiles,
                        int32_t* tiles, hipStream_t s) {
-  if (B > kPlanMaxBatch) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, seq_lens, block_table, B, max_blocks,
-                     P, num_blocks, cu_tiles, tiles);
+  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGroups), dim3(kPlanThreads), 0, s, seq_lens,
+                     block_table, B, max_blocks, P, num_blocks, cu_tiles, tiles);
   return hipGetLastError();
 }
 
@@ -204,9 +147,13 @@ static hipError_t absorb_t(const mla_decode_params& p, const void* q, const void
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 hipError_t launch_absorb(const mla_decode_params& p, const void* q, const void* W_UK, void* q_lat,
-                         int32_t ot, hipStream_t s) {
-  if (proj_mfma_supported(p) && aligned16(q) && aligned16(W_UK) && (p.d_nope + p.d_rope) % 8 == 0)
-    return launch_absorb_mfma(p, q, W_UK, q_lat, ot, s);
+                         int32_t ot, const PlanRequest* plan, bool* planned, hipStream_t s) {
+  if (planned) *planned = false;
+  if (proj_mfma_supported(p) && aligned16(q) && aligned16(W_UK) && aligned16(q_lat) &&
+      (p.d_nope + p.d_rope) % 8 == 0) {
+    if (planned) *planned = plan != nullptr;
+    return launch_absorb_mfma(p, q, W_UK, q_lat, ot, plan, s);
+  }
   const int32_t qt = p.q_dtype, wt = p.weight_dtype;
 #define MLA_ABSORB(Q, W, O) \
   if (qt == Q && wt == W && ot == O) return absorb_t<Q, W, O>(p, q, W_UK, q_lat, s);
@@ -331,8 +278,113 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
   }
 }
 
+// The same merge over fragment-major partials (frag_offset; 512 latent values,
+// heads a multiple of 32).  Work group = (sequence, 32-head block, 32-value
+// latent block); a thread owns one 16-byte piece (4 latent values of one
+// head), so each wave reads 1 KiB contiguous per slot.  Slots are taken in
+// chunks of 32: a thread first issues the loads of its piece in every slot of
+// the chunk, then the chunk's weights are formed in LDS (running maximum per
+// head across chunks) while the loads are in flight.
+constexpr int kFragLat = 512;
+constexpr int kFragChunk = 32;
+
+__global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __restrict__ o_lat) {
+  __shared__ float s_w[kFragChunk][32];
+  __shared__ int32_t s_own[kFragChunk];
+  __shared__ float s_red[8][32];
+  __shared__ float s_M[32], s_alpha[32];
+  const int32_t b = blockIdx.x, hblk = blockIdx.y, mdg = blockIdx.z;
+  const int tid = threadIdx.x, jj = tid >> 6, lane = tid & 63;
+  const int r = lane & 31;                 // head of this thread's piece
+  const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of this thread's weights
+  const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
+  float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * a.h + hblk * 32 + r) * kFragLat + d);
+  const int32_t n_total = load_ro(a.cu_tiles, a.B);
+  const int32_t first = load_ro(a.cu_tiles, b), last = load_ro(a.cu_tiles, b + 1) - 1;
+  if (last < first) {
+    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int32_t g_lo = split_owner(n_total, a.splits, first);
+  const int32_t n_cand = split_owner(n_total, a.splits, last) - g_lo + 1;
+  const int64_t slot_stride = (int64_t)a.h * kFragLat;
+  const float* src = a.part_o + (int64_t)(g_lo + b) * slot_stride + frag_offset(hblk, mdg, jj, lane);
+  const float* lse = a.part_lse + (int64_t)(g_lo + b) * a.h + hblk * 32 + wr;
+  if (tid < 32) s_M[tid] = -INFINITY;
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int32_t c0 = 0; c0 < n_cand; c0 += kFragChunk) {
+    const int32_t n = min(kFragChunk, n_cand - c0);
+    // splits in the range that own no tile wrote nothing: weight 0
+    if (tid < kFragChunk) {
+      const int32_t gg = g_lo + c0 + tid;
+      s_own[tid] = tid < n && split_begin(n_total, a.splits, gg) <
+                                  split_begin(n_total, a.splits, gg + 1);
+    }
+    __syncthreads();
+    float4 v[kFragChunk];
+#pragma unroll
+    for (int k = 0; k < kFragChunk; k++)
+      v[k] = s_own[k] ? *reinterpret_cast<const float4*>(src + (int64_t)(c0 + k) * slot_stride)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    float l4[kFragChunk / 8];
+    float mc = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kFragChunk / 8; u++) {
+      const int k = wk + 8 * u;
+      l4[u] = s_own[k] ? lse[(int64_t)(c0 + k) * a.h] : -INFINITY;
+      mc = fmaxf(mc, l4[u]);
+    }
+    s_red[wk][wr] = mc;
+    __syncthreads();
+    if (tid < 32) {
+      float m = s_red[0][tid];
+      for (int i = 1; i < 8; i++) m = fmaxf(m, s_red[i][tid]);
+      const float m_old = s_M[tid], m_new = fmaxf(m_old, m);
+      s_alpha[tid] = m_old == -INFINITY ? 0.f : expf(m_old - m_new);
+      s_M[tid] = m_new;
+    }
+    __syncthreads();
+    {
+      const float m = s_M[wr];
+      float ws = 0.f;
+#pragma unroll
+      for (int u = 0; u < kFragChunk / 8; u++) {
+        const float w = l4[u] == -INFINITY ? 0.f : expf(l4[u] - m);
+        s_w[wk + 8 * u][wr] = w;
+        ws += w;
+      }
+      wsum = wsum * s_alpha[wr] + ws;
+    }
+    __syncthreads();
+    const float al = s_alpha[r];
+    acc.x *= al; acc.y *= al; acc.z *= al; acc.w *= al;
+#pragma unroll
+    for (int k = 0; k < kFragChunk; k++) {
+      const float w = s_w[k][r];
+      acc.x = fmaf(w, v[k].x, acc.x);
+      acc.y = fmaf(w, v[k].y, acc.y);
+      acc.z = fmaf(w, v[k].z, acc.z);
+      acc.w = fmaf(w, v[k].w, acc.w);
+    }
+    __syncthreads();
+  }
+  s_red[wk][wr] = wsum;
+  __syncthreads();
+  float W = 0.f;
+  for (int i = 0; i < 8; i++) W += s_red[i][r];
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
 hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B, a.h), dim3(kCombThreads), 0, s, a, o_lat);
+  if (a.frag_layout) {
+    if (a.d_c != kFragLat || a.h % 32 || a.streams != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_frag_kernel, dim3(a.B, a.h / 32, kFragLat / 32), dim3(256), 0, s,
+                       a, o_lat);
+  } else {
+    hipLaunchKernelGGL(combine_kernel, dim3(a.B, a.h), dim3(kCombThreads), 0, s, a, o_lat);
+  }
   return hipGetLastError();
 }
 

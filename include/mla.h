@@ -68,7 +68,8 @@ typedef enum {
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
 
 typedef struct {
-  int32_t batch;              /* B, 1..16384                                 */
+  int32_t batch;              /* B >= 1, with B x ceil(max_blocks_per_seq x
+                               * page_size / 32) below 2^31                  */
   int32_t num_heads;          /* h  >= 1                                     */
   int32_t d_nope;             /* width of q_nope, rows of W_UK[i]            */
   int32_t d_rope;             /* width of q_rope and k_rope (may be 0)       */

@@ -59,7 +59,7 @@ def test_workspace_size_without_device():
 
 @pytest.mark.parametrize("bad,status", [
     (dict(batch=0), _lib.MLA_ERR_INVALID_ARG),
-    (dict(batch=16385), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(batch=65536, max_blocks_per_seq=1 << 14), _lib.MLA_ERR_UNSUPPORTED),  # 2^31 tiles
     (dict(num_heads=-1), _lib.MLA_ERR_INVALID_ARG),
     (dict(page_size=0), _lib.MLA_ERR_INVALID_ARG),
     (dict(page_size=5000), _lib.MLA_ERR_INVALID_ARG),
