@@ -43,16 +43,18 @@
 // per latent row, eight rope rows per instruction) two steps ahead of use.
 // The 16-byte chunk index is XOR-swizzled with a permutation of the row's low
 // four bits, which keeps both the row reads of the score product and the
-// 4-row transposing reads of the value product free of bank conflicts.
+// 4-row transposing reads of the value product free of bank conflicts (64
+// four-byte banks).
 //
-// Step i (three work-group barriers):
+// Step i (two work-group barriers):
 //   score waves kh = 1 wait for their loads of step i; barrier
-//   score waves: partial S(i) | value waves: read P(i-1) and the rescale
-//   factors, first row blocks of O += C(i-1) P(i-1)
+//   score waves: partial S(i) | value waves: take P(i-1) and the rescale
+//   factors
 //   barrier
 //   score waves kh = 0: merge partial scores, softmax, publish P(i) |
-//   kh = 1: issue the loads of step i+2 | value waves: remaining row blocks
-//   barrier
+//   kh = 1: issue the loads of step i+2 | value waves: O += C(i-1) P(i-1)
+// (the first barrier of step i+1 orders the softmax of step i before its
+// consumers).
 //
 // Softmax rescaling is lazy: after the first four steps of a sequence segment
 // (which track the exact maximum, so an early dominant token gets weight
@@ -103,17 +105,16 @@ struct Shape {
   static constexpr int NP = HB == 2 ? 4 : 2;    // value waves
   static constexpr int NW = NQ + NP;
   static constexpr int MDP = kDc / 32 / NP;     // 32-row output blocks per value wave
-#ifndef MLA_MDA
-  static constexpr int MDA = MDP / 4;           // of which computed before the softmax barrier
-#else
-  static constexpr int MDA = MLA_MDA;
-#endif
   static constexpr int LDS = kRing + kWinBytes + HB * (kXBytes + kPBytes) + HB * 32 * 4 * 2 + 16;
 };
 
-// Chunk swizzles: row bits (b3 b2 b1 b0) -> chunk bits (b2 b1 b0 b3) for latent
-// rows; rope rows share 256-byte bank lines in pairs.
-__device__ inline int swz_c(int r) { return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1); }
+// Chunk swizzles (LDS of 64 four-byte banks, one 256-byte bank line).  Latent
+// rows: row bits (b3 b2 b1 b0) -> chunk bits (b1 b0 b3 b2), so 16 consecutive
+// rows read at one chunk index hit 16 different chunks of the bank line (the
+// score product's 16-byte row reads), and so do the 4-row groups of the
+// transposing reads (rows 4m..4m+3 map to chunk bits b3 b2 = 0..3 and each lane
+// group adds its own chunk bits b1 b0).  Rope rows share bank lines in pairs.
+__device__ inline int swz_c(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ inline int swz_r(int r) { return (r >> 1) & 7; }
 
 // Work-group barrier that only waits for this wave's LDS traffic.  Unlike
@@ -303,7 +304,7 @@ void attend_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
   lds_t* ring = (lds_t*)smem;
   lds_t* win = ring + kRing;                        // [2][kWin] tile descriptors
-  lds_t* xbuf = win + kWinBytes;                    // [HB][64 lanes][16 floats]
+  lds_t* xbuf = win + kWinBytes;                    // [HB][4][64 lanes][4 floats]
   lds_t* pbuf = xbuf + HB * kXBytes;                // [HB][2 k-steps][64 lanes][16 B]
   float* s_alpha = (float*)(smem + kRing + kWinBytes + HB * (kXBytes + kPBytes));  // [HB][32]
   float* s_invl = s_alpha + HB * 32;                // [HB][32]
@@ -361,7 +362,7 @@ void attend_mfma_kernel(AttnArgs a) {
     load_q(cur.b);
     float m_run = -INFINITY, l_run = 0.f;
     int32_t seg_step = 0;  // steps of the current segment seen so far
-    lds_t* xb = xbuf + hb * kXBytes + lane * 64;
+    lds_t* xb = xbuf + hb * kXBytes + lane * 16;
     lds_t* pb = pbuf + hb * kPBytes + lane * 16;
     // the kh = 1 waves issue the loads: HB loader waves of kLoadsPerStep / HB
     Loader<HB> ld;
@@ -400,11 +401,14 @@ void attend_mfma_kernel(AttnArgs a) {
         if (kh == 1) {
 #pragma unroll
           for (int q = 0; q < 4; q++)
-            *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 16 * q) =
+            *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q) =
                 f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
         }
       }
       wg_barrier();
+      // the next step's descriptor, read early so that its latency is hidden
+      Tile nxt{};
+      if (i + 1 < n) nxt = read_tile(win, i + 1);
       if (kh == 1) {
         // loads of step i+2, into the stage last read in step i-2, issued
         // while the partner wave runs the softmax
@@ -412,7 +416,7 @@ void attend_mfma_kernel(AttnArgs a) {
       } else if (valid) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          const f32x4 o = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 16 * q);
+          const f32x4 o = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q);
           s[4 * q] += o[0];
           s[4 * q + 1] += o[1];
           s[4 * q + 2] += o[2];
@@ -480,13 +484,9 @@ void attend_mfma_kernel(AttnArgs a) {
           }
         }
       }
-      if (kh == 1)
-        wg_barrier_nowait();
-      else
-        wg_barrier();
       if (!valid) break;  // that was the value waves' final step
       if (i + 1 < n) {
-        cur = read_tile(win, i + 1);
+        cur = nxt;
         if (seg_last) {
           load_q(cur.b);
           m_run = -INFINITY;
@@ -498,7 +498,6 @@ void attend_mfma_kernel(AttnArgs a) {
   } else {
     // ================================================================ value waves
     constexpr int MDP = S::MDP;
-    constexpr int kMdFirst = S::MDA;  // row blocks computed before the softmax barrier
     const int pw_id = wave - S::NQ;
     const int j16 = lane & 15, grp = lane >> 4, e = j16 >> 2, qd = j16 & 3;
     f32x16 o[MDP][HB];
@@ -552,7 +551,7 @@ void attend_mfma_kernel(AttnArgs a) {
       };
       if (have) {
         // everything published with the step being consumed is read now: the
-        // score waves overwrite it after the next barrier
+        // softmax overwrites it after the next barrier
 #pragma unroll
         for (int hb = 0; hb < HB; hb++) {
           if (s_flag[hb]) {
@@ -566,11 +565,10 @@ void attend_mfma_kernel(AttnArgs a) {
             pf[hb][kk] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
                 pbuf + hb * kPBytes + (kk * 64 + lane) * 16);
         }
-        products(std::integral_constant<int, 0>{}, std::integral_constant<int, kMdFirst>{});
       }
       wg_barrier();
       if (have) {
-        products(std::integral_constant<int, kMdFirst>{}, std::integral_constant<int, MDP>{});
+        products(std::integral_constant<int, 0>{}, std::integral_constant<int, MDP>{});
         if (last) {
           const int64_t slot = (int64_t)(g + prev.b);
 #pragma unroll
@@ -591,7 +589,6 @@ void attend_mfma_kernel(AttnArgs a) {
           }
         }
       }
-      wg_barrier();
     }
   }
 }
