@@ -58,7 +58,7 @@ mla_status validate(const mla_decode_params* p) {
                 p->q_dtype, p->cache_dtype, p->rope_dtype, p->weight_dtype, p->out_dtype);
   if (p->d_nope > 1024 || p->d_rope > 1024 || p->d_v > 4096)
     return fail(MLA_ERR_UNSUPPORTED, "d_nope <= 1024, d_rope <= 1024 and d_v <= 4096 required");
-  if (!mla::mfma_supported(*p) && p->d_latent > 1024)
+  if (!mla::mfma_any_supported(*p) && p->d_latent > 1024)
     return fail(MLA_ERR_UNSUPPORTED, "d_latent %d above 1024 outside the matrix-core shape",
                 p->d_latent);
   return MLA_OK;
@@ -76,11 +76,13 @@ struct Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 // Token splits.  The matrix-core kernel serves a split's heads with HG work
 // groups that must share an XCD, which needs the split count to be a multiple
 // of 8 when HG > 1; by default one work group runs per compute unit.
 mla_status resolve_splits(const mla_decode_params& p, int32_t* splits) {
-  const int32_t hg = mla::mfma_supported(p) ? mla::mfma_head_groups(p.num_heads) : 1;
+  const int32_t hg = mla::mfma_any_supported(p) ? mla::mfma_head_groups(p.num_heads) : 1;
   int32_t n = p.num_splits;
   if (n <= 0) {
     int dev = 0, cus = 0;
@@ -99,7 +101,7 @@ mla_status resolve_splits(const mla_decode_params& p, int32_t* splits) {
 mla_status layout(const mla_decode_params& p, Layout* L) {
   mla_status st = resolve_splits(p, &L->splits);
   if (st != MLA_OK) return st;
-  L->streams = mla::mfma_supported(p) ? mla::mfma_streams(p.num_heads) : 1;
+  L->streams = mla::mfma_any_supported(p) ? mla::mfma_streams(p.num_heads) : 1;
   L->slots = ((int64_t)L->splits + p.batch) * L->streams;
   const size_t B = p.batch, h = p.num_heads, dc = p.d_latent, dr = p.d_rope;
   size_t off = 0;
@@ -170,7 +172,12 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.num_blocks = p.num_blocks;
   a.splits = L.splits;
   a.streams = L.streams;
-  a.frag_layout = mla::mfma_supported(p) ? 1 : 0;
+  // matrix-core kernels read 16-byte pieces of the pools; other pointers go
+  // to the generic kernel (same workspace layout, row-major partials)
+  const bool aligned = aligned16(c_kv) && aligned16(k_rope) && aligned16(c_kv_scale);
+  const bool use_bf16 = aligned && mla::mfma_supported(p);
+  const bool use_fp8 = aligned && mla::mfma_fp8_supported(p);
+  a.frag_layout = use_bf16 || use_fp8 ? 1 : 0;
   a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
 
   hipError_t e = hipSuccess;
@@ -181,8 +188,10 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
     if (e != hipSuccess) return hip_fail(e, "plan launch");
   }
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (mla::mfma_supported(p))
+  if (use_bf16)
     e = mla::launch_attend_mfma(a, p.cache_dtype, s);
+  else if (use_fp8)
+    e = mla::launch_attend_fp8(a, s);
   else
     e = mla::launch_attend_simt(a, p.cache_dtype, p.rope_dtype, absorbed_dtype(p), s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");

@@ -1,0 +1,567 @@
+// Matrix-core split attention over an fp8 latent cache (gfx950).
+//
+// Shape: d_c = 512 latent values stored as OCP E4M3FN bytes with one fp32
+// scale per cached token (the row's value is scale * e4m3), d_r = 64 bf16 rope
+// values per token, heads a multiple of 32, bf16 absorbed query.
+//
+// The work decomposition, split plan, tile descriptors, head groups and the
+// two-barrier step are those of the bf16 kernel (mla_attend_mfma.hip); what
+// differs is how the 8-bit latent tile is consumed:
+//
+//  * Scores.  S^T[t, i] = scale_t * sum_d e4m3[t, d] q[i, d] + rope term.  The
+//    latent part runs on the fp8 matrix core (32x32x64, both operands E4M3):
+//    the A operand is the cached bytes as they are, the B operand is the
+//    absorbed query split into two E4M3 terms, q * 2^k = hi + lo with
+//    hi = e4m3(q * 2^k) and lo = e4m3(q * 2^k - hi), where 2^k (one power of two
+//    per head and key half) brings the largest |q| into [128, 256).  The two
+//    products share the accumulator; the split keeps about 8 significant bits
+//    of q (one term would keep 4).  The result is multiplied by 2^-k (exact)
+//    and by the token's scale.  The rope part is bf16 as in the bf16 kernel.
+//  * Values.  O^T[d, i] += sum_t e4m3[t, d] (p[i, t] * scale_t): the token
+//    scale is folded into the bf16 weight, and the latent tile is read with the
+//    8-bit transposing LDS read (8 tokens of one latent column per lane) and
+//    widened to bf16 exactly (every E4M3 value is a bf16 value), feeding the
+//    bf16 matrix core.
+//  * The per-token scales of a step are loaded from global memory by the
+//    softmax waves at the end of the previous step and used after the score
+//    products (these waves issue no direct-to-LDS loads, so the wait for the
+//    scales never waits for the tile prefetch); the kh = 1 waves hand over
+//    their latent and rope partial scores separately and the softmax wave
+//    applies the scales.
+//
+// LDS ring: six stages of 32 latent rows of 512 B plus 32 rope rows of 128 B
+// (20 KiB), loaded four steps ahead.  The 16-byte chunk index of a latent row
+// is XOR-swizzled with a permutation of the row's low four bits chosen so that
+// the 16-row reads of the score product and the 8-row transposing reads of the
+// value product both spread over the 64 banks.
+#include "mla_mfma_util.hpp"
+
+namespace mla {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDc8 = 512, kDr8 = 64;
+constexpr int kStep8 = kTile;                         // tokens per pipeline step
+constexpr int kCRow8 = kDc8;                          // 512 bytes per latent row
+constexpr int kRRow8 = kDr8 * 2;                      // 128 bytes per rope row
+constexpr int kStageC8 = kStep8 * kCRow8;             // 16384
+constexpr int kStage8 = kStageC8 + kStep8 * kRRow8;   // 20480
+constexpr int kStages8 = 6;
+constexpr int kAhead8 = kStages8 - 2;                 // steps loaded ahead of use
+constexpr int kRing8 = kStages8 * kStage8;            // 122880
+constexpr int kLoadsPerStep8 = kStep8 / 2 + kStep8 / 8;  // 2 latent rows or 8 rope rows each
+constexpr int kBlocksHalf = 4;                        // 64-byte key blocks per score wave
+constexpr int kRopeKs = kDr8 / 16;                    // bf16 rope k-steps (kh = 1)
+constexpr int kX8Bytes = 2 * 64 * 64;                 // latent and rope partial scores
+constexpr int kP8Bytes = 2 * 64 * 16;
+constexpr float kLazy8 = 8.0f;
+constexpr int kExactSteps8 = 4;
+static_assert(kStep8 == 32, "the score and value products are laid out for 32-token steps");
+
+template <int HB>
+struct Shape8 {
+  static constexpr int NQ = 2 * HB;
+  static constexpr int NP = HB == 2 ? 4 : 2;
+  static constexpr int NW = NQ + NP;
+  static constexpr int MDP = kDc8 / 32 / NP;
+  static constexpr int LDS = kRing8 + kWinBytes + HB * (kX8Bytes + kP8Bytes) + HB * 32 * 4 * 2 + 16;
+};
+
+// Latent rows: row bits (b3 b2 b1 b0) -> chunk bits (b3 b1 b0 b2).
+__device__ inline int swz8(int r) { return ((r & 3) << 1) | (((r >> 3) & 1) << 3) | ((r >> 2) & 1); }
+__device__ inline int swz_r8(int r) { return (r >> 1) & 7; }
+
+// Direct-to-LDS loads of one step by the NL loader waves: latent instruction
+// q covers rows 2q and 2q+1 (lane l: row 2q + l/32, LDS chunk l%32), rope
+// instruction j covers rows 8j..8j+7.  Fast path as in the bf16 kernel; rows
+// past the end repeat the last valid token.
+template <int NL>
+struct StepIssue8 {
+  static constexpr int kLat = kStep8 / 2 / NL;
+  static constexpr int kRope = kStep8 / 8 / NL;
+  static constexpr int kPer = kLat + kRope;
+  static_assert(kPer * NL == kLoadsPerStep8, "uniform load counts");
+
+  __device__ static void issue(const AttnArgs& a, lds_t* stage, const Tile& d, int lw, int lane) {
+    const uint32_t st = (uint32_t)(uintptr_t)stage;
+    const int64_t base = (int64_t)d.blk * a.P + d.off;
+    if (d.blk >= 0 && d.nv == kStep8) {
+      const char* cb = static_cast<const char*>(a.c_kv) + base * kCRow8;
+      const char* rb = static_cast<const char*>(a.k_rope) + base * kRRow8;
+#pragma unroll
+      for (int m = 0; m < kLat; m++) {
+        const int q = lw + NL * m;
+        const int r = 2 * q + (lane >> 5);
+        dma16s(cb, (uint32_t)(r * kCRow8 + (((lane & 31) ^ swz8(r)) << 4)), st + q * 1024);
+      }
+#pragma unroll
+      for (int m = 0; m < kRope; m++) {
+        const int j = lw + NL * m;
+        const int r = 8 * j + (lane >> 3);
+        dma16s(rb, (uint32_t)(r * kRRow8 + (((lane & 7) ^ swz_r8(r)) << 4)), st + kStageC8 + j * 1024);
+      }
+      return;
+    }
+    const char* ckv = static_cast<const char*>(a.c_kv);
+    const char* krp = static_cast<const char*>(a.k_rope);
+    const int32_t rmax = d.nv - 1;
+#pragma unroll
+    for (int m = 0; m < kLat; m++) {
+      const int q = lw + NL * m;
+      const int r = 2 * q + (lane >> 5);
+      const int64_t slot = d.blk >= 0 ? base + min(r, rmax)
+                                      : phys_slot(a.block_table, d.b, d.t0 + min(r, rmax), a.P,
+                                                  a.max_blocks, a.num_blocks);
+      dma16(ckv + slot * kCRow8 + (((lane & 31) ^ swz8(r)) << 4), stage + q * 1024);
+    }
+#pragma unroll
+    for (int m = 0; m < kRope; m++) {
+      const int j = lw + NL * m;
+      const int r = 8 * j + (lane >> 3);
+      const int64_t slot = d.blk >= 0 ? base + min(r, rmax)
+                                      : phys_slot(a.block_table, d.b, d.t0 + min(r, rmax), a.P,
+                                                  a.max_blocks, a.num_blocks);
+      dma16(krp + slot * kRRow8 + (((lane & 7) ^ swz_r8(r)) << 4), stage + kStageC8 + j * 1024);
+    }
+  }
+};
+
+// Wait until at most `newer` batches of kPer loads issued after the awaited
+// one are outstanding.
+template <int kPer>
+__device__ inline void wait_batches(int newer) {
+  switch (newer) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<kPer>(); break;
+    case 2: wait_vmcnt<2 * kPer>(); break;
+    default: wait_vmcnt<3 * kPer>(); break;
+  }
+}
+
+// Load schedule of one loader wave: steps are loaded kAhead8 ahead.  Loader 0
+// refills the descriptor window w + 1 into the buffer of window w - 1 with the
+// loads of step kWin w + kAhead8 + 2, when the value waves (furthest behind,
+// then at step kWin w + 1) have left window w - 1.
+template <int NL>
+struct Loader8 {
+  static constexpr int kPerWave = StepIssue8<NL>::kPer;
+  static_assert(3 * kPerWave + 1 < 64, "vmcnt range");
+  static_assert(kAhead8 - 1 <= 3, "wait_batches cases");
+  int32_t next, n;
+
+  __device__ void issue_next(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
+                             int lane) {
+    constexpr int kRefill = kAhead8 + 2;
+    if (lw == 0 && next >= kWin + kRefill && next % kWin == kRefill && next + kWin - kRefill < n)
+      load_window(a, win, t_begin, t_begin + n, next / kWin + 1, lane);
+    const Tile d = read_tile(win, next);
+    StepIssue8<NL>::issue(a, ring + (next % kStages8) * kStage8, d, lw, lane);
+    next++;
+  }
+  __device__ void start(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int32_t steps,
+                        int lw, int lane) {
+    next = 0;
+    n = steps;
+    for (int s = 0; s < kAhead8 && next < n; s++) issue_next(a, ring, win, t_begin, lw, lane);
+  }
+  // before step i: its loads are complete (later batches may be in flight)
+  __device__ void wait_for(int32_t i) const { wait_batches<kPerWave>(next - i - 1); }
+};
+
+// fp32 pair -> two E4M3 bytes (round to nearest even) in the low half of a word.
+__device__ inline uint32_t e4m3_pair(float x, float y) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, y, 0, false) & 0xffffu;
+}
+
+template <int HB>
+__global__ __attribute__((amdgpu_flat_work_group_size(Shape8<HB>::NW * 64, Shape8<HB>::NW * 64)))
+void attend_fp8_kernel(AttnArgs a) {
+  using S = Shape8<HB>;
+  __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
+  lds_t* ring = (lds_t*)smem;
+  lds_t* win = ring + kRing8;                       // [2][kWin] tile descriptors
+  lds_t* xbuf = win + kWinBytes;                    // [HB][latent, rope][4][64 lanes][16 B]
+  lds_t* pbuf = xbuf + HB * kX8Bytes;               // [HB][2 k-steps][64 lanes][16 B]
+  float* s_alpha = (float*)(smem + kRing8 + kWinBytes + HB * (kX8Bytes + kP8Bytes));  // [HB][32]
+  float* s_invl = s_alpha + HB * 32;                // [HB][32]
+  int* s_flag = (int*)(s_invl + HB * 32);           // [HB]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g32 = lane >> 5;
+
+  const int32_t HG = a.h / (32 * HB);
+  int32_t g, hg;
+  if (HG > 1) {
+    const int32_t L = blockIdx.x, span = 8 * HG;
+    hg = (L % span) / 8;
+    g = (L / span) * 8 + (L % 8);
+  } else {
+    hg = 0;
+    g = blockIdx.x;
+  }
+  if (g >= a.splits) return;
+  const int32_t n_total = load_ro(a.cu_tiles, a.B);
+  if (n_total == 0) return;
+  const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);
+  const int32_t t_end = (int32_t)split_begin(n_total, a.splits, g + 1);
+  if (t_begin >= t_end) return;
+  const int32_t n = t_end - t_begin;
+
+  if (wave == 1) {
+    load_window(a, win, t_begin, t_end, 0, lane);
+    if (n > kWin) load_window(a, win, t_begin, t_end, 1, lane);
+    wait_vmcnt<0>();
+  }
+  wg_barrier();
+  const float sm = a.sm_scale_log2;
+
+  if (wave < S::NQ) {
+    // ================================================================ score waves
+    const int hb = wave >> 1, kh = wave & 1;
+    const int32_t head = hg * 32 * HB + hb * 32 + (lane & 31);
+    const int row = lane & 31;
+    // the absorbed query as two E4M3 terms per 64-byte key block, times 2^k
+    i32x8 qhi[kBlocksHalf], qlo[kBlocksHalf];
+    bf16x8 qr[kRopeKs];
+    float qinv = 1.f;  // 2^-k
+    auto load_q = [&](int32_t bb) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc8 + kDr8);
+      // lane half g32 holds key bytes 32 g32 .. 32 g32 + 31 of every block
+      // (bf16 pairs read as words and widened with integer operations); the
+      // query is read twice, for the largest |q| and then block by block for
+      // the split, which keeps few registers live
+      auto chunk = [&](int kb, int c) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(qp + 64 * (kh * kBlocksHalf + kb) + 32 * g32 + 8 * c);
+      };
+      auto elem = [](const u32x4& w, int e) -> float {  // element e (0..7) of a chunk
+        const uint32_t x = w[e >> 1];
+        return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+      };
+      float mx = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < kBlocksHalf; kb++) {
+        u32x4 w[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) w[c] = chunk(kb, c);
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) mx = fmaxf(mx, fabsf(elem(w[c], e)));
+      }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // 2^k with max|q| 2^k in [128, 256) (1 for an all-zero query)
+      const int k = mx > 0.f ? min(max(8 - __builtin_amdgcn_frexp_expf(mx), -120), 120) : 0;
+      const float qs = __builtin_amdgcn_ldexpf(1.f, k);
+      qinv = __builtin_amdgcn_ldexpf(1.f, -k);
+#pragma unroll
+      for (int kb = 0; kb < kBlocksHalf; kb++) {
+        u32x4 w[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) w[c] = chunk(kb, c);
+        uint32_t h[8], l[8];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+#pragma unroll
+          for (int hw = 0; hw < 2; hw++) {
+            float x[4], r[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) x[e] = elem(w[c], 4 * hw + e) * qs;
+            const uint32_t h01 = e4m3_pair(x[0], x[1]), h23 = e4m3_pair(x[2], x[3]);
+            r[0] = x[0] - __builtin_amdgcn_cvt_f32_fp8((int)h01, 0);
+            r[1] = x[1] - __builtin_amdgcn_cvt_f32_fp8((int)h01, 1);
+            r[2] = x[2] - __builtin_amdgcn_cvt_f32_fp8((int)h23, 0);
+            r[3] = x[3] - __builtin_amdgcn_cvt_f32_fp8((int)h23, 1);
+            h[2 * c + hw] = h01 | (h23 << 16);
+            l[2 * c + hw] = e4m3_pair(r[0], r[1]) | (e4m3_pair(r[2], r[3]) << 16);
+          }
+        }
+        qhi[kb] = i32x8{(int)h[0], (int)h[1], (int)h[2], (int)h[3], (int)h[4], (int)h[5], (int)h[6], (int)h[7]};
+        qlo[kb] = i32x8{(int)l[0], (int)l[1], (int)l[2], (int)l[3], (int)l[4], (int)l[5], (int)l[6], (int)l[7]};
+      }
+      if (kh == 1) {
+#pragma unroll
+        for (int kr = 0; kr < kRopeKs; kr++)
+          qr[kr] = *reinterpret_cast<const bf16x8*>(qp + kDc8 + 16 * kr + 8 * g32);
+      }
+      // nothing the compiler tracks stays in flight: its per-use waits would
+      // also count the tile loads
+      wait_vmcnt<0>();
+    };
+    // per-token scales of a step, rows 8 (j/4) + 4 g32 + j%4 of accumulator slot j
+    auto load_scales = [&](const Tile& d, float* sc) {
+      const int32_t rmax = d.nv - 1;
+      if (d.blk >= 0 && d.nv == kStep8) {
+        const float* sb = a.c_kv_scale + (int64_t)d.blk * a.P + d.off + 4 * g32;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sb + 8 * q);
+#pragma unroll
+          for (int e = 0; e < 4; e++) sc[4 * q + e] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int r = min(8 * (j >> 2) + 4 * g32 + (j & 3), rmax);
+          const int64_t slot = d.blk >= 0 ? (int64_t)d.blk * a.P + d.off + r
+                                          : phys_slot(a.block_table, d.b, d.t0 + r, a.P, a.max_blocks,
+                                                      a.num_blocks);
+          sc[j] = a.c_kv_scale[slot];
+        }
+      }
+    };
+    Tile cur = read_tile(win, 0);
+    load_q(cur.b);
+    float sc[16];
+    if (kh == 0) load_scales(cur, sc);
+    float m_run = -INFINITY, l_run = 0.f;
+    int32_t seg_step = 0;
+    lds_t* xb = xbuf + hb * kX8Bytes + lane * 16;
+    lds_t* pb = pbuf + hb * kP8Bytes + lane * 16;
+    Loader8<HB> ld;
+    if (kh == 1) ld.start(a, ring, win, t_begin, n, hb, lane);
+    for (int32_t i = 0;; i++) {
+      const bool valid = i < n;
+      const bool seg_last = valid && (cur.last || i + 1 == n);
+      if (kh == 1) {
+        ld.wait_for(i);
+        wg_barrier_nowait();  // step i's tile is in LDS
+      } else {
+        wg_barrier();
+      }
+      lds_t* st = ring + (i % kStages8) * kStage8;
+      f32x16 s = f32x16{}, sr = f32x16{};
+      if (valid) {
+        auto ld_a = [&](int kb) -> i32x8 {  // key bytes 64 kb + 32 g32 .. +31 of row `row`
+          const int c0 = 4 * (kh * kBlocksHalf + kb) + 2 * g32;
+          const i32x4 x0 = *reinterpret_cast<const i32x4 __attribute__((address_space(3)))*>(
+              st + row * kCRow8 + ((c0 ^ swz8(row)) << 4));
+          const i32x4 x1 = *reinterpret_cast<const i32x4 __attribute__((address_space(3)))*>(
+              st + row * kCRow8 + (((c0 + 1) ^ swz8(row)) << 4));
+          return i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        };
+        i32x8 av = ld_a(0);
+#pragma unroll
+        for (int kb = 0; kb < kBlocksHalf; kb++) {
+          const i32x8 an = kb + 1 < kBlocksHalf ? ld_a(kb + 1) : av;
+          s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qhi[kb], s, 0, 0, 0, 127, 0, 127);
+          s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qlo[kb], s, 0, 0, 0, 127, 0, 127);
+          av = an;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kh == 1) {
+#pragma unroll
+          for (int k = 0; k < kRopeKs; k++) {
+            const bf16x8 ar = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+                st + kStageC8 + row * kRRow8 + (((2 * k + g32) ^ swz_r8(row)) << 4));
+            sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qr[k], sr, 0, 0, 0);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q) =
+                f32x4{s[4 * q] * qinv, s[4 * q + 1] * qinv, s[4 * q + 2] * qinv, s[4 * q + 3] * qinv};
+            *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 4096 + 1024 * q) =
+                f32x4{sr[4 * q], sr[4 * q + 1], sr[4 * q + 2], sr[4 * q + 3]};
+          }
+        }
+      }
+      wg_barrier();
+      Tile nxt{};
+      if (i + 1 < n) nxt = read_tile(win, i + 1);
+      if (kh == 1) {
+        // loads of step i + kAhead8, into the stage last read in step i - 2
+        if (ld.next < n) ld.issue_next(a, ring, win, t_begin, hb, lane);
+      } else if (valid) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const f32x4 xl = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q);
+          const f32x4 xr = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 4096 + 1024 * q);
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            s[4 * q + e] = __builtin_fmaf(__builtin_fmaf(s[4 * q + e], qinv, xl[e]), sc[4 * q + e], xr[e]);
+        }
+        const int32_t nv = cur.nv;
+        if (nv < kStep8) {
+#pragma unroll
+          for (int j = 0; j < 16; j++)
+            if (8 * (j >> 2) + 4 * g32 + (j & 3) >= nv) s[j] = -INFINITY;
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int j = 1; j < 16; j++) mx = fmaxf(mx, s[j]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mt = mx * sm;
+        const float thr = seg_step < kExactSteps8 ? 0.f : kLazy8;
+        const bool any = __any(mt > m_run + thr);
+        float alpha = 1.f;
+        if (any) {
+          const float m_new = fmaxf(m_run, mt);
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float mref = m_run == -INFINITY ? 0.f : m_run;
+        // weights p (normaliser) and p * scale_t (value product operand, bf16)
+        uint32_t pk[8];
+        float lsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q], sm, -mref));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + 1], sm, -mref));
+          lsum += p0 + p1;
+          const f32x2 e = {p0 * sc[2 * q], p1 * sc[2 * q + 1]};
+          pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(e, bf16x2));
+        }
+        l_run += lsum;
+        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb + 64 * 16) =
+            u32x4{pk[4], pk[5], pk[6], pk[7]};
+        seg_step++;
+        if (g32 == 0) s_alpha[hb * 32 + lane] = alpha;
+        if (lane == 0) s_flag[hb] = any ? 1 : 0;
+        if (seg_last) {
+          const float ltot = l_run + __shfl_xor(l_run, 32);
+          if (g32 == 0) {
+            s_invl[hb * 32 + lane] = ltot > 0.f ? 1.f / ltot : 0.f;
+            a.part_lse[(int64_t)(g + cur.b) * a.h + head] =
+                ltot > 0.f ? (m_run + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+          }
+        }
+      }
+      if (!valid) break;
+      if (i + 1 < n) {
+        cur = nxt;
+        // the next step's scales, used after its score products
+        if (kh == 0) load_scales(cur, sc);
+        if (seg_last) {
+          load_q(cur.b);
+          m_run = -INFINITY;
+          l_run = 0.f;
+          seg_step = 0;
+        }
+      }
+    }
+  } else {
+    // ================================================================ value waves
+    constexpr int MDP = S::MDP;
+    const int pw_id = wave - S::NQ;
+    const int grp16 = lane >> 4, i16 = lane & 15;
+    f32x16 o[MDP][HB];
+#pragma unroll
+    for (int md = 0; md < MDP; md++)
+#pragma unroll
+      for (int hb = 0; hb < HB; hb++) o[md][hb] = f32x16{};
+    for (int32_t i = 0; i <= n; i++) {
+      wg_barrier();
+      lds_t* st = ring + ((i + kStages8 - 1) % kStages8) * kStage8;
+      const bool have = i > 0;
+      Tile prev{};
+      if (have) prev = read_tile(win, i - 1);
+      const bool last = have && (prev.last || i == n);
+      bf16x8 pf[HB][2];
+      float inv[HB];
+      if (have) {
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++) {
+          if (s_flag[hb]) {
+            const float al = s_alpha[hb * 32 + (lane & 31)];
+#pragma unroll
+            for (int md = 0; md < MDP; md++) o[md][hb] *= al;
+          }
+          inv[hb] = last ? s_invl[hb * 32 + (lane & 31)] : 0.f;
+#pragma unroll
+          for (int kk = 0; kk < 2; kk++)
+            pf[hb][kk] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+                pbuf + hb * kP8Bytes + (kk * 64 + lane) * 16);
+        }
+      }
+      wg_barrier();
+      if (have) {
+        // A operand: 8 tokens of latent column 32 mb + 16 (grp16 % 2) + i16 per
+        // lane, from the 8-bit transposing read (lane 2 j + h of a 16-lane group
+        // reads row j of the group's tokens, bytes 8 h .. 8 h + 7), widened to bf16
+        auto ld_c = [&](int md, int kk) -> bf16x8 {
+          const int mb = pw_id * MDP + md;
+          const int jj = i16 >> 1, h = i16 & 1;
+          const int r = 16 * kk + 8 * (jj >> 2) + 4 * (grp16 >> 1) + (jj & 3);
+          const int cc = 2 * mb + (grp16 & 1);
+          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              reinterpret_cast<i32x2 __attribute__((address_space(3)))*>(
+                  st + r * kCRow8 + ((cc ^ swz8(r)) << 4) + 8 * h));
+          const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)w[0], 1.f, false);
+          const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)w[0], 1.f, true);
+          const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)w[1], 1.f, false);
+          const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)w[1], 1.f, true);
+          const u32x4 u = {__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                           __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3)};
+          return __builtin_bit_cast(bf16x8, u);
+        };
+        constexpr int NSTEP = 2 * MDP;
+        constexpr int D = 4;
+        bf16x8 cv[D];
+#pragma unroll
+        for (int k = 0; k < D; k++) cv[k] = ld_c(k >> 1, k & 1);
+#pragma unroll
+        for (int s = 0; s < NSTEP; s++) {
+          const int md = s >> 1, kk = s & 1;
+#pragma unroll
+          for (int hb = 0; hb < HB; hb++)
+            o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[s % D], pf[hb][kk], o[md][hb], 0, 0, 0);
+          if (s + D < NSTEP) cv[s % D] = ld_c((s + D) >> 1, (s + D) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (last) {
+          const int64_t slot = (int64_t)(g + prev.b);
+#pragma unroll
+          for (int hb = 0; hb < HB; hb++) {
+            float* dst = a.part_o + slot * a.h * kDc8 + frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
+#pragma unroll
+            for (int md = 0; md < MDP; md++) {
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++) {
+                const f32x4 v = {o[md][hb][4 * jj] * inv[hb], o[md][hb][4 * jj + 1] * inv[hb],
+                                 o[md][hb][4 * jj + 2] * inv[hb], o[md][hb][4 * jj + 3] * inv[hb]};
+                *reinterpret_cast<f32x4*>(dst + (md * 4 + jj) * 256) = v;
+              }
+              o[md][hb] = f32x16{};
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+int32_t heads_per_group8(int32_t heads) { return heads % 64 == 0 ? 64 : 32; }
+
+}  // namespace
+
+bool mfma_fp8_supported(const mla_decode_params& p) {
+  return p.cache_dtype == MLA_FP8_E4M3 && p.rope_dtype == MLA_BF16 && p.d_latent == kDc8 &&
+         p.d_rope == kDr8 && p.num_heads % 32 == 0;
+}
+
+hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s) {
+  if (a.d_c != kDc8 || a.d_r != kDr8 || a.h % 32 || !a.c_kv_scale) return hipErrorInvalidValue;
+  const int32_t hpg = heads_per_group8(a.h);
+  const int32_t HG = a.h / hpg;
+  if (HG > 1 && a.splits % 8) return hipErrorInvalidValue;
+  const dim3 grid(a.splits * HG);
+  if (hpg == 64)
+    hipLaunchKernelGGL((attend_fp8_kernel<2>), grid, dim3(Shape8<2>::NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_fp8_kernel<1>), grid, dim3(Shape8<1>::NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -39,6 +39,17 @@ int32_t mfma_streams(int32_t heads);
 int32_t mfma_head_groups(int32_t heads);
 hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s);
 
+// Matrix-core split attention for an fp8 (E4M3) latent with per-token scales,
+// d_c = 512, d_r = 64 bf16, h % 32 == 0, bf16 absorbed query; same head groups
+// and partial layout as launch_attend_mfma.
+bool mfma_fp8_supported(const mla_decode_params& p);
+hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s);
+
+// Either matrix-core attention kernel serves this shape.
+inline bool mfma_any_supported(const mla_decode_params& p) {
+  return mfma_supported(p) || mfma_fp8_supported(p);
+}
+
 // Matrix-core absorb / up-projection for bf16 q and weights, d_c = 512
 // (d_nope <= 128, multiple of 16; d_v multiple of 32).
 bool proj_mfma_supported(const mla_decode_params& p);

@@ -91,6 +91,9 @@ SMALL_CASES = {
     "heads64": (small("dsv3_b64_4k", batch=2, heads=64), [200, 31]),
     "heads256": (small("dsv3_b64_4k", batch=2, heads=256), [130, 64]),
     "fp8_ragged": (small("dsv3_fp8_16k", batch=3), [5, 190, 64]),
+    "fp8_page16": (small("dsv3_fp8_16k", batch=3, page_size=16), [17, 200, 64]),
+    "fp8_heads32": (small("dsv3_fp8_16k", batch=2, heads=32), [300, 31]),
+    "fp8_heads64": (small("dsv3_fp8_16k", batch=2, heads=64), [130, 64]),
     "dsv3_bf16_out": (small("dsv3_b64_4k", batch=4, out_dtype="bf16"), [0, 1, 64, 333]),
     "llama2_bf16_out": (small("transmla_llama2_7b", batch=2, out_dtype="bf16"), [700, 9]),
     "odd_shape_bf16": (small("dsv3_b64_4k", batch=3, heads=3, d_nope=24, d_latent=48, d_rope=16,
@@ -114,6 +117,16 @@ def test_split_counts_agree_with_oracle(splits):
     cfg = small("dsv3_b64_4k", batch=3)
     inp = generate(cfg, seq_lens=[400, 1, 257])
     _say(f"splits={splits}")
+    check_close(inp, run_gpu(inp, num_splits=splits))
+
+
+@pytest.mark.parametrize("name", ["dsv3_b64_4k", "dsv3_fp8_16k"])
+@pytest.mark.parametrize("splits", [1, 8])
+def test_long_splits_refill_the_descriptor_window(name, splits):
+    # a split of more than 64 + 6 steps refills the descriptor window
+    cfg = small(name, batch=2)
+    inp = generate(cfg, seq_lens=[5000, 2100])
+    _say(f"{name} splits={splits}")
     check_close(inp, run_gpu(inp, num_splits=splits))
 
 
