@@ -103,9 +103,9 @@ struct Shape {
 __device__ inline int swz_c(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ inline int swz_r(int r) { return (r >> 1) & 7; }
 
-// Work-group barrier that only waits for this wave's LDS traffic.  Unlike
-// __syncthreads() it does not drain the vector-memory counter, so the
-// direct-to-Ltep / NL loads per wave on every path).  A full step inside one
+// Direct-to-LDS loads of one step, issued by the NL loader waves: wave lw
+// loads latent rows lw, lw + NL, ... and rope groups lw, lw + NL, ...
+// (kLoadsPerStep / NL loads per wave on every path).  A full step inside one
 // page takes straight-line code: one scalar base per step, one offset per
 // row.  Otherwise rows past the end repeat the last valid token (finite data,
 // masked in the softmax) and, when a step can span pages, every lane looks up
