@@ -30,10 +30,11 @@ constexpr int kUpKs = kLat / 16;      // k-steps of the up-projection
 // rows of 32 sequences at a time are staged in LDS, split into a bf16 high
 // part and a bf16 remainder (16-byte chunks XOR-swizzled by the row); both
 // are multiplied and the products summed in fp32, which keeps about 16
-// significant bits of o_lat.  All global loads of a stage are issued before
-// the first is waited for.
+// significant bits of o_lat.  The first o_lat rows are loaded before the
+// W_UV rows, so that (the load counter being in order) their conversion does
+// not wait for W_UV, and the products run as four independent accumulator
+// chains.
 constexpr int kUpWaves = 2;
-constexpr int kUpStage = 32 * kLat / 4 / (64 * kUpWaves);  // float4 loads per thread per stage
 
 __device__ inline int up_swz(int row) { return row & 15; }
 
@@ -46,27 +47,31 @@ __global__ __launch_bounds__(64 * kUpWaves) void up_project_mfma_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
   const int32_t v0 = (blockIdx.y * kUpWaves + wave) * 32;
   const bool live_w = v0 < d_v;
+  static_assert(64 * kUpWaves * 4 == kLat, "one float4 of a row per thread");
+  // 8 o_lat rows (sequences b0 .. b0 + 7, clamped to the batch; rows past it
+  // only feed outputs that are not stored)
+  float4 x[8];
+  auto load8 = [&](int32_t b0) {
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int32_t b = min(b0 + u, B - 1);
+      x[u] = *reinterpret_cast<const float4*>(o_lat + ((int64_t)b * h + head) * kLat + 4 * tid);
+    }
+  };
+  load8(0);
+  asm volatile("" ::: "memory");  // keep the W_UV loads behind these
   bf16x8 wf[kUpKs];
   {
     const uint16_t* wrow = W_UV + ((int64_t)head * d_v + (live_w ? v0 : 0) + r) * kLat + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < kUpKs; ks++) wf[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
   }
-  for (int32_t b0 = 0; b0 < B; b0 += 32) {
-    if (b0 > 0) __syncthreads();  // the previous stage has been read
-    float4 x[kUpStage];
+  // x (8 rows) -> LDS rows i0 .. i0 + 7 as bf16 high and low parts
+  auto convert = [&](int i0) {
 #pragma unroll
-    for (int i = 0; i < kUpStage; i++) {
-      const int idx = tid + 64 * kUpWaves * i, row = idx >> 7, c4 = idx & 127;
-      const int32_t b = b0 + row;
-      x[i] = b < B ? *reinterpret_cast<const float4*>(o_lat + ((int64_t)b * h + head) * kLat + 4 * c4)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < kUpStage; i++) {
-      const int idx = tid + 64 * kUpWaves * i, row = idx >> 7, c4 = idx & 127;
-      const f32x4 v = {x[i].x, x[i].y, x[i].z, x[i].w};
-      const f32x2 v01 = {v[0], v[1]}, v23 = {v[2], v[3]};
+    for (int u = 0; u < 8; u++) {
+      const int row = i0 + u, c4 = tid;
+      const f32x2 v01 = {x[u].x, x[u].y}, v23 = {x[u].z, x[u].w};
       const bf16x2 h01 = __builtin_convertvector(v01, bf16x2);
       const bf16x2 h23 = __builtin_convertvector(v23, bf16x2);
       const bf16x2 l01 = __builtin_convertvector(v01 - __builtin_convertvector(h01, f32x2), bf16x2);
@@ -77,23 +82,42 @@ __global__ __launch_bounds__(64 * kUpWaves) void up_project_mfma_kernel(
       *reinterpret_cast<u32x2*>(os[0] + off) = hv;
       *reinterpret_cast<u32x2*>(os[1] + off) = lv;
     }
-    __syncthreads();
-    if (!live_w) continue;
-    f32x16 acc = f32x16{};
+  };
+  // products and stores for sequences b0 .. b0 + 31
+  auto products = [&](int32_t b0) {
+    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < kUpKs; ks++) {
       const int off = r * 1024 + (((2 * ks + g) ^ up_swz(r)) << 4);
       const bf16x8 hi = *reinterpret_cast<const bf16x8*>(os[0] + off);
       const bf16x8 lo = *reinterpret_cast<const bf16x8*>(os[1] + off);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[ks], acc, 0, 0, 0);
+      acc[2 * (ks & 1)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[ks], acc[2 * (ks & 1)], 0, 0, 0);
+      acc[2 * (ks & 1) + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[ks], acc[2 * (ks & 1) + 1], 0, 0, 0);
     }
+    const f32x16 sum = (acc[0] + acc[2]) + (acc[1] + acc[3]);
     // D[m = sequence][n = row]: lane holds row v0 + r, sequences 8(j/4) + 4g + j%4
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const int32_t bb = b0 + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (bb < B) store_elem<OT>(out, ((int64_t)bb * h + head) * d_v + v0 + r, acc[j]);
+      if (bb < B) store_elem<OT>(out, ((int64_t)bb * h + head) * d_v + v0 + r, sum[j]);
     }
+  };
+  // first block of sequences: the first 8 rows were loaded before W_UV
+  convert(0);
+  for (int32_t i0 = 8; i0 < min(32, B); i0 += 8) {
+    load8(i0);
+    convert(i0);
+  }
+  __syncthreads();
+  if (live_w) products(0);
+  for (int32_t b0 = 32; b0 < B; b0 += 32) {
+    __syncthreads();  // the previous block has been read
+    for (int32_t i0 = 0; i0 < min(32, B - b0); i0 += 8) {
+      load8(b0 + i0);
+      convert(i0);
+    }
+    __syncthreads();
+    if (live_w) products(b0);
   }
 }
 
