@@ -10,9 +10,10 @@ timed region.  Several copies of the cache pool are rotated from step to step
 so that the steps together touch more than 2x the 256 MB Infinity Cache and
 the latent-cache reads come from HBM.
 
-The attention kernel is timed alone with HIP events recorded on its own
-stream around its launch (mla_decode_timed); `roofline.achieved` is the
-algorithmic latent-cache bytes of one launch over that average duration.
+The step is timed over K plain mla_decode calls.  The attention kernel is then
+timed alone over K more steps with HIP events recorded on its stream around
+its launch (mla_decode_timed); `roofline.achieved` is the algorithmic
+latent-cache bytes of one launch over that average duration.
 """
 from __future__ import annotations
 
@@ -78,26 +79,36 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
 
     def step(k, evb=None, eva=None):
         i = k % copies
-        _lib.mla_decode_timed(p, dev.q, c_copies[i], s_copies[i], r_copies[i], dev.block_table,
-                              dev.seq_lens, dev.W_UK, dev.W_UV, dec.out, dec.workspace,
-                              dec.ws_bytes, stream, evb, eva)
+        if evb is None:
+            _lib.mla_decode(p, dev.q, c_copies[i], s_copies[i], r_copies[i], dev.block_table,
+                            dev.seq_lens, dev.W_UK, dev.W_UV, dec.out, dec.workspace, dec.ws_bytes,
+                            stream)
+        else:
+            _lib.mla_decode_timed(p, dev.q, c_copies[i], s_copies[i], r_copies[i], dev.block_table,
+                                  dev.seq_lens, dev.W_UK, dev.W_UV, dec.out, dec.workspace,
+                                  dec.ws_bytes, stream, evb, eva)
 
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
+    # the step: plain mla_decode calls between two events
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        step(warmup + k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # the attention kernel alone: the same steps again, with events around it
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for a, b in evs:            # torch creates the HIP events on first record
         a.record(stream)
         b.record(stream)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
     for k in range(steps):
         step(warmup + k, *evs[k])
-    stop.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg = sum(attn_ms) / len(attn_ms)
     cache_bytes = inp.cache_bytes()

@@ -187,15 +187,18 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
                          reinterpret_cast<int32_t*>(ws + L.tiles), s);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
   }
-  if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (use_bf16)
-    e = mla::launch_attend_mfma(a, p.cache_dtype, s);
-  else if (use_fp8)
-    e = mla::launch_attend_fp8(a, s);
-  else
+  // matrix-core kernels take the events into their dispatch (start/end of the
+  // kernel itself); the generic one is bracketed by event records
+  if (use_bf16) {
+    e = mla::launch_attend_mfma(a, p.cache_dtype, s, ev_before, ev_after);
+  } else if (use_fp8) {
+    e = mla::launch_attend_fp8(a, s, ev_before, ev_after);
+  } else {
+    if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = mla::launch_attend_simt(a, p.cache_dtype, p.rope_dtype, absorbed_dtype(p), s);
+    if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (ev_after && (e = hipEventRecord(ev_after, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = mla::launch_combine(a, o_lat, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MLA_OK;

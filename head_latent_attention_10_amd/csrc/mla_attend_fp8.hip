@@ -36,6 +36,8 @@
 // value product both spread over the 64 banks.
 #include "mla_mfma_util.hpp"
 
+#include <hip/hip_ext.h>
+
 namespace mla {
 namespace {
 
@@ -551,16 +553,19 @@ bool mfma_fp8_supported(const mla_decode_params& p) {
          p.d_rope == kDr8 && p.num_heads % 32 == 0;
 }
 
-hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start,
+                             hipEvent_t ev_stop) {
   if (a.d_c != kDc8 || a.d_r != kDr8 || a.h % 32 || !a.c_kv_scale) return hipErrorInvalidValue;
   const int32_t hpg = heads_per_group8(a.h);
   const int32_t HG = a.h / hpg;
   if (HG > 1 && a.splits % 8) return hipErrorInvalidValue;
   const dim3 grid(a.splits * HG);
   if (hpg == 64)
-    hipLaunchKernelGGL((attend_fp8_kernel<2>), grid, dim3(Shape8<2>::NW * 64), 0, s, a);
+    hipExtLaunchKernelGGL((attend_fp8_kernel<2>), grid, dim3(Shape8<2>::NW * 64), 0, s, ev_start,
+                          ev_stop, 0, a);
   else
-    hipLaunchKernelGGL((attend_fp8_kernel<1>), grid, dim3(Shape8<1>::NW * 64), 0, s, a);
+    hipExtLaunchKernelGGL((attend_fp8_kernel<1>), grid, dim3(Shape8<1>::NW * 64), 0, s, ev_start,
+                          ev_stop, 0, a);
   return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@
 // bf16-rounded weights that the MFMA consumes.
 #include "mla_mfma_util.hpp"
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 namespace mla {
@@ -514,16 +516,19 @@ int32_t mfma_streams(int32_t) { return 1; }
 
 int32_t mfma_head_groups(int32_t heads) { return heads / heads_per_group(heads); }
 
-hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s) {
+hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s,
+                              hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (cache_dtype != MLA_BF16 || a.d_c != kDc || a.d_r != kDr || a.h % 32) return hipErrorInvalidValue;
   const int32_t hpg = heads_per_group(a.h);
   const int32_t HG = a.h / hpg;
   if (HG > 1 && a.splits % 8) return hipErrorInvalidValue;  // XCD pairing uses whole groups of 8
   const dim3 grid(a.splits * HG);
   if (hpg == 64)
-    hipLaunchKernelGGL((attend_mfma_kernel<2>), grid, dim3(Shape<2>::NW * 64), 0, s, a);
+    hipExtLaunchKernelGGL((attend_mfma_kernel<2>), grid, dim3(Shape<2>::NW * 64), 0, s, ev_start,
+                          ev_stop, 0, a);
   else
-    hipLaunchKernelGGL((attend_mfma_kernel<1>), grid, dim3(Shape<1>::NW * 64), 0, s, a);
+    hipExtLaunchKernelGGL((attend_mfma_kernel<1>), grid, dim3(Shape<1>::NW * 64), 0, s, ev_start,
+                          ev_stop, 0, a);
   return hipGetLastError();
 }
 

@@ -37,13 +37,17 @@ int32_t mfma_streams(int32_t heads);
 // Work groups that share one token split (head groups of 64 or 32 heads); with
 // more than one, the split count must be a multiple of 8 (XCD pairing).
 int32_t mfma_head_groups(int32_t heads);
-hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s);
+// The optional events are stamped by the kernel's own dispatch (start and end
+// of execution), not by separate markers queued around it.
+hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s,
+                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Matrix-core split attention for an fp8 (E4M3) latent with per-token scales,
 // d_c = 512, d_r = 64 bf16, h % 32 == 0, bf16 absorbed query; same head groups
 // and partial layout as launch_attend_mfma.
 bool mfma_fp8_supported(const mla_decode_params& p);
-hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start = nullptr,
+                             hipEvent_t ev_stop = nullptr);
 
 // Either matrix-core attention kernel serves this shape.
 inline bool mfma_any_supported(const mla_decode_params& p) {

@@ -123,9 +123,11 @@ mla_status mla_decode(const mla_decode_params* p, const void* q, const void* c_k
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* mla_decode that also records two caller-created hipEvent_t (may be NULL)
- * on `stream` immediately before and after the split-attention kernel, so the
- * caller can time that kernel alone (hipEventElapsedTime).  Same arguments,
- * results and errors as mla_decode otherwise. */
+ * at the start and end of the split-attention kernel, so the caller can time
+ * that kernel alone (hipEventElapsedTime).  The matrix-core kernels take the
+ * events into their own dispatch, so the interval is the kernel's execution;
+ * the generic kernel is bracketed by event records on `stream`.  Same
+ * arguments, results and errors as mla_decode otherwise. */
 mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const void* c_kv,
                             const float* c_kv_scale, const void* k_rope,
                             const int32_t* block_table, const int32_t* seq_lens,
