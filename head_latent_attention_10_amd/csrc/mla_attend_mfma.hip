@@ -19,42 +19,46 @@
 //
 // Inside a work group the waves specialise:
 //  * 2*HB score waves.  Wave (hb, kh) holds the absorbed query of 32 heads for
-//    half of the 576-wide key (kh = 0: latent 0..287; kh = 1: latent 288..511
-//    and the 64 rope values) in registers and computes, for each step,
+//    one part of the 576-wide key (kh = 0: latent 0..255; kh = 1: latent
+//    256..511 and the 64 rope values) in registers and computes, for each step,
 //      S^T[t, i] = sum_d KV[t, d] Q[i, d]      (MFMA 32x32x16 bf16, M = tokens,
-//                                              N = heads, K = its 288 values)
-//    The kh = 1 wave hands its partial scores to its partner through LDS; the
-//    partner adds them, runs the online softmax (one lane = one head) and
-//    publishes the bf16 weights P, the per-head rescale factors and, at the
-//    end of a sequence segment, 1/l and the log-sum-exp.  The kh = 1 waves
-//    issue the tile loads meanwhile (below).
-//  * 4 (HB = 2) or 2 (HB = 1) value waves.  Each owns a slice of 128 (or 256)
+//                                              N = heads, K = its key part)
+//    The kh = 1 wave hands its partial scores to its partner through LDS; in
+//    the next step the partner adds them to its own, runs the online softmax
+//    (one lane = one head) and publishes the bf16 weights P, the per-head
+//    rescale factors and, at the end of a sequence segment, 1/l and the
+//    log-sum-exp.  The kh = 0 part is the shorter one: its wave also runs the
+//    softmax.
+//  * 4*HB value waves.  Each owns a slice of 64 (HB = 2) or 128 (HB = 1)
 //    latent rows of the output for all heads of the group and computes
 //      O^T[d, i] += sum_t C[t, d] P[i, t]      (M = latent rows, N = heads,
 //                                              K = tokens)
-//    one step behind the score waves.  The latent tile is read with the
-//    transposing LDS read; each such read feeds HB MFMAs.  The weights are in
-//    a permuted token order (slot i of lane group g is token 8*(i/4) + 4*g +
-//    i%4 of the 16-token k-step) that matches the score accumulator layout,
-//    and the latent tile is read in the same order.
+//    two steps behind the score waves.  It reads its latent fragments of a
+//    step with the transposing LDS read in the step of that tile and keeps
+//    them in registers until the weights arrive; each such read feeds HB
+//    MFMAs.  The weights are in a permuted token order (slot i of lane group
+//    g is token 8*(i/4) + 4*g + i%4 of the 16-token k-step) that matches the
+//    score accumulator layout, and the latent tile is read in the same order.
+//    The first four value waves issue the tile loads.
 //
-// LDS ring.  Four stages of one step: 32 latent rows of 1 KiB and 32 rope
+// LDS ring.  Three stages of one step: 32 latent rows of 1 KiB and 32 rope
 // rows of 128 B, written by direct global->LDS 16-byte loads (one instruction
 // per latent row, eight rope rows per instruction) two steps ahead of use.
-// The 16-byte chunk index is XOR-swizzled with a permutation of the row's low
-// four bits, which keeps both the row reads of the score product and the
-// 4-row transposing reads of the value product free of bank conflicts (64
-// four-byte banks).
+// Every wave reads a stage only in the step of its tile, so a stage is free
+// again one step later.  The 16-byte chunk index is XOR-swizzled with a
+// permutation of the row's low four bits, which keeps both the row reads of
+// the score product and the 4-row transposing reads of the value product
+// free of bank conflicts (64 four-byte banks).  The partial scores, weights
+// and rescale factors are double-buffered by step parity.
 //
-// Step i (two work-group barriers):
-//   score waves kh = 1 wait for their loads of step i; barrier
-//   score waves: partial S(i) | value waves: take P(i-1) and the rescale
-//   factors
-//   barrier
-//   score waves kh = 0: merge partial scores, softmax, publish P(i) |
-//   kh = 1: issue the loads of step i+2 | value waves: O += C(i-1) P(i-1)
-// (the first barrier of step i+1 orders the softmax of step i before its
-// consumers).
+// Step j (one work-group barrier; every wave runs n + 2 steps):
+//   loader waves wait for their loads of step j; barrier
+//   loader waves: issue the loads of step j + 2
+//   score waves kh = 0: softmax of step j - 1, publish P(j-1); partial S(j)
+//   score waves kh = 1: partial S(j), hand it over
+//   value waves: read P(j-2) and the latent fragments of step j;
+//                O += C(j-2) P(j-2); at a segment end, store the partial.
+// The barrier of step j + 1 orders what step j published before its readers.
 //
 // Softmax rescaling is lazy: after the first four steps of a sequence segment
 // (which track the exact maximum, so an early dominant token gets weight
@@ -77,23 +81,28 @@ constexpr int kCRow = kDc * 2;                    // 1024 bytes per latent row
 constexpr int kRRow = kDr * 2;                    // 128 bytes per rope row
 constexpr int kStageC = kStep * kCRow;            // 32768
 constexpr int kStage = kStageC + kStep * kRRow;   // 36864
-constexpr int kStages = 4;
-constexpr int kRing = kStages * kStage;           // 147456
+constexpr int kStages = 3;
+constexpr int kRing = kStages * kStage;           // 110592
 constexpr int kLoadsPerStep = kStep + kStep / 8;  // 32 latent rows + 4 rope groups
-constexpr int kKsHalf = 18;                       // score k-steps per score wave
+constexpr int kKs0 = 16, kKs1 = 20;               // score k-steps of the two key parts (36 in all)
+constexpr int kNL = 4;                            // loader waves (the first value waves)
 constexpr int kXBytes = 64 * 64;                  // one wave's partial scores
 constexpr int kPBytes = 2 * 64 * 16;              // weights of one head block, two k-steps
 constexpr float kLazy = 8.0f;                     // log2 of the largest unnormalised weight
 constexpr int kExactSteps = 4;                    // steps per segment with an exact maximum
 static_assert(kStep == 32, "the score and value products are laid out for 32-token steps");
+static_assert(kKs0 + kKs1 == (kDc + kDr) / 16, "the key parts cover the whole key");
 
 template <int HB>
 struct Shape {
   static constexpr int NQ = 2 * HB;             // score waves
-  static constexpr int NP = HB == 2 ? 4 : 2;    // value waves
+  static constexpr int NP = 4 * HB;             // value waves
   static constexpr int NW = NQ + NP;
   static constexpr int MDP = kDc / 32 / NP;     // 32-row output blocks per value wave
-  static constexpr int LDS = kRing + kWinBytes + HB * (kXBytes + kPBytes) + HB * 32 * 4 * 2 + 16;
+  static constexpr int kStores = MDP * 4 * HB;  // partial-output stores of a value wave per segment
+  // ring | descriptor window | xbuf [2][HB] | pbuf [2][HB] | alpha, 1/l [2][HB][32] | flag [2][HB]
+  static constexpr int LDS =
+      kRing + kWinBytes + 2 * HB * (kXBytes + kPBytes) + 2 * HB * 32 * 4 * 2 + 2 * HB * 4;
 };
 
 // Chunk swizzles (LDS of 64 four-byte banks, one 256-byte bank line).  Latent
@@ -116,6 +125,9 @@ template <int NL>
 __device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d, int lw,
                                   int lane) {
   static_assert(kStep % NL == 0 && (kStep / 8) % NL == 0, "uniform row assignment");
+  // recompute the per-lane offsets in every call instead of keeping them live
+  // across the step loop (they would cost registers in every wave)
+  asm volatile("" : "+v"(lane));
   const uint32_t st = (uint32_t)(uintptr_t)stage;
   const int64_t base = (int64_t)d.blk * a.P + d.off;
   if (d.blk >= 0 && d.nv == kStep) {
@@ -157,12 +169,13 @@ __device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d
   }
 }
 
-// The load schedule of one of the NL loader waves (lane group lw).  Loader 0
-// also refills the descriptor window: window w + 1 goes into the buffer of
-// window w - 1 together with the loads of step kWin w + 4, when every wave has
-// moved past window w - 1 (the value waves, the furthest behind, are then at
-// step kWin w + 1).  It is complete before step kWin w + 4 starts, long before
-// its first use.
+// The load schedule of one of the NL loader waves (lane group lw): the loads
+// of step i + 2 are issued in step i, into the stage that step i - 1 read.
+// Loader 0 also refills the descriptor window: window w + 1 goes into the
+// buffer of window w - 1 together with the loads of step kWin w + 4, issued in
+// step kWin w + 2, when every wave has moved past window w - 1 (the value
+// waves, the furthest behind, then consume step kWin w).  It is complete
+// before step kWin w + 4 starts, long before its first use.
 template <int NL>
 struct Loader {
   static_assert(kLoadsPerStep % NL == 0, "equal load counts per wave");
@@ -172,29 +185,39 @@ struct Loader {
   bool newer_issued;   // the batch after the awaited one was issued
 
   __device__ void issue_next(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
-                             int lane) {
+                             int lane, bool from_table = false) {
     if (lw == 0 && next >= kWin + 4 && next % kWin == 4 && next + kWin - 4 < n)
       load_window(a, win, t_begin, t_begin + n, next / kWin + 1, lane);
-    const Tile d = read_tile(win, next);
+    const Tile d = from_table ? global_tile(a, t_begin + next) : read_tile(win, next);
     issue_step<NL>(a, ring + (next % kStages) * kStage, d, lw, lane);
     next++;
   }
+  // The first two steps, issued at kernel entry from the planner's table.
   __device__ void start(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int32_t steps,
                         int lw, int lane) {
     next = 0;
     n = steps;
-    for (int s = 0; s < 2 && next < n; s++) issue_next(a, ring, win, t_begin, lw, lane);
+    for (int s = 0; s < 2 && next < n; s++) issue_next(a, ring, win, t_begin, lw, lane, true);
     newer_issued = next == 2;
   }
-  // Wait for this wave's loads of step i (only batch i+1 may stay in flight;
-  // an extra window load in that batch only makes the wait longer).
-  __device__ void wait_current() {
-    if (newer_issued)
-      wait_vmcnt<kPerWave>();
-    else
-      wait_vmcnt<0>();
+  // Wait for this wave's loads of step i.  What may stay in flight: the batch
+  // of step i+1 and sb groups of KS partial-output stores issued after the
+  // awaited batch (the hardware counter retires in issue order).  The counts
+  // are exact or smaller, so the wait never ends early; an extra window load
+  // in the newer batch only makes it longer.
+  template <int KS>
+  __device__ void wait_current(int sb) {
+    if (newer_issued) {
+      if (sb == 0) wait_vmcnt<kPerWave>();
+      else if (sb == 1) wait_vmcnt<kPerWave + KS>();
+      else wait_vmcnt<kPerWave + 2 * KS>();
+    } else {
+      if (sb == 0) wait_vmcnt<0>();
+      else if (sb == 1) wait_vmcnt<KS>();
+      else wait_vmcnt<2 * KS>();
+    }
   }
-  // During the softmax of step i: issue step i+2.
+  // In step i: issue step i+2.
   __device__ void issue_ahead(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
                               int lane) {
     if (next < n) {
@@ -213,11 +236,11 @@ void attend_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
   lds_t* ring = (lds_t*)smem;
   lds_t* win = ring + kRing;                        // [2][kWin] tile descriptors
-  lds_t* xbuf = win + kWinBytes;                    // [HB][4][64 lanes][4 floats]
-  lds_t* pbuf = xbuf + HB * kXBytes;                // [HB][2 k-steps][64 lanes][16 B]
-  float* s_alpha = (float*)(smem + kRing + kWinBytes + HB * (kXBytes + kPBytes));  // [HB][32]
-  float* s_invl = s_alpha + HB * 32;                // [HB][32]
-  int* s_flag = (int*)(s_invl + HB * 32);           // [HB]
+  lds_t* xbuf = win + kWinBytes;                    // [2][HB][4][64 lanes][4 floats]
+  lds_t* pbuf = xbuf + 2 * HB * kXBytes;            // [2][HB][2 k-steps][64 lanes][16 B]
+  float* s_alpha = (float*)(smem + kRing + kWinBytes + 2 * HB * (kXBytes + kPBytes));  // [2][HB][32]
+  float* s_invl = s_alpha + 2 * HB * 32;            // [2][HB][32]
+  int* s_flag = (int*)(s_invl + 2 * HB * 32);       // [2][HB]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -243,245 +266,266 @@ void attend_mfma_kernel(AttnArgs a) {
   if (t_begin >= t_end) return;
   const int32_t n = t_end - t_begin;  // steps of this split
 
-  // descriptor windows 0 and 1, visible to every wave after the barrier
-  if (wave == 1) {
+  // Descriptor windows 0 and 1, visible to every wave after the first
+  // barrier; the query and the first two tiles are requested before it.
+  auto load_windows = [&]() {
     load_window(a, win, t_begin, t_end, 0, lane);
     if (n > kWin) load_window(a, win, t_begin, t_end, 1, lane);
     wait_vmcnt<0>();
-  }
-  wg_barrier();
+  };
   const float sm = a.sm_scale_log2;
 
+  // Every wave runs n + 2 steps, each opened by one work-group barrier.
   if (wave < S::NQ) {
     // ================================================================ score waves
-    const int hb = wave >> 1, kh = wave & 1;
+    const int hb = wave >> 1;
     const int32_t head = hg * 32 * HB + hb * 32 + (lane & 31);
-    bf16x8 qf[kKsHalf];
-    auto load_q = [&](int32_t bb) {
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-          static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc + kDr));
+    auto score_wave = [&](auto kh_c) {
+      constexpr int KH = decltype(kh_c)::value;
+      constexpr int KS = KH ? kKs1 : kKs0;  // k-steps of this key part
+      constexpr int K0 = KH ? kKs0 : 0;     // its first k-step
+      bf16x8 qf[KS];
+      // the absorbed query of sequence bb; awaited explicitly, once per
+      // segment (otherwise the compiler, unable to tell whether a segment
+      // started, waits for these loads in every step)
+      auto issue_q = [&](int32_t bb) {
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc + kDr));
 #pragma unroll
-      for (int k = 0; k < kKsHalf; k++) qf[k] = qp[2 * (kh * kKsHalf + k) + g32];
-      // wait here, once per segment: otherwise the compiler, unable to tell
-      // whether a segment started, waits for these loads in every step, and
-      // the hardware counter it waits on also counts the loader's tile loads
-      wait_vmcnt<0>();
-    };
-    Tile cur = read_tile(win, 0);
-    load_q(cur.b);
-    float m_run = -INFINITY, l_run = 0.f;
-    int32_t seg_step = 0;  // steps of the current segment seen so far
-    lds_t* xb = xbuf + hb * kXBytes + lane * 16;
-    lds_t* pb = pbuf + hb * kPBytes + lane * 16;
-    // the kh = 1 waves issue the loads: HB loader waves of kLoadsPerStep / HB
-    Loader<HB> ld;
-    if (kh == 1) ld.start(a, ring, win, t_begin, n, hb, lane);
-    // n steps of scores plus one final step in which only the value waves work
-    for (int32_t i = 0;; i++) {
-      const bool valid = i < n;
-      const bool seg_last = valid && (cur.last || i + 1 == n);
-      if (kh == 1) {
-        ld.wait_current();
-        wg_barrier_nowait();  // step i's tile is in LDS
-      } else {
-        wg_barrier();
-      }
-      lds_t* st = ring + (i % kStages) * kStage;
-      f32x16 s = f32x16{};
-      if (valid) {
-        const int row = lane & 31;
-        auto ld_a = [&](int k) -> bf16x8 {
-          const int ks = kh * kKsHalf + k;
-          const lds_t* p = ks < 32
-              ? st + row * kCRow + (((2 * ks + g32) ^ swz_c(row)) << 4)
-              : st + kStageC + row * kRRow + (((2 * (ks - 32) + g32) ^ swz_r(row)) << 4);
-          return *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(p);
-        };
-        constexpr int D = 4;
-        bf16x8 av[D];
-#pragma unroll
-        for (int k = 0; k < D; k++) av[k] = ld_a(k);
-#pragma unroll
-        for (int k = 0; k < kKsHalf; k++) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k % D], qf[k], s, 0, 0, 0);
-          if (k + D < kKsHalf) av[k % D] = ld_a(k + D);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (kh == 1) {
-#pragma unroll
-          for (int q = 0; q < 4; q++)
-            *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q) =
-                f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-        }
-      }
+        for (int k = 0; k < KS; k++) qf[k] = qp[2 * (K0 + k) + g32];
+      };
+      Tile cur = global_tile(a, t_begin), prev{};
+      issue_q(cur.b);
+      if (wave == 1) load_windows();
       wg_barrier();
-      // the next step's descriptor, read early so that its latency is hidden
-      Tile nxt{};
-      if (i + 1 < n) nxt = read_tile(win, i + 1);
-      if (kh == 1) {
-        // loads of step i+2, into the stage last read in step i-2, issued
-        // while the partner wave runs the softmax
-        ld.issue_ahead(a, ring, win, t_begin, hb, lane);
-      } else if (valid) {
+      wait_vmcnt<0>();
+      float m_run = -INFINITY, l_run = 0.f;
+      int32_t seg_step = 0;  // steps of the current segment seen so far
+      f32x16 s_own = f32x16{};  // KH = 0: own partial scores of the previous step
+      for (int32_t j = 0; j <= n + 1; j++) {
+        wg_barrier();
+        // a new sequence segment starts at step j: its query was requested at
+        // the end of step j - 1, before the softmax below stores the previous
+        // segment's LSE
+        const bool new_seg = j > 0 && j < n && prev.last;
+        if (KH == 0 && j >= 1 && j <= n) {
+          // ---- softmax of step j - 1: own partial + the partner's from xbuf
+          const int par = (j - 1) & 1;
+          const bool seg_last = prev.last || j == n;
+          f32x16 s = s_own;
+          const lds_t* xb = xbuf + (par * HB + hb) * kXBytes + lane * 16;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const f32x4 o = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q);
-          s[4 * q] += o[0];
-          s[4 * q + 1] += o[1];
-          s[4 * q + 2] += o[2];
-          s[4 * q + 3] += o[3];
-        }
-        // mask the tokens past the end (only the last step of a sequence)
-        const int32_t nv = cur.nv;
-        if (nv < kStep) {
+          for (int q = 0; q < 4; q++) {
+            const f32x4 o = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q);
+            s[4 * q] += o[0];
+            s[4 * q + 1] += o[1];
+            s[4 * q + 2] += o[2];
+            s[4 * q + 3] += o[3];
+          }
+          // mask the tokens past the end (only the last step of a sequence)
+          const int32_t nv = prev.nv;
+          if (nv < kStep) {
 #pragma unroll
-          for (int j = 0; j < 16; j++)
-            if (8 * (j >> 2) + 4 * g32 + (j & 3) >= nv) s[j] = -INFINITY;
-        }
-        // step maximum per head: over the lane's 16 tokens, then across the
-        // two lane halves that hold the same head (the scale is positive)
-        float mx = s[0];
+            for (int jj = 0; jj < 16; jj++)
+              if (8 * (jj >> 2) + 4 * g32 + (jj & 3) >= nv) s[jj] = -INFINITY;
+          }
+          // step maximum per head: over the lane's 16 tokens, then across the
+          // two lane halves that hold the same head (the scale is positive)
+          float mx = s[0];
 #pragma unroll
-        for (int j = 1; j < 16; j++) mx = fmaxf(mx, s[j]);
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                           false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float mt = mx * sm;
-        // exact running maximum for the first steps of a segment (the largest
-        // weight is then exactly 1 in bf16), lazy afterwards
-        const float thr = seg_step < kExactSteps ? 0.f : kLazy;
-        const bool any = __any(mt > m_run + thr);
-        float alpha = 1.f;
-        if (any) {
-          const float m_new = fmaxf(m_run, mt);
-          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-          m_run = m_new;
-        }
-        const float mref = m_run == -INFINITY ? 0.f : m_run;
-        // weights as bf16 pairs (one pair per conversion: extracting elements
-        // from a wider bf16 vector is not lowered correctly); the normaliser
-        // sums exactly the bf16 weights the value product consumes
-        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-        uint32_t pk[8];
-        float lsum = 0.f;
+          for (int jj = 1; jj < 16; jj++) mx = fmaxf(mx, s[jj]);
+          {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                             false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          }
+          const float mt = mx * sm;
+          // exact running maximum for the first steps of a segment (the largest
+          // weight is then exactly 1 in bf16), lazy afterwards
+          const float thr = seg_step < kExactSteps ? 0.f : kLazy;
+          const bool any = __any(mt > m_run + thr);
+          float alpha = 1.f;
+          if (any) {
+            const float m_new = fmaxf(m_run, mt);
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+          }
+          const float mref = m_run == -INFINITY ? 0.f : m_run;
+          // weights as bf16 pairs (one pair per conversion: extracting elements
+          // from a wider bf16 vector is not lowered correctly); the normaliser
+          // sums exactly the bf16 weights the value product consumes
+          const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+          uint32_t pk[8];
+          float lsum = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-          const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q], sm, -mref)),
-                           __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + 1], sm, -mref))};
-          const bf16x2 pr = __builtin_convertvector(e, bf16x2);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-          pk[q] = __builtin_bit_cast(uint32_t, pr);
+          for (int q = 0; q < 8; q++) {
+            const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q], sm, -mref)),
+                             __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + 1], sm, -mref))};
+            const bf16x2 pr = __builtin_convertvector(e, bf16x2);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+            pk[q] = __builtin_bit_cast(uint32_t, pr);
+          }
+          l_run += lsum;
+          // publish the weights in the value product's operand layout
+          lds_t* pb = pbuf + (par * HB + hb) * kPBytes + lane * 16;
+          *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+          *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb + 64 * 16) =
+              u32x4{pk[4], pk[5], pk[6], pk[7]};
+          seg_step++;
+          if (g32 == 0) s_alpha[(par * HB + hb) * 32 + lane] = alpha;
+          if (lane == 0) s_flag[par * HB + hb] = any ? 1 : 0;
+          if (seg_last) {
+            const float ltot = l_run + __shfl_xor(l_run, 32);
+            if (g32 == 0) {
+              s_invl[(par * HB + hb) * 32 + lane] = ltot > 0.f ? 1.f / ltot : 0.f;
+              const int64_t slot = (int64_t)(g + prev.b);
+              a.part_lse[slot * a.h + head] =
+                  ltot > 0.f ? (m_run + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+            }
+            m_run = -INFINITY;
+            l_run = 0.f;
+            seg_step = 0;
+          }
         }
-        l_run += lsum;
-        // publish the weights in the value product's operand layout
-        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb + 64 * 16) =
-            u32x4{pk[4], pk[5], pk[6], pk[7]};
-        seg_step++;
-        if (g32 == 0) s_alpha[hb * 32 + lane] = alpha;
-        if (lane == 0) s_flag[hb] = any ? 1 : 0;
-        if (seg_last) {
-          const float ltot = l_run + __shfl_xor(l_run, 32);
-          if (g32 == 0) {
-            s_invl[hb * 32 + lane] = ltot > 0.f ? 1.f / ltot : 0.f;
-            const int64_t slot = (int64_t)(g + cur.b);
-            a.part_lse[slot * a.h + head] =
-                ltot > 0.f ? (m_run + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+        if (j < n) {
+          // ---- partial scores of step j over this wave's key part
+          if (new_seg) {
+            // the softmax stored one LSE after the query loads (KH = 0)
+            if (KH == 0)
+              wait_vmcnt<1>();
+            else
+              wait_vmcnt<0>();
+          }
+          const lds_t* st = ring + (j % kStages) * kStage;
+          const int row = lane & 31;
+          auto ld_a = [&](int k) -> bf16x8 {
+            const int ks = K0 + k;
+            const lds_t* p = ks < 32
+                ? st + row * kCRow + (((2 * ks + g32) ^ swz_c(row)) << 4)
+                : st + kStageC + row * kRRow + (((2 * (ks - 32) + g32) ^ swz_r(row)) << 4);
+            return *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(p);
+          };
+          f32x16 s = f32x16{};
+          constexpr int D = 4;
+          bf16x8 av[D];
+#pragma unroll
+          for (int k = 0; k < D; k++) av[k] = ld_a(k);
+#pragma unroll
+          for (int k = 0; k < KS; k++) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k % D], qf[k], s, 0, 0, 0);
+            if (k + D < KS) av[k % D] = ld_a(k + D);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (KH == 1) {
+            lds_t* xb = xbuf + ((j & 1) * HB + hb) * kXBytes + lane * 16;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+              *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q) =
+                  f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+          } else {
+            s_own = s;
+          }
+          prev = cur;
+          if (j + 1 < n) {
+            cur = read_tile(win, j + 1);
+            // the products above have read the query registers: the next
+            // segment's query can be requested now, a step ahead of its use
+            if (prev.last) issue_q(cur.b);
           }
         }
       }
-      if (!valid) break;  // that was the value waves' final step
-      if (i + 1 < n) {
-        cur = nxt;
-        if (seg_last) {
-          load_q(cur.b);
-          m_run = -INFINITY;
-          l_run = 0.f;
-          seg_step = 0;
-        }
-      }
-    }
+    };
+    if (wave & 1)
+      score_wave(std::integral_constant<int, 1>{});
+    else
+      score_wave(std::integral_constant<int, 0>{});
   } else {
     // ================================================================ value waves
     constexpr int MDP = S::MDP;
     const int pw_id = wave - S::NQ;
+    const bool loader = pw_id < kNL;
     const int j16 = lane & 15, grp = lane >> 4, e = j16 >> 2, qd = j16 & 3;
+    Loader<kNL> ld;
+    if (loader) ld.start(a, ring, win, t_begin, n, pw_id, lane);
+    wg_barrier();
+    int sb1 = 0, sb2 = 0;  // partial-store groups issued in the previous two steps
     f32x16 o[MDP][HB];
 #pragma unroll
     for (int md = 0; md < MDP; md++)
 #pragma unroll
       for (int hb = 0; hb < HB; hb++) o[md][hb] = f32x16{};
-    // iteration i consumes the weights of step i - 1
-    for (int32_t i = 0; i <= n; i++) {
+    // latent operand fragments of three steps: those of step j are read at
+    // the start of step j and consumed in step j + 2
+    bf16x8 cb[3][MDP][2];
+    auto ld_c = [&](lds_t* st, int md, int kk) -> bf16x8 {
+      const int dd = 32 * (pw_id * MDP + md) + 16 * (grp & 1) + 4 * qd;
+      const int chunk = dd >> 3, hoff = (dd & 7) * 2;
+      const int r0 = 16 * kk + 4 * g32 + e;
+      const int r1 = r0 + 8;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+              st + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+              st + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
+      const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, cat);
+    };
+    // step j: issue the reads of P(j-2) and C(j), then O += C(j-2) P(j-2)
+    auto step = [&](auto par_c, int32_t j) {
+      constexpr int PAR = decltype(par_c)::value;  // j % 3 (also the ring stage of step j)
+      constexpr int C = (PAR + 1) % 3;             // buffer of step j - 2
+      if (loader) ld.template wait_current<S::kStores>(sb1 + sb2);
       wg_barrier();
-      lds_t* st = ring + ((i + kStages - 1) % kStages) * kStage;
-      const bool have = i > 0;
-      Tile prev{};
-      if (have) prev = read_tile(win, i - 1);
-      const bool last = have && (prev.last || i == n);
+      if (loader) ld.issue_ahead(a, ring, win, t_begin, pw_id, lane);
+      const bool have = j >= 2;
+      const int par = j & 1;  // parity of step j - 2
       bf16x8 pf[HB][2];
-      float inv[HB];
-      auto ld_c = [&](int md, int kk) -> bf16x8 {
-        const int dd = 32 * (pw_id * MDP + md) + 16 * (grp & 1) + 4 * qd;
-        const int chunk = dd >> 3, hoff = (dd & 7) * 2;
-        const int r0 = 16 * kk + 4 * g32 + e;
-        const int r1 = r0 + 8;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-                st + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-                st + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
-        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, cat);
-      };
-      // O[md] += C(i-1) P(i-1) for the 32-row blocks md0 <= md < md1
-      auto products = [&](auto md0_c, auto md1_c) {
-        constexpr int md0 = decltype(md0_c)::value, md1 = decltype(md1_c)::value;
-        if constexpr (md1 > md0) {
-          constexpr int NSTEP = 2 * (md1 - md0);
-          constexpr int D = NSTEP < 4 ? NSTEP : 4;
-          bf16x8 cv[D];
-#pragma unroll
-          for (int k = 0; k < D; k++) cv[k] = ld_c(md0 + (k >> 1), k & 1);
-#pragma unroll
-          for (int s = 0; s < NSTEP; s++) {
-            const int md = md0 + (s >> 1), kk = s & 1;
-#pragma unroll
-            for (int hb = 0; hb < HB; hb++)
-              o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv[s % D], pf[hb][kk], o[md][hb], 0, 0, 0);
-            if (s + D < NSTEP) cv[s % D] = ld_c(md0 + ((s + D) >> 1), (s + D) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      };
       if (have) {
-        // everything published with the step being consumed is read now: the
-        // softmax overwrites it after the next barrier
 #pragma unroll
-        for (int hb = 0; hb < HB; hb++) {
-          if (s_flag[hb]) {
-            const float al = s_alpha[hb * 32 + (lane & 31)];
-#pragma unroll
-            for (int md = 0; md < MDP; md++) o[md][hb] *= al;
-          }
-          inv[hb] = last ? s_invl[hb * 32 + (lane & 31)] : 0.f;
+        for (int hb = 0; hb < HB; hb++)
 #pragma unroll
           for (int kk = 0; kk < 2; kk++)
             pf[hb][kk] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
-                pbuf + hb * kPBytes + (kk * 64 + lane) * 16);
-        }
+                pbuf + (par * HB + hb) * kPBytes + (kk * 64 + lane) * 16);
       }
-      wg_barrier();
+      if (j < n) {
+        // the stage offset is kept opaque so that the compiler does not keep
+        // three sets of fragment addresses live across the loop
+        int stage_off = PAR * kStage;
+        asm volatile("" : "+s"(stage_off));
+        lds_t* st = ring + stage_off;
+#pragma unroll
+        for (int md = 0; md < MDP; md++)
+#pragma unroll
+          for (int kk = 0; kk < 2; kk++) cb[PAR][md][kk] = ld_c(st, md, kk);
+      }
+      int sb = 0;
       if (have) {
-        products(std::integral_constant<int, 0>{}, std::integral_constant<int, MDP>{});
-        if (last) {
-          const int64_t slot = (int64_t)(g + prev.b);
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++) {
+          if (s_flag[par * HB + hb]) {
+            const float al = s_alpha[(par * HB + hb) * 32 + (lane & 31)];
+#pragma unroll
+            for (int md = 0; md < MDP; md++) o[md][hb] *= al;
+          }
+        }
+#pragma unroll
+        for (int md = 0; md < MDP; md++)
+#pragma unroll
+          for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++)
+              o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[C][md][kk], pf[hb][kk],
+                                                                  o[md][hb], 0, 0, 0);
+        // the descriptor of step j - 2, read after the fragment loads
+        const Tile pv = read_tile(win, j - 2);
+        if (pv.last || j - 2 == n - 1) {
+          const int64_t slot = (int64_t)(g + pv.b);
 #pragma unroll
           for (int hb = 0; hb < HB; hb++) {
+            const float inv = s_invl[(par * HB + hb) * 32 + (lane & 31)];
             // fragment-major partial: one store instruction writes 1 KiB contiguous
             float* dst = a.part_o + slot * a.h * kDc +
                          frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
@@ -489,15 +533,25 @@ void attend_mfma_kernel(AttnArgs a) {
             for (int md = 0; md < MDP; md++) {
 #pragma unroll
               for (int jj = 0; jj < 4; jj++) {
-                const f32x4 v = {o[md][hb][4 * jj] * inv[hb], o[md][hb][4 * jj + 1] * inv[hb],
-                                 o[md][hb][4 * jj + 2] * inv[hb], o[md][hb][4 * jj + 3] * inv[hb]};
+                const f32x4 v = {o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
+                                 o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv};
                 *reinterpret_cast<f32x4*>(dst + (md * 4 + jj) * 256) = v;
               }
               o[md][hb] = f32x16{};
             }
           }
+          sb = 1;
         }
       }
+      sb2 = sb1;
+      sb1 = sb;
+    };
+    for (int32_t j = 0; j <= n + 1; j += 3) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 > n + 1) break;
+      step(std::integral_constant<int, 1>{}, j + 1);
+      if (j + 2 > n + 1) break;
+      step(std::integral_constant<int, 2>{}, j + 2);
     }
   }
 }

@@ -79,18 +79,29 @@ struct Tile {
   bool last;  // last tile of its sequence
 };
 
-__device__ inline Tile read_tile(const lds_t* win, int32_t local) {
-  const i32x4 v = *reinterpret_cast<const i32x4 __attribute__((address_space(3)))*>(
-      win + (((local / kWin) & 1) * kWin + (local % kWin)) * 16);
+__device__ inline Tile decode_tile(int32_t blk, int32_t b, int32_t t0, int32_t w) {
   Tile t;
-  t.blk = __builtin_amdgcn_readfirstlane(v[0]);
-  t.b = __builtin_amdgcn_readfirstlane(v[1]);
-  t.t0 = __builtin_amdgcn_readfirstlane(v[2]);
-  const int32_t w = __builtin_amdgcn_readfirstlane(v[3]);
+  t.blk = blk;
+  t.b = b;
+  t.t0 = t0;
   t.nv = w & 63;
   t.last = (w >> 6) & 1;
   t.off = w >> 7;
   return t;
+}
+
+__device__ inline Tile read_tile(const lds_t* win, int32_t local) {
+  const i32x4 v = *reinterpret_cast<const i32x4 __attribute__((address_space(3)))*>(
+      win + (((local / kWin) & 1) * kWin + (local % kWin)) * 16);
+  return decode_tile(__builtin_amdgcn_readfirstlane(v[0]), __builtin_amdgcn_readfirstlane(v[1]),
+                     __builtin_amdgcn_readfirstlane(v[2]), __builtin_amdgcn_readfirstlane(v[3]));
+}
+
+// The descriptor of tile t straight from the planner's table (scalar loads),
+// for the first steps, before the LDS window has arrived.
+__device__ inline Tile global_tile(const AttnArgs& a, int32_t t) {
+  return decode_tile(load_ro(a.tiles, 4 * (int64_t)t), load_ro(a.tiles, 4 * (int64_t)t + 1),
+                     load_ro(a.tiles, 4 * (int64_t)t + 2), load_ro(a.tiles, 4 * (int64_t)t + 3));
 }
 
 // Descriptors of tiles [t_begin + kWin w, +kWin) of the split ending at t_end
