@@ -279,16 +279,18 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
 }
 
 // The same merge over fragment-major partials (frag_offset; 512 latent values,
-// heads a multiple of 32).  Work group = (sequence, 32-head block, 32-value
-// latent block); a thread owns one 16-byte piece (4 latent values of one
-// head), so each wave reads 1 KiB contiguous per slot.  Slots are taken in
-// chunks of 32: a thread first issues the loads of its piece in every slot of
-// the chunk, then the chunk's weights are formed in LDS (running maximum per
-// head across chunks) while the loads are in flight.
+// heads a multiple of 32), two variants.  Work group = (sequence, 32-head
+// block, 32-value latent block); a thread owns one 16-byte piece (4 latent
+// values of one head), so each wave reads 1 KiB contiguous per slot.
+//
+// For sequences that span many splits: slots are taken in chunks of 32; a
+// thread first issues the loads of its piece in every slot of the chunk, then
+// the chunk's weights are formed in LDS (running maximum per head across
+// chunks) while the loads are in flight.
 constexpr int kFragLat = 512;
 constexpr int kFragChunk = 32;
 
-__global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __restrict__ o_lat) {
+__global__ __launch_bounds__(256) void combine_frag_chunk_kernel(AttnArgs a, float* __restrict__ o_lat) {
   __shared__ float s_w[kFragChunk][32];
   __shared__ int32_t s_own[kFragChunk];
   __shared__ float s_red[8][32];
@@ -377,11 +379,132 @@ __global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __
   *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
+// For sequences that span few splits (many work groups, few slots each): a
+// thread holds at most 12 slots' pieces, which keeps registers and so
+// occupancy high.  It issues their loads first; while they are in flight the
+// work group forms, per head, the largest LSE over all slots and the sum of
+// exp(lse - largest) in one read of the LSEs, then the weights in LDS.
+constexpr int kCombPer = 12;  // slots per pass
+
+__global__ __launch_bounds__(256) void combine_frag_few_kernel(AttnArgs a, float* __restrict__ o_lat) {
+  constexpr int NPH = 8;  // slot phases of the LSE work
+  __shared__ float s_w[kCombPer][32];  // LSE of the pass's slots, then their weights
+  __shared__ float s_red[2][NPH][32];
+  __shared__ float s_M[32], s_W[32];
+  const int32_t b = blockIdx.x, hblk = blockIdx.y, mdg = blockIdx.z;
+  const int tid = threadIdx.x, jj = tid >> 6, lane = tid & 63;
+  const int r = lane & 31;                 // head of this thread's piece
+  const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of the LSE work
+  const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
+  float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * a.h + hblk * 32 + r) * kFragLat + d);
+  const int32_t n_total = load_ro(a.cu_tiles, a.B);
+  const int32_t first = load_ro(a.cu_tiles, b), last = load_ro(a.cu_tiles, b + 1) - 1;
+  if (last < first) {
+    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int32_t g_lo = split_owner(n_total, a.splits, first);
+  const int32_t n_cand = split_owner(n_total, a.splits, last) - g_lo + 1;
+  // with no more splits than tiles every split owns a tile; otherwise splits
+  // that own none wrote nothing and get weight 0
+  const bool all_own = a.splits <= n_total;
+  auto owns = [&](int32_t k) {
+    return all_own || split_begin(n_total, a.splits, g_lo + k) <
+                          split_begin(n_total, a.splits, g_lo + k + 1);
+  };
+  const int64_t slot_stride = (int64_t)a.h * kFragLat;
+  const float* src = a.part_o + (int64_t)(g_lo + b) * slot_stride + frag_offset(hblk, mdg, jj, lane);
+  const float* lse = a.part_lse + (int64_t)(g_lo + b) * a.h + hblk * 32 + wr;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int32_t c0 = 0; c0 < n_cand; c0 += kCombPer) {
+    // the pass's slots (the condition is uniform); slots that own no tile
+    // hold no data and get weight 0
+    float4 v[kCombPer];
+#pragma unroll
+    for (int i = 0; i < kCombPer; i++) {
+      const int32_t k = c0 + i;
+      v[i] = k < n_cand ? *reinterpret_cast<const float4*>(src + (int64_t)k * slot_stride)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (!all_own) {
+#pragma unroll
+      for (int i = 0; i < kCombPer; i++)
+        if (c0 + i < n_cand && !owns(c0 + i)) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (c0 == 0) {
+      // per head: the largest LSE over all slots and the sum of
+      // exp(lse - largest), online per slot phase, then merged; the first
+      // pass's LSEs stay in LDS
+      float mx = -INFINITY, sum = 0.f;
+      for (int32_t k = wk; k < n_cand; k += NPH) {
+        const float l = owns(k) ? lse[(int64_t)k * a.h] : -INFINITY;
+        if (k < kCombPer) s_w[k][wr] = l;
+        if (l > mx) {
+          sum = sum * expf(mx - l) + 1.f;  // exp(-inf) = 0 for the first one
+          mx = l;
+        } else if (l != -INFINITY) {
+          sum += expf(l - mx);
+        }
+      }
+      s_red[0][wk][wr] = mx;
+      s_red[1][wk][wr] = sum;
+      __syncthreads();
+      if (tid < 32) {
+        float m = -INFINITY;
+        for (int i = 0; i < NPH; i++) m = fmaxf(m, s_red[0][i][tid]);
+        float W = 0.f;
+        for (int i = 0; i < NPH; i++) {
+          const float mi = s_red[0][i][tid];
+          if (mi != -INFINITY) W += s_red[1][i][tid] * expf(mi - m);
+        }
+        s_M[tid] = m;
+        s_W[tid] = W;
+      }
+      __syncthreads();
+      for (int i = tid; i < kCombPer * 32; i += 256) {
+        const int32_t k = i >> 5;
+        const int hh = i & 31;
+        const float l = k < n_cand ? s_w[k][hh] : -INFINITY;
+        s_w[k][hh] = l == -INFINITY ? 0.f : expf(l - s_M[hh]);
+      }
+    } else {
+      // a later pass's weights (0 past the end and for slots that own no tile)
+      for (int i = tid; i < kCombPer * 32; i += 256) {
+        const int32_t k = c0 + (i >> 5);
+        const int hh = i & 31;
+        float w = 0.f;
+        if (k < n_cand && owns(k)) {
+          const float l = a.part_lse[(int64_t)(g_lo + b + k) * a.h + hblk * 32 + hh];
+          w = l == -INFINITY ? 0.f : expf(l - s_M[hh]);
+        }
+        s_w[i >> 5][hh] = w;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCombPer; i++) {
+      const float w = s_w[i][r];
+      acc.x = fmaf(w, v[i].x, acc.x);
+      acc.y = fmaf(w, v[i].y, acc.y);
+      acc.z = fmaf(w, v[i].z, acc.z);
+      acc.w = fmaf(w, v[i].w, acc.w);
+    }
+    __syncthreads();
+  }
+  const float W = s_W[r];
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
 hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s) {
   if (a.frag_layout) {
     if (a.d_c != kFragLat || a.h % 32 || a.streams != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(combine_frag_kernel, dim3(a.B, a.h / 32, kFragLat / 32), dim3(256), 0, s,
-                       a, o_lat);
+    // chunked merge when sequences span four or more splits on average
+    const dim3 grid(a.B, a.h / 32, kFragLat / 32);
+    if (a.splits >= 4 * a.B)
+      hipLaunchKernelGGL(combine_frag_chunk_kernel, grid, dim3(256), 0, s, a, o_lat);
+    else
+      hipLaunchKernelGGL(combine_frag_few_kernel, grid, dim3(256), 0, s, a, o_lat);
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3(a.B, a.h), dim3(kCombThreads), 0, s, a, o_lat);
   }
