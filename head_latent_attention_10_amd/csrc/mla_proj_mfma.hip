@@ -86,13 +86,24 @@ __global__ __launch_bounds__(64 * kUpWaves) void up_project_mfma_kernel(
   // products and stores for sequences b0 .. b0 + 31
   auto products = [&](int32_t b0) {
     f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    // the o_lat operands are read kPre k-steps ahead of their products
+    constexpr int kPre = 4;
+    bf16x8 hi[kPre], lo[kPre];
+    auto ld_o = [&](int ks, int slot) {
+      const int off = r * 1024 + (((2 * ks + g) ^ up_swz(r)) << 4);
+      hi[slot] = *reinterpret_cast<const bf16x8*>(os[0] + off);
+      lo[slot] = *reinterpret_cast<const bf16x8*>(os[1] + off);
+    };
+#pragma unroll
+    for (int ks = 0; ks < kPre; ks++) ld_o(ks, ks);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kUpKs; ks++) {
-      const int off = r * 1024 + (((2 * ks + g) ^ up_swz(r)) << 4);
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(os[0] + off);
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(os[1] + off);
-      acc[2 * (ks & 1)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[ks], acc[2 * (ks & 1)], 0, 0, 0);
-      acc[2 * (ks & 1) + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[ks], acc[2 * (ks & 1) + 1], 0, 0, 0);
+      const int slot = ks % kPre;
+      acc[2 * (ks & 1)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi[slot], wf[ks], acc[2 * (ks & 1)], 0, 0, 0);
+      acc[2 * (ks & 1) + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo[slot], wf[ks], acc[2 * (ks & 1) + 1], 0, 0, 0);
+      if (ks + kPre < kUpKs) ld_o(ks + kPre, slot);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their products
     }
     const f32x16 sum = (acc[0] + acc[2]) + (acc[1] + acc[3]);
     // D[m = sequence][n = row]: lane holds row v0 + r, sequences 8(j/4) + 4g + j%4
