@@ -41,6 +41,24 @@ class MlaDecodeParams(ctypes.Structure):
     ]
 
 
+class MlaCacheWriteParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("x_dtype", ctypes.c_int32),
+        ("weight_dtype", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32),
+        ("rope_dtype", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("rope_base", ctypes.c_float),
+    ]
+
+
 class MlaError(RuntimeError):
     def __init__(self, status: int, fn: str, msg: str):
         super().__init__(f"{fn} failed with status {status}: {msg}")
@@ -50,6 +68,7 @@ class MlaError(RuntimeError):
 _lib: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(MlaDecodeParams)
+_WP = ctypes.POINTER(MlaCacheWriteParams)
 
 _SIGNATURES = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -65,6 +84,9 @@ _SIGNATURES = {
     "mla_gather_cache": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "mla_split_begin": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
     "mla_split_owner": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]),
+    "mla_cache_write_workspace_size": (ctypes.c_int, [_WP, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_cache_write": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_quantize_e4m3_rows": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
 }
 
 
@@ -201,3 +223,34 @@ def mla_split_begin(n_tiles: int, splits: int, g: int) -> int:
 
 def mla_split_owner(n_tiles: int, splits: int, tile: int) -> int:
     return load_library().mla_split_owner(n_tiles, splits, tile)
+
+
+def make_write_params(batch, d_model, d_latent, d_rope, page_size, max_blocks_per_seq, num_blocks,
+                      x_dtype="bf16", weight_dtype="bf16", cache_dtype="bf16", rope_dtype="bf16",
+                      rms_eps=1e-6, rope_base=10000.0):
+    code = lambda d: DTYPE_CODES[d] if isinstance(d, str) else int(d)
+    return MlaCacheWriteParams(batch, d_model, d_latent, d_rope, page_size, max_blocks_per_seq,
+                               num_blocks, code(x_dtype), code(weight_dtype), code(cache_dtype),
+                               code(rope_dtype), float(rms_eps), float(rope_base))
+
+
+def mla_cache_write_workspace_size(p: MlaCacheWriteParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_cache_write_workspace_size",
+           load_library().mla_cache_write_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def mla_cache_write(p, x, W_DKV, gamma, W_KR, positions, block_table, c_kv, c_kv_scale, k_rope,
+                    workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_cache_write", load_library().mla_cache_write(
+        ctypes.byref(p), _ptr(x), _ptr(W_DKV), _ptr(gamma), _ptr(W_KR), _ptr(positions),
+        _ptr(block_table), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope), _ptr(workspace),
+        workspace_bytes, _stream(stream)))
+
+
+def mla_quantize_e4m3_rows(x, rows: int, d: int, codes, scales, stream=None):
+    _check("mla_quantize_e4m3_rows", load_library().mla_quantize_e4m3_rows(
+        _ptr(x), int(rows), int(d), _ptr(codes), _ptr(scales), _stream(stream)))

@@ -206,6 +206,40 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------- writer
+mla_status validate_writer(const mla_cache_write_params* p) {
+  if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0 || p->d_model < 1 || p->d_latent < 1 || p->d_rope < 0 || p->d_rope % 2)
+    return fail(MLA_ERR_INVALID_ARG,
+                "shape out of range (batch=%d d_model=%d d_latent=%d d_rope=%d, d_rope even)",
+                p->batch, p->d_model, p->d_latent, p->d_rope);
+  if (p->page_size < 1 || p->page_size > 4096 || p->max_blocks_per_seq < 1 || p->num_blocks < 1)
+    return fail(MLA_ERR_INVALID_ARG, "page_size=%d max_blocks_per_seq=%d num_blocks=%d",
+                p->page_size, p->max_blocks_per_seq, p->num_blocks);
+  if (!is_dtype(p->x_dtype, false) || !is_dtype(p->weight_dtype, false) ||
+      !is_dtype(p->cache_dtype, true) || !is_dtype(p->rope_dtype, false))
+    return fail(MLA_ERR_INVALID_ARG, "unknown dtype code (x=%d weight=%d cache=%d rope=%d)",
+                p->x_dtype, p->weight_dtype, p->cache_dtype, p->rope_dtype);
+  if (!std::isfinite(p->rms_eps) || p->rms_eps < 0.f)
+    return fail(MLA_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (!std::isfinite(p->rope_base) || p->rope_base <= 0.f)
+    return fail(MLA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (p->d_latent + p->d_rope > 8192)
+    return fail(MLA_ERR_UNSUPPORTED, "d_latent + d_rope above 8192");
+  if ((int64_t)p->batch * p->d_model >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "batch x d_model at or above 2^31");
+  return MLA_OK;
+}
+
+size_t writer_ws_bytes(const mla_cache_write_params& p) {
+  return align256((size_t)mla::writer_chunks(p) * (size_t)p.batch *
+                  (size_t)(p.d_latent + p.d_rope) * sizeof(float));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mla_status_string(int32_t st) {
@@ -347,6 +381,53 @@ mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const 
                                     max_tokens, c_out, scale_out, rope_out,
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "gather launch");
+}
+
+mla_status mla_cache_write_workspace_size(const mla_cache_write_params* p, size_t* bytes) {
+  const mla_status st = validate_writer(p);
+  if (st != MLA_OK) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = writer_ws_bytes(*p);
+  return MLA_OK;
+}
+
+mla_status mla_cache_write(const mla_cache_write_params* p, const void* x, const void* W_DKV,
+                           const void* gamma, const void* W_KR, const int32_t* positions,
+                           const int32_t* block_table, void* c_kv, float* c_kv_scale,
+                           void* k_rope, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = validate_writer(p);
+  if (st != MLA_OK) return st;
+  if (p->batch == 0) return MLA_OK;
+  if (!x || !W_DKV || !gamma || !positions || !block_table || !c_kv ||
+      (p->d_rope > 0 && (!W_KR || !k_rope)))
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((p->cache_dtype == MLA_FP8_E4M3) != (c_kv_scale != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "c_kv_scale must be given exactly for an fp8 cache");
+  const size_t need = writer_ws_bytes(*p);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (mla::writer_mfma_ok(*p) && !(aligned16(x) && aligned16(W_DKV) && aligned16(W_KR)))
+    return fail(MLA_ERR_INVALID_ARG, "bf16 x, W_DKV and W_KR must be 16-byte aligned");
+  const hipError_t e = mla::launch_cache_write(*p, x, W_DKV, gamma, W_KR, positions, block_table,
+                                               c_kv, c_kv_scale, k_rope,
+                                               static_cast<float*>(workspace),
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache writer launch");
+  return MLA_OK;
+}
+
+mla_status mla_quantize_e4m3_rows(const float* x, int64_t rows, int32_t d, uint8_t* codes,
+                                  float* scales, void* stream) {
+  if (rows < 0 || rows >= ((int64_t)1 << 31) || d < 1 || d > 8192)
+    return fail(MLA_ERR_INVALID_ARG, "rows=%lld d=%d (1 <= d <= 8192)", (long long)rows, d);
+  if (rows == 0) return MLA_OK;
+  if (!x || !codes || !scales) return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL");
+  const hipError_t e =
+      mla::launch_quantize_rows(x, rows, d, codes, scales, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantiser launch");
+  return MLA_OK;
 }
 
 int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g) {

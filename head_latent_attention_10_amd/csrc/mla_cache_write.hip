@@ -1,0 +1,340 @@
+// Latent-cache writer (gfx950): one new token per sequence appended to the
+// paged cache.
+//
+// "TransMLA: Multi-Head Latent Attention Is All You Need", the MLA structure
+// after conversion: the cached latent is a down projection of the hidden
+// state and the decoupled RoPE key a second projection rotated to the token's
+// position.  "TPLA: Tensor Parallel Latent Attention ...", "RMSNorm Slicing"
+// (Eqs. 8-9): the latent is RMS-normalised before attention.  Per sequence b
+// with position t = positions[b]:
+//   y = [W_DKV; W_KR] x_b                       (d_latent + d_rope values)
+//   c = y[:d_latent] / sqrt(mean(y[:d_latent]^2) + eps) * gamma
+//   k = RoPE(y[d_latent:], t): pair i turned by t * base^(-2i / d_rope)
+// stored at slot (block_table[b][t / P], t % P); an fp8 latent row is stored
+// as E4M3FN codes of c / s with s = max|c| / 448 (fp32, ties to even).
+//
+// Projection: a matrix-core kernel (bf16 x and weights) or a generic kernel
+// writes fp32 partial sums over KC chunks of the model dimension; the finish
+// kernel (one work group per sequence) adds them in a fixed order, so the
+// result is deterministic, then normalises, rotates, encodes and stores.
+#include <algorithm>
+
+#include "mla_kernels.hpp"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWrThreads = 256;
+constexpr int kProjWaves = 4;     // waves of a projection work group (k-steps interleaved)
+constexpr int kProjBatch = 8;     // k-steps a wave loads before its products
+constexpr int kMaxChunks = 16;    // K chunks of the matrix-core projection
+
+// ------------------------------------------------------------------ E4M3FN
+// The OCP E4M3FN code of y, |y| <= 448 (callers clamp), rounded to nearest
+// with ties to even.  Every step is exact in fp32: scaling by powers of two,
+// 2m - 1 for m in [0.5, 1), and rintf (round to nearest even).
+__device__ inline uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 31) << 7;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: steps of 2^-9
+    code = (uint32_t)rintf(a * 512.0f);      // 8 is the smallest normal, 0x08
+  } else {
+    int e;
+    const float m = frexpf(a, &e);           // a = m 2^e, m in [0.5, 1)
+    uint32_t q = (uint32_t)rintf((2.0f * m - 1.0f) * 8.0f);
+    int be = e - 1 + 7;                      // biased exponent of 2^(e-1)
+    if (q == 8) {
+      q = 0;
+      be += 1;
+    }
+    code = ((uint32_t)be << 3) | q;
+  }
+  return code | sign;
+}
+
+// Block reductions over kWrThreads threads (s_red holds one value per wave).
+__device__ inline float block_sum(float v, float* s_red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWrThreads / 64; i++) t += s_red[i];
+  return t;
+}
+
+__device__ inline float block_max(float v, float* s_red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = s_red[0];
+#pragma unroll
+  for (int i = 1; i < kWrThreads / 64; i++) t = fmaxf(t, s_red[i]);
+  return t;
+}
+
+// Quantise the row vals[0..d) (LDS) into codes/scale; every thread of the
+// block calls it.
+__device__ inline void quantize_row(const float* vals, int32_t d, uint8_t* codes, float* scale,
+                                    float* s_red) {
+  float am = 0.f;
+  for (int i = threadIdx.x; i < d; i += kWrThreads) am = fmaxf(am, fabsf(vals[i]));
+  am = block_max(am, s_red);
+  const float s = am / 448.0f;  // IEEE division
+  if (threadIdx.x == 0) *scale = s;
+  for (int i = threadIdx.x; i < d; i += kWrThreads) {
+    uint32_t c = 0;
+    if (s > 0.f) c = e4m3_encode(fminf(fmaxf(vals[i] / s, -448.0f), 448.0f));
+    codes[i] = (uint8_t)c;
+  }
+}
+
+// ------------------------------------------------------------------ projection
+// Matrix-core partial sums: work group = (32 output columns, K chunk, 64 rows
+// of the batch); its four waves take interleaved k-steps of the chunk and add
+// their products in LDS.  Output column n < d_c is row n of W_DKV, else row
+// n - d_c of W_KR; both operands are read straight from global memory (a lane
+// reads 16 contiguous bytes of one x row and one weight row per k-step).
+//   part[kc][b][n] = sum over the chunk's k of x[b][k] W[n][k]
+__global__ __launch_bounds__(64 * kProjWaves) void writer_proj_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_DKV,
+    const uint16_t* __restrict__ W_KR, float* __restrict__ part, int32_t B, int32_t d_model,
+    int32_t d_c, int32_t d_r, int32_t chunks) {
+  __shared__ float s_acc[kProjWaves - 1][2][16][64];
+  const int32_t N = d_c + d_r;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, r = lane & 31;
+  const int32_t n = blockIdx.x * 32 + r;
+  const int32_t kc = blockIdx.y, b0 = blockIdx.z * 64;
+  const int32_t nks = d_model / 16;
+  const int32_t s_lo = (int32_t)(((int64_t)nks * kc) / chunks);
+  const int32_t s_hi = (int32_t)(((int64_t)nks * (kc + 1)) / chunks);
+  const uint16_t* wrow = n < d_c ? W_DKV + (int64_t)n * d_model : W_KR + (int64_t)(n - d_c) * d_model;
+  const bool two = b0 + 32 < B;  // a second 32-row tile has rows
+  const int32_t ra = min(b0 + r, B - 1), rb = min(b0 + 32 + r, B - 1);
+  const uint16_t* xa = x + (int64_t)ra * d_model;
+  const uint16_t* xb = x + (int64_t)rb * d_model;
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  for (int32_t s0 = s_lo + wave; s0 < s_hi; s0 += kProjWaves * kProjBatch) {
+    bf16x8 w[kProjBatch], p[kProjBatch], q[kProjBatch];
+#pragma unroll
+    for (int i = 0; i < kProjBatch; i++) {
+      const int32_t s = min(s0 + kProjWaves * i, s_hi - 1);
+      const int32_t k = 16 * s + 8 * g;
+      w[i] = *reinterpret_cast<const bf16x8*>(wrow + k);
+      p[i] = *reinterpret_cast<const bf16x8*>(xa + k);
+      q[i] = *reinterpret_cast<const bf16x8*>(xb + k);
+    }
+#pragma unroll
+    for (int i = 0; i < kProjBatch; i++) {
+      if (s0 + kProjWaves * i >= s_hi) break;  // uniform
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p[i], w[i], acc0, 0, 0, 0);
+      if (two) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[i], w[i], acc1, 0, 0, 0);
+    }
+  }
+  // add the four waves' products (fixed order) and store the chunk's partial
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      s_acc[wave - 1][0][j][lane] = acc0[j];
+      s_acc[wave - 1][1][j][lane] = acc1[j];
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && n < N) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      float v0 = acc0[j], v1 = acc1[j];
+#pragma unroll
+      for (int w2 = 0; w2 < kProjWaves - 1; w2++) {
+        v0 += s_acc[w2][0][j][lane];
+        v1 += s_acc[w2][1][j][lane];
+      }
+      // D[m = row][n]: lane holds column n, rows 8(j/4) + 4g + j%4
+      const int32_t m = 8 * (j >> 2) + 4 * g + (j & 3);
+      if (b0 + m < B) part[((int64_t)kc * B + b0 + m) * N + n] = v0;
+      if (b0 + 32 + m < B) part[((int64_t)kc * B + b0 + 32 + m) * N + n] = v1;
+    }
+  }
+}
+
+// Generic projection (any x/weight dtype): thread = one output column of one
+// sequence, one chunk (part[0]).
+template <int XT, int WT>
+__global__ __launch_bounds__(kWrThreads) void writer_proj_simt_kernel(
+    const void* __restrict__ x, const void* __restrict__ W_DKV, const void* __restrict__ W_KR,
+    float* __restrict__ part, int32_t B, int32_t d_model, int32_t d_c, int32_t d_r) {
+  const int32_t N = d_c + d_r;
+  const int32_t b = blockIdx.y, n = blockIdx.x * kWrThreads + threadIdx.x;
+  if (n >= N) return;
+  const void* W = n < d_c ? W_DKV : W_KR;
+  const int64_t row = (int64_t)(n < d_c ? n : n - d_c) * d_model;
+  float acc = 0.f;
+  for (int32_t k = 0; k < d_model; k++)
+    acc = fmaf(load_elem<XT>(x, (int64_t)b * d_model + k), load_elem<WT>(W, row + k), acc);
+  part[(int64_t)b * N + n] = acc;
+}
+
+// ------------------------------------------------------------------ finish
+struct FinishArgs {
+  const float* part;
+  const void* gamma;
+  const int32_t* positions;
+  const int32_t* block_table;
+  void* c_kv;
+  float* c_kv_scale;
+  void* k_rope;
+  int32_t B, d_c, d_r, chunks, P, max_blocks, num_blocks;
+  float eps, base;
+};
+
+template <int WT, int CT, int RT>
+__global__ __launch_bounds__(kWrThreads) void writer_finish_kernel(FinishArgs f) {
+  extern __shared__ float s_y[];  // [d_c + d_r]
+  __shared__ float s_red[kWrThreads / 64];
+  const int32_t b = blockIdx.x, N = f.d_c + f.d_r;
+  const int32_t t = f.positions[b];
+  if (t < 0 || t / f.P >= f.max_blocks) return;
+  const int32_t blk = f.block_table[(int64_t)b * f.max_blocks + t / f.P];
+  if (blk < 0 || blk >= f.num_blocks) return;
+  const int64_t slot = (int64_t)blk * f.P + t % f.P;
+  for (int32_t i = threadIdx.x; i < N; i += kWrThreads) {
+    float v = 0.f;
+    for (int32_t kc = 0; kc < f.chunks; kc++) v += f.part[((int64_t)kc * f.B + b) * N + i];
+    s_y[i] = v;
+  }
+  __syncthreads();
+  // RMSNorm of the latent
+  float ss = 0.f;
+  for (int32_t i = threadIdx.x; i < f.d_c; i += kWrThreads) ss = fmaf(s_y[i], s_y[i], ss);
+  ss = block_sum(ss, s_red);
+  const float inv = 1.0f / sqrtf(ss / (float)f.d_c + f.eps);
+  for (int32_t i = threadIdx.x; i < f.d_c; i += kWrThreads)
+    s_y[i] = s_y[i] * inv * load_elem<WT>(f.gamma, i);
+  __syncthreads();
+  if constexpr (CT == MLA_FP8_E4M3) {
+    quantize_row(s_y, f.d_c, static_cast<uint8_t*>(f.c_kv) + slot * f.d_c, f.c_kv_scale + slot, s_red);
+  } else {
+    for (int32_t i = threadIdx.x; i < f.d_c; i += kWrThreads)
+      store_elem<CT>(f.c_kv, slot * f.d_c + i, s_y[i]);
+  }
+  // RoPE of the rope key: the angle and its sine and cosine in fp64 (t * theta
+  // reaches 10^5 rad), the rotation in fp32
+  for (int32_t i = threadIdx.x; i < f.d_r / 2; i += kWrThreads) {
+    const double ang = (double)t * pow((double)f.base, -2.0 * (double)i / (double)f.d_r);
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    const float sn = (float)sd, cs = (float)cd;
+    const float xv = s_y[f.d_c + 2 * i], yv = s_y[f.d_c + 2 * i + 1];
+    store_elem<RT>(f.k_rope, slot * f.d_r + 2 * i, xv * cs - yv * sn);
+    store_elem<RT>(f.k_rope, slot * f.d_r + 2 * i + 1, xv * sn + yv * cs);
+  }
+}
+
+// ------------------------------------------------------------------ quantiser
+__global__ __launch_bounds__(kWrThreads) void quantize_rows_kernel(const float* __restrict__ x,
+                                                                   int32_t d, uint8_t* codes,
+                                                                   float* scales) {
+  extern __shared__ float s_row[];
+  __shared__ float s_red[kWrThreads / 64];
+  const int64_t row = blockIdx.x;
+  for (int32_t i = threadIdx.x; i < d; i += kWrThreads) s_row[i] = x[row * d + i];
+  __syncthreads();
+  quantize_row(s_row, d, codes + row * d, scales + row, s_red);
+}
+
+}  // namespace
+
+// Chunks of the model dimension the matrix-core projection splits into: about
+// 16, fewer when the batch is large (the partials are KC x B x N fp32).
+int32_t writer_chunks(const mla_cache_write_params& p) {
+  if (!writer_mfma_ok(p)) return 1;
+  int32_t kc = kMaxChunks;
+  while (kc > 1 && (int64_t)kc * p.batch > 1024) kc /= 2;
+  return std::min<int32_t>(kc, p.d_model / 16);
+}
+
+bool writer_mfma_ok(const mla_cache_write_params& p) {
+  return p.x_dtype == MLA_BF16 && p.weight_dtype == MLA_BF16 && p.d_model % 16 == 0 &&
+         (p.d_latent + p.d_rope) % 32 == 0;
+}
+
+hipError_t launch_cache_write(const mla_cache_write_params& p, const void* x, const void* W_DKV,
+                              const void* gamma, const void* W_KR, const int32_t* positions,
+                              const int32_t* block_table, void* c_kv, float* c_kv_scale,
+                              void* k_rope, float* part, hipStream_t s) {
+  const int32_t N = p.d_latent + p.d_rope;
+  const int32_t chunks = writer_chunks(p);
+  if (writer_mfma_ok(p)) {
+    const dim3 grid(N / 32, chunks, (p.batch + 63) / 64);
+    hipLaunchKernelGGL(writer_proj_mfma_kernel, grid, dim3(64 * kProjWaves), 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W_DKV),
+                       static_cast<const uint16_t*>(W_KR), part, p.batch, p.d_model, p.d_latent,
+                       p.d_rope, chunks);
+  } else {
+    const dim3 grid((N + kWrThreads - 1) / kWrThreads, p.batch);
+#define MLA_PROJ(XT, WT)                                                                        \
+  hipLaunchKernelGGL((writer_proj_simt_kernel<XT, WT>), grid, dim3(kWrThreads), 0, s, x, W_DKV, \
+                     W_KR, part, p.batch, p.d_model, p.d_latent, p.d_rope)
+    if (p.x_dtype == MLA_F32 && p.weight_dtype == MLA_F32) MLA_PROJ(MLA_F32, MLA_F32);
+    else if (p.x_dtype == MLA_F32) MLA_PROJ(MLA_F32, MLA_BF16);
+    else if (p.weight_dtype == MLA_F32) MLA_PROJ(MLA_BF16, MLA_F32);
+    else MLA_PROJ(MLA_BF16, MLA_BF16);
+#undef MLA_PROJ
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FinishArgs f;
+  f.part = part;
+  f.gamma = gamma;
+  f.positions = positions;
+  f.block_table = block_table;
+  f.c_kv = c_kv;
+  f.c_kv_scale = c_kv_scale;
+  f.k_rope = k_rope;
+  f.B = p.batch;
+  f.d_c = p.d_latent;
+  f.d_r = p.d_rope;
+  f.chunks = chunks;
+  f.P = p.page_size;
+  f.max_blocks = p.max_blocks_per_seq;
+  f.num_blocks = p.num_blocks;
+  f.eps = p.rms_eps;
+  f.base = p.rope_base;
+  const size_t lds = (size_t)N * sizeof(float);
+#define MLA_FIN(WT, CT, RT) \
+  hipLaunchKernelGGL((writer_finish_kernel<WT, CT, RT>), dim3(p.batch), dim3(kWrThreads), lds, s, f)
+  const bool wf = p.weight_dtype == MLA_F32, rf = p.rope_dtype == MLA_F32;
+  switch (p.cache_dtype) {
+    case MLA_F32:
+      if (wf) { if (rf) MLA_FIN(MLA_F32, MLA_F32, MLA_F32); else MLA_FIN(MLA_F32, MLA_F32, MLA_BF16); }
+      else { if (rf) MLA_FIN(MLA_BF16, MLA_F32, MLA_F32); else MLA_FIN(MLA_BF16, MLA_F32, MLA_BF16); }
+      break;
+    case MLA_BF16:
+      if (wf) { if (rf) MLA_FIN(MLA_F32, MLA_BF16, MLA_F32); else MLA_FIN(MLA_F32, MLA_BF16, MLA_BF16); }
+      else { if (rf) MLA_FIN(MLA_BF16, MLA_BF16, MLA_F32); else MLA_FIN(MLA_BF16, MLA_BF16, MLA_BF16); }
+      break;
+    default:
+      if (wf) { if (rf) MLA_FIN(MLA_F32, MLA_FP8_E4M3, MLA_F32); else MLA_FIN(MLA_F32, MLA_FP8_E4M3, MLA_BF16); }
+      else { if (rf) MLA_FIN(MLA_BF16, MLA_FP8_E4M3, MLA_F32); else MLA_FIN(MLA_BF16, MLA_FP8_E4M3, MLA_BF16); }
+      break;
+  }
+#undef MLA_FIN
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const float* x, int64_t rows, int32_t d, uint8_t* codes,
+                                float* scales, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((uint32_t)rows), dim3(kWrThreads),
+                     (size_t)d * sizeof(float), s, x, d, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace mla

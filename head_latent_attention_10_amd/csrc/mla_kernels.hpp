@@ -79,4 +79,14 @@ hipError_t launch_gather(const mla_decode_params& p, const void* c_kv, const flo
 
 inline int32_t dtype_size(int32_t dt) { return dt == MLA_F32 ? 4 : (dt == MLA_BF16 ? 2 : 1); }
 
+// Latent-cache writer (mla_cache_write.hip).
+bool writer_mfma_ok(const mla_cache_write_params& p);
+int32_t writer_chunks(const mla_cache_write_params& p);
+hipError_t launch_cache_write(const mla_cache_write_params& p, const void* x, const void* W_DKV,
+                              const void* gamma, const void* W_KR, const int32_t* positions,
+                              const int32_t* block_table, void* c_kv, float* c_kv_scale,
+                              void* k_rope, float* part, hipStream_t s);
+hipError_t launch_quantize_rows(const float* x, int64_t rows, int32_t d, uint8_t* codes,
+                                float* scales, hipStream_t s);
+
 }  // namespace mla

@@ -179,6 +179,68 @@ mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const 
 int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g);
 int32_t mla_split_owner(int64_t n_tiles, int32_t splits, int64_t tile);
 
+/* ------------------------------------------------------------------------
+ * Latent-cache writer: appends one new token per sequence to the paged cache
+ * above ("TransMLA: Multi-Head Latent Attention Is All You Need", the MLA
+ * structure after conversion: the cached latent is a down projection of the
+ * hidden state, the decoupled RoPE key a second projection rotated to the
+ * token's position; "TPLA: ...", "RMSNorm Slicing", Eqs. 8-9: the latent is
+ * RMS-normalised).  For each sequence b with t = positions[b]:
+ *   y      = W_DKV x[b]            (d_latent; fp32 accumulation)
+ *   c      = y / sqrt(mean(y^2) + rms_eps) * gamma
+ *   r      = W_KR x[b]             (d_rope)
+ *   k      = r with pair i (dims 2i, 2i+1) turned by t * rope_base^(-2i/d_rope):
+ *            (u, v) -> (u cos a - v sin a, u sin a + v cos a)
+ *   c_kv[blk][t % P] = c, k_rope[blk][t % P] = k, blk = block_table[b][t / P].
+ * An fp8 latent row is stored as the OCP E4M3FN codes of c / s, s = max|c| / 448
+ * (fp32, round to nearest even, values clamped to +-448; an all-zero row has
+ * s = 0 and zero codes), with s in c_kv_scale[blk][t % P].
+ * A sequence whose position is negative, or whose table entry is past the row
+ * or outside [0, num_blocks), is skipped (nothing written).  Two sequences
+ * naming the same slot race; the caller keeps slots distinct.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch;              /* sequences (one new token each); 0 = no-op   */
+  int32_t d_model;            /* hidden size of x                            */
+  int32_t d_latent;           /* latent width (rows of W_DKV)                */
+  int32_t d_rope;             /* rope key width (rows of W_KR), even; d_latent
+                                 + d_rope <= 8192                             */
+  int32_t page_size;          /* tokens per block                            */
+  int32_t max_blocks_per_seq; /* block_table row stride                      */
+  int32_t num_blocks;         /* pool size                                   */
+  int32_t x_dtype;            /* F32 or BF16                                 */
+  int32_t weight_dtype;       /* W_DKV, W_KR and gamma: F32 or BF16          */
+  int32_t cache_dtype;        /* c_kv: F32, BF16 or FP8_E4M3                 */
+  int32_t rope_dtype;         /* k_rope: F32 or BF16                         */
+  float rms_eps;              /* >= 0                                        */
+  float rope_base;            /* > 0, e.g. 10000                             */
+} mla_cache_write_params;
+
+/* Workspace bytes mla_cache_write needs (fp32 partial projections). */
+mla_status mla_cache_write_workspace_size(const mla_cache_write_params* p, size_t* bytes);
+
+/* The writer.
+ *   x           [batch, d_model]            x_dtype
+ *   W_DKV       [d_latent, d_model]         weight_dtype
+ *   gamma       [d_latent]                  weight_dtype
+ *   W_KR        [d_rope, d_model]           weight_dtype
+ *   positions   [batch] int32 (device)      0-based position of the new token
+ *   block_table [batch, max_blocks_per_seq] int32 (device)
+ *   c_kv, c_kv_scale, k_rope                the pools, as at the top of this
+ *               header; c_kv_scale must be non-NULL iff cache_dtype is FP8
+ *   workspace   >= mla_cache_write_workspace_size bytes, 256-byte aligned
+ * For fixed parameters the result is bitwise deterministic run to run. */
+mla_status mla_cache_write(const mla_cache_write_params* p, const void* x, const void* W_DKV,
+                           const void* gamma, const void* W_KR, const int32_t* positions,
+                           const int32_t* block_table, void* c_kv, float* c_kv_scale,
+                           void* k_rope, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The writer's fp8 row encoding on its own: rows x [rows, d] fp32 ->
+ * codes [rows, d] (E4M3FN) and scales [rows], by the rule above.
+ * 1 <= d <= 8192; rows >= 0 (0 = no-op). */
+mla_status mla_quantize_e4m3_rows(const float* x, int64_t rows, int32_t d, uint8_t* codes,
+                                  float* scales, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
