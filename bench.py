@@ -10,6 +10,13 @@ timed region.  Several copies of the cache pool are rotated from step to step
 so that the steps together touch more than 2x the 256 MB Infinity Cache and
 the latent-cache reads come from HBM.
 
+The latent-cache writer (one new token per sequence appended to the paged
+cache, mla_cache_write) is measured on its own under `extra`: a HIP graph of
+64 calls, each on its own copy of the projection weights (over 512 MB, so they
+are read from HBM), is replayed and timed with events; reported are the time
+per call and its algorithmic bytes (weights, hidden states, the rows written)
+per second against the 8 TB/s peak.
+
 The step is timed over K plain mla_decode calls.  The attention kernel is then
 timed alone over K more steps with HIP events recorded on its stream around
 its launch (mla_decode_timed); `roofline.achieved` is the algorithmic
@@ -183,6 +190,77 @@ def _counter_rows(directory: str):
     return rows
 
 
+def measure_writer(name: str, steps: int, warmup: int, copies: int = 64):
+    """Time mla_cache_write on the writer workload `name` (weights rotated)."""
+    import torch
+    from head_latent_attention_10_amd import _lib
+    from head_latent_attention_10_amd.device import to_device_array
+    from mla_inputs.writer import WRITER_CONFIGS, generate_writer
+
+    cfg = WRITER_CONFIGS[name]
+    w = generate_writer(cfg)
+    dev = torch.device("cuda")
+    d = {k: to_device_array(getattr(w, k), dev)
+         for k in ("x", "gamma", "positions", "block_table", "c_kv", "k_rope")}
+    scale = None if w.c_kv_scale is None else to_device_array(w.c_kv_scale, dev)
+    wd = [to_device_array(w.W_DKV, dev) for _ in range(copies)]
+    wr = [to_device_array(w.W_KR, dev) for _ in range(copies)]
+    p = _lib.make_write_params(cfg.batch, cfg.d_model, cfg.d_latent, cfg.d_rope, cfg.page_size,
+                               w.block_table.shape[1], w.num_blocks, cfg.x_dtype, cfg.weight_dtype,
+                               cfg.cache_dtype, cfg.rope_dtype, cfg.rms_eps, cfg.rope_base)
+    nbytes = _lib.mla_cache_write_workspace_size(p)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(k, stream):
+        _lib.mla_cache_write(p, d["x"], wd[k % copies], d["gamma"], wr[k % copies],
+                             d["positions"], d["block_table"], d["c_kv"], scale, d["k_rope"],
+                             ws, nbytes, stream)
+
+    # the eager result, for checking the graph replays below
+    call(0, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (d["c_kv"], d["k_rope"], scale) if t is not None]
+    # one HIP graph of `copies` calls (kernel launches only), replayed, so that
+    # the time is the GPU's and not the host's launch path
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(warmup):
+            call(k, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(copies):
+            call(k, torch.cuda.current_stream())
+    reps = max(1, steps // copies)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (reps * copies)
+    got = [t for t in (d["c_kv"], d["k_rope"], scale) if t is not None]
+    # bitwise: untouched slots hold NaN
+    if not all(torch.equal(u.view(torch.uint8), v.view(torch.uint8)) for u, v in zip(got, want)):
+        raise RuntimeError("graph replays of the cache writer differ from the eager call")
+    esz = {"f32": 4, "bf16": 2, "e4m3": 1}
+    n_out = cfg.d_latent + cfg.d_rope
+    alg = (n_out * cfg.d_model + cfg.d_latent) * esz[cfg.weight_dtype] \
+        + cfg.batch * cfg.d_model * esz[cfg.x_dtype] \
+        + cfg.batch * (cfg.d_latent * esz[cfg.cache_dtype] + cfg.d_rope * esz[cfg.rope_dtype]
+                       + (4 if cfg.cache_dtype == "e4m3" else 0))
+    gbps = alg / (ms * 1e-3) / 1e9
+    return {"us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": int(alg),
+            "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "batch": cfg.batch, "d_model": cfg.d_model, "cache_dtype": cfg.cache_dtype,
+            "weight_copies_rotated": copies}
+
+
 def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: int, commands):
     """HBM bytes per attention launch from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB
@@ -228,6 +306,10 @@ def main():
     ap.add_argument("--also", default="dsv3_b8_32k,dsv3_b64_4k,transmla_llama2_7b,dsv3_fp8_16k",
                     help="other workloads reported under 'extra' (comma list, may be empty)")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--writers", default="writer_dsv3_b8,writer_dsv3_b64,writer_dsv3_fp8_b32",
+                    help="latent-cache writer workloads reported under 'extra' (comma list)")
+    ap.add_argument("--writer-only", action="store_true",
+                    help="measure only the latent-cache writer workloads (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -257,6 +339,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.writer_only:
+        out = {w: measure_writer(w, max(320, args.steps), args.warmup)
+               for w in args.writers.split(",") if w}
+        print(json.dumps({"cache_writer": out}))
+        return
+
     main_run = measure(args.workload, args.steps, args.warmup, args.num_splits)
     extra = {}
     for w in [w for w in args.also.split(",") if w]:
@@ -267,6 +355,8 @@ def main():
                     "attn_cache_GBps": round(r["attn_gbps"], 1),
                     "attn_frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4)}
         del r
+    for w in [w for w in args.writers.split(",") if w]:
+        extra["cache_" + w] = measure_writer(w, max(320, args.steps), max(5, args.warmup))
 
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20
