@@ -59,6 +59,14 @@ class MlaCacheWriteParams(ctypes.Structure):
     ]
 
 
+class MlaDsaParams(ctypes.Structure):
+    _fields_ = [
+        ("index_heads", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+    ]
+
+
 class MlaError(RuntimeError):
     def __init__(self, status: int, fn: str, msg: str):
         super().__init__(f"{fn} failed with status {status}: {msg}")
@@ -69,6 +77,8 @@ _lib: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(MlaDecodeParams)
 _WP = ctypes.POINTER(MlaCacheWriteParams)
+_DP = ctypes.POINTER(MlaDsaParams)
+_I32 = ctypes.c_int32
 
 _SIGNATURES = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -87,6 +97,14 @@ _SIGNATURES = {
     "mla_cache_write_workspace_size": (ctypes.c_int, [_WP, ctypes.POINTER(ctypes.c_size_t)]),
     "mla_cache_write": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_quantize_e4m3_rows": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+    "mla_indexer_scores": (ctypes.c_int, [_PP, _DP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
+    "mla_topk_select": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P]),
+    "mla_decode_sparse_workspace_size": (ctypes.c_int, [_PP, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_decode_sparse": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "mla_dsa_decode_workspace_size": (ctypes.c_int, [_PP, _DP, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_dsa_decode": (ctypes.c_int, [_PP, _DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -254,3 +272,64 @@ def mla_cache_write(p, x, W_DKV, gamma, W_KR, positions, block_table, c_kv, c_kv
 def mla_quantize_e4m3_rows(x, rows: int, d: int, codes, scales, stream=None):
     _check("mla_quantize_e4m3_rows", load_library().mla_quantize_e4m3_rows(
         _ptr(x), int(rows), int(d), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+# ------------------------------------------------------------------ DSA
+
+def make_dsa_params(index_heads=64, index_dim=128, topk=2048) -> MlaDsaParams:
+    return MlaDsaParams(int(index_heads), int(index_dim), int(topk))
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def mla_indexer_scores(p, d, q_I, q_I_scale, w_I, k_I, k_I_scale, block_table, seq_lens, scores,
+                       score_stride: int, stream=None):
+    _check("mla_indexer_scores", load_library().mla_indexer_scores(
+        ctypes.byref(p), ctypes.byref(d), _ptr(q_I), _ptr(q_I_scale), _ptr(w_I), _ptr(k_I),
+        _ptr(k_I_scale), _ptr(block_table), _ptr(seq_lens), _ptr(scores), int(score_stride),
+        _stream(stream)))
+
+
+def mla_topk_select(scores, score_stride: int, seq_lens, batch: int, k: int, indices,
+                    index_stride: int, counts, stream=None):
+    _check("mla_topk_select", load_library().mla_topk_select(
+        _ptr(scores), int(score_stride), _ptr(seq_lens), int(batch), int(k), _ptr(indices),
+        int(index_stride), _ptr(counts), _stream(stream)))
+
+
+def mla_decode_sparse_workspace_size(p, index_stride: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_decode_sparse_workspace_size", load_library().mla_decode_sparse_workspace_size(
+        ctypes.byref(p), int(index_stride), ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode_sparse(p, q, c_kv, c_kv_scale, k_rope, block_table, indices, index_stride: int,
+                      counts, W_UK, W_UV, out, workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    _check("mla_decode_sparse", load_library().mla_decode_sparse(
+        ctypes.byref(p), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope), _ptr(block_table),
+        _ptr(indices), int(index_stride), _ptr(counts), _ptr(W_UK), _ptr(W_UV), _ptr(out),
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mla_dsa_decode_workspace_size(p, d) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_dsa_decode_workspace_size", load_library().mla_dsa_decode_workspace_size(
+        ctypes.byref(p), ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def mla_dsa_decode(p, d, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, q_I, q_I_scale, w_I,
+                   k_I, k_I_scale, W_UK, W_UV, out, indices_out, workspace, workspace_bytes=None,
+                   stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    _check("mla_dsa_decode", load_library().mla_dsa_decode(
+        ctypes.byref(p), ctypes.byref(d), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope),
+        _ptr(block_table), _ptr(seq_lens), _ptr(q_I), _ptr(q_I_scale), _ptr(w_I), _ptr(k_I),
+        _ptr(k_I_scale), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(indices_out), _ptr(workspace),
+        workspace_bytes, _stream(stream)))

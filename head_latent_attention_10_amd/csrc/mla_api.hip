@@ -69,7 +69,7 @@ int32_t absorbed_dtype(const mla_decode_params& p) {
 }
 
 struct Layout {
-  size_t q_lat, cu_tiles, tiles, part_o, part_lse, o_lat, total;
+  size_t q_lat, cu_tiles, tiles, part_o, part_lse, o_lat, entry_slots, total;
   int32_t splits, streams;
   int64_t slots;
 };
@@ -98,7 +98,9 @@ mla_status resolve_splits(const mla_decode_params& p, int32_t* splits) {
   return MLA_OK;
 }
 
-mla_status layout(const mla_decode_params& p, Layout* L) {
+// sparse_stride > 0: the sparse decode (index lists of that stride) -- tiles
+// cover at most sparse_stride entries per sequence, plus the slot list.
+mla_status layout(const mla_decode_params& p, Layout* L, int32_t sparse_stride = 0) {
   mla_status st = resolve_splits(p, &L->splits);
   if (st != MLA_OK) return st;
   L->streams = mla::mfma_any_supported(p) ? mla::mfma_streams(p.num_heads) : 1;
@@ -110,8 +112,9 @@ mla_status layout(const mla_decode_params& p, Layout* L) {
   L->cu_tiles = off;
   off = align256(off + (B + 1) * sizeof(int32_t));
   L->tiles = off;
-  const size_t tiles_per_seq =
-      ((size_t)p.max_blocks_per_seq * p.page_size + mla::kTile - 1) / mla::kTile;
+  const size_t cap = sparse_stride > 0 ? (size_t)sparse_stride
+                                        : (size_t)p.max_blocks_per_seq * p.page_size;
+  const size_t tiles_per_seq = (cap + mla::kTile - 1) / mla::kTile;
   off = align256(off + B * tiles_per_seq * 4 * sizeof(int32_t));
   L->part_o = off;
   off = align256(off + (size_t)L->slots * h * dc * sizeof(float));
@@ -119,7 +122,18 @@ mla_status layout(const mla_decode_params& p, Layout* L) {
   off = align256(off + (size_t)L->slots * h * sizeof(float));
   L->o_lat = off;
   off = align256(off + B * h * dc * sizeof(float));
+  L->entry_slots = off;
+  if (sparse_stride > 0) off = align256(off + B * (size_t)sparse_stride * sizeof(int32_t));
   L->total = off;
+  return MLA_OK;
+}
+
+mla_status validate_sparse(const mla_decode_params& p, int32_t stride) {
+  if (stride < 1) return fail(MLA_ERR_INVALID_ARG, "index_stride %d must be >= 1", stride);
+  if ((int64_t)p.batch * stride >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "batch x index_stride at or above 2^31");
+  if ((int64_t)p.num_blocks * p.page_size >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "pool of 2^31 slots or more (slot list is int32)");
   return MLA_OK;
 }
 
@@ -146,11 +160,27 @@ mla_status check_workspace(const Layout& L, void* ws, size_t bytes) {
   return MLA_OK;
 }
 
+// The planner's inputs and outputs for this layout (dense, or sparse when
+// indices is given).
+mla::PlanRequest plan_request(const Layout& L, char* ws, const int32_t* block_table,
+                              const int32_t* seq_lens, const int32_t* indices = nullptr,
+                              int32_t stride = 0) {
+  mla::PlanRequest r{seq_lens, block_table, reinterpret_cast<int32_t*>(ws + L.cu_tiles),
+                     reinterpret_cast<int32_t*>(ws + L.tiles)};
+  if (indices) {
+    r.indices = indices;
+    r.idx_stride = stride;
+    r.slots = reinterpret_cast<int32_t*>(ws + L.entry_slots);
+  }
+  return r;
+}
+
 mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat, const void* c_kv,
-                  const float* c_kv_scale, const void* k_rope, const int32_t* block_table,
-                  const int32_t* seq_lens, float* o_lat, char* ws, hipStream_t s,
-                  bool planned = false, hipEvent_t ev_before = nullptr,
-                  hipEvent_t ev_after = nullptr) {
+                  const float* c_kv_scale, const void* k_rope, const mla::PlanRequest& req,
+                  float* o_lat, char* ws, hipStream_t s, bool planned = false,
+                  hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr) {
+  const int32_t* block_table = req.block_table;
+  const int32_t* seq_lens = req.seq_lens;
   mla::AttnArgs a;
   a.q_lat = q_lat;
   a.c_kv = c_kv;
@@ -172,6 +202,8 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.num_blocks = p.num_blocks;
   a.splits = L.splits;
   a.streams = L.streams;
+  a.slots = req.indices ? req.slots : nullptr;
+  a.idx_stride = req.indices ? req.idx_stride : 0;
   // matrix-core kernels read 16-byte pieces of the pools; other pointers go
   // to the generic kernel (same workspace layout, row-major partials)
   const bool aligned = aligned16(c_kv) && aligned16(k_rope) && aligned16(c_kv_scale);
@@ -182,9 +214,7 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
 
   hipError_t e = hipSuccess;
   if (!planned) {
-    e = mla::launch_plan(seq_lens, block_table, p.batch, p.max_blocks_per_seq, p.page_size,
-                         p.num_blocks, reinterpret_cast<int32_t*>(ws + L.cu_tiles),
-                         reinterpret_cast<int32_t*>(ws + L.tiles), s);
+    e = mla::launch_plan(mla::plan_input(p, req), s);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
   }
   // matrix-core kernels take the events into their dispatch (start/end of the
@@ -230,6 +260,87 @@ mla_status validate_writer(const mla_cache_write_params* p) {
     return fail(MLA_ERR_UNSUPPORTED, "d_latent + d_rope above 8192");
   if ((int64_t)p->batch * p->d_model >= ((int64_t)1 << 31))
     return fail(MLA_ERR_UNSUPPORTED, "batch x d_model at or above 2^31");
+  return MLA_OK;
+}
+
+// The decode step, dense (indices == null) or over index lists.
+mla_status decode_impl(const mla_decode_params* p, const void* q, const void* c_kv,
+                       const float* c_kv_scale, const void* k_rope, const int32_t* block_table,
+                       const int32_t* lens, const int32_t* indices, int32_t stride,
+                       const void* W_UK, const void* W_UV, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream, void* ev_before, void* ev_after) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, lens);
+  if (st != MLA_OK) return st;
+  if (!q || !W_UK || !W_UV || !out) return fail(MLA_ERR_INVALID_ARG, "null q, W_UK, W_UV or out");
+  if (indices) {
+    st = validate_sparse(*p, stride);
+    if (st != MLA_OK) return st;
+  }
+  Layout L;
+  st = layout(*p, &L, indices ? stride : 0);
+  if (st != MLA_OK) return st;
+  st = check_workspace(L, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mla::PlanRequest plan = plan_request(L, ws, block_table, lens, indices, stride);
+  bool planned = false;
+  hipError_t e =
+      mla::launch_absorb(*p, q, W_UK, ws + L.q_lat, absorbed_dtype(*p), &plan, &planned, s);
+  if (e != hipSuccess) return hip_fail(e, "absorb launch");
+  float* o_lat = reinterpret_cast<float*>(ws + L.o_lat);
+  st = attend(*p, L, ws + L.q_lat, c_kv, c_kv_scale, k_rope, plan, o_lat, ws, s, planned,
+              static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after));
+  if (st != MLA_OK) return st;
+  e = mla::launch_up_project(*p, o_lat, W_UV, out, s);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
+}
+
+// ---------------------------------------------------------------- DSA
+mla_status validate_dsa(const mla_dsa_params* d, bool need_topk) {
+  if (!d) return fail(MLA_ERR_INVALID_ARG, "dsa params is NULL");
+  if (d->index_heads < 1 || d->index_heads > 1024 || d->index_dim < 1 || d->index_dim > 1024)
+    return fail(MLA_ERR_INVALID_ARG, "index_heads=%d index_dim=%d outside [1, 1024]",
+                d->index_heads, d->index_dim);
+  if (need_topk && (d->topk < 1 || d->topk > (1 << 24)))
+    return fail(MLA_ERR_INVALID_ARG, "topk %d outside [1, 2^24]", d->topk);
+  return MLA_OK;
+}
+
+mla_status check_indexer_ptrs(const mla_decode_params& p, const mla_dsa_params& d,
+                              const uint8_t* q_I, const float* q_I_scale, const float* w_I,
+                              const uint8_t* k_I, const float* k_I_scale) {
+  if (!q_I || !q_I_scale || !w_I || !k_I || !k_I_scale)
+    return fail(MLA_ERR_INVALID_ARG, "null indexer pointer");
+  if (mla::indexer_mfma_ok(d.index_heads, d.index_dim) && !(aligned16(q_I) && aligned16(k_I)))
+    return fail(MLA_ERR_INVALID_ARG, "q_I and k_I must be 16-byte aligned");
+  (void)p;
+  return MLA_OK;
+}
+
+int32_t score_cap(const mla_decode_params& p) { return p.max_blocks_per_seq * p.page_size; }
+
+struct DsaLayout {
+  size_t scores, indices, counts, decode, total;
+  Layout dec;
+};
+
+mla_status dsa_layout(const mla_decode_params& p, const mla_dsa_params& d, DsaLayout* L) {
+  const size_t B = p.batch;
+  size_t off = 0;
+  L->scores = off;
+  off = align256(off + B * (size_t)score_cap(p) * sizeof(float));
+  L->indices = off;
+  off = align256(off + B * (size_t)d.topk * sizeof(int32_t));
+  L->counts = off;
+  off = align256(off + B * sizeof(int32_t));
+  L->decode = off;
+  mla_status st = layout(p, &L->dec, d.topk);
+  if (st != MLA_OK) return st;
+  L->total = off + L->dec.total;
   return MLA_OK;
 }
 
@@ -310,8 +421,9 @@ mla_status mla_attend_latent(const mla_decode_params* p, const void* q_lat, cons
   if (st != MLA_OK) return st;
   st = check_workspace(L, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
-  return attend(*p, L, q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens, o_lat,
-                static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  char* ws = static_cast<char*>(workspace);
+  return attend(*p, L, q_lat, c_kv, c_kv_scale, k_rope, plan_request(L, ws, block_table, seq_lens),
+                o_lat, ws, static_cast<hipStream_t>(stream));
 }
 
 mla_status mla_up_project(const mla_decode_params* p, const float* o_lat, const void* W_UV,
@@ -330,31 +442,8 @@ mla_status mla_decode_timed(const mla_decode_params* p, const void* q, const voi
                             const void* W_UK, const void* W_UV, void* out, void* workspace,
                             size_t workspace_bytes, void* stream, void* ev_before,
                             void* ev_after) {
-  g_last_error.clear();
-  mla_status st = validate(p);
-  if (st != MLA_OK) return st;
-  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
-  if (st != MLA_OK) return st;
-  if (!q || !W_UK || !W_UV || !out) return fail(MLA_ERR_INVALID_ARG, "null q, W_UK, W_UV or out");
-  Layout L;
-  st = layout(*p, &L);
-  if (st != MLA_OK) return st;
-  st = check_workspace(L, workspace, workspace_bytes);
-  if (st != MLA_OK) return st;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const mla::PlanRequest plan{seq_lens, block_table, reinterpret_cast<int32_t*>(ws + L.cu_tiles),
-                              reinterpret_cast<int32_t*>(ws + L.tiles)};
-  bool planned = false;
-  hipError_t e =
-      mla::launch_absorb(*p, q, W_UK, ws + L.q_lat, absorbed_dtype(*p), &plan, &planned, s);
-  if (e != hipSuccess) return hip_fail(e, "absorb launch");
-  float* o_lat = reinterpret_cast<float*>(ws + L.o_lat);
-  st = attend(*p, L, ws + L.q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens, o_lat, ws, s,
-              planned, static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after));
-  if (st != MLA_OK) return st;
-  e = mla::launch_up_project(*p, o_lat, W_UV, out, s);
-  return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
+  return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, nullptr, 0, W_UK,
+                     W_UV, out, workspace, workspace_bytes, stream, ev_before, ev_after);
 }
 
 mla_status mla_decode(const mla_decode_params* p, const void* q, const void* c_kv,
@@ -363,6 +452,32 @@ mla_status mla_decode(const mla_decode_params* p, const void* q, const void* c_k
                       void* workspace, size_t workspace_bytes, void* stream) {
   return mla_decode_timed(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK, W_UV, out,
                           workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+mla_status mla_decode_sparse_workspace_size(const mla_decode_params* p, int32_t index_stride,
+                                            size_t* bytes) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = validate_sparse(*p, index_stride);
+  if (st != MLA_OK) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  Layout L;
+  st = layout(*p, &L, index_stride);
+  if (st != MLA_OK) return st;
+  *bytes = L.total;
+  return MLA_OK;
+}
+
+mla_status mla_decode_sparse(const mla_decode_params* p, const void* q, const void* c_kv,
+                             const float* c_kv_scale, const void* k_rope,
+                             const int32_t* block_table, const int32_t* indices,
+                             int32_t index_stride, const int32_t* counts, const void* W_UK,
+                             const void* W_UV, void* out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!indices) return fail(MLA_ERR_INVALID_ARG, "indices is NULL");
+  return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, counts, indices, index_stride,
+                     W_UK, W_UV, out, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const float* c_kv_scale,
@@ -428,6 +543,104 @@ mla_status mla_quantize_e4m3_rows(const float* x, int64_t rows, int32_t d, uint8
       mla::launch_quantize_rows(x, rows, d, codes, scales, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quantiser launch");
   return MLA_OK;
+}
+
+mla_status mla_indexer_scores(const mla_decode_params* p, const mla_dsa_params* d,
+                              const uint8_t* q_I, const float* q_I_scale, const float* w_I,
+                              const uint8_t* k_I, const float* k_I_scale,
+                              const int32_t* block_table, const int32_t* seq_lens, float* scores,
+                              int32_t score_stride, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = validate_dsa(d, false);
+  if (st != MLA_OK) return st;
+  st = check_indexer_ptrs(*p, *d, q_I, q_I_scale, w_I, k_I, k_I_scale);
+  if (st != MLA_OK) return st;
+  if (!block_table || !seq_lens || !scores)
+    return fail(MLA_ERR_INVALID_ARG, "null table, length or score pointer");
+  if (score_stride < 1) return fail(MLA_ERR_INVALID_ARG, "score_stride %d < 1", score_stride);
+  const hipError_t e = mla::launch_indexer(
+      q_I, q_I_scale, w_I, k_I, k_I_scale, block_table, seq_lens, scores, p->batch,
+      d->index_heads, d->index_dim, p->page_size, p->max_blocks_per_seq, p->num_blocks,
+      score_stride, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "indexer launch");
+}
+
+mla_status mla_topk_select(const float* scores, int32_t score_stride, const int32_t* seq_lens,
+                           int32_t batch, int32_t k, int32_t* indices, int32_t index_stride,
+                           int32_t* counts, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || batch > (1 << 24) || k < 1 || k > (1 << 24) || score_stride < 1 ||
+      index_stride < k)
+    return fail(MLA_ERR_INVALID_ARG,
+                "batch=%d k=%d score_stride=%d index_stride=%d (need k >= 1, index_stride >= k)",
+                batch, k, score_stride, index_stride);
+  if (batch == 0) return MLA_OK;
+  if (!scores || !seq_lens || !indices || !counts)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL");
+  const hipError_t e = mla::launch_topk(scores, score_stride, seq_lens, batch, k, indices,
+                                        index_stride, counts, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "top-k launch");
+}
+
+mla_status mla_dsa_decode_workspace_size(const mla_decode_params* p, const mla_dsa_params* d,
+                                         size_t* bytes) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = validate_dsa(d, true);
+  if (st != MLA_OK) return st;
+  st = validate_sparse(*p, d->topk);
+  if (st != MLA_OK) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  DsaLayout L;
+  st = dsa_layout(*p, *d, &L);
+  if (st != MLA_OK) return st;
+  *bytes = L.total;
+  return MLA_OK;
+}
+
+mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, const void* q,
+                          const void* c_kv, const float* c_kv_scale, const void* k_rope,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const uint8_t* q_I, const float* q_I_scale, const float* w_I,
+                          const uint8_t* k_I, const float* k_I_scale, const void* W_UK,
+                          const void* W_UV, void* out, int32_t* indices_out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = validate_dsa(d, true);
+  if (st != MLA_OK) return st;
+  st = validate_sparse(*p, d->topk);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
+  if (st != MLA_OK) return st;
+  st = check_indexer_ptrs(*p, *d, q_I, q_I_scale, w_I, k_I, k_I_scale);
+  if (st != MLA_OK) return st;
+  DsaLayout L;
+  st = dsa_layout(*p, *d, &L);
+  if (st != MLA_OK) return st;
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, %zu required", workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = indices_out ? indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  const int32_t cap = score_cap(*p);
+  hipError_t e = mla::launch_indexer(q_I, q_I_scale, w_I, k_I, k_I_scale, block_table, seq_lens,
+                                     scores, p->batch, d->index_heads, d->index_dim,
+                                     p->page_size, p->max_blocks_per_seq, p->num_blocks, cap, s);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  e = mla::launch_topk(scores, cap, seq_lens, p->batch, d->topk, idx, d->topk, counts, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, counts, idx, d->topk, W_UK,
+                     W_UV, out, ws + L.decode, workspace_bytes - L.decode, stream, nullptr,
+                     nullptr);
 }
 
 int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g) {

@@ -79,14 +79,14 @@ __device__ inline int swz_r8(int r) { return (r >> 1) & 7; }
 // q covers rows 2q and 2q+1 (lane l: row 2q + l/32, LDS chunk l%32), rope
 // instruction j covers rows 8j..8j+7.  Fast path as in the bf16 kernel; rows
 // past the end repeat the last valid token.
-template <int NL>
+template <int NL, bool SP>
 struct StepIssue8 {
   static constexpr int kLat = kStep8 / 2 / NL;
   static constexpr int kRope = kStep8 / 8 / NL;
   static constexpr int kPer = kLat + kRope;
   static_assert(kPer * NL == kLoadsPerStep8, "uniform load counts");
 
-  __device__ static void issue(const AttnArgs& a, lds_t* stage, const Tile& d, int lw, int lane) {
+  __device__ __forceinline__ static void issue(const AttnArgs& a, lds_t* stage, const Tile& d, int lw, int lane) {
     const uint32_t st = (uint32_t)(uintptr_t)stage;
     const int64_t base = (int64_t)d.blk * a.P + d.off;
     if (d.blk >= 0 && d.nv == kStep8) {
@@ -109,6 +109,32 @@ struct StepIssue8 {
     const char* ckv = static_cast<const char*>(a.c_kv);
     const char* krp = static_cast<const char*>(a.k_rope);
     const int32_t rmax = d.nv - 1;
+    if constexpr (SP) {
+      // sparse: slots from the planner's list, read with scalar loads (two
+      // rows per latent load, eight per rope load, picked per lane)
+#pragma unroll
+      for (int m = 0; m < kLat; m++) {
+        const int q = lw + NL * m;
+        const int32_t s0 = sparse_slot_uniform(a, d.b, d.t0 + min(2 * q, rmax));
+        const int32_t s1 = sparse_slot_uniform(a, d.b, d.t0 + min(2 * q + 1, rmax));
+        const int64_t slot = (lane >> 5) ? s1 : s0;
+        const int r = 2 * q + (lane >> 5);
+        dma16(ckv + slot * kCRow8 + (((lane & 31) ^ swz8(r)) << 4), stage + q * 1024);
+      }
+#pragma unroll
+      for (int m = 0; m < kRope; m++) {
+        const int j = lw + NL * m;
+        int32_t sl = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int32_t si = sparse_slot_uniform(a, d.b, d.t0 + min(8 * j + i, rmax));
+          sl = (lane >> 3) == i ? si : sl;
+        }
+        const int r = 8 * j + (lane >> 3);
+        dma16(krp + (int64_t)sl * kRRow8 + (((lane & 7) ^ swz_r8(r)) << 4), stage + kStageC8 + j * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int m = 0; m < kLat; m++) {
       const int q = lw + NL * m;
@@ -146,9 +172,9 @@ __device__ inline void wait_batches(int newer) {
 // refills the descriptor window w + 1 into the buffer of window w - 1 with the
 // loads of step kWin w + kAhead8 + 2, when the value waves (furthest behind,
 // then at step kWin w + 1) have left window w - 1.
-template <int NL>
+template <int NL, bool SP>
 struct Loader8 {
-  static constexpr int kPerWave = StepIssue8<NL>::kPer;
+  static constexpr int kPerWave = StepIssue8<NL, SP>::kPer;
   static_assert(3 * kPerWave + 1 < 64, "vmcnt range");
   static_assert(kAhead8 - 1 <= 3, "wait_batches cases");
   int32_t next, n;
@@ -159,7 +185,7 @@ struct Loader8 {
     if (lw == 0 && next >= kWin + kRefill && next % kWin == kRefill && next + kWin - kRefill < n)
       load_window(a, win, t_begin, t_begin + n, next / kWin + 1, lane);
     const Tile d = read_tile(win, next);
-    StepIssue8<NL>::issue(a, ring + (next % kStages8) * kStage8, d, lw, lane);
+    StepIssue8<NL, SP>::issue(a, ring + (next % kStages8) * kStage8, d, lw, lane);
     next++;
   }
   __device__ void start(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int32_t steps,
@@ -177,7 +203,7 @@ __device__ inline uint32_t e4m3_pair(float x, float y) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, y, 0, false) & 0xffffu;
 }
 
-template <int HB>
+template <int HB, bool SP>
 __global__ __attribute__((amdgpu_flat_work_group_size(Shape8<HB>::NW * 64, Shape8<HB>::NW * 64)))
 void attend_fp8_kernel(AttnArgs a) {
   using S = Shape8<HB>;
@@ -312,8 +338,7 @@ void attend_fp8_kernel(AttnArgs a) {
         for (int j = 0; j < 16; j++) {
           const int r = min(8 * (j >> 2) + 4 * g32 + (j & 3), rmax);
           const int64_t slot = d.blk >= 0 ? (int64_t)d.blk * a.P + d.off + r
-                                          : phys_slot(a.block_table, d.b, d.t0 + r, a.P, a.max_blocks,
-                                                      a.num_blocks);
+                                          : entry_slot(a, d.b, d.t0 + r);
           sc[j] = a.c_kv_scale[slot];
         }
       }
@@ -326,7 +351,7 @@ void attend_fp8_kernel(AttnArgs a) {
     int32_t seg_step = 0;
     lds_t* xb = xbuf + hb * kX8Bytes + lane * 16;
     lds_t* pb = pbuf + hb * kP8Bytes + lane * 16;
-    Loader8<HB> ld;
+    Loader8<HB, SP> ld;
     if (kh == 1) ld.start(a, ring, win, t_begin, n, hb, lane);
     for (int32_t i = 0;; i++) {
       const bool valid = i < n;
@@ -560,12 +585,19 @@ hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s, hipEvent_t ev_sta
   const int32_t HG = a.h / hpg;
   if (HG > 1 && a.splits % 8) return hipErrorInvalidValue;
   const dim3 grid(a.splits * HG);
-  if (hpg == 64)
-    hipExtLaunchKernelGGL((attend_fp8_kernel<2>), grid, dim3(Shape8<2>::NW * 64), 0, s, ev_start,
-                          ev_stop, 0, a);
+  const bool sp = a.slots != nullptr;
+  if (hpg == 64 && !sp)
+    hipExtLaunchKernelGGL((attend_fp8_kernel<2, false>), grid, dim3(Shape8<2>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
+  else if (hpg == 64)
+    hipExtLaunchKernelGGL((attend_fp8_kernel<2, true>), grid, dim3(Shape8<2>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
+  else if (!sp)
+    hipExtLaunchKernelGGL((attend_fp8_kernel<1, false>), grid, dim3(Shape8<1>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
   else
-    hipExtLaunchKernelGGL((attend_fp8_kernel<1>), grid, dim3(Shape8<1>::NW * 64), 0, s, ev_start,
-                          ev_stop, 0, a);
+    hipExtLaunchKernelGGL((attend_fp8_kernel<1, true>), grid, dim3(Shape8<1>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
   return hipGetLastError();
 }
 

@@ -121,8 +121,8 @@ __device__ inline int swz_r(int r) { return (r >> 1) & 7; }
 // row.  Otherwise rows past the end repeat the last valid token (finite data,
 // masked in the softmax) and, when a step can span pages, every lane looks up
 // its own block.
-template <int NL>
-__device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d, int lw,
+template <int NL, bool SP>
+__device__ __forceinline__ void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d, int lw,
                                   int lane) {
   static_assert(kStep % NL == 0 && (kStep / 8) % NL == 0, "uniform row assignment");
   // recompute the per-lane offsets in every call instead of keeping them live
@@ -150,6 +150,29 @@ __device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d
   const char* ckv = static_cast<const char*>(a.c_kv);
   const char* krp = static_cast<const char*>(a.k_rope);
   const int32_t rmax = d.nv - 1;
+  if constexpr (SP) {
+    // sparse: slots from the planner's list, read with scalar loads (one row
+    // per latent load; the eight rows of a rope load picked per lane)
+#pragma unroll
+    for (int m = 0; m < kStep / NL; m++) {
+      const int r = lw + NL * m;
+      const int64_t slot = sparse_slot_uniform(a, d.b, d.t0 + min(r, rmax));
+      dma16(ckv + slot * kCRow + ((lane ^ swz_c(r)) << 4), stage + r * kCRow);
+    }
+#pragma unroll
+    for (int m = 0; m < kStep / 8 / NL; m++) {
+      const int j = lw + NL * m;
+      int32_t sl = 0;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int32_t si = sparse_slot_uniform(a, d.b, d.t0 + min(8 * j + i, rmax));
+        sl = (lane >> 3) == i ? si : sl;
+      }
+      const int r = 8 * j + (lane >> 3);
+      dma16(krp + (int64_t)sl * kRRow + (((lane & 7) ^ swz_r(r)) << 4), stage + kStageC + j * 1024);
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < kStep / NL; m++) {
     const int r = lw + NL * m;
@@ -176,7 +199,7 @@ __device__ inline void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d
 // step kWin w + 2, when every wave has moved past window w - 1 (the value
 // waves, the furthest behind, then consume step kWin w).  It is complete
 // before step kWin w + 4 starts, long before its first use.
-template <int NL>
+template <int NL, bool SP>
 struct Loader {
   static_assert(kLoadsPerStep % NL == 0, "equal load counts per wave");
   static constexpr int kPerWave = kLoadsPerStep / NL;
@@ -189,7 +212,7 @@ struct Loader {
     if (lw == 0 && next >= kWin + 4 && next % kWin == 4 && next + kWin - 4 < n)
       load_window(a, win, t_begin, t_begin + n, next / kWin + 1, lane);
     const Tile d = from_table ? global_tile(a, t_begin + next) : read_tile(win, next);
-    issue_step<NL>(a, ring + (next % kStages) * kStage, d, lw, lane);
+    issue_step<NL, SP>(a, ring + (next % kStages) * kStage, d, lw, lane);
     next++;
   }
   // The first two steps, issued at kernel entry from the planner's table.
@@ -229,7 +252,7 @@ struct Loader {
   }
 };
 
-template <int HB>
+template <int HB, bool SP>
 __global__ __attribute__((amdgpu_flat_work_group_size(Shape<HB>::NW * 64, Shape<HB>::NW * 64)))
 void attend_mfma_kernel(AttnArgs a) {
   using S = Shape<HB>;
@@ -446,7 +469,7 @@ void attend_mfma_kernel(AttnArgs a) {
     const int pw_id = wave - S::NQ;
     const bool loader = pw_id < kNL;
     const int j16 = lane & 15, grp = lane >> 4, e = j16 >> 2, qd = j16 & 3;
-    Loader<kNL> ld;
+    Loader<kNL, SP> ld;
     if (loader) ld.start(a, ring, win, t_begin, n, pw_id, lane);
     wg_barrier();
     int sb1 = 0, sb2 = 0;  // partial-store groups issued in the previous two steps
@@ -577,12 +600,20 @@ hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_
   const int32_t HG = a.h / hpg;
   if (HG > 1 && a.splits % 8) return hipErrorInvalidValue;  // XCD pairing uses whole groups of 8
   const dim3 grid(a.splits * HG);
-  if (hpg == 64)
-    hipExtLaunchKernelGGL((attend_mfma_kernel<2>), grid, dim3(Shape<2>::NW * 64), 0, s, ev_start,
-                          ev_stop, 0, a);
+  // sparse index lists get their own instantiations (slot-list loads)
+  const bool sp = a.slots != nullptr;
+  if (hpg == 64 && !sp)
+    hipExtLaunchKernelGGL((attend_mfma_kernel<2, false>), grid, dim3(Shape<2>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
+  else if (hpg == 64)
+    hipExtLaunchKernelGGL((attend_mfma_kernel<2, true>), grid, dim3(Shape<2>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
+  else if (!sp)
+    hipExtLaunchKernelGGL((attend_mfma_kernel<1, false>), grid, dim3(Shape<1>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
   else
-    hipExtLaunchKernelGGL((attend_mfma_kernel<1>), grid, dim3(Shape<1>::NW * 64), 0, s, ev_start,
-                          ev_stop, 0, a);
+    hipExtLaunchKernelGGL((attend_mfma_kernel<1, true>), grid, dim3(Shape<1>::NW * 64), 0, s,
+                          ev_start, ev_stop, 0, a);
   return hipGetLastError();
 }
 

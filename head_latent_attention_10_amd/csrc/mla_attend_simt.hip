@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
       fresh = false;
       __syncthreads();
     }
-    const int32_t T = seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
+    const int32_t T = attn_len(a, b);
     const int32_t t0 = (int32_t)(tile - a.cu_tiles[b]) * kTile;
     const int32_t nvalid = min(kTile, T - t0);
 
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
       const int32_t tt = tid >> 2, part = tid & 3;
       float s = 0.f;
       if (tt < nvalid) {
-        const int64_t slot = phys_slot(a.block_table, b, t0 + tt, a.P, a.max_blocks, a.num_blocks);
+        const int64_t slot = entry_slot(a, b, t0 + tt);
         float cs = 1.f;
         if (CT == MLA_FP8_E4M3) cs = a.c_kv_scale[slot];
         float sc = 0.f, sr = 0.f;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
       if (d < d_c) {
         float acc = o[k] * alpha;
         for (int32_t tt = 0; tt < nvalid; tt++) {
-          const int64_t slot = phys_slot(a.block_table, b, t0 + tt, a.P, a.max_blocks, a.num_blocks);
+          const int64_t slot = entry_slot(a, b, t0 + tt);
           float c = load_elem<CT>(a.c_kv, slot * d_c + d);
           if (CT == MLA_FP8_E4M3) c *= a.c_kv_scale[slot];
           acc = fmaf(ps[tt], c, acc);

@@ -64,6 +64,11 @@ struct AttnArgs {
   int32_t streams;           // partial slots per (split, sequence)
   int32_t frag_layout;       // part_o in fragment-major layout (frag_offset), else row-major
   float sm_scale_log2;       // sm_scale * log2(e)
+  // Sparse mode (slots != null): sequence b attends to seq_lens[b] entries
+  // (at most idx_stride) whose physical slots (block * P + offset) the planner
+  // wrote to slots[b * idx_stride + n]; tiles number those entries.
+  const int32_t* slots;
+  int32_t idx_stride;
 };
 
 // Read of a table that no kernel of the launch writes (sequence lengths, block
@@ -90,7 +95,42 @@ __device__ inline int64_t phys_slot(const int32_t* block_table, int32_t b, int32
   return (int64_t)blk * P + (t % P);
 }
 
+// Entries sequence b attends to: its tokens (dense) or its index list (sparse).
+__device__ inline int32_t attn_len(const AttnArgs& a, int32_t b) {
+  if (!a.slots) return seq_len_clamped(a.seq_lens, b, a.max_blocks, a.P);
+  const int32_t n = a.seq_lens[b];
+  return n < 0 ? 0 : (n > a.idx_stride ? a.idx_stride : n);
+}
+
+// Physical slot of entry n of sequence b (any lane may differ).
+__device__ inline int64_t entry_slot(const AttnArgs& a, int32_t b, int32_t n) {
+  if (a.slots) return a.slots[(int64_t)b * a.idx_stride + n];
+  return phys_slot(a.block_table, b, n, a.P, a.max_blocks, a.num_blocks);
+}
+
+// Physical slot of entry n of sequence b in sparse mode, for a wave-uniform
+// (b, n): a scalar load, which the vector-memory counter does not track.
+__device__ inline int32_t sparse_slot_uniform(const AttnArgs& a, int32_t b, int32_t n) {
+  return load_ro(a.slots, __builtin_amdgcn_readfirstlane(b * a.idx_stride + n));
+}
+
 // ---------------------------------------------------------------- planner
+// What the planner reads and writes.  Sparse mode (indices != null): sequence
+// b attends to the first seq_lens[b] (clamped to [0, idx_stride]) entries of
+// its row of indices [B, idx_stride], token positions that are clamped into
+// the table row [0, max_blocks * P) and resolved through the block table into
+// slots[b * idx_stride + n].
+struct PlanInput {
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t B, max_blocks, P, num_blocks;
+  const int32_t* indices;
+  int32_t idx_stride;
+  int32_t* slots;
+  int32_t* cu_tiles;
+  int32_t* tiles;
+};
+
 // LDS of one planning work group.
 struct PlanShared {
   int32_t scan[kPlanThreads];
@@ -104,13 +144,15 @@ struct PlanShared {
 // and the groups share out the chunk's tiles, writing one descriptor per tile
 // (tile_word).  The tile's page is resolved here when no tile can span two
 // pages (P a multiple of kTile).
-__device__ inline void plan_block(const int32_t* __restrict__ seq_lens,
-                                  const int32_t* __restrict__ block_table, int32_t B,
-                                  int32_t max_blocks, int32_t P, int32_t num_blocks,
-                                  int32_t* __restrict__ cu_tiles, int32_t* __restrict__ tiles,
-                                  int32_t wg, int32_t nwg, PlanShared& sh) {
+__device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, PlanShared& sh) {
+  const int32_t* __restrict__ seq_lens = in.seq_lens;
+  const int32_t* __restrict__ block_table = in.block_table;
+  const int32_t B = in.B, max_blocks = in.max_blocks, P = in.P, num_blocks = in.num_blocks;
+  int32_t* __restrict__ cu_tiles = in.cu_tiles;
+  int32_t* __restrict__ tiles = in.tiles;
+  const bool sparse = in.indices != nullptr;
   const int tid = threadIdx.x;
-  const bool one_page = P % kTile == 0;
+  const bool one_page = !sparse && P % kTile == 0;
   int32_t carry = 0;
   if (wg == 0 && tid == 0) cu_tiles[0] = 0;
   for (int32_t base = 0; base < B; base += kPlanThreads) {
@@ -118,7 +160,13 @@ __device__ inline void plan_block(const int32_t* __restrict__ seq_lens,
     const int32_t b = base + tid;
     int32_t n = 0;
     if (tid < cnt) {
-      const int32_t T = seq_len_clamped(seq_lens, b, max_blocks, P);
+      int32_t T;
+      if (sparse) {
+        T = seq_lens[b];
+        T = T < 0 ? 0 : (T > in.idx_stride ? in.idx_stride : T);
+      } else {
+        T = seq_len_clamped(seq_lens, b, max_blocks, P);
+      }
       sh.len[tid] = T;
       n = (T + kTile - 1) / kTile;
     }
@@ -158,6 +206,19 @@ __device__ inline void plan_block(const int32_t* __restrict__ seq_lens,
     }
     carry = t_end;
     __syncthreads();
+  }
+  if (!sparse) return;
+  // slot list: entry e = b * idx_stride + n, every planning thread a share
+  const int32_t cap = max_blocks * P;
+  const int64_t total = (int64_t)B * in.idx_stride;
+#pragma unroll 4
+  for (int64_t e = (int64_t)wg * kPlanThreads + tid; e < total; e += (int64_t)nwg * kPlanThreads) {
+    const int32_t b = (int32_t)(e / in.idx_stride), n = (int32_t)(e % in.idx_stride);
+    int32_t T = seq_lens[b];
+    if (n >= T) continue;
+    int32_t t = in.indices[e];
+    t = t < 0 ? 0 : (t >= cap ? cap - 1 : t);
+    in.slots[e] = (int32_t)phys_slot(block_table, b, t, P, max_blocks, num_blocks);
   }
 }
 

@@ -5,19 +5,26 @@
 
 namespace mla {
 
-// Prefix sums of ceil(T_b / kTile) over the batch -> cu_tiles[B + 1], and the
-// descriptor of every tile -> tiles[n][4].
-hipError_t launch_plan(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
-                       int32_t max_blocks, int32_t P, int32_t num_blocks, int32_t* cu_tiles,
-                       int32_t* tiles, hipStream_t s);
+// Prefix sums of ceil(T_b / kTile) over the batch -> cu_tiles[B + 1], the
+// descriptor of every tile -> tiles[n][4], and in sparse mode the slot list.
+hipError_t launch_plan(const PlanInput& in, hipStream_t s);
 
-// Where the split planner writes when it shares the absorption's launch.
+// Where the split planner writes when it shares the absorption's launch
+// (the PlanInput fields that do not come from the decode parameters).
 struct PlanRequest {
   const int32_t* seq_lens;
   const int32_t* block_table;
   int32_t* cu_tiles;
   int32_t* tiles;
+  const int32_t* indices = nullptr;  // sparse mode
+  int32_t idx_stride = 0;
+  int32_t* slots = nullptr;
 };
+
+inline PlanInput plan_input(const mla_decode_params& p, const PlanRequest& r) {
+  return PlanInput{r.seq_lens, r.block_table, p.batch, p.max_blocks_per_seq, p.page_size,
+                   p.num_blocks, r.indices, r.idx_stride, r.slots, r.cu_tiles, r.tiles};
+}
 
 // q_lat[b,i,:d_c] = W_UK[i]^T q_nope[b,i,:]; q_lat[b,i,d_c:] = q_rope[b,i,:].
 // With plan != null the matrix-core absorption also runs the split planner in
@@ -88,5 +95,16 @@ hipError_t launch_cache_write(const mla_cache_write_params& p, const void* x, co
                               void* k_rope, float* part, hipStream_t s);
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int32_t d, uint8_t* codes,
                                 float* scales, hipStream_t s);
+
+// DSA indexer and top-k (mla_dsa.hip).
+bool indexer_mfma_ok(int32_t heads, int32_t dim);
+hipError_t launch_indexer(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* k,
+                          const float* k_scale, const int32_t* block_table,
+                          const int32_t* seq_lens, float* scores, int32_t B, int32_t H, int32_t d,
+                          int32_t P, int32_t max_blocks, int32_t num_blocks, int32_t stride,
+                          hipStream_t s);
+hipError_t launch_topk(const float* scores, int32_t score_stride, const int32_t* seq_lens,
+                       int32_t B, int32_t k, int32_t* indices, int32_t index_stride,
+                       int32_t* counts, hipStream_t s);
 
 }  // namespace mla

@@ -53,7 +53,9 @@ __device__ inline void wg_barrier_nowait() {
 // results, so nothing the compiler allocates is written behind its back; M0 is
 // a reserved register that the compiler sets before each of its own uses.
 __device__ inline void dma16(const void* g, lds_t* l) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)l;
+  // the LDS base is wave-uniform at every call; readfirstlane keeps it in a
+  // scalar register where the compiler cannot prove that itself
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
                : "memory");
 }

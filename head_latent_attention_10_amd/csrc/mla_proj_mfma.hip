@@ -152,11 +152,7 @@ __device__ inline int abs_swz(int row) { return row & 15; }
 
 struct PlanArgs {
   int32_t groups;  // planning work groups at the start of the launch (0: none)
-  const int32_t* seq_lens;
-  const int32_t* block_table;
-  int32_t max_blocks, P, num_blocks;
-  int32_t* cu_tiles;
-  int32_t* tiles;
+  PlanInput in;
 };
 
 template <int OT>
@@ -168,8 +164,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) char ws[kAbsMaxN * kAbsCols * 2];
   static_assert(sizeof(PlanShared) <= sizeof(ws), "planner LDS");
   if ((int32_t)blockIdx.x < pl.groups) {
-    plan_block(pl.seq_lens, pl.block_table, B, pl.max_blocks, pl.P, pl.num_blocks, pl.cu_tiles,
-               pl.tiles, blockIdx.x, pl.groups, *reinterpret_cast<PlanShared*>(ws));
+    plan_block(pl.in, blockIdx.x, pl.groups, *reinterpret_cast<PlanShared*>(ws));
     return;
   }
   const int32_t id = blockIdx.x - pl.groups;
@@ -276,9 +271,7 @@ bool proj_mfma_supported(const mla_decode_params& p) {
 hipError_t launch_absorb_mfma(const mla_decode_params& p, const void* q, const void* W_UK,
                               void* q_lat, int32_t ot, const PlanRequest* plan, hipStream_t s) {
   PlanArgs pl{};
-  if (plan)
-    pl = PlanArgs{kPlanGroups, plan->seq_lens, plan->block_table, p.max_blocks_per_seq,
-                  p.page_size, p.num_blocks, plan->cu_tiles, plan->tiles};
+  if (plan) pl = PlanArgs{kPlanGroups, plan_input(p, *plan)};
   const dim3 grid(p.num_heads * kAbsColGroups + pl.groups);
   if (ot == MLA_BF16)
     hipLaunchKernelGGL((absorb_mfma_kernel<MLA_BF16>), grid, dim3(256), 0, s,

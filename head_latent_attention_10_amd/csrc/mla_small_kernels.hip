@@ -5,22 +5,13 @@ namespace mla {
 
 // ------------------------------------------------------------------ planner
 // kPlanGroups work groups running plan_block.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seq_lens,
-                                                             const int32_t* __restrict__ block_table,
-                                                             int32_t B, int32_t max_blocks, int32_t P,
-                                                             int32_t num_blocks,
-                                                             int32_t* __restrict__ cu_tiles,
-                                                             int32_t* __restrict__ tiles) {
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanInput in) {
   __shared__ PlanShared sh;
-  plan_block(seq_lens, block_table, B, max_blocks, P, num_blocks, cu_tiles, tiles, blockIdx.x,
-             gridDim.x, sh);
+  plan_block(in, blockIdx.x, gridDim.x, sh);
 }
 
-hipError_t launch_plan(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
-                       int32_t max_blocks, int32_t P, int32_t num_blocks, int32_t* cu_tiles,
-                       int32_t* tiles, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGroups), dim3(kPlanThreads), 0, s, seq_lens,
-                     block_table, B, max_blocks, P, num_blocks, cu_tiles, tiles);
+hipError_t launch_plan(const PlanInput& in, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(kPlanGroups), dim3(kPlanThreads), 0, s, in);
   return hipGetLastError();
 }
 

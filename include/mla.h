@@ -241,6 +241,91 @@ mla_status mla_cache_write(const mla_cache_write_params* p, const void* x, const
 mla_status mla_quantize_e4m3_rows(const float* x, int64_t rows, int32_t d, uint8_t* codes,
                                   float* scales, void* stream);
 
+/* ------------------------------------------------------------------------
+ * DeepSeek Sparse Attention (DSA) at decode time ("TransMLA & Sparse Latent
+ * Attention", Chapter 6 "DeepSeek's Second Wall": "The lightning indexer",
+ * "Fine-grained token selection"; Chapter 7: DSA runs on MLA's absorbed
+ * (MQA-mode) decode path, one selection per token shared by all heads, and
+ * every cached position keeps an indexer key beside its latent).
+ *
+ *   I[b, s] = sum_j w[b, j] * ReLU(q_I[b, j, :] . k_I[b, s, :])  (no softmax)
+ *   S_b     = the k positions s < T_b with the largest I[b, s]; equal scores
+ *             go to the earlier position; every position when T_b <= k
+ *   out     = the decode step above with the softmax over S_b only.
+ *
+ * Indexer storage (fp8, as the chapter runs it):
+ *   q_I       [batch, index_heads, index_dim]  E4M3FN codes
+ *   q_I_scale [batch, index_heads] fp32        value = scale * e4m3(code), > 0
+ *   w_I       [batch, index_heads] fp32        head weights (any sign)
+ *   k_I       [num_blocks, page_size, index_dim] E4M3FN codes, paged through
+ *             the same block table as c_kv
+ *   k_I_scale [num_blocks, page_size] fp32     per-slot scale, >= 0
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t index_heads;  /* H_I >= 1 (64 in DeepSeek-V3.2; the matrix-core
+                           indexer serves 64 heads of width 128)           */
+  int32_t index_dim;    /* d_I, 1..1024 (128 in DeepSeek-V3.2)              */
+  int32_t topk;         /* k >= 1 (2048 in DeepSeek-V3.2)                   */
+} mla_dsa_params;
+
+/* Index scores of every cached position of every sequence.  Uses batch,
+ * page_size, max_blocks_per_seq and num_blocks of *p.
+ *   scores [batch, score_stride] fp32: scores[b][s] for s < min(T_b,
+ *   max_blocks_per_seq * page_size, score_stride); other entries untouched.
+ * The matrix-core path (64 heads, width 128) needs q_I and k_I 16-byte
+ * aligned.  fp32 accumulation; the head sum is in a fixed order, so results
+ * are bitwise reproducible. */
+mla_status mla_indexer_scores(const mla_decode_params* p, const mla_dsa_params* d,
+                              const uint8_t* q_I, const float* q_I_scale, const float* w_I,
+                              const uint8_t* k_I, const float* k_I_scale,
+                              const int32_t* block_table, const int32_t* seq_lens, float* scores,
+                              int32_t score_stride, void* stream);
+
+/* Top-k selection per sequence: with T_b = clamp(seq_lens[b], 0,
+ * score_stride), writes min(T_b, k) positions, increasing, to
+ * indices[b][0 ..) (row stride index_stride >= k) and that count to
+ * counts[b].  Scores are ordered as floats (-0 equals +0; NaN by its bits);
+ * equal scores go to the earlier position.  Integer-exact: the same scores
+ * always give the same selection. */
+mla_status mla_topk_select(const float* scores, int32_t score_stride, const int32_t* seq_lens,
+                           int32_t batch, int32_t k, int32_t* indices, int32_t index_stride,
+                           int32_t* counts, void* stream);
+
+/* Bytes of workspace mla_decode_sparse needs for index lists of row stride
+ * index_stride (>= 1). */
+mla_status mla_decode_sparse_workspace_size(const mla_decode_params* p, int32_t index_stride,
+                                            size_t* bytes);
+
+/* The decode step over index lists: sequence b attends to the counts[b]
+ * (clamped to [0, index_stride]) cached positions indices[b][0 .. counts[b])
+ * instead of all its tokens.  Positions are clamped into
+ * [0, max_blocks_per_seq * page_size) and resolved through block_table; a
+ * position past T_b reads whatever its slot holds.  A repeated position
+ * counts twice.  Other arguments and rules as for mla_decode. */
+mla_status mla_decode_sparse(const mla_decode_params* p, const void* q, const void* c_kv,
+                             const float* c_kv_scale, const void* k_rope,
+                             const int32_t* block_table, const int32_t* indices,
+                             int32_t index_stride, const int32_t* counts, const void* W_UK,
+                             const void* W_UV, void* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Bytes of workspace mla_dsa_decode needs. */
+mla_status mla_dsa_decode_workspace_size(const mla_decode_params* p, const mla_dsa_params* d,
+                                         size_t* bytes);
+
+/* The whole DSA decode step: index scores, top-k, and the decode over the
+ * selection (mla_indexer_scores, mla_topk_select, mla_decode_sparse on the
+ * workspace).  indices_out [batch, topk] int32 may be NULL; when given it
+ * receives the selection (min(T_b, topk) positions per row, increasing; the
+ * rest of the row is untouched). */
+mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, const void* q,
+                          const void* c_kv, const float* c_kv_scale, const void* k_rope,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const uint8_t* q_I, const float* q_I_scale, const float* w_I,
+                          const uint8_t* k_I, const float* k_I_scale, const void* W_UK,
+                          const void* W_UV, void* out, int32_t* indices_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
