@@ -17,6 +17,10 @@ are read from HBM), is replayed and timed with events; reported are the time
 per call and its algorithmic bytes (weights, hidden states, the rows written)
 per second against the 8 TB/s peak.
 
+The DSA sparse decode step (lightning indexer, top-k, decode over the
+selected tokens; mla_dsa_decode) is measured the same way under `extra` on
+its own workloads, with each stage also timed alone.
+
 The step is timed over K plain mla_decode calls.  The attention kernel is then
 timed alone over K more steps with HIP events recorded on its stream around
 its launch (mla_decode_timed); `roofline.achieved` is the algorithmic
@@ -261,6 +265,106 @@ def measure_writer(name: str, steps: int, warmup: int, copies: int = 64):
             "weight_copies_rotated": copies}
 
 
+def measure_dsa(name: str, steps: int, warmup: int):
+    """Time the DSA decode step (mla_dsa_decode: indexer, top-k, decode over the
+    selection) on the workload `name`, with copies of the indexer keys and the
+    latent cache rotated so that every step reads them from HBM; then each
+    stage alone (its entry point between two events)."""
+    import numpy as np
+    import torch
+
+    from head_latent_attention_10_amd import _lib
+    from head_latent_attention_10_amd.device import DeviceInputs, out_torch_dtype, to_device_array
+    from mla_inputs.dsa import DSA_CONFIGS, generate_dsa
+
+    dcfg = DSA_CONFIGS[name]
+    t0 = time.time()
+    inp = generate_dsa(dcfg)
+    cfg, k = inp.cfg, dcfg.topk
+    dev = DeviceInputs(inp.dense)
+    ix = {f: to_device_array(getattr(inp, f), dev.device)
+          for f in ("q_I", "q_I_scale", "w_I", "k_I", "k_I_scale")}
+    p = dev.params()
+    d = _lib.make_dsa_params(dcfg.index_heads, dcfg.index_dim, k)
+    lens = inp.seq_lens.astype(np.int64)
+    sel = np.minimum(lens, k)
+    touched = int(lens.sum()) * (dcfg.index_dim + 4) + int(sel.sum()) * 1152
+    copies = max(2, math.ceil(768e6 / touched))
+    c_copies = [dev.c_kv] + [dev.c_kv.clone() for _ in range(copies - 1)]
+    r_copies = [dev.k_rope] + [dev.k_rope.clone() for _ in range(copies - 1)]
+    s_copies = [dev.c_kv_scale] * copies
+    if dev.c_kv_scale is not None:
+        s_copies = [dev.c_kv_scale] + [dev.c_kv_scale.clone() for _ in range(copies - 1)]
+    k_copies = [ix["k_I"]] + [ix["k_I"].clone() for _ in range(copies - 1)]
+    ks_copies = [ix["k_I_scale"]] + [ix["k_I_scale"].clone() for _ in range(copies - 1)]
+    ws_bytes = _lib.mla_dsa_decode_workspace_size(p, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev.device)
+    out = torch.empty((cfg.batch, cfg.heads, cfg.d_v), dtype=out_torch_dtype(cfg.out_dtype),
+                      device=dev.device)
+    torch.cuda.synchronize()
+    print(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s, {copies} copies",
+          file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def step(j):
+        i = j % copies
+        _lib.mla_dsa_decode(p, d, dev.q, c_copies[i], s_copies[i], r_copies[i], dev.block_table,
+                            dev.seq_lens, ix["q_I"], ix["q_I_scale"], ix["w_I"], k_copies[i],
+                            ks_copies[i], dev.W_UK, dev.W_UV, out, None, ws, ws_bytes, stream)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for j in range(steps):
+        step(warmup + j)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+
+    # the stages alone, each between two events (marker events: a few us of
+    # launch overhead included)
+    cap = int(inp.block_table.shape[1] * cfg.page_size)
+    scores = torch.empty((cfg.batch, cap), dtype=torch.float32, device=dev.device)
+    idx = torch.empty((cfg.batch, k), dtype=torch.int32, device=dev.device)
+    cnt = torch.empty((cfg.batch,), dtype=torch.int32, device=dev.device)
+    sws = _lib.mla_decode_sparse_workspace_size(p, k)
+    sw = torch.empty(sws, dtype=torch.uint8, device=dev.device)
+
+    def stage(fn, n=steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for j, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(j)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / n
+
+    t_idx = stage(lambda j: _lib.mla_indexer_scores(
+        p, d, ix["q_I"], ix["q_I_scale"], ix["w_I"], k_copies[j % copies], ks_copies[j % copies],
+        dev.block_table, dev.seq_lens, scores, cap, stream))
+    t_topk = stage(lambda j: _lib.mla_topk_select(scores, cap, dev.seq_lens, cfg.batch, k, idx, k,
+                                                  cnt, stream))
+    t_dec = stage(lambda j: _lib.mla_decode_sparse(
+        p, dev.q, c_copies[j % copies], s_copies[j % copies], r_copies[j % copies],
+        dev.block_table, idx, k, cnt, dev.W_UK, dev.W_UV, out, sw, sws, stream))
+    esz = 1 if cfg.cache_dtype == "e4m3" else 2
+    row = cfg.d_latent * esz + cfg.d_rope * 2 + (4 if cfg.cache_dtype == "e4m3" else 0)
+    idx_bytes = int(lens.sum()) * (dcfg.index_dim + 4 + 4)
+    dec_bytes = int(sel.sum()) * row + 2 * cfg.heads * cfg.d_latent * cfg.d_nope * 2
+    alg = idx_bytes + int(lens.sum()) * 4 + int(sel.sum()) * 4 + dec_bytes
+    return {"us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
+            "batch": cfg.batch, "topk": k, "context_tokens": int(lens.sum()),
+            "selected_tokens": int(sel.sum()), "cache_dtype": cfg.cache_dtype,
+            "algorithmic_bytes": alg, "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "stage_us": {"indexer": round(t_idx * 1e3, 2), "topk": round(t_topk * 1e3, 2),
+                         "sparse_decode": round(t_dec * 1e3, 2)},
+            "indexer_key_GBps": round(idx_bytes / (t_idx * 1e-3) / 1e9, 1),
+            "copies_rotated": copies}
+
+
 def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: int, commands):
     """HBM bytes per attention launch from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB
@@ -310,6 +414,10 @@ def main():
                     help="latent-cache writer workloads reported under 'extra' (comma list)")
     ap.add_argument("--writer-only", action="store_true",
                     help="measure only the latent-cache writer workloads (for profiling)")
+    ap.add_argument("--dsa", default="dsa_dsv3_ragged_32k,dsa_dsv3_b4_128k,dsa_dsv3_fp8_16k",
+                    help="DSA sparse-decode workloads reported under 'extra' (comma list)")
+    ap.add_argument("--dsa-only", action="store_true",
+                    help="measure only the DSA workloads (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -345,6 +453,11 @@ def main():
         print(json.dumps({"cache_writer": out}))
         return
 
+    if args.dsa_only:
+        out = {w: measure_dsa(w, args.steps, args.warmup) for w in args.dsa.split(",") if w}
+        print(json.dumps({"dsa": out}))
+        return
+
     main_run = measure(args.workload, args.steps, args.warmup, args.num_splits)
     extra = {}
     for w in [w for w in args.also.split(",") if w]:
@@ -357,6 +470,8 @@ def main():
         del r
     for w in [w for w in args.writers.split(",") if w]:
         extra["cache_" + w] = measure_writer(w, max(320, args.steps), max(5, args.warmup))
+    for w in [w for w in args.dsa.split(",") if w]:
+        extra[w] = measure_dsa(w, max(10, args.steps // 2), max(3, args.warmup // 2))
 
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20

@@ -208,17 +208,30 @@ __device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, 
     __syncthreads();
   }
   if (!sparse) return;
-  // slot list: entry e = b * idx_stride + n, every planning thread a share
+  // slot list: entries e = b * idx_stride + n, eight per thread at a time so
+  // that their index and table loads are in flight together
   const int32_t cap = max_blocks * P;
-  const int64_t total = (int64_t)B * in.idx_stride;
-#pragma unroll 4
-  for (int64_t e = (int64_t)wg * kPlanThreads + tid; e < total; e += (int64_t)nwg * kPlanThreads) {
-    const int32_t b = (int32_t)(e / in.idx_stride), n = (int32_t)(e % in.idx_stride);
-    int32_t T = seq_lens[b];
-    if (n >= T) continue;
-    int32_t t = in.indices[e];
-    t = t < 0 ? 0 : (t >= cap ? cap - 1 : t);
-    in.slots[e] = (int32_t)phys_slot(block_table, b, t, P, max_blocks, num_blocks);
+  const int32_t total = B * in.idx_stride;  // < 2^31 (checked on the host)
+  const int32_t nthr = nwg * kPlanThreads;
+  for (int32_t e0 = wg * kPlanThreads + tid; e0 < total; e0 += 8 * nthr) {
+    int32_t t[8], bb[8];
+    bool ok[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int32_t e = e0 + j * nthr;
+      bb[j] = e < total ? e / in.idx_stride : 0;
+      ok[j] = e < total && e - bb[j] * in.idx_stride < seq_lens[bb[j]];
+      t[j] = in.indices[e < total ? e : 0];
+    }
+    int32_t sl[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {  // unconditional (valid addresses), so they overlap
+      const int32_t tc = t[j] < 0 ? 0 : (t[j] >= cap ? cap - 1 : t[j]);
+      sl[j] = (int32_t)phys_slot(block_table, bb[j], tc, P, max_blocks, num_blocks);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (ok[j]) in.slots[e0 + j * nthr] = sl[j];
   }
 }
 

@@ -18,10 +18,11 @@
 // holds 16 heads of one token and the head sum is in-lane plus one exchange.
 //
 // Top-k: one work group per sequence.  Scores map to unsigned keys that order
-// like the floats (-0 taken as +0); an MSB-first radix select (11 + 11 + 10
-// bits, LDS histograms) finds the k-th largest key K and how many keys equal
-// to K are taken (the earliest positions); a final pass writes the selected
-// positions in increasing order.
+// like the floats (-0 taken as +0).  A sample bounds the k-th largest key from
+// below, the keys above the bound are gathered in position order in LDS, and
+// the k-th largest key K and how many keys equal to K are taken (the earliest
+// positions) are found there by counting; the selected positions come out in
+// increasing order (details at topk_kernel).
 #include "mla_mfma_util.hpp"
 
 namespace mla {
@@ -143,6 +144,14 @@ __global__ __launch_bounds__(kIdxSimt) void indexer_simt_kernel(IndexerArgs a) {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;
+constexpr int kCandCap = 12288;                 // candidates kept in LDS
+constexpr int kSeg = kCandCap / kTopkWaves;     // candidates per wave segment (768)
+constexpr int kSegLane = kSeg / 64;             // per lane (12)
+constexpr int kSample = 4096;                   // sampled keys (4 per thread)
+constexpr int kAllCand = 6144;                  // up to this length every key is a candidate
+constexpr int kMaxBlocks = 256;                 // 1024-position blocks of the fast path
+constexpr int kFastMaxT = kMaxBlocks * kTopkThreads;
+constexpr int kGrp = 32;                        // position blocks whose loads go out together
 
 // Unsigned key ordering like the float (-0 is +0; larger float, larger key).
 __device__ inline uint32_t score_key(float f) {
@@ -167,6 +176,32 @@ __device__ inline uint32_t block_scan(uint32_t v, uint32_t* s_wave) {
   return v + add;
 }
 
+// Sum over the work group.
+__device__ inline uint32_t block_sum_u32(uint32_t v, uint32_t* s_wave) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; w++) t += s_wave[w];
+  return t;
+}
+
+// Maximum over the work group (two barriers).
+__device__ inline uint32_t block_max_u32(uint32_t v, uint32_t* s_wave) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; w++) t = max(t, s_wave[w]);
+  return t;
+}
+
 struct TopkArgs {
   const float* scores;
   int32_t score_stride;
@@ -177,77 +212,297 @@ struct TopkArgs {
   int32_t* counts;
 };
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t s_hist[kBins];
-  __shared__ uint32_t s_wave[kTopkWaves];
-  __shared__ uint32_t s_pick[2];
-  const int32_t b = blockIdx.x;
-  const int tid = threadIdx.x;
-  int32_t T = a.seq_lens[b];
-  T = T < 0 ? 0 : (T > a.score_stride ? a.score_stride : T);
-  int32_t* out = a.indices + (int64_t)b * a.index_stride;
-  if (T <= a.k) {  // everything is selected
-    for (int32_t i = tid; i < T; i += kTopkThreads) out[i] = i;
-    if (tid == 0) a.counts[b] = T;
-    return;
+struct TopkShared {
+  uint32_t cand_key[kCandCap];
+  int32_t cand_pos[kCandCap];
+  union {
+    uint32_t bits[kFastMaxT / 32];  // selected positions (fast path)
+    uint32_t hist[kBins];           // radix histogram (general path)
+  };
+  uint32_t whist[kTopkWaves][256];  // per-wave digit histograms (fast path)
+  uint32_t wave[kTopkWaves];
+  uint32_t seg[kTopkWaves];  // candidates of each wave's segment
+  uint32_t pick[4];
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: row shifts, then
+// the row totals broadcast to the rows after them).
+__device__ inline uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Radix select over keys held by the threads (key[i] for i < n, n
+// wave-uniform, where ok[i]): K = the rank-th largest key, searched over bits
+// [low, top) eight at a time from the top (bits at and above top are base's,
+// those below low stay zero).  Each wave counts its keys' digits in its own
+// LDS histogram; wave 0 then adds the sixteen histograms (lane l: bins
+// 255 - 4l down to 252 - 4l), scans them from the top bin down and publishes
+// the digit, so a round costs two barriers.  With low = 0, *rem = rank -
+// #(keys > K) and *eq = #(keys == K).
+template <int N>
+__device__ uint32_t radix_rank(const uint32_t (&key)[N], const bool (&ok)[N], int n, uint32_t rank,
+                               uint32_t base, int top, int low, TopkShared& sh, uint32_t* rem_out,
+                               uint32_t* eq_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t K = base, rem = rank, eq = 0;
+  for (int hi = top; hi > low;) {
+    const int width = min(8, hi - low);
+    const int sft = hi - width;
+    reinterpret_cast<u32x4*>(sh.whist[wave])[lane] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      if (i < n && ok[i] && (hi >= 32 || (key[i] >> hi) == (K >> hi)))
+        atomicAdd(&sh.whist[wave][(key[i] >> sft) & ((1u << width) - 1u)], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l: bins 4 (63 - l) .. 4 (63 - l) + 3, i.e. descending with l
+      const int b0 = 4 * (63 - lane);
+      u32x4 t = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; w++) t += reinterpret_cast<const u32x4*>(sh.whist[w])[63 - lane];
+      const uint32_t mine = t[0] + t[1] + t[2] + t[3];
+      const uint32_t incl = wave_incl_scan(mine);      // keys in bins >= b0
+      uint32_t above = incl - mine;                     // keys in bins >= b0 + 4
+#pragma unroll
+      for (int e = 3; e >= 0; e--) {
+        if (above < rem && rem <= above + t[e]) {
+          sh.pick[0] = (uint32_t)(b0 + e);
+          sh.pick[1] = above;
+          sh.pick[2] = t[e];
+        }
+        above += t[e];
+      }
+    }
+    __syncthreads();
+    K |= sh.pick[0] << sft;
+    rem -= sh.pick[1];
+    eq = sh.pick[2];
+    hi = sft;
   }
-  const float* sc = a.scores + (int64_t)b * a.score_stride;
-  // radix select, most significant digit first
-  uint32_t prefix = 0, rem = (uint32_t)a.k;
+  if (rem_out) *rem_out = rem;
+  if (eq_out) *eq_out = eq;
+  return K;
+}
+
+// Radix select over all T keys in global memory (11 + 11 + 10 bits, LDS
+// histograms): the k-th largest key K and how many keys equal to K are taken.
+__device__ void radix_select_global(const float* sc, int32_t T, uint32_t k, TopkShared& sh,
+                                    uint32_t* K_out, uint32_t* rem_out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, rem = k;
   constexpr int kShift[3] = {21, 10, 0};
   constexpr int kWidth[3] = {11, 11, 10};
 #pragma unroll
   for (int pass = 0; pass < 3; pass++) {
     const int shift = kShift[pass], width = kWidth[pass];
     const uint32_t hi_mask = pass == 0 ? 0u : ~((1u << (shift + width)) - 1u);
-    for (int i = tid; i < kBins; i += kTopkThreads) s_hist[i] = 0;
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int32_t i = tid; i < T; i += kTopkThreads) {
       const uint32_t key = score_key(sc[i]);
-      if ((key & hi_mask) == prefix) atomicAdd(&s_hist[(key >> shift) & ((1u << width) - 1u)], 1u);
+      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & ((1u << width) - 1u)], 1u);
     }
     __syncthreads();
     // counts from the top bin down: thread t owns bins 2047 - 2t and 2046 - 2t
     const int hb = kBins - 1 - 2 * tid;
-    const uint32_t c0 = s_hist[hb], c1 = s_hist[hb - 1];
-    const uint32_t incl = block_scan(c0 + c1, s_wave);  // keys in bins >= hb - 1
+    const uint32_t c0 = sh.hist[hb], c1 = sh.hist[hb - 1];
+    const uint32_t incl = block_scan(c0 + c1, sh.wave);  // keys in bins >= hb - 1
     const uint32_t above = incl - c0 - c1;                // keys in bins > hb
-    // the bin holding the rem-th largest key
     if (above < rem && rem <= above + c0) {
-      s_pick[0] = hb;
-      s_pick[1] = above;
+      sh.pick[0] = hb;
+      sh.pick[1] = above;
     } else if (above + c0 < rem && rem <= incl) {
-      s_pick[0] = hb - 1;
-      s_pick[1] = above + c0;
+      sh.pick[0] = hb - 1;
+      sh.pick[1] = above + c0;
     }
     __syncthreads();
-    prefix |= s_pick[0] << shift;
-    rem -= s_pick[1];
+    prefix |= sh.pick[0] << shift;
+    rem -= sh.pick[1];
     __syncthreads();
   }
-  // prefix = K (the k-th largest key); take every key above it and the first
-  // rem keys equal to it, in position order.  Thread t walks positions
-  // [t * chunk, (t + 1) * chunk).
-  const uint32_t K = prefix;
-  const int32_t chunk = (T + kTopkThreads - 1) / kTopkThreads;
-  const int32_t p0 = min(T, tid * chunk), p1 = min(T, p0 + chunk);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int32_t i = p0; i < p1; i++) {
-    const uint32_t key = score_key(sc[i]);
-    n_gt += key > K;
-    n_eq += key == K;
+  *K_out = prefix;
+  *rem_out = rem;
+}
+
+// One work group per sequence.  Fast path (k < T <= 262144):
+//  1. L = the R-th largest of 4096 keys at evenly spaced positions, R a few
+//     standard deviations above the sample rank of the k-th largest key, so
+//     that at least k keys are >= L and not many more (L = 0, every key, when
+//     T <= 6144);
+//  2. one pass over the scores: each wave appends its keys >= L (the
+//     candidates) with their positions to its own LDS segment (ballots, no
+//     atomics);
+//  3. K = the k-th largest candidate key, by counting; the keys above K and,
+//     of those equal to K, the rem = k - #(keys > K) earliest (the rem-th
+//     smallest position found the same way when there are more) are marked in
+//     a bitmap of the positions;
+//  4. a scan of the bitmap writes the positions in increasing order.
+// When the sample bound misses (fewer than k candidates, or a full segment)
+// or T is larger, a radix select over global memory gives K and rem and the
+// output pass walks all T positions.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+  __shared__ TopkShared sh;
+  const int32_t b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t T = a.seq_lens[b];
+  T = T < 0 ? 0 : (T > a.score_stride ? a.score_stride : T);
+  int32_t* out = a.indices + (int64_t)b * a.index_stride;
+  const uint32_t k = (uint32_t)a.k;
+  if (T <= a.k) {  // everything is selected
+    for (int32_t i = tid; i < T; i += kTopkThreads) out[i] = i;
+    if (tid == 0) a.counts[b] = T;
+    return;
   }
-  uint32_t gt = block_scan(n_gt, s_wave) - n_gt;
-  __syncthreads();
-  uint32_t eq = block_scan(n_eq, s_wave) - n_eq;
-  for (int32_t i = p0; i < p1; i++) {
-    const uint32_t key = score_key(sc[i]);
-    if (key > K) {
-      out[gt + min(eq, rem)] = i;
-      gt++;
-    } else if (key == K) {
-      if (eq < rem) out[gt + eq] = i;
-      eq++;
+  const float* sc = a.scores + (int64_t)b * a.score_stride;
+  bool fast = T <= kFastMaxT;
+  uint32_t L = 0;
+  if (fast && T > kAllCand) {
+    const uint32_t r = (uint32_t)(((uint64_t)k * kSample + T - 1) / T);
+    const uint32_t R = r + 4 * (uint32_t)ceilf(sqrtf((float)r)) + 16;
+    if (R >= kSample) {
+      fast = false;
+    } else {
+      uint32_t key[4];
+      bool ok[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        key[e] = score_key(sc[((int64_t)(tid + kTopkThreads * e) * T) / kSample]);
+        ok[e] = true;
+      }
+      // the top 16 bits of the R-th largest sampled key: a lower bound is all
+      // the candidate pass needs
+      L = radix_rank<4>(key, ok, 4, R, 0u, 32, 16, sh, nullptr, nullptr);
+    }
+  }
+  if (fast) {
+    const int32_t nwords = (T + 31) / 32;
+    for (int32_t w = tid; w < nwords; w += kTopkThreads) sh.bits[w] = 0;
+    // one pass: wave w appends its candidates to segment w
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int32_t nblk = (T + kTopkThreads - 1) / kTopkThreads;
+    const int32_t seg0 = wave * kSeg;
+    uint32_t cnt = 0;  // wave-uniform
+    for (int32_t j0 = 0; j0 < nblk; j0 += kGrp) {
+      float v[kGrp];
+#pragma unroll
+      for (int g = 0; g < kGrp; g++) {
+        const int32_t i = (j0 + g) * kTopkThreads + tid;
+        v[g] = i < T ? sc[i] : 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < kGrp; g++) {
+        const int32_t i = (j0 + g) * kTopkThreads + tid;
+        const uint32_t key = score_key(v[g]);
+        const bool c = i < T && key >= L;
+        const uint64_t m = __ballot(c);
+        const uint32_t o = cnt + (uint32_t)__popcll(m & below);
+        if (c && o < (uint32_t)kSeg) {
+          sh.cand_key[seg0 + o] = key;
+          sh.cand_pos[seg0 + o] = i;
+        }
+        cnt += (uint32_t)__popcll(m);
+      }
+    }
+    if (lane == 0) sh.seg[wave] = cnt;
+    __syncthreads();
+    uint32_t ncand = 0;
+    bool full = false;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; w++) {
+      ncand += sh.seg[w];
+      full |= sh.seg[w] > (uint32_t)kSeg;
+    }
+    fast = ncand >= k && !full;
+  }
+  if (fast) {
+    // this wave's segment: lane l holds entries l, l + 64, ...
+    const uint32_t n_seg = sh.seg[wave];
+    const int ne = (int)((n_seg + 63) / 64);  // wave-uniform
+    uint32_t key[kSegLane];
+    int32_t pos[kSegLane];
+    bool ok[kSegLane];
+    uint32_t kmax = 0;
+#pragma unroll
+    for (int e = 0; e < kSegLane; e++) {
+      const uint32_t x = lane + 64 * e;
+      ok[e] = x < n_seg;
+      key[e] = ok[e] ? sh.cand_key[wave * kSeg + x] : 0u;
+      pos[e] = ok[e] ? sh.cand_pos[wave * kSeg + x] : 0;
+      kmax = max(kmax, key[e]);
+    }
+    // every candidate lies in [L, max]; K shares their common leading bits
+    kmax = block_max_u32(kmax, sh.wave);
+    const int common = (L ^ kmax) == 0 ? 32 : __clz(L ^ kmax);
+    const int top = max(8, 32 - common);  // at least one pass (it counts the equal keys)
+    const uint32_t base = top == 32 ? 0u : (L & ~((1u << top) - 1u));
+    uint32_t rem, eq;
+    const uint32_t K = radix_rank<kSegLane>(key, ok, ne, k, base, top, 0, sh, &rem, &eq);
+    uint32_t last = 0xffffffffu;  // equal keys at positions <= last are taken
+    if (eq > rem) {
+      uint32_t pk[kSegLane];      // larger for earlier positions, among the equal keys
+      bool pok[kSegLane];
+#pragma unroll
+      for (int e = 0; e < kSegLane; e++) {
+        pok[e] = ok[e] && key[e] == K;
+        pk[e] = ~(uint32_t)pos[e];
+      }
+      last = ~radix_rank<kSegLane>(pk, pok, ne, rem, 0u, 32, 0, sh, nullptr, nullptr);
+    }
+#pragma unroll
+    for (int e = 0; e < kSegLane; e++) {
+      if (ok[e] && (key[e] > K || (key[e] == K && (uint32_t)pos[e] <= last)))
+        atomicOr(&sh.bits[pos[e] >> 5], 1u << (pos[e] & 31));
+    }
+    __syncthreads();
+    // positions in increasing order: thread t scans words [8t, 8t + 8)
+    const int32_t nwords = (T + 31) / 32;
+    uint32_t wv[8], nb = 0;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int32_t w = 8 * tid + e;
+      wv[e] = w < nwords ? sh.bits[w] : 0u;
+      nb += (uint32_t)__popc(wv[e]);
+    }
+    uint32_t o = block_scan(nb, sh.wave) - nb;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      uint32_t x = wv[e];
+      while (x) {
+        const int bit = __ffs(x) - 1;
+        out[o++] = (8 * tid + e) * 32 + bit;
+        x &= x - 1;
+      }
+    }
+  } else {
+    uint32_t K, rem;
+    radix_select_global(sc, T, k, sh, &K, &rem);
+    // thread t walks positions [t * chunk, (t + 1) * chunk)
+    const int32_t chunk = (T + kTopkThreads - 1) / kTopkThreads;
+    const int32_t p0 = min(T, tid * chunk), p1 = min(T, p0 + chunk);
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int32_t i = p0; i < p1; i++) {
+      const uint32_t key = score_key(sc[i]);
+      n_gt += key > K;
+      n_eq += key == K;
+    }
+    uint32_t gt = block_scan(n_gt, sh.wave) - n_gt;
+    uint32_t eq = block_scan(n_eq, sh.wave) - n_eq;
+    for (int32_t i = p0; i < p1; i++) {
+      const uint32_t key = score_key(sc[i]);
+      if (key > K) {
+        out[gt + min(eq, rem)] = i;
+        gt++;
+      } else if (key == K) {
+        if (eq < rem) out[gt + eq] = i;
+        eq++;
+      }
     }
   }
   if (tid == 0) a.counts[b] = a.k;

@@ -134,6 +134,36 @@ def test_topk_bit_exact(k, lens):
         assert (idx[b, len(want):] == -7).all()
 
 
+def test_topk_paths_past_the_sample_bound():
+    """Inputs the sampled lower bound cannot serve: a sequence longer than the
+    in-LDS path allows, large scores only between the sampled positions, and k
+    close to T -- all must still match the oracle bit for bit."""
+    rng = np.random.default_rng(4242)
+    T1, T2, T3 = 300000, 20000, 20000
+    lens, ks = [T1, T2, T3], 2048
+    stride = T1
+    scores = np.full((3, stride), np.nan, np.float32)
+    scores[0, :T1] = _scores_with_ties(rng, T1)
+    s2 = rng.standard_normal(T2).astype(np.float32)
+    sampled = (np.arange(1024, dtype=np.int64) * T2) // 1024
+    s2 += 10.0
+    s2[sampled] -= 20.0          # the sample sees only the small scores
+    scores[1, :T2] = s2
+    scores[2, :T3] = _scores_with_ties(rng, T3)
+    dev = torch.device("cuda")
+    st = torch.from_numpy(scores).to(dev)
+    for k in (ks, 19000):
+        lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+        idx = torch.full((3, k), -7, dtype=torch.int32, device=dev)
+        cnt = torch.empty((3,), dtype=torch.int32, device=dev)
+        _lib.mla_topk_select(st, stride, lt, 3, k, idx, k, cnt)
+        torch.cuda.synchronize()
+        got, c = idx.cpu().numpy(), cnt.cpu().numpy()
+        for b, T in enumerate(lens):
+            want = topk_select(scores[b, :T], k)
+            assert c[b] == len(want) and np.array_equal(got[b, :len(want)], want), (k, b)
+
+
 def test_topk_all_equal_scores_take_the_earliest():
     dev = torch.device("cuda")
     T, k = 10000, 2048
