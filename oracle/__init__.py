@@ -1,5 +1,5 @@
 """CPU oracle for the MLA decode step (mla_oracle), the latent-cache writer
-(cache_writer) and the DSA sparse decode step (dsa).
+(cache_writer), the DSA sparse decode step (dsa) and TPLA decode (tpla).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The HIP library never

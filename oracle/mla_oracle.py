@@ -71,6 +71,8 @@ def e4m3_code_to_f64(codes: np.ndarray) -> np.ndarray:
 
 
 def decode_storage(raw: np.ndarray, tag: str) -> np.ndarray:
+    if tag == "f64":   # values already in fp64 (oracle-side transforms)
+        return np.asarray(raw, dtype=np.float64)
     if tag == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if tag == "bf16":
