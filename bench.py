@@ -365,6 +365,54 @@ def measure_dsa(name: str, steps: int, warmup: int):
             "copies_rotated": copies}
 
 
+def measure_tpla(workload: str, shards: int, steps: int, warmup: int):
+    """Time the TPLA decode step (mla_tpla_decode, `shards` latent shards on
+    one GPU) on `workload`, cache copies rotated as for the dense step."""
+    import torch
+
+    from head_latent_attention_10_amd import _lib
+    from head_latent_attention_10_amd.device import DeviceInputs, out_torch_dtype
+    from mla_inputs import CONFIGS, generate
+
+    cfg = CONFIGS[workload]
+    inp = generate(cfg)
+    dev = DeviceInputs(inp)
+    p = dev.params()
+    t = _lib.make_tpla_params(shards)
+    pool = dev.c_kv.numel() * dev.c_kv.element_size() + dev.k_rope.numel() * dev.k_rope.element_size()
+    copies = max(2, math.ceil(768e6 / pool))
+    c_copies = [dev.c_kv] + [dev.c_kv.clone() for _ in range(copies - 1)]
+    r_copies = [dev.k_rope] + [dev.k_rope.clone() for _ in range(copies - 1)]
+    s_copies = [dev.c_kv_scale] * copies
+    if dev.c_kv_scale is not None:
+        s_copies = [dev.c_kv_scale] + [dev.c_kv_scale.clone() for _ in range(copies - 1)]
+    n = _lib.mla_tpla_decode_workspace_size(p, t)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev.device)
+    out = torch.empty((cfg.batch, cfg.heads, cfg.d_v), dtype=out_torch_dtype(cfg.out_dtype),
+                      device=dev.device)
+    stream = torch.cuda.current_stream()
+
+    def step(j):
+        i = j % copies
+        _lib.mla_tpla_decode(p, t, dev.q, c_copies[i], s_copies[i], r_copies[i], dev.block_table,
+                             dev.seq_lens, dev.W_UK, dev.W_UV, out, ws, n, stream)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for j in range(steps):
+        step(warmup + j)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    cache = inp.cache_bytes()
+    return {"us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
+            "shards": shards, "shard_heads": cfg.heads * shards, "cache_bytes": cache,
+            "cache_GBps_step": round(cache / (ms * 1e-3) / 1e9, 1), "copies_rotated": copies}
+
+
 def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: int, commands):
     """HBM bytes per attention launch from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB
@@ -418,6 +466,10 @@ def main():
                     help="DSA sparse-decode workloads reported under 'extra' (comma list)")
     ap.add_argument("--dsa-only", action="store_true",
                     help="measure only the DSA workloads (for profiling)")
+    ap.add_argument("--tpla", default="dsv3_ragged_32k:2",
+                    help="TPLA workloads workload:shards reported under 'extra' (comma list)")
+    ap.add_argument("--tpla-only", action="store_true",
+                    help="measure only the TPLA workloads (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -453,6 +505,12 @@ def main():
         print(json.dumps({"cache_writer": out}))
         return
 
+    if args.tpla_only:
+        out = {w: measure_tpla(w.split(":")[0], int(w.split(":")[1]), args.steps, args.warmup)
+               for w in args.tpla.split(",") if w}
+        print(json.dumps({"tpla": out}))
+        return
+
     if args.dsa_only:
         out = {w: measure_dsa(w, args.steps, args.warmup) for w in args.dsa.split(",") if w}
         print(json.dumps({"dsa": out}))
@@ -472,6 +530,10 @@ def main():
         extra["cache_" + w] = measure_writer(w, max(320, args.steps), max(5, args.warmup))
     for w in [w for w in args.dsa.split(",") if w]:
         extra[w] = measure_dsa(w, max(10, args.steps // 2), max(3, args.warmup // 2))
+    for w in [w for w in args.tpla.split(",") if w]:
+        name, g = w.split(":")
+        extra[f"tpla_{name}_g{g}"] = measure_tpla(name, int(g), max(10, args.steps // 2),
+                                                  max(3, args.warmup // 2))
 
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20

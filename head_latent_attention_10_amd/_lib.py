@@ -67,6 +67,13 @@ class MlaDsaParams(ctypes.Structure):
     ]
 
 
+class MlaTplaParams(ctypes.Structure):
+    _fields_ = [
+        ("shards", ctypes.c_int32),
+        ("mu", ctypes.c_float * 4),
+    ]
+
+
 class MlaError(RuntimeError):
     def __init__(self, status: int, fn: str, msg: str):
         super().__init__(f"{fn} failed with status {status}: {msg}")
@@ -78,6 +85,7 @@ _P = ctypes.c_void_p
 _PP = ctypes.POINTER(MlaDecodeParams)
 _WP = ctypes.POINTER(MlaCacheWriteParams)
 _DP = ctypes.POINTER(MlaDsaParams)
+_TP = ctypes.POINTER(MlaTplaParams)
 _I32 = ctypes.c_int32
 
 _SIGNATURES = {
@@ -103,6 +111,9 @@ _SIGNATURES = {
     "mla_decode_sparse": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
     "mla_dsa_decode_workspace_size": (ctypes.c_int, [_PP, _DP, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_tpla_decode_workspace_size": (ctypes.c_int, [_PP, _TP, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_tpla_decode": (ctypes.c_int, [_PP, _TP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
     "mla_dsa_decode": (ctypes.c_int, [_PP, _DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _P, ctypes.c_size_t, _P]),
 }
@@ -332,4 +343,28 @@ def mla_dsa_decode(p, d, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, q_I
         ctypes.byref(p), ctypes.byref(d), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope),
         _ptr(block_table), _ptr(seq_lens), _ptr(q_I), _ptr(q_I_scale), _ptr(w_I), _ptr(k_I),
         _ptr(k_I_scale), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(indices_out), _ptr(workspace),
+        workspace_bytes, _stream(stream)))
+
+
+# ------------------------------------------------------------------ TPLA
+
+def make_tpla_params(shards=2, mu=None) -> MlaTplaParams:
+    mu = [1.0] * 4 if mu is None else list(mu) + [1.0] * (4 - len(mu))
+    return MlaTplaParams(int(shards), (ctypes.c_float * 4)(*[float(x) for x in mu[:4]]))
+
+
+def mla_tpla_decode_workspace_size(p, t) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_tpla_decode_workspace_size", load_library().mla_tpla_decode_workspace_size(
+        ctypes.byref(p), ctypes.byref(t), ctypes.byref(n)))
+    return n.value
+
+
+def mla_tpla_decode(p, t, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK, W_UV, out,
+                    workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    _check("mla_tpla_decode", load_library().mla_tpla_decode(
+        ctypes.byref(p), ctypes.byref(t), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope),
+        _ptr(block_table), _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(workspace),
         workspace_bytes, _stream(stream)))

@@ -344,6 +344,44 @@ mla_status dsa_layout(const mla_decode_params& p, const mla_dsa_params& d, DsaLa
   return MLA_OK;
 }
 
+// ---------------------------------------------------------------- TPLA
+mla_status validate_tpla(const mla_decode_params& p, const mla_tpla_params* t,
+                         mla_decode_params* p2) {
+  if (!t) return fail(MLA_ERR_INVALID_ARG, "tpla params is NULL");
+  if (t->shards != 1 && t->shards != 2 && t->shards != 4)
+    return fail(MLA_ERR_INVALID_ARG, "shards %d not 1, 2 or 4", t->shards);
+  if (p.d_latent % t->shards)
+    return fail(MLA_ERR_INVALID_ARG, "d_latent %d does not divide into %d shards", p.d_latent,
+                t->shards);
+  for (int j = 0; j < t->shards; j++)
+    if (!std::isfinite(t->mu[j])) return fail(MLA_ERR_INVALID_ARG, "mu[%d] not finite", j);
+  if ((int64_t)p.num_heads * t->shards > 65536)
+    return fail(MLA_ERR_UNSUPPORTED, "num_heads x shards above 65536");
+  *p2 = p;
+  p2->num_heads = p.num_heads * t->shards;
+  return validate(p2);
+}
+
+struct TplaLayout {
+  Layout dec;       // the shard heads' decode workspace
+  size_t q_lat1;    // absorbed queries of the num_heads heads
+  size_t o_lat1;    // gathered latent outputs of the num_heads heads
+  size_t total;
+};
+
+mla_status tpla_layout(const mla_decode_params& p, const mla_decode_params& p2, TplaLayout* L) {
+  mla_status st = layout(p2, &L->dec);
+  if (st != MLA_OK) return st;
+  size_t off = L->dec.total;
+  L->q_lat1 = off;
+  off = align256(off + (size_t)p.batch * p.num_heads * (p.d_latent + p.d_rope) *
+                           mla::dtype_size(absorbed_dtype(p)));
+  L->o_lat1 = off;
+  off = align256(off + (size_t)p.batch * p.num_heads * p.d_latent * sizeof(float));
+  L->total = off;
+  return MLA_OK;
+}
+
 size_t writer_ws_bytes(const mla_cache_write_params& p) {
   return align256((size_t)mla::writer_chunks(p) * (size_t)p.batch *
                   (size_t)(p.d_latent + p.d_rope) * sizeof(float));
@@ -641,6 +679,66 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
   return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, counts, idx, d->topk, W_UK,
                      W_UV, out, ws + L.decode, workspace_bytes - L.decode, stream, nullptr,
                      nullptr);
+}
+
+mla_status mla_tpla_decode_workspace_size(const mla_decode_params* p, const mla_tpla_params* t,
+                                          size_t* bytes) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  mla_decode_params p2;
+  st = validate_tpla(*p, t, &p2);
+  if (st != MLA_OK) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  TplaLayout L;
+  st = tpla_layout(*p, p2, &L);
+  if (st != MLA_OK) return st;
+  *bytes = L.total;
+  return MLA_OK;
+}
+
+mla_status mla_tpla_decode(const mla_decode_params* p, const mla_tpla_params* t, const void* q,
+                           const void* c_kv, const float* c_kv_scale, const void* k_rope,
+                           const int32_t* block_table, const int32_t* seq_lens, const void* W_UK,
+                           const void* W_UV, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  mla_decode_params p2;
+  st = validate_tpla(*p, t, &p2);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
+  if (st != MLA_OK) return st;
+  if (!q || !W_UK || !W_UV || !out) return fail(MLA_ERR_INVALID_ARG, "null q, W_UK, W_UV or out");
+  TplaLayout L;
+  st = tpla_layout(*p, p2, &L);
+  if (st != MLA_OK) return st;
+  st = check_workspace(L.dec, workspace, workspace_bytes);  // alignment
+  if (st != MLA_OK) return st;
+  if (workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, %zu required", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t qt = absorbed_dtype(*p);
+  // absorption of the num_heads heads (its planner groups plan the split)
+  const mla::PlanRequest plan = plan_request(L.dec, ws, block_table, seq_lens);
+  bool planned = false;
+  hipError_t e = mla::launch_absorb(*p, q, W_UK, ws + L.q_lat1, qt, &plan, &planned, s);
+  if (e != hipSuccess) return hip_fail(e, "absorb launch");
+  mla::TplaMu mu{};
+  for (int j = 0; j < t->shards; j++) mu.v[j] = t->mu[j];
+  e = mla::launch_tpla_expand(ws + L.q_lat1, ws + L.dec.q_lat, qt, p->batch, p->num_heads,
+                              t->shards, p->d_latent, p->d_rope, mu, s);
+  if (e != hipSuccess) return hip_fail(e, "expand launch");
+  float* o2 = reinterpret_cast<float*>(ws + L.dec.o_lat);
+  st = attend(p2, L.dec, ws + L.dec.q_lat, c_kv, c_kv_scale, k_rope, plan, o2, ws, s, planned);
+  if (st != MLA_OK) return st;
+  float* o1 = reinterpret_cast<float*>(ws + L.o_lat1);
+  e = mla::launch_tpla_gather(o2, o1, p->batch, p->num_heads, t->shards, p->d_latent, s);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  e = mla::launch_up_project(*p, o1, W_UV, out, s);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
 }
 
 int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g) {

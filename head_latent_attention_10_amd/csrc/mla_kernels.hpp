@@ -96,6 +96,17 @@ hipError_t launch_cache_write(const mla_cache_write_params& p, const void* x, co
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int32_t d, uint8_t* codes,
                                 float* scales, hipStream_t s);
 
+// TPLA decode (mla_tpla.hip): per-shard content factors, and the kernels that
+// turn h heads into h g shard heads and back.
+struct TplaMu {
+  float v[4];
+};
+hipError_t launch_tpla_expand(const void* q1, void* q2, int32_t q_dtype, int32_t B, int32_t h,
+                              int32_t g, int32_t d_c, int32_t d_r, const TplaMu& mu,
+                              hipStream_t s);
+hipError_t launch_tpla_gather(const float* o2, float* o1, int32_t B, int32_t h, int32_t g,
+                              int32_t d_c, hipStream_t s);
+
 // DSA indexer and top-k (mla_dsa.hip).
 bool indexer_mfma_ok(int32_t heads, int32_t dim);
 hipError_t launch_indexer(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* k,

@@ -326,6 +326,38 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
                           const void* W_UV, void* out, int32_t* indices_out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * TPLA decode ("TPLA: Tensor Parallel Latent Attention for Efficient
+ * Disaggregated Prefill and Decode Inference", "The Core TPLA Computation and
+ * Structural Differences from GLA", Eqs. 6-7; "TPLA as a special case of GLA",
+ * Section 4.4), emulated on one GPU: the latent dimension is cut into
+ * `shards` contiguous equal slices S_j; for every head
+ *   o_j = softmax_t(sm_scale (mu_j q_lat[S_j] . c_t[S_j] + q_rope . k_rope_t)) c[:, S_j]
+ *   out = sum_j W_UV[i][:, S_j] o_j
+ * (each shard its own softmax; the rope key replicated on every shard).  With
+ * shards = 1 and mu_0 = 1 this is mla_decode.  The cache and weights are used
+ * as given: a change of latent basis (the page's Hadamard or PCA
+ * reparameterisation) is applied to them beforehand by the caller.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t shards;  /* g: 1, 2 or 4; d_latent must divide by it              */
+  float mu[4];     /* content-score factor of each shard (finite; 1 = none) */
+} mla_tpla_params;
+
+/* Bytes of workspace mla_tpla_decode needs. */
+mla_status mla_tpla_decode_workspace_size(const mla_decode_params* p, const mla_tpla_params* t,
+                                          size_t* bytes);
+
+/* The TPLA decode step above; arguments and rules as for mla_decode.
+ * Runs as: absorption, expansion to shards x num_heads shard heads (zero
+ * outside their shard), the split attention and merge over those heads, the
+ * gather of each head's shard columns, and the up-projection. */
+mla_status mla_tpla_decode(const mla_decode_params* p, const mla_tpla_params* t, const void* q,
+                           const void* c_kv, const float* c_kv_scale, const void* k_rope,
+                           const int32_t* block_table, const int32_t* seq_lens, const void* W_UK,
+                           const void* W_UV, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif
