@@ -175,10 +175,12 @@ mla::PlanRequest plan_request(const Layout& L, char* ws, const int32_t* block_ta
   return r;
 }
 
+// `groups` > 1: grouped latent, group-major pools (mla_grouped_decode).
 mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat, const void* c_kv,
                   const float* c_kv_scale, const void* k_rope, const mla::PlanRequest& req,
                   float* o_lat, char* ws, hipStream_t s, bool planned = false,
-                  hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr) {
+                  hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
+                  int32_t groups = 1) {
   const int32_t* block_table = req.block_table;
   const int32_t* seq_lens = req.seq_lens;
   mla::AttnArgs a;
@@ -204,11 +206,17 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.streams = L.streams;
   a.slots = req.indices ? req.slots : nullptr;
   a.idx_stride = req.indices ? req.idx_stride : 0;
+  a.group_heads = groups > 1 ? p.num_heads / groups : 0;
+  const int64_t pool_slots = (int64_t)p.num_blocks * p.page_size;
+  a.c_group_bytes = groups > 1 ? pool_slots * p.d_latent * mla::dtype_size(p.cache_dtype) : 0;
+  a.c_group_scales = groups > 1 ? pool_slots : 0;
   // matrix-core kernels read 16-byte pieces of the pools; other pointers go
   // to the generic kernel (same workspace layout, row-major partials)
   const bool aligned = aligned16(c_kv) && aligned16(k_rope) && aligned16(c_kv_scale);
-  const bool use_bf16 = aligned && mla::mfma_supported(p);
-  const bool use_fp8 = aligned && mla::mfma_fp8_supported(p);
+  // a matrix-core work group serves 64 (or 32) heads, which must share a latent group
+  const bool groups_fit = groups <= 1 || (p.num_heads / groups) % mla::mfma_heads_per_group(p.num_heads) == 0;
+  const bool use_bf16 = aligned && groups_fit && mla::mfma_supported(p);
+  const bool use_fp8 = aligned && groups_fit && mla::mfma_fp8_supported(p);
   a.frag_layout = use_bf16 || use_fp8 ? 1 : 0;
   a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
 
@@ -268,7 +276,8 @@ mla_status decode_impl(const mla_decode_params* p, const void* q, const void* c_
                        const float* c_kv_scale, const void* k_rope, const int32_t* block_table,
                        const int32_t* lens, const int32_t* indices, int32_t stride,
                        const void* W_UK, const void* W_UV, void* out, void* workspace,
-                       size_t workspace_bytes, void* stream, void* ev_before, void* ev_after) {
+                       size_t workspace_bytes, void* stream, void* ev_before, void* ev_after,
+                       int32_t groups = 1) {
   g_last_error.clear();
   mla_status st = validate(p);
   if (st != MLA_OK) return st;
@@ -293,7 +302,7 @@ mla_status decode_impl(const mla_decode_params* p, const void* q, const void* c_
   if (e != hipSuccess) return hip_fail(e, "absorb launch");
   float* o_lat = reinterpret_cast<float*>(ws + L.o_lat);
   st = attend(*p, L, ws + L.q_lat, c_kv, c_kv_scale, k_rope, plan, o_lat, ws, s, planned,
-              static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after));
+              static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after), groups);
   if (st != MLA_OK) return st;
   e = mla::launch_up_project(*p, o_lat, W_UV, out, s);
   return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
@@ -516,6 +525,23 @@ mla_status mla_decode_sparse(const mla_decode_params* p, const void* q, const vo
   if (!indices) return fail(MLA_ERR_INVALID_ARG, "indices is NULL");
   return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, counts, indices, index_stride,
                      W_UK, W_UV, out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+mla_status mla_grouped_decode(const mla_decode_params* p, int32_t latent_groups, const void* q,
+                              const void* c_kv, const float* c_kv_scale, const void* k_rope,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const void* W_UK, const void* W_UV, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (latent_groups < 1 || p->num_heads % latent_groups)
+    return fail(MLA_ERR_INVALID_ARG, "latent_groups %d must be >= 1 and divide num_heads %d",
+                latent_groups, p->num_heads);
+  if ((int64_t)latent_groups * p->num_blocks * p->page_size * p->d_latent >= ((int64_t)1 << 40))
+    return fail(MLA_ERR_UNSUPPORTED, "grouped pools above 2^40 values");
+  return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, nullptr, 0, W_UK,
+                     W_UV, out, workspace, workspace_bytes, stream, nullptr, nullptr,
+                     latent_groups);
 }
 
 mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const float* c_kv_scale,

@@ -232,6 +232,7 @@ void attend_fp8_kernel(AttnArgs a) {
     g = blockIdx.x;
   }
   if (g >= a.splits) return;
+  select_latent_group(a, hg * 32 * HB);  // the host keeps a head group inside one latent group
   const int32_t n_total = load_ro(a.cu_tiles, a.B);
   if (n_total == 0) return;
   const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);

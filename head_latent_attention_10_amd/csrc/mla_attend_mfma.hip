@@ -282,6 +282,7 @@ void attend_mfma_kernel(AttnArgs a) {
     g = blockIdx.x;
   }
   if (g >= a.splits) return;
+  select_latent_group(a, hg * 32 * HB);  // the host keeps a head group inside one latent group
   const int32_t n_total = load_ro(a.cu_tiles, a.B);
   if (n_total == 0) return;
   const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);
@@ -592,6 +593,8 @@ bool mfma_supported(const mla_decode_params& p) {
 int32_t mfma_streams(int32_t) { return 1; }
 
 int32_t mfma_head_groups(int32_t heads) { return heads / heads_per_group(heads); }
+
+int32_t mfma_heads_per_group(int32_t heads) { return heads_per_group(heads); }
 
 hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s,
                               hipEvent_t ev_start, hipEvent_t ev_stop) {

@@ -21,6 +21,7 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
 
   const int32_t g = blockIdx.x, head = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  select_latent_group(a, head);
   const int32_t n_total = a.cu_tiles[a.B];
   if (n_total == 0) return;
   const int64_t t_begin = split_begin(n_total, a.splits, g);

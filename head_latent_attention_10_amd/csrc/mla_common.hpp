@@ -69,7 +69,23 @@ struct AttnArgs {
   // wrote to slots[b * idx_stride + n]; tiles number those entries.
   const int32_t* slots;
   int32_t idx_stride;
+  // Grouped latent (group_heads > 0): heads [g group_heads, (g + 1) group_heads)
+  // read latent pool g, which starts c_group_bytes after pool g - 1 (and its
+  // fp8 scales c_group_scales floats after), all sharing one rope pool.
+  int32_t group_heads;
+  int64_t c_group_bytes;
+  int64_t c_group_scales;
 };
+
+// Point a's latent pool (and scales) at the group of the heads starting at
+// head0 (no change without groups).
+__device__ inline void select_latent_group(AttnArgs& a, int32_t head0) {
+  if (a.group_heads > 0) {
+    const int32_t grp = head0 / a.group_heads;
+    a.c_kv = static_cast<const char*>(a.c_kv) + grp * a.c_group_bytes;
+    if (a.c_kv_scale) a.c_kv_scale += grp * a.c_group_scales;
+  }
+}
 
 // Read of a table that no kernel of the launch writes (sequence lengths, block
 // table, tile prefix sums).  The constant address space lets the compiler use

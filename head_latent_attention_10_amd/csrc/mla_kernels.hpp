@@ -44,6 +44,8 @@ int32_t mfma_streams(int32_t heads);
 // Work groups that share one token split (head groups of 64 or 32 heads); with
 // more than one, the split count must be a multiple of 8 (XCD pairing).
 int32_t mfma_head_groups(int32_t heads);
+// Heads one matrix-core work group serves (64, or 32 when heads is not a multiple of 64).
+int32_t mfma_heads_per_group(int32_t heads);
 // The optional events are stamped by the kernel's own dispatch (start and end
 // of execution), not by separate markers queued around it.
 hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_t s,

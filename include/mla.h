@@ -327,6 +327,27 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped MLA decode (the TransMLA OpenReview discussion, reply A2 to the
+ * FlashMLA question: a kv_rank of 1088 held as two 512-wide latent groups plus
+ * one 64-wide positional part, each group served like an ordinary 576-wide MLA
+ * cache).  The heads are split evenly over latent_groups groups; head i reads
+ * latent group g = i / (num_heads / latent_groups) and the shared rope key:
+ *   c_kv       [latent_groups][num_blocks, page_size, d_latent]  group-major pools
+ *   c_kv_scale [latent_groups][num_blocks, page_size] fp32       (fp8 only)
+ *   k_rope     [num_blocks, page_size, d_rope]                    shared
+ * W_UK[i] and W_UV[i] act on head i's group (shapes as for mla_decode).  Every
+ * other argument, the workspace size (mla_decode_workspace_size) and the rules
+ * are mla_decode's; latent_groups = 1 is mla_decode.  The matrix-core kernels
+ * serve it when num_heads / latent_groups is a multiple of 64 (32 when
+ * num_heads is not a multiple of 64); other splits use the generic kernel.
+ * ------------------------------------------------------------------------ */
+mla_status mla_grouped_decode(const mla_decode_params* p, int32_t latent_groups, const void* q,
+                              const void* c_kv, const float* c_kv_scale, const void* k_rope,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const void* W_UK, const void* W_UV, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * TPLA decode ("TPLA: Tensor Parallel Latent Attention for Efficient
  * Disaggregated Prefill and Decode Inference", "The Core TPLA Computation and
  * Structural Differences from GLA", Eqs. 6-7; "TPLA as a special case of GLA",
