@@ -413,6 +413,57 @@ def measure_tpla(workload: str, shards: int, steps: int, warmup: int):
             "cache_GBps_step": round(cache / (ms * 1e-3) / 1e9, 1), "copies_rotated": copies}
 
 
+def measure_grouped(workload: str, groups: int, steps: int, warmup: int):
+    """Time the grouped-MLA decode step (mla_grouped_decode, `groups` latent
+    pools) on `workload`, copies of the pools rotated."""
+    import torch
+
+    from head_latent_attention_10_amd import _lib
+    from head_latent_attention_10_amd.device import DeviceInputs, out_torch_dtype, to_device_array
+    from mla_inputs import CONFIGS
+    from mla_inputs.grouped import generate_grouped
+
+    cfg = CONFIGS[workload]
+    gi = generate_grouped(cfg, groups)
+    dev = DeviceInputs(gi.dense)
+    pools = to_device_array(gi.c_pools, dev.device)
+    scales = None if gi.scale_pools is None else to_device_array(gi.scale_pools, dev.device)
+    p = dev.params()
+    size = pools.numel() * pools.element_size() + dev.k_rope.numel() * dev.k_rope.element_size()
+    copies = max(2, math.ceil(768e6 / size))
+    c_copies = [pools] + [pools.clone() for _ in range(copies - 1)]
+    r_copies = [dev.k_rope] + [dev.k_rope.clone() for _ in range(copies - 1)]
+    s_copies = [scales] * copies if scales is None else [scales] + [scales.clone() for _ in range(copies - 1)]
+    n = _lib.mla_decode_workspace_size(p)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev.device)
+    out = torch.empty((cfg.batch, cfg.heads, cfg.d_v), dtype=out_torch_dtype(cfg.out_dtype),
+                      device=dev.device)
+    stream = torch.cuda.current_stream()
+
+    def step(j):
+        i = j % copies
+        _lib.mla_grouped_decode(p, groups, dev.q, c_copies[i], s_copies[i], r_copies[i],
+                                dev.block_table, dev.seq_lens, dev.W_UK, dev.W_UV, out, ws, n,
+                                stream)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for j in range(steps):
+        step(warmup + j)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    per_tok = groups * cfg.d_latent * (1 if cfg.cache_dtype == "e4m3" else 2) + cfg.d_rope * 2
+    cache = int(gi.seq_lens.astype("int64").sum()) * per_tok
+    return {"us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
+            "latent_groups": groups, "kv_rank": groups * cfg.d_latent + cfg.d_rope,
+            "cache_bytes": cache, "cache_GBps_step": round(cache / (ms * 1e-3) / 1e9, 1),
+            "copies_rotated": copies}
+
+
 def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: int, commands):
     """HBM bytes per attention launch from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB
@@ -468,6 +519,8 @@ def main():
                     help="measure only the DSA workloads (for profiling)")
     ap.add_argument("--tpla", default="dsv3_ragged_32k:2",
                     help="TPLA workloads workload:shards reported under 'extra' (comma list)")
+    ap.add_argument("--grouped", default="dsv3_ragged_32k:2",
+                    help="grouped-MLA workloads workload:groups reported under 'extra' (comma list)")
     ap.add_argument("--tpla-only", action="store_true",
                     help="measure only the TPLA workloads (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -530,6 +583,10 @@ def main():
         extra["cache_" + w] = measure_writer(w, max(320, args.steps), max(5, args.warmup))
     for w in [w for w in args.dsa.split(",") if w]:
         extra[w] = measure_dsa(w, max(10, args.steps // 2), max(3, args.warmup // 2))
+    for w in [w for w in args.grouped.split(",") if w]:
+        name, g = w.split(":")
+        extra[f"grouped_{name}_G{g}"] = measure_grouped(name, int(g), max(10, args.steps // 2),
+                                                        max(3, args.warmup // 2))
     for w in [w for w in args.tpla.split(",") if w]:
         name, g = w.split(":")
         extra[f"tpla_{name}_g{g}"] = measure_tpla(name, int(g), max(10, args.steps // 2),
