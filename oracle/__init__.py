@@ -1,5 +1,6 @@
 """CPU oracle for the MLA decode step (mla_oracle), the latent-cache writer
-(cache_writer), the DSA sparse decode step (dsa) and TPLA decode (tpla).
+(cache_writer), the DSA sparse decode step (dsa), TPLA decode (tpla), grouped MLA
+decode (grouped) and MHA-mode prefill (prefill).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The HIP library never
