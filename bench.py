@@ -40,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), DSV3 shape @32K ctx"
 ATTN_SOURCE = os.path.join(ROOT, "head_latent_attention_10_amd", "csrc", "mla_attend_mfma.hip")
 
@@ -464,6 +465,67 @@ def measure_grouped(workload: str, groups: int, steps: int, warmup: int):
             "copies_rotated": copies}
 
 
+def prefill_flops(seq_lens, q_lens, heads, d_qk=192, d_v=128, d_c=512):
+    """Algorithmic flops of one MHA-mode prefill call: the reconstruction of the
+    keys (no rope part) and values of every cached token (2 d_c flops per output
+    value), and per query the score and value products over the positions it
+    sees (2 (d_qk + d_v) per head and key)."""
+    dec = 0
+    att = 0
+    for T, L in zip(seq_lens, q_lens):
+        T, L = int(T), int(min(L, T))
+        dec += T * heads * 2 * d_c * ((d_qk - 64) + d_v)
+        keys = L * (T - L) + L * (L + 1) // 2
+        att += keys * heads * 2 * (d_qk + d_v)
+    return dec, att
+
+
+def measure_prefill(spec: str, steps: int, warmup: int):
+    """Time MHA-mode prefill (mla_prefill) on the DeepSeek-V3 shape: spec
+    'batch:context:chunk' = `batch` sequences of `context` cached tokens whose
+    last `chunk` are the new query tokens."""
+    import torch
+
+    from head_latent_attention_10_amd import _lib
+    from head_latent_attention_10_amd.device import DeviceInputs, out_torch_dtype, to_device_array
+    from mla_inputs import CONFIGS
+    from mla_inputs.prefill import generate_prefill
+
+    B, T, L = (int(x) for x in spec.split(":"))
+    cfg = CONFIGS["dsv3_b8_32k"].replace(batch=B, seq_len=T, out_dtype="bf16", seed=1200)
+    pi = generate_prefill(cfg, L)
+    dev = DeviceInputs(pi.dense)
+    q = to_device_array(pi.q, dev.device)
+    ql = to_device_array(pi.q_lens, dev.device)
+    p = dev.params()
+    n = _lib.mla_prefill_workspace_size(p)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev.device)
+    out = torch.empty((B, L, cfg.heads, cfg.d_v), dtype=out_torch_dtype(cfg.out_dtype),
+                      device=dev.device)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        _lib.mla_prefill(p, L, q, ql, dev.c_kv, dev.k_rope, dev.block_table, dev.seq_lens,
+                         dev.W_UK, dev.W_UV, out, ws, n, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    dec, att = prefill_flops(pi.seq_lens, pi.q_lens, cfg.heads)
+    return {"ms_per_call": round(ms, 4), "new_tokens_per_s": round(B * L / (ms * 1e-3), 1),
+            "decompress_tflop": round(dec / 1e12, 4), "attention_tflop": round(att / 1e12, 4),
+            "TFLOPs": round((dec + att) / (ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_peak": round((dec + att) / (ms * 1e-3) / BF16_PEAK_TFLOPS / 1e12, 4),
+            "workspace_bytes": n}
+
+
 def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: int, commands):
     """HBM bytes per attention launch from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB
@@ -521,6 +583,11 @@ def main():
                     help="TPLA workloads workload:shards reported under 'extra' (comma list)")
     ap.add_argument("--grouped", default="dsv3_ragged_32k:2",
                     help="grouped-MLA workloads workload:groups reported under 'extra' (comma list)")
+    ap.add_argument("--prefill", default="2:16384:4096",
+                    help="MHA-mode prefill workloads batch:context:chunk (DeepSeek-V3 shape) "
+                         "reported under 'extra' (comma list)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="measure only the prefill workloads (for profiling)")
     ap.add_argument("--tpla-only", action="store_true",
                     help="measure only the TPLA workloads (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -564,6 +631,12 @@ def main():
         print(json.dumps({"tpla": out}))
         return
 
+    if args.prefill_only:
+        out = {w: measure_prefill(w, max(3, args.steps), args.warmup)
+               for w in args.prefill.split(",") if w}
+        print(json.dumps({"prefill": out}))
+        return
+
     if args.dsa_only:
         out = {w: measure_dsa(w, args.steps, args.warmup) for w in args.dsa.split(",") if w}
         print(json.dumps({"dsa": out}))
@@ -591,6 +664,9 @@ def main():
         name, g = w.split(":")
         extra[f"tpla_{name}_g{g}"] = measure_tpla(name, int(g), max(10, args.steps // 2),
                                                   max(3, args.warmup // 2))
+
+    for w in [w for w in args.prefill.split(",") if w]:
+        extra[f"prefill_dsv3_{w.replace(':', '_')}"] = measure_prefill(w, 5, 2)
 
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb << 20

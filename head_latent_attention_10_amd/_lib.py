@@ -114,6 +114,9 @@ _SIGNATURES = {
     "mla_tpla_decode_workspace_size": (ctypes.c_int, [_PP, _TP, ctypes.POINTER(ctypes.c_size_t)]),
     "mla_grouped_decode": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    "mla_prefill_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_prefill": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P]),
     "mla_tpla_decode": (ctypes.c_int, [_PP, _TP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
     "mla_dsa_decode": (ctypes.c_int, [_PP, _DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -380,5 +383,24 @@ def mla_grouped_decode(p, latent_groups: int, q, c_kv, c_kv_scale, k_rope, block
         workspace_bytes = _nbytes(workspace)
     _check("mla_grouped_decode", load_library().mla_grouped_decode(
         ctypes.byref(p), int(latent_groups), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope),
+        _ptr(block_table), _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(workspace),
+        workspace_bytes, _stream(stream)))
+
+
+# ------------------------------------------------------------------ prefill
+
+def mla_prefill_workspace_size(p) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_prefill_workspace_size",
+           load_library().mla_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def mla_prefill(p, max_q_len: int, q, q_lens, c_kv, k_rope, block_table, seq_lens, W_UK, W_UV,
+                out, workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    _check("mla_prefill", load_library().mla_prefill(
+        ctypes.byref(p), int(max_q_len), _ptr(q), _ptr(q_lens), _ptr(c_kv), _ptr(k_rope),
         _ptr(block_table), _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(workspace),
         workspace_bytes, _stream(stream)))

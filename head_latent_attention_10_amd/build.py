@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libmla_hip.so")
 
 SOURCES = ["mla_api.hip", "mla_small_kernels.hip", "mla_attend_simt.hip", "mla_attend_mfma.hip",
            "mla_attend_fp8.hip", "mla_proj_mfma.hip", "mla_cache_write.hip", "mla_dsa.hip",
-           "mla_tpla.hip"]
+           "mla_tpla.hip", "mla_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -327,6 +327,31 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Prefill in MHA mode ("TransMLA & Sparse Latent Attention", Chapter 7: MLA
+ * runs in its MHA-like mode for prefill, reconstructing full-width keys and
+ * values; "TPLA: ...", section 3.4, Eq. 4).  For sequence b with T_b cached
+ * tokens (seq_lens; the new tokens already written to the cache) and
+ * L_b = clamp(q_lens[b], 0, min(max_q_len, T_b)) new query tokens, query l sits
+ * at position T_b - L_b + l and, per head i,
+ *   out[b, l, i] = softmax_{t <= T_b - L_b + l}(sm_scale (q_nope . W_UK[i] c_t
+ *                  + q_rope . k_rope_t)) (W_UV[i] c_t)
+ *   q   [B, max_q_len, h, d_nope + d_rope]   bf16, q_rope pre-rotated
+ *   out [B, max_q_len, h, d_v]               out_dtype (rows l >= L_b untouched)
+ * Supported: bf16 q, cache, rope and weights with d_latent 512, d_nope 128,
+ * d_rope 64, d_v 128 (else MLA_ERR_UNSUPPORTED); q, c_kv, k_rope, W_UK and W_UV
+ * 16-byte aligned.  The workspace holds the reconstructed keys and values of
+ * every cached token: 2 x batch x h x Tpad x 128 bf16 values, Tpad =
+ * max_blocks_per_seq x page_size rounded up to 128.
+ * ------------------------------------------------------------------------ */
+mla_status mla_prefill_workspace_size(const mla_decode_params* p, size_t* bytes);
+
+mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void* q,
+                       const int32_t* q_lens, const void* c_kv, const void* k_rope,
+                       const int32_t* block_table, const int32_t* seq_lens, const void* W_UK,
+                       const void* W_UV, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Grouped MLA decode (the TransMLA OpenReview discussion, reply A2 to the
  * FlashMLA question: a kv_rank of 1088 held as two 512-wide latent groups plus
  * one 64-wide positional part, each group served like an ordinary 576-wide MLA

@@ -144,3 +144,53 @@ def test_split_slots_are_unique():
                 assert s not in slots
                 assert s < G + len(lens_tiles)
                 slots.add(s)
+
+
+def _prefill_params(**kw):
+    base = dict(batch=3, num_heads=4, d_nope=128, d_rope=64, d_latent=512, d_v=128, page_size=64,
+                max_blocks_per_seq=5, num_blocks=16, q_dtype="bf16", cache_dtype="bf16",
+                rope_dtype="bf16", weight_dtype="bf16", out_dtype="bf16", sm_scale=0.0,
+                num_splits=0)
+    base.update(kw)
+    return _lib.make_params(**base)
+
+
+def test_prefill_workspace_size_without_device():
+    # reconstructed keys and transposed values: 2 x B x h x Tpad x 128 bf16,
+    # Tpad = 5 blocks x 64 rounded up to 128
+    assert _lib.mla_prefill_workspace_size(_prefill_params()) == 2 * 3 * 4 * 384 * 128 * 2
+
+
+@pytest.mark.parametrize("bad", [dict(cache_dtype="f32"), dict(q_dtype="f32"),
+                                 dict(cache_dtype="e4m3"), dict(d_nope=64), dict(d_v=64),
+                                 dict(d_latent=256), dict(d_rope=32)])
+def test_prefill_unsupported_shapes(bad):
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_prefill_workspace_size(_prefill_params(**bad))
+    assert ei.value.status == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_prefill_rejects_bad_arguments_before_launch():
+    p = _prefill_params()
+    fake = 0x10000
+    n = _lib.mla_prefill_workspace_size(p)
+    args = [fake] * 9
+    for bad_len in (0, -1, (1 << 24) + 1):
+        with pytest.raises(_lib.MlaError) as ei:
+            _lib.mla_prefill(p, bad_len, *args, fake, n)
+        assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    for i in range(9):
+        a = list(args)
+        a[i] = None
+        with pytest.raises(_lib.MlaError) as ei:
+            _lib.mla_prefill(p, 16, *a, fake, n)
+        assert ei.value.status == _lib.MLA_ERR_INVALID_ARG, i
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_prefill(p, 16, *args, fake, n - 1)
+    assert ei.value.status == _lib.MLA_ERR_WORKSPACE
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_prefill(p, 16, *args, fake + 128, n)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    with pytest.raises(_lib.MlaError) as ei:  # misaligned query
+        _lib.mla_prefill(p, 16, fake + 2, *args[1:], fake, n)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
