@@ -768,7 +768,8 @@ mla_status mla_tpla_decode(const mla_decode_params* p, const mla_tpla_params* t,
 }
 
 static size_t prefill_ws_bytes(const mla_decode_params& p) {
-  return 2 * align256((size_t)p.batch * p.num_heads * mla::prefill_tpad(p) * 128 * sizeof(uint16_t));
+  const size_t per_head = (size_t)p.batch * p.num_heads * mla::prefill_tpad(p) * sizeof(uint16_t);
+  return align256(per_head * 192) + align256(per_head * 128);
 }
 
 mla_status mla_prefill_workspace_size(const mla_decode_params* p, size_t* bytes) {
@@ -796,6 +797,10 @@ mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void
     return fail(MLA_ERR_INVALID_ARG, "max_q_len %d outside [1, 2^24]", max_q_len);
   if ((int64_t)p->batch * max_q_len * p->num_heads * 192 >= ((int64_t)1 << 40))
     return fail(MLA_ERR_UNSUPPORTED, "query tensor too large");
+  if (p->batch > 65535 || 2 * (int64_t)p->num_heads > 65535 ||
+      (int64_t)p->batch * p->num_heads * ((max_q_len + 127) / 128) >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "prefill grid too large (batch %d, heads %d, max_q_len %d)",
+                p->batch, p->num_heads, max_q_len);
   if (!q || !q_lens || !c_kv || !k_rope || !block_table || !seq_lens || !W_UK || !W_UV || !out)
     return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!(aligned16(q) && aligned16(c_kv) && aligned16(k_rope) && aligned16(W_UK) && aligned16(W_UV)))
@@ -807,7 +812,9 @@ mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void
     return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
   const hipError_t e = mla::launch_prefill(*p, max_q_len, q, q_lens, c_kv, k_rope, block_table,
-                                           seq_lens, W_UK, W_UV, out, ws, ws + need / 2,
+                                           seq_lens, W_UK, W_UV, out, ws,
+                                           ws + align256((size_t)p->batch * p->num_heads *
+                                                         mla::prefill_tpad(*p) * 2 * 192),
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "prefill launch");
 }

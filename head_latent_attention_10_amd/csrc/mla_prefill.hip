@@ -10,10 +10,11 @@
 // at position T_b - L_b + l and sees positions 0 .. T_b - L_b + l.
 //
 // Two kernels:
-//  * decompress: K[b, i, t, :] = W_UK[i] c_t and V^T[b, i, :, t] = W_UV[i] c_t
-//    for every cached t < T_b, a bf16 matrix-core GEMM per (128 tokens, head,
-//    K or V) tile with both operands staged in LDS;
-//  * attention: a work group per (64 queries, head, sequence), a wave per 16
+//  * decompress: K[b, i, t, :] = [W_UK[i] c_t ; k_rope_t] and V^T[b, i, :, t] =
+//    W_UV[i] c_t for every cached t < T_b, a bf16 matrix-core GEMM per (128
+//    tokens, head, K or V) tile, both operands arriving in LDS by direct loads,
+//    the next latent chunk in flight while the current one is multiplied;
+//  * attention: a work group per (128 queries, head, sequence), a wave per 32
 //    queries; per 64-key tile S^T = K Q^T (16x16x32 MFMA, keys on M), the
 //    causal mask, an online softmax per query, and O^T += V^T P^T (the key
 //    order of this product is the one the score fragments already hold).
@@ -23,17 +24,16 @@ namespace mla {
 namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPDc = 512, kPDn = 128, kPDr = 64, kPDv = 128;
 constexpr int kPDq = kPDn + kPDr;          // 192 query/key width
 constexpr int kDecTok = 128;               // tokens per decompression tile
 constexpr int kDecChunk = 64;              // latent values per LDS stage
-constexpr int kDecRow = kDecChunk * 2 + 16;  // LDS bytes per staged row
-constexpr int kQTile = 64;                 // queries per attention work group
+constexpr int kDecHalf = kDecTok * kDecChunk * 2;  // 16 KB: 128 rows of 128 bytes
+constexpr int kQTile = 128;                // queries per attention work group
 constexpr int kKTile = 64;                 // keys per attention step
-constexpr int kKRow = kPDq * 2 + 16;       // LDS bytes per key row (400)
-constexpr int kVRow = kKTile * 2 + 16;     // LDS bytes per V^T row (144)
+constexpr int kKStage = kKTile * kPDq * 2;  // 24 KB of keys per step
+constexpr int kVStage = kPDv * kKTile * 2;  // 16 KB of transposed values per step
 
 struct PrefillArgs {
   const uint16_t* q;        // [B, Lq, h, 192]
@@ -44,8 +44,8 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   const uint16_t* W_UK;     // [h, 128, 512]
   const uint16_t* W_UV;     // [h, 128, 512]
-  uint16_t* Kn;             // [B, h, Tpad, 128]
-  uint16_t* Vt;             // [B, h, 128, Tpad]
+  uint16_t* Kn;             // [B, h, Tpad, 192]: reconstructed nope part, then rope
+  uint16_t* Vt;             // [B, h, 128, Tpad]: tokens permuted within 32 (vt_pos)
   void* out;                // [B, Lq, h, 128]
   int32_t B, h, Lq, P, max_blocks, num_blocks, Tpad;
   float sm_log2;            // sm_scale * log2(e)
@@ -62,51 +62,83 @@ __device__ inline int32_t query_len(const PrefillArgs& a, int32_t b, int32_t T) 
   return L < 0 ? 0 : min(L, min(a.Lq, T));
 }
 
+// Column of token t in a V^T row.  Within each block of 32 tokens, token
+// 16 h + 4 q + j (h < 2, q < 4, j < 4) sits at 8 q + 4 h + j: the eight tokens a
+// lane group multiplies in one value-product step (see the attention kernel)
+// are then 16 contiguous bytes.
+__device__ inline int32_t vt_pos(int32_t t) {
+  const int32_t w = t & 31;
+  return (t & ~31) + 8 * ((w >> 2) & 3) + 4 * (w >> 4) + (w & 3);
+}
+
+// LDS rows are stored in 16-byte pieces, piece p of row n at position
+// p ^ swz(n): the 16 rows a quarter-wave reads then fall on distinct banks.
+__device__ inline int swz(int n) { return (n >> 1) & 7; }
+
+template <typename T>
+__device__ inline T lds_read(const lds_t* p) {
+  return *reinterpret_cast<const T __attribute__((address_space(3)))*>(p);
+}
+
 // ------------------------------------------------------------------ decompress
 // blockIdx = (token tile, 2 i + which, b); wave (wm, wn) computes tokens
-// 64 wm .. +63 by outputs 64 wn .. +63 of the 128 x 128 tile.
-__global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_a[kDecTok * kDecRow];
-  __shared__ __attribute__((aligned(16))) char s_b[kPDn * kDecRow];
+// 64 wm .. +63 by outputs 64 wm .. +63 of the 128 x 128 tile.  A stage holds 64
+// latent values of the 128 tokens (rows 0..127) and of the 128 weight rows;
+// the wave loads 1 KB chunks wave + 4 u of each half (8 rows of 8 pieces).
+__global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kDecHalf];  // two stages of A | B
+  const PrefillArgs a = args;
   const int32_t b = blockIdx.z, head = blockIdx.y >> 1, which = blockIdx.y & 1;
   const int32_t T = cached_len(a, b);
   const int32_t t0 = blockIdx.x * kDecTok;
   if (t0 >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, r = lane & 31;
+  lds_t* ring = (lds_t*)smem;
   const uint16_t* W = (which ? a.W_UV : a.W_UK) + (int64_t)head * kPDn * kPDc;
-  // this thread's staged pieces: rows idx / 8, 16-byte piece idx % 8
-  int64_t arow[4];
-#pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const int32_t idx = tid + 256 * u, row = idx >> 3;
+  // DMA sources of this lane: row 8 (wave + 4 u) + lane / 8, piece (lane & 7) ^ swz(row)
+  auto src_a = [&](int u) -> const uint16_t* {
+    const int row = 8 * (wave + 4 * u) + (lane >> 3);
     const int32_t t = min(t0 + row, T - 1);  // rows past T repeat the last token (finite)
-    arow[u] = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks) * kPDc;
-  }
+    const int64_t slot = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks);
+    return a.c_kv + slot * kPDc + 8 * ((lane & 7) ^ swz(row));
+  };
+  auto src_b = [&](int u) -> const uint16_t* {
+    const int row = 8 * (wave + 4 * u) + (lane >> 3);
+    return W + (int64_t)row * kPDc + 8 * ((lane & 7) ^ swz(row));
+  };
+  const uint16_t *pa0 = src_a(0), *pa1 = src_a(1), *pa2 = src_a(2), *pa3 = src_a(3);
+  const uint16_t *pb0 = src_b(0), *pb1 = src_b(1), *pb2 = src_b(2), *pb3 = src_b(3);
+  auto issue = [&](int32_t k0, lds_t* st) {
+    dma16(pa0 + k0, st + (wave + 0) * 1024);
+    dma16(pa1 + k0, st + (wave + 4) * 1024);
+    dma16(pa2 + k0, st + (wave + 8) * 1024);
+    dma16(pa3 + k0, st + (wave + 12) * 1024);
+    dma16(pb0 + k0, st + kDecHalf + (wave + 0) * 1024);
+    dma16(pb1 + k0, st + kDecHalf + (wave + 4) * 1024);
+    dma16(pb2 + k0, st + kDecHalf + (wave + 8) * 1024);
+    dma16(pb3 + k0, st + kDecHalf + (wave + 12) * 1024);
+  };
   f32x16 acc[2][2] = {};
-  for (int32_t k0 = 0; k0 < kPDc; k0 += kDecChunk) {
-    uint4 va[4], vb[4];
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int32_t idx = tid + 256 * u, row = idx >> 3, pc = idx & 7;
-      va[u] = *reinterpret_cast<const uint4*>(a.c_kv + arow[u] + k0 + 8 * pc);
-      vb[u] = *reinterpret_cast<const uint4*>(W + (int64_t)row * kPDc + k0 + 8 * pc);
+  constexpr int kChunks = kPDc / kDecChunk;
+  issue(0, ring);
+  for (int cc = 0; cc < kChunks; cc++) {
+    if (cc + 1 < kChunks) {
+      issue((cc + 1) * kDecChunk, ring + ((cc + 1) & 1) * 2 * kDecHalf);
+      wait_vmcnt<8>();
+    } else {
+      wait_vmcnt<0>();
     }
-    __syncthreads();  // the previous chunk's products are done
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int32_t idx = tid + 256 * u, row = idx >> 3, pc = idx & 7;
-      *reinterpret_cast<uint4*>(s_a + row * kDecRow + 16 * pc) = va[u];
-      *reinterpret_cast<uint4*>(s_b + row * kDecRow + 16 * pc) = vb[u];
-    }
-    __syncthreads();
+    wg_barrier();  // chunk cc has landed for every wave
+    const lds_t* st = ring + (cc & 1) * 2 * kDecHalf;
 #pragma unroll
     for (int s = 0; s < kDecChunk / 16; s++) {
       bf16x8 av[2], bv[2];
 #pragma unroll
       for (int x = 0; x < 2; x++) {
-        av[x] = *reinterpret_cast<const bf16x8*>(s_a + (64 * wm + 32 * x + r) * kDecRow + 32 * s + 16 * g);
-        bv[x] = *reinterpret_cast<const bf16x8*>(s_b + (64 * wn + 32 * x + r) * kDecRow + 32 * s + 16 * g);
+        const int ra = 64 * wm + 32 * x + r, rb = 64 * wn + 32 * x + r;
+        av[x] = lds_read<bf16x8>(st + ra * 128 + (((2 * s + g) ^ swz(ra)) << 4));
+        bv[x] = lds_read<bf16x8>(st + kDecHalf + rb * 128 + (((2 * s + g) ^ swz(rb)) << 4));
       }
 #pragma unroll
       for (int x = 0; x < 2; x++)
@@ -114,6 +146,7 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs a) 
         for (int y = 0; y < 2; y++)
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
     }
+    wg_barrier();  // stage cc & 1 is refilled by the next iteration's issue
   }
   // D[token][output]: lane holds output column r, tokens 8 (j / 4) + 4 g + j % 4
   const int64_t bh = (int64_t)b * a.h + head;
@@ -128,132 +161,199 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs a) 
         if (which == 0) {
 #pragma unroll
           for (int e = 0; e < 4; e++)
-            a.Kn[(bh * a.Tpad + tok + e) * kPDn + col] = f32_to_bf16_bits(acc[x][y][4 * jb + e]);
+            a.Kn[(bh * a.Tpad + tok + e) * kPDq + col] = f32_to_bf16_bits(acc[x][y][4 * jb + e]);
         } else {
           const uint32_t lo = f32_to_bf16_bits(acc[x][y][4 * jb + 0]) |
                               ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * jb + 1]) << 16);
           const uint32_t hi = f32_to_bf16_bits(acc[x][y][4 * jb + 2]) |
                               ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * jb + 3]) << 16);
-          *reinterpret_cast<uint2*>(a.Vt + (bh * kPDv + col) * a.Tpad + tok) = uint2{lo, hi};
+          // tokens tok .. tok + 3 stay adjacent under vt_pos
+          *reinterpret_cast<uint2*>(a.Vt + (bh * kPDv + col) * a.Tpad + vt_pos(tok)) = uint2{lo, hi};
         }
       }
+    }
+  }
+  if (which == 0) {
+    // the key's rope part, copied beside the reconstructed part (rows past T
+    // repeat the last token, as above)
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int32_t idx = tid + 256 * u, row = idx >> 3, pc = idx & 7;
+      const int32_t t = min(t0 + row, T - 1);
+      const int64_t slot = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks);
+      *reinterpret_cast<uint4*>(a.Kn + (bh * a.Tpad + t0 + row) * kPDq + kPDn + 8 * pc) =
+          *reinterpret_cast<const uint4*>(a.k_rope + slot * kPDr + 8 * pc);
     }
   }
 }
 
 // ------------------------------------------------------------------ attention
+// One work group per (128 queries, head, sequence) on a 1-D grid, a wave per
+// 32 queries (two 16-query MFMA column blocks sharing every key fragment).
+// Key and value tiles arrive by direct-to-LDS loads into two stages, the tile
+// of step n + 1 in flight while step n is multiplied.  A stage holds 64 keys x
+// 192 (rows of 384 bytes) and then 128 value rows x 64 tokens (128 bytes),
+// 40 chunks of 1 KB; wave w loads chunks w + 4 u.
+__device__ inline void attn_issue(const PrefillArgs& a, int64_t bh, int32_t t0, lds_t* st,
+                                  int wave, int lane) {
+  const uint16_t* kbase = a.Kn + (bh * a.Tpad + t0) * kPDq;
+#pragma unroll
+  for (int u = 0; u < 6; u++) {
+    const int o = (wave + 4 * u) * 1024 + 16 * lane;
+    const int key = o / (kPDq * 2), pos = (o % (kPDq * 2)) >> 4;
+    dma16(kbase + key * kPDq + 8 * (pos ^ swz(key)), st + (wave + 4 * u) * 1024);
+  }
+  const uint16_t* vbase = a.Vt + bh * kPDv * a.Tpad + t0;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int o = (wave + 4 * u) * 1024 + 16 * lane;
+    const int row = o >> 7, pos = (o >> 4) & 7;
+    dma16(vbase + (int64_t)row * a.Tpad + 8 * (pos ^ swz(row)), st + kKStage + (wave + 4 * u) * 1024);
+  }
+}
+
 template <int OT>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_k[kKTile * kKRow];
-  __shared__ __attribute__((aligned(16))) char s_v[kPDv * kVRow];
-  const int32_t b = blockIdx.z, head = blockIdx.y, q0 = blockIdx.x * kQTile;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
+    PrefillArgs args, int32_t n_qtiles) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (kKStage + kVStage)];
+  const PrefillArgs a = args;
+  // Block order: the 8 XCDs take block ids round-robin; regroup so that each
+  // XCD runs a contiguous range of (q-tile, head, sequence) work, the q-tiles
+  // of one head (which read the same keys and values) sharing its L2, and the
+  // causally heaviest q-tile of each head first.
+  const uint32_t nwg = gridDim.x, per = nwg / 8;
+  uint32_t id = blockIdx.x;
+  if (id < per * 8) id = (id % 8) * per + id / 8;
+  const int32_t qt = n_qtiles - 1 - (int32_t)(id % n_qtiles);
+  const int32_t head = (int32_t)((id / n_qtiles) % a.h);
+  const int32_t b = (int32_t)(id / n_qtiles / a.h);
   const int32_t T = cached_len(a, b);
   const int32_t Lb = query_len(a, b, T);
+  const int32_t q0 = qt * kQTile;
   if (q0 >= Lb) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int64_t bh = (int64_t)b * a.h + head;
-  // this lane's query (column c of the wave's 16) and its position
-  const int32_t ql = q0 + 16 * wave + c;
-  const bool q_live = ql < Lb;
-  const int32_t qpos = T - Lb + min(ql, Lb - 1);
-  bf16x8 qv[kPDq / 32];
-  {
-    const uint16_t* qrow = a.q + (((int64_t)b * a.Lq + min(ql, Lb - 1)) * a.h + head) * kPDq + 8 * g;
+  lds_t* ring = (lds_t*)smem;
+  constexpr int kStage = kKStage + kVStage;
+  const int32_t t_end = T - Lb + min(q0 + kQTile, Lb);  // keys this work group needs
+  const int32_t n_tiles = (t_end + kKTile - 1) / kKTile;
+  attn_issue(a, bh, 0, ring, wave, lane);
+  // this lane's queries: column c of the wave's two 16-query blocks
+  int32_t qpos[2];
+  bf16x8 qv[2][kPDq / 32];
 #pragma unroll
-    for (int ks = 0; ks < kPDq / 32; ks++) qv[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  for (int qb = 0; qb < 2; qb++) {
+    const int32_t ql = min(q0 + 32 * wave + 16 * qb + c, Lb - 1);
+    qpos[qb] = T - Lb + ql;
+    const uint16_t* qrow = a.q + (((int64_t)b * a.Lq + ql) * a.h + head) * kPDq + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kPDq / 32; ks++)
+      qv[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
-  const int32_t last_q = min(q0 + kQTile, Lb) - 1;
-  const int32_t t_end = T - Lb + last_q + 1;  // keys this work group needs
-  f32x4v o[kPDv / 16] = {};
-  float m = -INFINITY, l_part = 0.f;
-  for (int32_t t0 = 0; t0 < t_end; t0 += kKTile) {
-    __syncthreads();  // previous tile consumed
-    // K tile: 64 keys x (128 reconstructed + 64 rope); V^T tile: 128 x 64 keys
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int32_t idx = tid + 256 * u, key = idx >> 4, pc = idx & 15;
-      const uint4 v = *reinterpret_cast<const uint4*>(a.Kn + (bh * a.Tpad + t0 + key) * kPDn + 8 * pc);
-      *reinterpret_cast<uint4*>(s_k + key * kKRow + 16 * pc) = v;
+  // the wave's first and last query positions (wave-uniform)
+  const int32_t wave_lo = T - Lb + min(q0 + 32 * wave, Lb - 1);
+  const int32_t wave_hi = T - Lb + min(q0 + 32 * wave + 31, Lb - 1);
+  const float cs = a.sm_log2;  // > 0: the max commutes with it
+  const int sw = (c >> 1) & 7;  // swz() of every row this lane reads
+  f32x4v o[2][kPDv / 16] = {};
+  float m[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  for (int32_t n = 0; n < n_tiles; n++) {
+    const int32_t t0 = n * kKTile;
+    if (n + 1 < n_tiles) {
+      attn_issue(a, bh, t0 + kKTile, ring + ((n + 1) & 1) * kStage, wave, lane);
+      wait_vmcnt<10>();
+    } else {
+      wait_vmcnt<0>();
     }
+    wg_barrier();  // tile n has landed for every wave
+    const lds_t* sk = ring + (n & 1) * kStage;
+    const lds_t* sv = sk + kKStage;
+    if (t0 <= wave_hi) {  // else every key of the tile comes after every query of the wave
+      const bool diag = t0 + kKTile - 1 > wave_lo;
+      // S^T[key][query]: lane holds query c of block qb, keys 16 kb + 4 g + j
+      f32x4v s[2][4];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int32_t idx = tid + 256 * u, key = idx >> 3, pc = idx & 7;
-      const int32_t t = min(t0 + key, T - 1);
-      const int64_t slot = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks);
-      const uint4 v = *reinterpret_cast<const uint4*>(a.k_rope + slot * kPDr + 8 * pc);
-      *reinterpret_cast<uint4*>(s_k + key * kKRow + 2 * kPDn + 16 * pc) = v;
-    }
+      for (int kb = 0; kb < 4; kb++) {
+        s[0][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        s[1][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int32_t idx = tid + 256 * u, row = idx >> 3, pc = idx & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(a.Vt + (bh * kPDv + row) * a.Tpad + t0 + 8 * pc);
-      *reinterpret_cast<uint4*>(s_v + row * kVRow + 16 * pc) = v;
-    }
-    __syncthreads();
-    // S^T[key][query]: lane holds query c, keys 16 kb + 4 g + j
-    f32x4v s[4];
+        for (int ks = 0; ks < kPDq / 32; ks++) {
+          const bf16x8 kv = lds_read<bf16x8>(sk + (16 * kb + c) * (kPDq * 2) + (((4 * ks + g) ^ sw) << 4));
+          s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[0][ks], s[0][kb], 0, 0, 0);
+          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[1][ks], s[1][kb], 0, 0, 0);
+        }
+      }
+      bf16x8 pb[2][2];
+      float alpha[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
-      s[kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < 2; qb++) {
+        if (diag) {
 #pragma unroll
-      for (int ks = 0; ks < kPDq / 32; ks++) {
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(s_k + (16 * kb + c) * kKRow + 64 * ks + 16 * g);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[ks], s[kb], 0, 0, 0);
+          for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              if (t0 + 16 * kb + 4 * g + j > qpos[qb]) s[qb][kb][j] = -INFINITY;
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) tmax = fmaxf(tmax, s[qb][kb][j]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        // key 0 is visible to every query, so m is finite from the first tile on
+        const float m_new = fmaxf(m[qb], tmax);
+        alpha[qb] = __builtin_amdgcn_exp2f((m[qb] - m_new) * cs);
+        m[qb] = m_new;
+        const float mc = m_new * cs;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][j], cs, -mc));
+            psum += p;
+            pb[qb][kb >> 1][4 * (kb & 1) + j] = (__bf16)p;  // round to nearest even
+          }
+        l_part[qb] = l_part[qb] * alpha[qb] + psum;
+      }
+      if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+        for (int mb = 0; mb < kPDv / 16; mb++) {
+          o[0][mb] *= alpha[0];
+          o[1][mb] *= alpha[1];
+        }
+      }
+      // O^T[d][query] += V^T[d][keys] P^T[keys][query]: in step k2 lane group g
+      // multiplies keys 32 k2 + 16 h + 4 g + j (element 4 h + j of its weight
+      // fragment), which vt_pos stores as the 16 bytes at 32 k2 + 8 g
+#pragma unroll
+      for (int mb = 0; mb < kPDv / 16; mb++) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; k2++) {
+          const bf16x8 vv = lds_read<bf16x8>(sv + (16 * mb + c) * (kKTile * 2) + (((4 * k2 + g) ^ sw) << 4));
+          o[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[0][k2], o[0][mb], 0, 0, 0);
+          o[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[1][k2], o[1][mb], 0, 0, 0);
+        }
       }
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int32_t t = t0 + 16 * kb + 4 * g + j;
-        s[kb][j] = t <= qpos ? s[kb][j] * a.sm_log2 : -INFINITY;
-        tmax = fmaxf(tmax, s[kb][j]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
-    m = m_new;
-    // weights in bf16 (the product's operand); the normaliser adds the same values
-    bf16x8 pb[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const float p = m_new == -INFINITY ? 0.f : exp2f(s[kb][j] - m_new);
-        const uint16_t pbits = f32_to_bf16_bits(p);
-        psum += bf16_bits_to_f32(pbits);
-        pb[kb >> 1][4 * (kb & 1) + j] = __builtin_bit_cast(__bf16, pbits);
-      }
-    l_part = l_part * alpha + psum;
-    // O^T[d][query] += V^T[d][keys] P^T[keys][query], keys in the fragments' order:
-    // lane group g takes keys 16 (2 k2) + 4 g + (0..3) and 16 (2 k2 + 1) + 4 g + (0..3)
-#pragma unroll
-    for (int mb = 0; mb < kPDv / 16; mb++) {
-      o[mb] *= alpha;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; k2++) {
-        const char* vrow = s_v + (16 * mb + c) * kVRow;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * k2 + 4 * g));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * k2 + 16 + 4 * g));
-        const bf16x8 vv = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[k2], o[mb], 0, 0, 0);
-      }
-    }
+    wg_barrier();  // stage n & 1 is refilled by the next iteration's issue
   }
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (!q_live) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t orow = (((int64_t)b * a.Lq + ql) * a.h + head) * kPDv;
-  // lane holds query c, value rows 16 mb + 4 g + j
 #pragma unroll
-  for (int mb = 0; mb < kPDv / 16; mb++)
+  for (int qb = 0; qb < 2; qb++) {
+    float l_tot = l_part[qb] + __shfl_xor(l_part[qb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const int32_t ql = q0 + 32 * wave + 16 * qb + c;
+    if (ql >= Lb) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t orow = (((int64_t)b * a.Lq + ql) * a.h + head) * kPDv;
+    // lane holds query c, value rows 16 mb + 4 g + j
 #pragma unroll
-    for (int j = 0; j < 4; j++) store_elem<OT>(a.out, orow + 16 * mb + 4 * g + j, o[mb][j] * inv);
+    for (int mb = 0; mb < kPDv / 16; mb++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) store_elem<OT>(a.out, orow + 16 * mb + 4 * g + j, o[qb][mb][j] * inv);
+  }
 }
 
 }  // namespace
@@ -298,11 +398,12 @@ hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const v
                      dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((max_q_len + kQTile - 1) / kQTile, p.num_heads, p.batch);
+  const int32_t n_qtiles = (max_q_len + kQTile - 1) / kQTile;
+  const dim3 grid((uint32_t)((int64_t)n_qtiles * p.num_heads * p.batch));
   if (p.out_dtype == MLA_BF16)
-    hipLaunchKernelGGL(prefill_attn_kernel<MLA_BF16>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_attn_kernel<MLA_BF16>, grid, dim3(256), 0, s, a, n_qtiles);
   else
-    hipLaunchKernelGGL(prefill_attn_kernel<MLA_F32>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_attn_kernel<MLA_F32>, grid, dim3(256), 0, s, a, n_qtiles);
   return hipGetLastError();
 }
 

@@ -339,9 +339,9 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
  *   out [B, max_q_len, h, d_v]               out_dtype (rows l >= L_b untouched)
  * Supported: bf16 q, cache, rope and weights with d_latent 512, d_nope 128,
  * d_rope 64, d_v 128 (else MLA_ERR_UNSUPPORTED); q, c_kv, k_rope, W_UK and W_UV
- * 16-byte aligned.  The workspace holds the reconstructed keys and values of
- * every cached token: 2 x batch x h x Tpad x 128 bf16 values, Tpad =
- * max_blocks_per_seq x page_size rounded up to 128.
+ * 16-byte aligned.  The workspace holds the keys (reconstructed part and
+ * rope part) and values of every cached token: batch x h x Tpad x (192 + 128)
+ * bf16 values, Tpad = max_blocks_per_seq x page_size rounded up to 128.
  * ------------------------------------------------------------------------ */
 mla_status mla_prefill_workspace_size(const mla_decode_params* p, size_t* bytes);
 

@@ -156,9 +156,9 @@ def _prefill_params(**kw):
 
 
 def test_prefill_workspace_size_without_device():
-    # reconstructed keys and transposed values: 2 x B x h x Tpad x 128 bf16,
-    # Tpad = 5 blocks x 64 rounded up to 128
-    assert _lib.mla_prefill_workspace_size(_prefill_params()) == 2 * 3 * 4 * 384 * 128 * 2
+    # keys with their rope part and transposed values: B x h x Tpad x (192 + 128)
+    # bf16, Tpad = 5 blocks x 64 rounded up to 128
+    assert _lib.mla_prefill_workspace_size(_prefill_params()) == 3 * 4 * 384 * (192 + 128) * 2
 
 
 @pytest.mark.parametrize("bad", [dict(cache_dtype="f32"), dict(q_dtype="f32"),
