@@ -14,7 +14,7 @@
 //    W_UV[i] c_t for every cached t < T_b, a bf16 matrix-core GEMM per (128
 //    tokens, head, K or V) tile, both operands arriving in LDS by direct loads,
 //    the next latent chunk in flight while the current one is multiplied;
-//  * attention: a work group per (128 queries, head, sequence), a wave per 32
+//  * attention: a work group per (256 queries, head, sequence), a wave per 32
 //    queries; per 64-key tile S^T = K Q^T (16x16x32 MFMA, keys on M), the
 //    causal mask, an online softmax per query, and O^T += V^T P^T (the key
 //    order of this product is the one the score fragments already hold).
@@ -30,7 +30,8 @@ constexpr int kPDq = kPDn + kPDr;          // 192 query/key width
 constexpr int kDecTok = 128;               // tokens per decompression tile
 constexpr int kDecChunk = 64;              // latent values per LDS stage
 constexpr int kDecHalf = kDecTok * kDecChunk * 2;  // 16 KB: 128 rows of 128 bytes
-constexpr int kQTile = 128;                // queries per attention work group
+constexpr int kQTile = 256;                // queries per attention work group (8 waves)
+constexpr int kAStages = 3;                // key/value stages in LDS
 constexpr int kKTile = 64;                 // keys per attention step
 constexpr int kKStage = kKTile * kPDq * 2;  // 24 KB of keys per step
 constexpr int kVStage = kPDv * kKTile * 2;  // 16 KB of transposed values per step
@@ -188,34 +189,47 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
 }
 
 // ------------------------------------------------------------------ attention
-// One work group per (128 queries, head, sequence) on a 1-D grid, a wave per
+// One work group per (256 queries, head, sequence) on a 1-D grid, a wave per
 // 32 queries (two 16-query MFMA column blocks sharing every key fragment).
-// Key and value tiles arrive by direct-to-LDS loads into two stages, the tile
-// of step n + 1 in flight while step n is multiplied.  A stage holds 64 keys x
-// 192 (rows of 384 bytes) and then 128 value rows x 64 tokens (128 bytes),
-// 40 chunks of 1 KB; wave w loads chunks w + 4 u.
-__device__ inline void attn_issue(const PrefillArgs& a, int64_t bh, int32_t t0, lds_t* st,
-                                  int wave, int lane) {
-  const uint16_t* kbase = a.Kn + (bh * a.Tpad + t0) * kPDq;
-#pragma unroll
-  for (int u = 0; u < 6; u++) {
-    const int o = (wave + 4 * u) * 1024 + 16 * lane;
-    const int key = o / (kPDq * 2), pos = (o % (kPDq * 2)) >> 4;
-    dma16(kbase + key * kPDq + 8 * (pos ^ swz(key)), st + (wave + 4 * u) * 1024);
-  }
-  const uint16_t* vbase = a.Vt + bh * kPDv * a.Tpad + t0;
-#pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const int o = (wave + 4 * u) * 1024 + 16 * lane;
-    const int row = o >> 7, pos = (o >> 4) & 7;
-    dma16(vbase + (int64_t)row * a.Tpad + 8 * (pos ^ swz(row)), st + kKStage + (wave + 4 * u) * 1024);
-  }
+// Key and value tiles arrive by direct-to-LDS loads into three stages, the
+// tiles of steps n + 1 and n + 2 in flight while step n is multiplied, one
+// barrier per step.  A stage holds 64 keys x 192 (rows of 384 bytes) and then
+// 128 value rows x 64 tokens (128 bytes), 40 chunks of 1 KB; wave w loads key
+// chunks w + 8 u (u < 3) and value chunks w + 8 u (u < 2).  Waves skip steps
+// wholly after their queries; only steps on a wave's diagonal are masked.
+// Element offsets of this lane's DMA sources within a step's key rows and
+// value rows; the same for every step.
+struct AttnSrc {
+  int32_t k0, k1, k2, v0, v1;
+};
+
+__device__ inline int32_t attn_koff(int wave, int lane, int u) {
+  const int o = (wave + 8 * u) * 1024 + 16 * lane;
+  const int key = o / (kPDq * 2), pos = (o % (kPDq * 2)) >> 4;
+  return key * kPDq + 8 * (pos ^ swz(key));
+}
+
+__device__ inline int32_t attn_voff(int wave, int lane, int u, int32_t Tpad) {
+  const int o = (wave + 8 * u) * 1024 + 16 * lane;
+  const int row = o >> 7, pos = (o >> 4) & 7;
+  return row * Tpad + 8 * (pos ^ swz(row));
+}
+
+__device__ inline void attn_issue(const uint16_t* kbase, const uint16_t* vbase, const AttnSrc& f,
+                                  lds_t* st, int wave) {
+  lds_t* sk = st + wave * 1024;
+  lds_t* sv = st + kKStage + wave * 1024;
+  dma16(kbase + f.k0, sk);
+  dma16(kbase + f.k1, sk + 8192);
+  dma16(kbase + f.k2, sk + 16384);
+  dma16(vbase + f.v0, sv);
+  dma16(vbase + f.v1, sv + 8192);
 }
 
 template <int OT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
     PrefillArgs args, int32_t n_qtiles) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * (kKStage + kVStage)];
+  __shared__ __attribute__((aligned(1024))) char smem[kAStages * (kKStage + kVStage)];
   const PrefillArgs a = args;
   // Block order: the 8 XCDs take block ids round-robin; regroup so that each
   // XCD runs a contiguous range of (q-tile, head, sequence) work, the q-tiles
@@ -231,14 +245,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int32_t Lb = query_len(a, b, T);
   const int32_t q0 = qt * kQTile;
   if (q0 >= Lb) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int64_t bh = (int64_t)b * a.h + head;
   lds_t* ring = (lds_t*)smem;
   constexpr int kStage = kKStage + kVStage;
   const int32_t t_end = T - Lb + min(q0 + kQTile, Lb);  // keys this work group needs
   const int32_t n_tiles = (t_end + kKTile - 1) / kKTile;
-  attn_issue(a, bh, 0, ring, wave, lane);
+  const AttnSrc src{attn_koff(wave, lane, 0), attn_koff(wave, lane, 1), attn_koff(wave, lane, 2),
+                    attn_voff(wave, lane, 0, a.Tpad), attn_voff(wave, lane, 1, a.Tpad)};
+  const uint16_t* kseq = a.Kn + bh * a.Tpad * kPDq;
+  const uint16_t* vseq = a.Vt + bh * kPDv * a.Tpad;
   // this lane's queries: column c of the wave's two 16-query blocks
   int32_t qpos[2];
   bf16x8 qv[2][kPDq / 32];
@@ -251,99 +269,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < kPDq / 32; ks++)
       qv[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
+  attn_issue(kseq, vseq, src, ring, wave);
+  if (n_tiles > 1) attn_issue(kseq + kKTile * kPDq, vseq + kKTile, src, ring + kStage, wave);
   // the wave's first and last query positions (wave-uniform)
   const int32_t wave_lo = T - Lb + min(q0 + 32 * wave, Lb - 1);
   const int32_t wave_hi = T - Lb + min(q0 + 32 * wave + 31, Lb - 1);
-  const float cs = a.sm_log2;  // > 0: the max commutes with it
+  const float cs = a.sm_log2;   // > 0: the max commutes with it
+  const float lazy = 8.f / cs;  // the running maximum moves only by more than 2^8 in weight
   const int sw = (c >> 1) & 7;  // swz() of every row this lane reads
+  const bf16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
   f32x4v o[2][kPDv / 16] = {};
-  float m[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  f32x4v lsum[2] = {};  // every element: the weights' sum for this lane's query
+  float m[2] = {-INFINITY, -INFINITY};
+  int stage = 0;  // n % kAStages
   for (int32_t n = 0; n < n_tiles; n++) {
     const int32_t t0 = n * kKTile;
-    if (n + 1 < n_tiles) {
-      attn_issue(a, bh, t0 + kKTile, ring + ((n + 1) & 1) * kStage, wave, lane);
-      wait_vmcnt<10>();
-    } else {
+    if (n + 1 < n_tiles)
+      wait_vmcnt<5>();  // tile n + 1 may stay in flight
+    else
       wait_vmcnt<0>();
+    // tile n has landed for every wave, and every wave is done with tile n - 1,
+    // whose stage tile n + 2 refills
+    wg_barrier();
+    if (n + 2 < n_tiles) {
+      const int st2 = stage == 0 ? 2 : stage - 1;  // (n + 2) % 3
+      attn_issue(kseq + (int64_t)(t0 + 2 * kKTile) * kPDq, vseq + t0 + 2 * kKTile, src,
+                 ring + st2 * kStage, wave);
     }
-    wg_barrier();  // tile n has landed for every wave
-    const lds_t* sk = ring + (n & 1) * kStage;
+    const lds_t* sk = ring + stage * kStage;
+    stage = stage == kAStages - 1 ? 0 : stage + 1;
     const lds_t* sv = sk + kKStage;
     if (t0 <= wave_hi) {  // else every key of the tile comes after every query of the wave
-      const bool diag = t0 + kKTile - 1 > wave_lo;
       // S^T[key][query]: lane holds query c of block qb, keys 16 kb + 4 g + j
       f32x4v s[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
-        s[0][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        s[1][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < 2; qb++)
 #pragma unroll
-        for (int ks = 0; ks < kPDq / 32; ks++) {
+        for (int kb = 0; kb < 4; kb++) s[qb][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kPDq / 32; ks++) {
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
           const bf16x8 kv = lds_read<bf16x8>(sk + (16 * kb + c) * (kPDq * 2) + (((4 * ks + g) ^ sw) << 4));
           s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[0][ks], s[0][kb], 0, 0, 0);
           s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[1][ks], s[1][kb], 0, 0, 0);
         }
       }
+      const bool diag = t0 + kKTile - 1 > wave_lo;
       bf16x8 pb[2][2];
+      bool moved = false;
       float alpha[2];
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) {
         if (diag) {
+          // causal mask: key t0 + 16 kb + 4 g + j is visible while it is <= qpos
+          const int32_t lim = qpos[qb] - t0 - 4 * g;
 #pragma unroll
           for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              if (t0 + 16 * kb + 4 * g + j > qpos[qb]) s[qb][kb][j] = -INFINITY;
+              if (16 * kb + j > lim) s[qb][kb][j] = -INFINITY;
         }
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
           for (int j = 0; j < 4; j++) tmax = fmaxf(tmax, s[qb][kb][j]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        // key 0 is visible to every query, so m is finite from the first tile on
-        const float m_new = fmaxf(m[qb], tmax);
+        // The running maximum is raised only when the tile's exceeds it by more
+        // than `lazy` (weights stay <= 2^8); the same maximum cancels in O / l.
+        // The four lanes of a query must agree on it, so the maximum over them
+        // is taken only when some lane of the wave would raise it.  Key 0 is
+        // visible to every query, so m is finite from the first tile on.
+        if (__builtin_amdgcn_ballot_w64(tmax > m[qb] + lazy)) {
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        }
+        const float m_new = tmax > m[qb] + lazy ? tmax : m[qb];
+        moved |= m_new != m[qb];
         alpha[qb] = __builtin_amdgcn_exp2f((m[qb] - m_new) * cs);
         m[qb] = m_new;
         const float mc = m_new * cs;
-        float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][j], cs, -mc));
-            psum += p;
-            pb[qb][kb >> 1][4 * (kb & 1) + j] = (__bf16)p;  // round to nearest even
-          }
-        l_part[qb] = l_part[qb] * alpha[qb] + psum;
+          for (int j = 0; j < 4; j++)  // rounded to nearest even
+            pb[qb][kb >> 1][4 * (kb & 1) + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][kb][j], cs, -mc));
       }
-      if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
+      if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-        for (int mb = 0; mb < kPDv / 16; mb++) {
-          o[0][mb] *= alpha[0];
-          o[1][mb] *= alpha[1];
+        for (int qb = 0; qb < 2; qb++) {
+          lsum[qb] *= alpha[qb];
+#pragma unroll
+          for (int mb = 0; mb < kPDv / 16; mb++) o[qb][mb] *= alpha[qb];
         }
       }
       // O^T[d][query] += V^T[d][keys] P^T[keys][query]: in step k2 lane group g
       // multiplies keys 32 k2 + 16 h + 4 g + j (element 4 h + j of its weight
-      // fragment), which vt_pos stores as the 16 bytes at 32 k2 + 8 g
+      // fragment), which vt_pos stores as the 16 bytes at 32 k2 + 8 g.  A row
+      // of ones in place of V^T sums the same bf16 weights for the normaliser.
 #pragma unroll
-      for (int mb = 0; mb < kPDv / 16; mb++) {
+      for (int k2 = 0; k2 < 2; k2++) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; k2++) {
+        for (int mb = 0; mb < kPDv / 16; mb++) {
           const bf16x8 vv = lds_read<bf16x8>(sv + (16 * mb + c) * (kKTile * 2) + (((4 * k2 + g) ^ sw) << 4));
           o[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[0][k2], o[0][mb], 0, 0, 0);
           o[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[1][k2], o[1][mb], 0, 0, 0);
         }
+        lsum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][k2], lsum[0], 0, 0, 0);
+        lsum[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][k2], lsum[1], 0, 0, 0);
       }
     }
-    wg_barrier();  // stage n & 1 is refilled by the next iteration's issue
   }
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
-    float l_tot = l_part[qb] + __shfl_xor(l_part[qb], 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = lsum[qb][0];
     const int32_t ql = q0 + 32 * wave + 16 * qb + c;
     if (ql >= Lb) continue;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -401,9 +440,9 @@ hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const v
   const int32_t n_qtiles = (max_q_len + kQTile - 1) / kQTile;
   const dim3 grid((uint32_t)((int64_t)n_qtiles * p.num_heads * p.batch));
   if (p.out_dtype == MLA_BF16)
-    hipLaunchKernelGGL(prefill_attn_kernel<MLA_BF16>, grid, dim3(256), 0, s, a, n_qtiles);
+    hipLaunchKernelGGL(prefill_attn_kernel<MLA_BF16>, grid, dim3(512), 0, s, a, n_qtiles);
   else
-    hipLaunchKernelGGL(prefill_attn_kernel<MLA_F32>, grid, dim3(256), 0, s, a, n_qtiles);
+    hipLaunchKernelGGL(prefill_attn_kernel<MLA_F32>, grid, dim3(512), 0, s, a, n_qtiles);
   return hipGetLastError();
 }
 
