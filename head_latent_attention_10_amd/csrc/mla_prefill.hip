@@ -24,6 +24,7 @@ namespace mla {
 namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPDc = 512, kPDn = 128, kPDr = 64, kPDv = 128;
 constexpr int kPDq = kPDn + kPDr;          // 192 query/key width
@@ -161,14 +162,14 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
         const int32_t tok = t0 + 64 * wm + 32 * x + 8 * jb + 4 * g;  // 4 consecutive tokens
         if (which == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; e++)
-            a.Kn[(bh * a.Tpad + tok + e) * kPDq + col] = f32_to_bf16_bits(acc[x][y][4 * jb + e]);
+          for (int e = 0; e < 4; e++)  // round to nearest even
+            reinterpret_cast<__bf16*>(a.Kn)[(bh * a.Tpad + tok + e) * kPDq + col] =
+                (__bf16)acc[x][y][4 * jb + e];
         } else {
-          const uint32_t lo = f32_to_bf16_bits(acc[x][y][4 * jb + 0]) |
-                              ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * jb + 1]) << 16);
-          const uint32_t hi = f32_to_bf16_bits(acc[x][y][4 * jb + 2]) |
-                              ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * jb + 3]) << 16);
-          // tokens tok .. tok + 3 stay adjacent under vt_pos
+          const bf16x4 v = {(__bf16)acc[x][y][4 * jb + 0], (__bf16)acc[x][y][4 * jb + 1],
+                            (__bf16)acc[x][y][4 * jb + 2], (__bf16)acc[x][y][4 * jb + 3]};
+          const uint2 lohi = __builtin_bit_cast(uint2, v);
+          const uint32_t lo = lohi.x, hi = lohi.y;
           *reinterpret_cast<uint2*>(a.Vt + (bh * kPDv + col) * a.Tpad + vt_pos(tok)) = uint2{lo, hi};
         }
       }
