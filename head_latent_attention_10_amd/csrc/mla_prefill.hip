@@ -83,21 +83,26 @@ __device__ inline T lds_read(const lds_t* p) {
 }
 
 // ------------------------------------------------------------------ decompress
-// blockIdx = (token tile, 2 i + which, b); wave (wm, wn) computes tokens
-// 64 wm .. +63 by outputs 64 wm .. +63 of the 128 x 128 tile.  A stage holds 64
+// blockIdx = (token tile, i, b); WHICH 0 reconstructs keys, 1 values.  Wave
+// (wm, wn) computes tokens 64 wm .. +63 by outputs 64 wn .. +63 of the
+// 128 x 128 tile, as outputs x tokens for keys and tokens x outputs for values,
+// so that each lane holds four adjacent values of its output row (key row
+// [token][output], value row [output][token]).  The finished tile is staged in
+// LDS and written out in 16-byte pieces.  A stage holds 64
 // latent values of the 128 tokens (rows 0..127) and of the 128 weight rows;
 // the wave loads 1 KB chunks wave + 4 u of each half (8 rows of 8 pieces).
+template <int WHICH>
 __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kDecHalf];  // two stages of A | B
   const PrefillArgs a = args;
-  const int32_t b = blockIdx.z, head = blockIdx.y >> 1, which = blockIdx.y & 1;
+  const int32_t b = blockIdx.z, head = blockIdx.y;
   const int32_t T = cached_len(a, b);
   const int32_t t0 = blockIdx.x * kDecTok;
   if (t0 >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, r = lane & 31;
   lds_t* ring = (lds_t*)smem;
-  const uint16_t* W = (which ? a.W_UV : a.W_UK) + (int64_t)head * kPDn * kPDc;
+  const uint16_t* W = (WHICH ? a.W_UV : a.W_UK) + (int64_t)head * kPDn * kPDc;
   // DMA sources of this lane: row 8 (wave + 4 u) + lane / 8, piece (lane & 7) ^ swz(row)
   auto src_a = [&](int u) -> const uint16_t* {
     const int row = 8 * (wave + 4 * u) + (lane >> 3);
@@ -146,36 +151,43 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
       for (int x = 0; x < 2; x++)
 #pragma unroll
         for (int y = 0; y < 2; y++)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
+          acc[x][y] = WHICH == 0
+                          ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[y], av[x], acc[x][y], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
     }
-    wg_barrier();  // stage cc & 1 is refilled by the next iteration's issue
+    wg_barrier();  // stage cc & 1 is refilled by the next iteration (or reused below)
   }
-  // D[token][output]: lane holds output column r, tokens 8 (j / 4) + 4 g + j % 4
-  const int64_t bh = (int64_t)b * a.h + head;
+  // Stage the tile as 128 rows of 128 bf16 (272-byte rows).  Keys: D[output]
+  // [token], lane holds token 64 wm + 32 x + r and outputs 64 wn + 32 y + 8 jb +
+  // 4 g + (0..3).  Values: D[token][output], lane holds output 64 wn + 32 y + r
+  // and tokens 64 wm + 32 x + 8 jb + 4 g + (0..3), stored at their vt_pos.
+  constexpr int kORow = 2 * kDecTok + 16;
+  lds_t* ot = ring;
 #pragma unroll
-  for (int x = 0; x < 2; x++) {
+  for (int x = 0; x < 2; x++)
 #pragma unroll
-    for (int y = 0; y < 2; y++) {
-      const int32_t col = 64 * wn + 32 * y + r;
+    for (int y = 0; y < 2; y++)
 #pragma unroll
       for (int jb = 0; jb < 4; jb++) {
-        const int32_t tok = t0 + 64 * wm + 32 * x + 8 * jb + 4 * g;  // 4 consecutive tokens
-        if (which == 0) {
-#pragma unroll
-          for (int e = 0; e < 4; e++)  // round to nearest even
-            reinterpret_cast<__bf16*>(a.Kn)[(bh * a.Tpad + tok + e) * kPDq + col] =
-                (__bf16)acc[x][y][4 * jb + e];
-        } else {
-          const bf16x4 v = {(__bf16)acc[x][y][4 * jb + 0], (__bf16)acc[x][y][4 * jb + 1],
-                            (__bf16)acc[x][y][4 * jb + 2], (__bf16)acc[x][y][4 * jb + 3]};
-          const uint2 lohi = __builtin_bit_cast(uint2, v);
-          const uint32_t lo = lohi.x, hi = lohi.y;
-          *reinterpret_cast<uint2*>(a.Vt + (bh * kPDv + col) * a.Tpad + vt_pos(tok)) = uint2{lo, hi};
-        }
+        const bf16x4 v = {(__bf16)acc[x][y][4 * jb + 0], (__bf16)acc[x][y][4 * jb + 1],
+                          (__bf16)acc[x][y][4 * jb + 2], (__bf16)acc[x][y][4 * jb + 3]};
+        const int quad = 8 * jb + 4 * g;
+        const int row = WHICH == 0 ? 64 * wm + 32 * x + r : 64 * wn + 32 * y + r;
+        const int col = WHICH == 0 ? 64 * wn + 32 * y + quad : vt_pos(64 * wm + 32 * x + quad);
+        *reinterpret_cast<bf16x4 __attribute__((address_space(3)))*>(ot + row * kORow + 2 * col) = v;
       }
-    }
+  wg_barrier();
+  const int64_t bh = (int64_t)b * a.h + head;
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int pi = tid + 256 * u, row = pi >> 4, pc = pi & 15;
+    const u32x4 v = lds_read<u32x4>(ot + row * kORow + 16 * pc);
+    if (WHICH == 0)  // key row t0 + row, reconstructed part
+      *reinterpret_cast<u32x4*>(a.Kn + (bh * a.Tpad + t0 + row) * kPDq + 8 * pc) = v;
+    else  // value row `row`, tokens t0 .. t0 + 127
+      *reinterpret_cast<u32x4*>(a.Vt + (bh * kPDv + row) * a.Tpad + t0 + 8 * pc) = v;
   }
-  if (which == 0) {
+  if (WHICH == 0) {
     // the key's rope part, copied beside the reconstructed part (rows past T
     // repeat the last token, as above)
 #pragma unroll
@@ -434,7 +446,9 @@ hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const v
   a.Tpad = prefill_tpad(p);
   const float sm = p.sm_scale > 0.f ? p.sm_scale : 1.0f / sqrtf((float)(p.d_nope + p.d_rope));
   a.sm_log2 = sm * 1.4426950408889634f;
-  hipLaunchKernelGGL(prefill_decompress_kernel, dim3(a.Tpad / kDecTok, 2 * p.num_heads, p.batch),
+  hipLaunchKernelGGL(prefill_decompress_kernel<0>, dim3(a.Tpad / kDecTok, p.num_heads, p.batch),
+                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(prefill_decompress_kernel<1>, dim3(a.Tpad / kDecTok, p.num_heads, p.batch),
                      dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
