@@ -127,3 +127,25 @@ def test_prefill_dsv3_heads_long_context_sampled():
     for b in range(2):
         assert np.all(np.isfinite(got[b, :int(pi.q_lens[b])])), b
     check(pi, got, heads=[0, 37, 127], rows=[0, 63, 64, 255, 299, 511], label="dsv3 long")
+
+
+def test_prefill_empty_sequences():
+    """A sequence with no cached tokens writes nothing, whatever q_lens says;
+    its neighbours are unaffected."""
+    cfg = DSV3.replace(heads=2, batch=3, seed=5204)
+    _say("prefill empty sequences")
+    pi = generate_prefill(cfg, 40, seq_lens=[0, 90, 0], q_lens=[0, 40, 0])
+    got = run_prefill(pi, q_lens=[7, 40, 40])
+    check(pi, got, label="empty")
+
+
+def test_prefill_bench_configuration_sampled():
+    """The benchmark's call (2 sequences of 16384 cached tokens, the last 4096
+    new, 128 heads, bf16 output, seed 1200): every output finite; rows at the
+    chunk's start, q-tile edges and end match the oracle on sampled heads."""
+    cfg = CONFIGS["dsv3_b8_32k"].replace(batch=2, seq_len=16384, out_dtype="bf16", seed=1200)
+    _say("prefill bench configuration")
+    pi = generate_prefill(cfg, 4096)
+    got = run_prefill(pi)
+    assert np.all(np.isfinite(got))
+    check(pi, got, heads=[0, 127], batches=[0, 1], rows=[0, 255, 256, 4095], label="bench config")
