@@ -17,6 +17,11 @@
  * which equals softmax((q_nope.(W_UK c) + q_rope.k_rope) * sm_scale) (W_UV c),
  * the unabsorbed form, by associativity.
  *
+ * Beside the decode step the library holds the latent-cache writer, DSA
+ * sparse decode (indexer, top-k, sparse step), TPLA decode, grouped-MLA
+ * decode and MHA-mode prefill; each entry point's comment below cites the
+ * passage that defines it.
+ *
  * Conventions shared by every entry point:
  *   - All tensor arguments are DEVICE pointers owned by the caller; the
  *     library never allocates, frees or retains them.  Scratch memory is the
