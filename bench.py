@@ -505,7 +505,8 @@ def measure_prefill(spec: str, steps: int, warmup: int):
     stream = torch.cuda.current_stream()
 
     def step():
-        _lib.mla_prefill(p, L, q, ql, dev.c_kv, dev.k_rope, dev.block_table, dev.seq_lens,
+        _lib.mla_prefill(p, L, q, ql, dev.c_kv, dev.c_kv_scale, dev.k_rope, dev.block_table,
+                         dev.seq_lens,
                          dev.W_UK, dev.W_UV, out, ws, n, stream)
 
     for _ in range(warmup):

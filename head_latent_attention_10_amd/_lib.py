@@ -115,7 +115,7 @@ _SIGNATURES = {
     "mla_grouped_decode": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
     "mla_prefill_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
-    "mla_prefill": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "mla_prefill": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]),
     "mla_tpla_decode": (ctypes.c_int, [_PP, _TP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
@@ -396,11 +396,12 @@ def mla_prefill_workspace_size(p) -> int:
     return n.value
 
 
-def mla_prefill(p, max_q_len: int, q, q_lens, c_kv, k_rope, block_table, seq_lens, W_UK, W_UV,
-                out, workspace, workspace_bytes=None, stream=None):
+def mla_prefill(p, max_q_len: int, q, q_lens, c_kv, c_kv_scale, k_rope, block_table, seq_lens,
+                W_UK, W_UV, out, workspace, workspace_bytes=None, stream=None):
     if workspace_bytes is None:
         workspace_bytes = _nbytes(workspace)
     _check("mla_prefill", load_library().mla_prefill(
-        ctypes.byref(p), int(max_q_len), _ptr(q), _ptr(q_lens), _ptr(c_kv), _ptr(k_rope),
+        ctypes.byref(p), int(max_q_len), _ptr(q), _ptr(q_lens), _ptr(c_kv), _ptr(c_kv_scale),
+        _ptr(k_rope),
         _ptr(block_table), _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(workspace),
         workspace_bytes, _stream(stream)))

@@ -777,14 +777,15 @@ mla_status mla_prefill_workspace_size(const mla_decode_params* p, size_t* bytes)
   mla_status st = validate(p);
   if (st != MLA_OK) return st;
   if (!mla::prefill_supported(*p))
-    return fail(MLA_ERR_UNSUPPORTED, "prefill needs bf16 and d_latent 512, d_nope 128, d_rope 64, d_v 128");
+    return fail(MLA_ERR_UNSUPPORTED, "prefill needs bf16 (cache bf16 or fp8) and d_latent 512, d_nope 128, d_rope 64, d_v 128");
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = prefill_ws_bytes(*p);
   return MLA_OK;
 }
 
 mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void* q,
-                       const int32_t* q_lens, const void* c_kv, const void* k_rope,
+                       const int32_t* q_lens, const void* c_kv, const float* c_kv_scale,
+                       const void* k_rope,
                        const int32_t* block_table, const int32_t* seq_lens, const void* W_UK,
                        const void* W_UV, void* out, void* workspace, size_t workspace_bytes,
                        void* stream) {
@@ -792,7 +793,7 @@ mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void
   mla_status st = validate(p);
   if (st != MLA_OK) return st;
   if (!mla::prefill_supported(*p))
-    return fail(MLA_ERR_UNSUPPORTED, "prefill needs bf16 and d_latent 512, d_nope 128, d_rope 64, d_v 128");
+    return fail(MLA_ERR_UNSUPPORTED, "prefill needs bf16 (cache bf16 or fp8) and d_latent 512, d_nope 128, d_rope 64, d_v 128");
   if (max_q_len < 1 || max_q_len > (1 << 24))
     return fail(MLA_ERR_INVALID_ARG, "max_q_len %d outside [1, 2^24]", max_q_len);
   if ((int64_t)p->batch * max_q_len * p->num_heads * 192 >= ((int64_t)1 << 40))
@@ -805,13 +806,16 @@ mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void
     return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!(aligned16(q) && aligned16(c_kv) && aligned16(k_rope) && aligned16(W_UK) && aligned16(W_UV)))
     return fail(MLA_ERR_INVALID_ARG, "q, c_kv, k_rope, W_UK and W_UV must be 16-byte aligned");
+  if ((p->cache_dtype == MLA_FP8_E4M3) != (c_kv_scale != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "c_kv_scale is required for an fp8 cache and only then");
   const size_t need = prefill_ws_bytes(*p);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
     return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  const hipError_t e = mla::launch_prefill(*p, max_q_len, q, q_lens, c_kv, k_rope, block_table,
+  const hipError_t e = mla::launch_prefill(*p, max_q_len, q, q_lens, c_kv, c_kv_scale, k_rope,
+                                           block_table,
                                            seq_lens, W_UK, W_UV, out, ws,
                                            ws + align256((size_t)p->batch * p->num_heads *
                                                          mla::prefill_tpad(*p) * 2 * 192),

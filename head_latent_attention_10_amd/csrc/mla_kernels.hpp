@@ -109,13 +109,14 @@ hipError_t launch_tpla_expand(const void* q1, void* q2, int32_t q_dtype, int32_t
 hipError_t launch_tpla_gather(const float* o2, float* o1, int32_t B, int32_t h, int32_t g,
                               int32_t d_c, hipStream_t s);
 
-// MHA-mode prefill (mla_prefill.hip): bf16, d_c 512, d_nope 128, d_rope 64, d_v 128.
+// MHA-mode prefill (mla_prefill.hip): bf16 or fp8 cache, d_c 512, d_nope 128, d_rope 64, d_v 128.
 bool prefill_supported(const mla_decode_params& p);
 int32_t prefill_tpad(const mla_decode_params& p);  // token stride of the K / V^T workspace
 hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const void* q,
-                          const int32_t* q_lens, const void* c_kv, const void* k_rope,
-                          const int32_t* block_table, const int32_t* seq_lens, const void* W_UK,
-                          const void* W_UV, void* out, void* Kn, void* Vt, hipStream_t s);
+                          const int32_t* q_lens, const void* c_kv, const float* c_kv_scale,
+                          const void* k_rope, const int32_t* block_table, const int32_t* seq_lens,
+                          const void* W_UK, const void* W_UV, void* out, void* Kn, void* Vt,
+                          hipStream_t s);
 
 // DSA indexer and top-k (mla_dsa.hip).
 bool indexer_mfma_ok(int32_t heads, int32_t dim);

@@ -25,6 +25,7 @@ namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPDc = 512, kPDn = 128, kPDr = 64, kPDv = 128;
 constexpr int kPDq = kPDn + kPDr;          // 192 query/key width
@@ -40,7 +41,9 @@ constexpr int kVStage = kPDv * kKTile * 2;  // 16 KB of transposed values per st
 struct PrefillArgs {
   const uint16_t* q;        // [B, Lq, h, 192]
   const int32_t* q_lens;    // [B]
-  const uint16_t* c_kv;     // [nb, P, 512]
+  const uint16_t* c_kv;     // [nb, P, 512] bf16, or
+  const uint8_t* c_kv8;     // [nb, P, 512] E4M3 codes with
+  const float* c_kv_scale;  // [nb, P] per-token scales
   const uint16_t* k_rope;   // [nb, P, 64]
   const int32_t* block_table;
   const int32_t* seq_lens;
@@ -91,9 +94,10 @@ __device__ inline T lds_read(const lds_t* p) {
 // LDS and written out in 16-byte pieces.  A stage holds 64
 // latent values of the 128 tokens (rows 0..127) and of the 128 weight rows;
 // the wave loads 1 KB chunks wave + 4 u of each half (8 rows of 8 pieces).
-template <int WHICH>
+template <int WHICH, bool F8>
 __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kDecHalf];  // two stages of A | B
+  __shared__ float s_scale[kDecTok];  // fp8: the tile's per-token scales
   const PrefillArgs a = args;
   const int32_t b = blockIdx.z, head = blockIdx.y;
   const int32_t T = cached_len(a, b);
@@ -114,13 +118,39 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
     const int row = 8 * (wave + 4 * u) + (lane >> 3);
     return W + (int64_t)row * kPDc + 8 * ((lane & 7) ^ swz(row));
   };
-  const uint16_t *pa0 = src_a(0), *pa1 = src_a(1), *pa2 = src_a(2), *pa3 = src_a(3);
+  // fp8 rows are 64 bytes a stage: row 16 (wave + 4 u) + lane / 4 (u < 2), piece
+  // (lane & 3) ^ swz8(row); the codes convert to bf16 exactly, and the token's
+  // scale multiplies the finished product
+  auto swz8 = [](int row) { return (row >> 1) & 3; };
+  auto src_a8 = [&](int u) -> const uint8_t* {
+    const int row = 16 * (wave + 4 * u) + (lane >> 2);
+    const int32_t t = min(t0 + row, T - 1);
+    const int64_t slot = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks);
+    return a.c_kv8 + slot * kPDc + 16 * ((lane & 3) ^ swz8(row));
+  };
+  const uint16_t *pa0 = nullptr, *pa1 = nullptr, *pa2 = nullptr, *pa3 = nullptr;
+  const uint8_t *pq0 = nullptr, *pq1 = nullptr;
+  if (F8) {
+    pq0 = src_a8(0);
+    pq1 = src_a8(1);
+    if (tid < kDecTok) {
+      const int32_t t = min(t0 + tid, T - 1);
+      s_scale[tid] = a.c_kv_scale[phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks)];
+    }
+  } else {
+    pa0 = src_a(0), pa1 = src_a(1), pa2 = src_a(2), pa3 = src_a(3);
+  }
   const uint16_t *pb0 = src_b(0), *pb1 = src_b(1), *pb2 = src_b(2), *pb3 = src_b(3);
   auto issue = [&](int32_t k0, lds_t* st) {
-    dma16(pa0 + k0, st + (wave + 0) * 1024);
-    dma16(pa1 + k0, st + (wave + 4) * 1024);
-    dma16(pa2 + k0, st + (wave + 8) * 1024);
-    dma16(pa3 + k0, st + (wave + 12) * 1024);
+    if (F8) {
+      dma16(pq0 + k0, st + (wave + 0) * 1024);
+      dma16(pq1 + k0, st + (wave + 4) * 1024);
+    } else {
+      dma16(pa0 + k0, st + (wave + 0) * 1024);
+      dma16(pa1 + k0, st + (wave + 4) * 1024);
+      dma16(pa2 + k0, st + (wave + 8) * 1024);
+      dma16(pa3 + k0, st + (wave + 12) * 1024);
+    }
     dma16(pb0 + k0, st + kDecHalf + (wave + 0) * 1024);
     dma16(pb1 + k0, st + kDecHalf + (wave + 4) * 1024);
     dma16(pb2 + k0, st + kDecHalf + (wave + 8) * 1024);
@@ -132,7 +162,7 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
   for (int cc = 0; cc < kChunks; cc++) {
     if (cc + 1 < kChunks) {
       issue((cc + 1) * kDecChunk, ring + ((cc + 1) & 1) * 2 * kDecHalf);
-      wait_vmcnt<8>();
+      wait_vmcnt<F8 ? 6 : 8>();
     } else {
       wait_vmcnt<0>();
     }
@@ -144,7 +174,17 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
 #pragma unroll
       for (int x = 0; x < 2; x++) {
         const int ra = 64 * wm + 32 * x + r, rb = 64 * wn + 32 * x + r;
-        av[x] = lds_read<bf16x8>(st + ra * 128 + (((2 * s + g) ^ swz(ra)) << 4));
+        if (F8) {
+          const u32x2 w = lds_read<u32x2>(st + ra * 64 + ((s ^ swz8(ra)) << 4) + 8 * g);
+          const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+          const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+          const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+          const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+          av[x] = bf16x8{(__bf16)f0[0], (__bf16)f0[1], (__bf16)f1[0], (__bf16)f1[1],
+                         (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
+        } else {
+          av[x] = lds_read<bf16x8>(st + ra * 128 + (((2 * s + g) ^ swz(ra)) << 4));
+        }
         bv[x] = lds_read<bf16x8>(st + kDecHalf + rb * 128 + (((2 * s + g) ^ swz(rb)) << 4));
       }
 #pragma unroll
@@ -169,9 +209,15 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
     for (int y = 0; y < 2; y++)
 #pragma unroll
       for (int jb = 0; jb < 4; jb++) {
-        const bf16x4 v = {(__bf16)acc[x][y][4 * jb + 0], (__bf16)acc[x][y][4 * jb + 1],
-                          (__bf16)acc[x][y][4 * jb + 2], (__bf16)acc[x][y][4 * jb + 3]};
         const int quad = 8 * jb + 4 * g;
+        float sc[4] = {1.f, 1.f, 1.f, 1.f};
+        if (F8) {
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            sc[e] = s_scale[WHICH == 0 ? 64 * wm + 32 * x + r : 64 * wm + 32 * x + quad + e];
+        }
+        const bf16x4 v = {(__bf16)(acc[x][y][4 * jb + 0] * sc[0]), (__bf16)(acc[x][y][4 * jb + 1] * sc[1]),
+                          (__bf16)(acc[x][y][4 * jb + 2] * sc[2]), (__bf16)(acc[x][y][4 * jb + 3] * sc[3])};
         const int row = WHICH == 0 ? 64 * wm + 32 * x + r : 64 * wn + 32 * y + r;
         const int col = WHICH == 0 ? 64 * wn + 32 * y + quad : vt_pos(64 * wm + 32 * x + quad);
         *reinterpret_cast<bf16x4 __attribute__((address_space(3)))*>(ot + row * kORow + 2 * col) = v;
@@ -411,7 +457,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }  // namespace
 
 bool prefill_supported(const mla_decode_params& p) {
-  return p.q_dtype == MLA_BF16 && p.cache_dtype == MLA_BF16 && p.rope_dtype == MLA_BF16 &&
+  return p.q_dtype == MLA_BF16 && (p.cache_dtype == MLA_BF16 || p.cache_dtype == MLA_FP8_E4M3) &&
+         p.rope_dtype == MLA_BF16 &&
          p.weight_dtype == MLA_BF16 && p.d_latent == kPDc && p.d_nope == kPDn &&
          p.d_rope == kPDr && p.d_v == kPDv;
 }
@@ -422,13 +469,16 @@ int32_t prefill_tpad(const mla_decode_params& p) {
 }
 
 hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const void* q,
-                          const int32_t* q_lens, const void* c_kv, const void* k_rope,
-                          const int32_t* block_table, const int32_t* seq_lens, const void* W_UK,
-                          const void* W_UV, void* out, void* Kn, void* Vt, hipStream_t s) {
+                          const int32_t* q_lens, const void* c_kv, const float* c_kv_scale,
+                          const void* k_rope, const int32_t* block_table, const int32_t* seq_lens,
+                          const void* W_UK, const void* W_UV, void* out, void* Kn, void* Vt,
+                          hipStream_t s) {
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.q_lens = q_lens;
   a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.c_kv8 = static_cast<const uint8_t*>(c_kv);
+  a.c_kv_scale = c_kv_scale;
   a.k_rope = static_cast<const uint16_t*>(k_rope);
   a.block_table = block_table;
   a.seq_lens = seq_lens;
@@ -446,10 +496,14 @@ hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const v
   a.Tpad = prefill_tpad(p);
   const float sm = p.sm_scale > 0.f ? p.sm_scale : 1.0f / sqrtf((float)(p.d_nope + p.d_rope));
   a.sm_log2 = sm * 1.4426950408889634f;
-  hipLaunchKernelGGL(prefill_decompress_kernel<0>, dim3(a.Tpad / kDecTok, p.num_heads, p.batch),
-                     dim3(256), 0, s, a);
-  hipLaunchKernelGGL(prefill_decompress_kernel<1>, dim3(a.Tpad / kDecTok, p.num_heads, p.batch),
-                     dim3(256), 0, s, a);
+  const dim3 dgrid(a.Tpad / kDecTok, p.num_heads, p.batch);
+  if (p.cache_dtype == MLA_FP8_E4M3) {
+    hipLaunchKernelGGL((prefill_decompress_kernel<0, true>), dgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_decompress_kernel<1, true>), dgrid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((prefill_decompress_kernel<0, false>), dgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_decompress_kernel<1, false>), dgrid, dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int32_t n_qtiles = (max_q_len + kQTile - 1) / kQTile;

@@ -342,8 +342,9 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
  *                  + q_rope . k_rope_t)) (W_UV[i] c_t)
  *   q   [B, max_q_len, h, d_nope + d_rope]   bf16, q_rope pre-rotated
  *   out [B, max_q_len, h, d_v]               out_dtype (rows l >= L_b untouched)
- * Supported: bf16 q, cache, rope and weights with d_latent 512, d_nope 128,
- * d_rope 64, d_v 128 (else MLA_ERR_UNSUPPORTED); q, c_kv, k_rope, W_UK and W_UV
+ * Supported: bf16 q, rope and weights, a bf16 or fp8 (E4M3 with c_kv_scale,
+ * which must be NULL otherwise) cache, with d_latent 512, d_nope 128, d_rope
+ * 64, d_v 128 (else MLA_ERR_UNSUPPORTED); q, c_kv, k_rope, W_UK and W_UV
  * 16-byte aligned.  The workspace holds the keys (reconstructed part and
  * rope part) and values of every cached token: batch x h x Tpad x (192 + 128)
  * bf16 values, Tpad = max_blocks_per_seq x page_size rounded up to 128.
@@ -351,7 +352,8 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
 mla_status mla_prefill_workspace_size(const mla_decode_params* p, size_t* bytes);
 
 mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void* q,
-                       const int32_t* q_lens, const void* c_kv, const void* k_rope,
+                       const int32_t* q_lens, const void* c_kv, const float* c_kv_scale,
+                       const void* k_rope,
                        const int32_t* block_table, const int32_t* seq_lens, const void* W_UK,
                        const void* W_UV, void* out, void* workspace, size_t workspace_bytes,
                        void* stream);

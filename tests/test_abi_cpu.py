@@ -162,7 +162,7 @@ def test_prefill_workspace_size_without_device():
 
 
 @pytest.mark.parametrize("bad", [dict(cache_dtype="f32"), dict(q_dtype="f32"),
-                                 dict(cache_dtype="e4m3"), dict(d_nope=64), dict(d_v=64),
+                                 dict(weight_dtype="f32"), dict(d_nope=64), dict(d_v=64),
                                  dict(d_latent=256), dict(d_rope=32)])
 def test_prefill_unsupported_shapes(bad):
     with pytest.raises(_lib.MlaError) as ei:
@@ -174,12 +174,14 @@ def test_prefill_rejects_bad_arguments_before_launch():
     p = _prefill_params()
     fake = 0x10000
     n = _lib.mla_prefill_workspace_size(p)
-    args = [fake] * 9
+    args = [fake, fake, fake, None, fake, fake, fake, fake, fake, fake]  # no scale: bf16 cache
     for bad_len in (0, -1, (1 << 24) + 1):
         with pytest.raises(_lib.MlaError) as ei:
             _lib.mla_prefill(p, bad_len, *args, fake, n)
         assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
-    for i in range(9):
+    for i in range(10):
+        if i == 3:
+            continue
         a = list(args)
         a[i] = None
         with pytest.raises(_lib.MlaError) as ei:
@@ -193,4 +195,11 @@ def test_prefill_rejects_bad_arguments_before_launch():
     assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
     with pytest.raises(_lib.MlaError) as ei:  # misaligned query
         _lib.mla_prefill(p, 16, fake + 2, *args[1:], fake, n)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    with pytest.raises(_lib.MlaError) as ei:  # a scale pointer with a bf16 cache
+        _lib.mla_prefill(p, 16, *args[:3], fake, *args[4:], fake, n)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    p8 = _prefill_params(cache_dtype="e4m3")
+    with pytest.raises(_lib.MlaError) as ei:  # an fp8 cache without its scales
+        _lib.mla_prefill(p8, 16, *args, fake, _lib.mla_prefill_workspace_size(p8))
     assert ei.value.status == _lib.MLA_ERR_INVALID_ARG

@@ -1,7 +1,7 @@
 """MHA-mode prefill on the GPU vs its CPU oracle, through the C ABI (needs an
 MI355X): ragged chunks over ragged cached contexts (one row, a partial first
 query tile, a ragged last one, whole-sequence prefill from an empty cache),
-pages smaller than a key tile, both output types, q_lens of zero and beyond
+pages smaller than a key tile, both output types, the fp8 cache, q_lens of zero and beyond
 the context, and the DeepSeek-V3 head count at a longer context on sampled
 rows and heads; rows past each chunk stay untouched."""
 import sys
@@ -53,8 +53,8 @@ def run_prefill(pi, q_lens=None):
         out.fill_(float("nan"))
     else:
         out.fill_(0x7FC0)
-    _lib.mla_prefill(p, pi.max_q_len, q, ql, dev.c_kv, dev.k_rope, dev.block_table, dev.seq_lens,
-                     dev.W_UK, dev.W_UV, out, ws, n)
+    _lib.mla_prefill(p, pi.max_q_len, q, ql, dev.c_kv, dev.c_kv_scale, dev.k_rope, dev.block_table,
+                     dev.seq_lens, dev.W_UK, dev.W_UV, out, ws, n)
     torch.cuda.synchronize()
     return (out if c.out_dtype == "f32" else out.view(torch.bfloat16)).float().double().cpu().numpy()
 
@@ -95,6 +95,10 @@ CASES = {
     # pages of 16 tokens, prefill from an empty cache, f32 output
     "whole_f32_p16": dict(cfg=DSV3.replace(heads=3, batch=2, seed=5201, page_size=16),
                           seq_lens=[129, 64], max_q_len=129, q_lens=[129, 64]),
+    # the fp8 cache (E4M3 codes and per-token scales; the oracle dequantises the same codes)
+    "fp8_ragged": dict(cfg=CONFIGS["dsv3_fp8_16k"].replace(heads=4, batch=3, seed=5205,
+                                                           seq_len=None, seq_len_range=(1, 400)),
+                       seq_lens=[1, 150, 333], max_q_len=140, q_lens=[1, 140, 77]),
 }
 
 
