@@ -482,8 +482,8 @@ def prefill_flops(seq_lens, q_lens, heads, d_qk=192, d_v=128, d_c=512):
 
 def measure_prefill(spec: str, steps: int, warmup: int):
     """Time MHA-mode prefill (mla_prefill) on the DeepSeek-V3 shape: spec
-    'batch:context:chunk' = `batch` sequences of `context` cached tokens whose
-    last `chunk` are the new query tokens."""
+    'batch:context:chunk[:fp8]' = `batch` sequences of `context` cached tokens
+    whose last `chunk` are the new query tokens, over a bf16 (or fp8) cache."""
     import torch
 
     from head_latent_attention_10_amd import _lib
@@ -491,8 +491,11 @@ def measure_prefill(spec: str, steps: int, warmup: int):
     from mla_inputs import CONFIGS
     from mla_inputs.prefill import generate_prefill
 
-    B, T, L = (int(x) for x in spec.split(":"))
-    cfg = CONFIGS["dsv3_b8_32k"].replace(batch=B, seq_len=T, out_dtype="bf16", seed=1200)
+    parts = spec.split(":")
+    B, T, L = (int(x) for x in parts[:3])
+    cache = "e4m3" if parts[3:] == ["fp8"] else "bf16"
+    cfg = CONFIGS["dsv3_b8_32k"].replace(batch=B, seq_len=T, out_dtype="bf16", seed=1200,
+                                         cache_dtype=cache)
     pi = generate_prefill(cfg, L)
     dev = DeviceInputs(pi.dense)
     q = to_device_array(pi.q, dev.device)
@@ -584,8 +587,8 @@ def main():
                     help="TPLA workloads workload:shards reported under 'extra' (comma list)")
     ap.add_argument("--grouped", default="dsv3_ragged_32k:2",
                     help="grouped-MLA workloads workload:groups reported under 'extra' (comma list)")
-    ap.add_argument("--prefill", default="2:16384:4096",
-                    help="MHA-mode prefill workloads batch:context:chunk (DeepSeek-V3 shape) "
+    ap.add_argument("--prefill", default="2:16384:4096,2:16384:4096:fp8",
+                    help="MHA-mode prefill workloads batch:context:chunk[:fp8] (DeepSeek-V3 shape) "
                          "reported under 'extra' (comma list)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="measure only the prefill workloads (for profiling)")
