@@ -808,6 +808,8 @@ mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void
     return fail(MLA_ERR_INVALID_ARG, "q, c_kv, k_rope, W_UK and W_UV must be 16-byte aligned");
   if ((p->cache_dtype == MLA_FP8_E4M3) != (c_kv_scale != nullptr))
     return fail(MLA_ERR_INVALID_ARG, "c_kv_scale is required for an fp8 cache and only then");
+  if (reinterpret_cast<uintptr_t>(c_kv_scale) & 3)
+    return fail(MLA_ERR_INVALID_ARG, "c_kv_scale must be 4-byte aligned");
   const size_t need = prefill_ws_bytes(*p);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);

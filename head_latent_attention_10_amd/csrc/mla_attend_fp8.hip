@@ -4,8 +4,12 @@
 // scale per cached token (the row's value is scale * e4m3), d_r = 64 bf16 rope
 // values per token, heads a multiple of 32, bf16 absorbed query.
 //
-// The work decomposition, split plan, tile descriptors, head groups and the
-// two-barrier step are those of the bf16 kernel (mla_attend_mfma.hip); what
+// The work decomposition, split plan, tile descriptors and head groups are
+// those of the bf16 kernel (mla_attend_mfma.hip).  The step schedule is not:
+// this kernel takes two work-group barriers per step (one when the step's tile
+// is in LDS, one after the softmax wave has published the weights, after which
+// the value waves run the value product of that same step), where the bf16
+// kernel takes one and runs its value product two steps behind.  What else
 // differs is how the 8-bit latent tile is consumed:
 //
 //  * Scores.  S^T[t, i] = scale_t * sum_d e4m3[t, d] q[i, d] + rope term.  The

@@ -259,7 +259,8 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
 // Element offsets of this lane's DMA sources within a step's key rows and
 // value rows; the same for every step.
 struct AttnSrc {
-  int32_t k0, k1, k2, v0, v1;
+  int32_t k0, k1, k2;
+  int64_t v0, v1;  // value rows are Tpad apart: 127 Tpad can pass 2^31
 };
 
 __device__ inline int32_t attn_koff(int wave, int lane, int u) {
@@ -268,10 +269,10 @@ __device__ inline int32_t attn_koff(int wave, int lane, int u) {
   return key * kPDq + 8 * (pos ^ swz(key));
 }
 
-__device__ inline int32_t attn_voff(int wave, int lane, int u, int32_t Tpad) {
+__device__ inline int64_t attn_voff(int wave, int lane, int u, int32_t Tpad) {
   const int o = (wave + 8 * u) * 1024 + 16 * lane;
   const int row = o >> 7, pos = (o >> 4) & 7;
-  return row * Tpad + 8 * (pos ^ swz(row));
+  return (int64_t)row * Tpad + 8 * (pos ^ swz(row));
 }
 
 __device__ inline void attn_issue(const uint16_t* kbase, const uint16_t* vbase, const AttnSrc& f,

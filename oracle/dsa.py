@@ -57,13 +57,14 @@ from .mla_oracle import _head_explicit, decode_storage
 # --------------------------------------------------------------------------
 
 def indexer_scores(q_I: np.ndarray, w: np.ndarray, K_I: np.ndarray) -> np.ndarray:
-    """[LESSON] Chapter 6, "The lightning indexer": for every candidate row
-    k_s of K_I [T, d_I], sum over heads j of w[j] * ReLU(q_I[j] . k_s).
-    q_I [H_I, d_I], w [H_I]; returns [T] in fp64."""
+    """[LESSON] Chapter 6, "The lightning indexer": the index score of a
+    candidate key is a weighted sum over the indexer heads of the rectified
+    query-key inner product (no softmax anywhere).
+    q_I [H_I, d_I], w [H_I], K_I [T, d_I]; returns [T] in fp64."""
     q = np.asarray(q_I, dtype=np.float64)
     k = np.asarray(K_I, dtype=np.float64)
-    dots = k @ q.T                      # [T, H_I]: one dot product per head
-    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+    rectified = np.maximum(np.einsum("hd,td->th", q, k), 0.0)
+    return np.einsum("th,h->t", rectified, np.asarray(w, dtype=np.float64))
 
 
 def decode_scaled_e4m3(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:

@@ -218,15 +218,22 @@ def gqa_decode(q, K, V, sm_scale):
 
 
 def build_selectors(h, g, d):
-    """[LESSON] Chapter 2: with the latent c = [k_1..k_g, v_1..v_g] (width 2gd),
-    head i's key up-projection is the d x 2gd matrix holding I_d over the key
-    block of its group j = i // (h/g) and zeros elsewhere; its value
-    up-projection holds I_d over the value block of group j."""
-    W_UK = np.zeros((h, d, 2 * g * d), dtype=np.float64)
-    W_UV = np.zeros((h, d, 2 * g * d), dtype=np.float64)
+    """[LESSON] Chapter 2 "GQA Is MLA in Disguise": the latent row is the
+    concatenation of every group's key and then every group's value (width
+    2gd); head i's key up-projection picks its own group's key block out of it
+    and its value up-projection its group's value block.
+
+    Written as a Kronecker product: with e_j the one-hot row of length g for
+    the head's group j = i // (h/g), the key selector is [e_j, 0] (x) I_d and
+    the value selector [0, e_j] (x) I_d, each d x 2gd."""
+    if h % g:
+        raise ValueError("h must be a multiple of g")
+    group_of_head = np.arange(h) // (h // g)
+    onehot = np.eye(g)[group_of_head]                  # [h, g]
+    zeros = np.zeros_like(onehot)
+    key_pick = np.concatenate([onehot, zeros], axis=1)  # [h, 2g]
+    val_pick = np.concatenate([zeros, onehot], axis=1)
     eye = np.eye(d)
-    for i in range(h):
-        j = i // (h // g)
-        W_UK[i, :, j * d:(j + 1) * d] = eye
-        W_UV[i, :, (g + j) * d:(g + j + 1) * d] = eye
+    W_UK = np.stack([np.kron(key_pick[i][None, :], eye) for i in range(h)])
+    W_UV = np.stack([np.kron(val_pick[i][None, :], eye) for i in range(h)])
     return W_UK, W_UV

@@ -203,3 +203,8 @@ def test_prefill_rejects_bad_arguments_before_launch():
     with pytest.raises(_lib.MlaError) as ei:  # an fp8 cache without its scales
         _lib.mla_prefill(p8, 16, *args, fake, _lib.mla_prefill_workspace_size(p8))
     assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    with pytest.raises(_lib.MlaError) as ei:  # fp8 scales not 4-byte aligned
+        _lib.mla_prefill(p8, 16, *args[:3], fake + 2, *args[4:], fake,
+                         _lib.mla_prefill_workspace_size(p8))
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    assert "aligned" in _lib.mla_last_error()

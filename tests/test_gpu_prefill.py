@@ -18,13 +18,13 @@ from oracle.prefill import mha_prefill
 
 pytestmark = pytest.mark.gpu
 
-# Bar per output row (b, l, i), relative to that row's RMS.  The MHA form
-# rounds three more operands to bf16 than the inputs are (reconstructed keys,
-# reconstructed values, softmax weights before the value product); on these
-# inputs an fp64 emulation of each rounding alone moves a row by up to 1e-2 of
-# its RMS, all three together by up to 1.5e-2, and a bf16 output adds up to
-# 2^-9 max|row| / RMS(row) (about 0.5e-2): 3e-2 per row.
-TOL = 3e-2
+# Bars (bf16 arithmetic with fp32 accumulation, as for the decode step):
+#  * whole output: max |err| <= 2e-2 RMS over every computed output value;
+#  * per output row (b, l, i): max |err| <= 2e-2 RMS of that row.  Rows that
+#    average many keys are small, and so are their rounding errors; the MHA
+#    form rounds the reconstructed keys, values and softmax weights to bf16,
+#    which the per-row bar still has to absorb.
+TOL = 2e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -81,6 +81,8 @@ def check(pi, got, heads=None, batches=None, rows=None, label=""):
          f"row RMS {rms[worst]:.3e}, ratio {ratio[worst]:.3e}; overall max err "
          f"{float(err[rows_done].max()):.3e}, RMS {float(np.sqrt(np.mean(ref[mask] ** 2))):.3e}")
     assert ratio[worst] <= TOL
+    whole = float(err[rows_done].max()) / float(np.sqrt(np.mean(ref[mask] ** 2)))
+    assert whole <= TOL, whole
     # rows past each chunk are never written
     for b in range(c.batch):
         assert np.isnan(got[b, int(pi.q_lens[b]):]).all(), b
@@ -120,17 +122,31 @@ def test_prefill_clamps_q_lens():
     check(pi, got, label="clamped")
 
 
-def test_prefill_dsv3_heads_long_context_sampled():
+CACHES = ["bf16", "e4m3"]
+
+
+@pytest.mark.parametrize("cache", CACHES)
+def test_prefill_dsv3_heads_long_context_sampled(cache):
     """128 heads, contexts of 4000 and 8192 cached tokens, chunks of 512 and 300
-    new tokens: every output is finite; sampled rows (tile edges, last row) and
-    heads match the oracle."""
-    cfg = DSV3.replace(batch=2, seed=5203)
-    _say("prefill dsv3 long")
+    new tokens, over a bf16 or fp8 cache: every output is finite; sampled rows
+    (tile edges, last row) and heads match the oracle."""
+    cfg = DSV3.replace(batch=2, seed=5203, cache_dtype=cache)
+    _say(f"prefill dsv3 long ({cache})")
     pi = generate_prefill(cfg, 512, seq_lens=[4000, 8192], q_lens=[512, 300])
     got = run_prefill(pi)
     for b in range(2):
         assert np.all(np.isfinite(got[b, :int(pi.q_lens[b])])), b
-    check(pi, got, heads=[0, 37, 127], rows=[0, 63, 64, 255, 299, 511], label="dsv3 long")
+    check(pi, got, heads=[0, 37, 127], rows=[0, 63, 64, 255, 299, 511], label=f"dsv3 long {cache}")
+
+
+def test_prefill_fp8_small_pages_many_tiles():
+    """fp8 cache with 16-token pages (eight pages per 128-token key tile),
+    contexts of 1500 and 2047 tokens (many key tiles, ragged last page) and
+    chunks crossing several query tiles."""
+    cfg = DSV3.replace(heads=4, batch=2, seed=5206, cache_dtype="e4m3", page_size=16)
+    _say("prefill fp8 small pages")
+    pi = generate_prefill(cfg, 400, seq_lens=[1500, 2047], q_lens=[400, 257])
+    check(pi, run_prefill(pi), label="fp8 p16")
 
 
 def test_prefill_empty_sequences():
@@ -143,13 +159,17 @@ def test_prefill_empty_sequences():
     check(pi, got, label="empty")
 
 
-def test_prefill_bench_configuration_sampled():
+@pytest.mark.parametrize("cache", CACHES)
+def test_prefill_bench_configuration_sampled(cache):
     """The benchmark's call (2 sequences of 16384 cached tokens, the last 4096
-    new, 128 heads, bf16 output, seed 1200): every output finite; rows at the
-    chunk's start, q-tile edges and end match the oracle on sampled heads."""
-    cfg = CONFIGS["dsv3_b8_32k"].replace(batch=2, seq_len=16384, out_dtype="bf16", seed=1200)
-    _say("prefill bench configuration")
+    new, 128 heads, bf16 output, seed 1200) over a bf16 or fp8 cache: every
+    output finite; rows at the chunk's start, q-tile edges and end match the
+    oracle on sampled heads."""
+    cfg = CONFIGS["dsv3_b8_32k"].replace(batch=2, seq_len=16384, out_dtype="bf16", seed=1200,
+                                         cache_dtype=cache)
+    _say(f"prefill bench configuration ({cache})")
     pi = generate_prefill(cfg, 4096)
     got = run_prefill(pi)
     assert np.all(np.isfinite(got))
-    check(pi, got, heads=[0, 127], batches=[0, 1], rows=[0, 255, 256, 4095], label="bench config")
+    check(pi, got, heads=[0, 127], batches=[0, 1], rows=[0, 255, 256, 4095],
+          label=f"bench config {cache}")
