@@ -102,6 +102,8 @@ _SIGNATURES = {
     "mla_gather_cache": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "mla_split_begin": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
     "mla_split_owner": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]),
+    "mla_split_plan": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
     "mla_cache_write_workspace_size": (ctypes.c_int, [_WP, ctypes.POINTER(ctypes.c_size_t)]),
     "mla_cache_write": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_quantize_e4m3_rows": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
@@ -257,6 +259,18 @@ def mla_split_begin(n_tiles: int, splits: int, g: int) -> int:
 
 def mla_split_owner(n_tiles: int, splits: int, tile: int) -> int:
     return load_library().mla_split_owner(n_tiles, splits, tile)
+
+
+def mla_split_plan(tiles, splits: int):
+    """Host split plan for tiles per sequence -> (split_first [splits + 1],
+    seq_splits [batch, 2]) as int32 numpy arrays."""
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(tiles, dtype=np.int32))
+    first = np.zeros(int(splits) + 1, dtype=np.int32)
+    seq = np.zeros((len(t), 2), dtype=np.int32)
+    _check("mla_split_plan", load_library().mla_split_plan(
+        t.ctypes.data, len(t), int(splits), first.ctypes.data, seq.ctypes.data))
+    return first, seq
 
 
 def make_write_params(batch, d_model, d_latent, d_rope, page_size, max_blocks_per_seq, num_blocks,

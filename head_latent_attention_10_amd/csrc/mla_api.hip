@@ -69,7 +69,8 @@ int32_t absorbed_dtype(const mla_decode_params& p) {
 }
 
 struct Layout {
-  size_t q_lat, cu_tiles, tiles, part_o, part_lse, o_lat, entry_slots, total;
+  size_t q_lat, cu_tiles, split_first, seq_splits, tiles, part_o, part_lse, o_lat, entry_slots,
+      total;
   int32_t splits, streams;
   int64_t slots;
 };
@@ -111,6 +112,10 @@ mla_status layout(const mla_decode_params& p, Layout* L, int32_t sparse_stride =
   off = align256(off + B * h * (dc + dr) * mla::dtype_size(absorbed_dtype(p)));
   L->cu_tiles = off;
   off = align256(off + (B + 1) * sizeof(int32_t));
+  L->split_first = off;
+  off = align256(off + ((size_t)L->splits + 1) * sizeof(int32_t));
+  L->seq_splits = off;
+  off = align256(off + 2 * B * sizeof(int32_t));
   L->tiles = off;
   const size_t cap = sparse_stride > 0 ? (size_t)sparse_stride
                                         : (size_t)p.max_blocks_per_seq * p.page_size;
@@ -166,7 +171,9 @@ mla::PlanRequest plan_request(const Layout& L, char* ws, const int32_t* block_ta
                               const int32_t* seq_lens, const int32_t* indices = nullptr,
                               int32_t stride = 0) {
   mla::PlanRequest r{seq_lens, block_table, reinterpret_cast<int32_t*>(ws + L.cu_tiles),
-                     reinterpret_cast<int32_t*>(ws + L.tiles)};
+                     reinterpret_cast<int32_t*>(ws + L.tiles), L.splits,
+                     reinterpret_cast<int32_t*>(ws + L.split_first),
+                     reinterpret_cast<int32_t*>(ws + L.seq_splits)};
   if (indices) {
     r.indices = indices;
     r.idx_stride = stride;
@@ -192,6 +199,8 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.seq_lens = seq_lens;
   a.cu_tiles = reinterpret_cast<int32_t*>(ws + L.cu_tiles);
   a.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  a.split_first = reinterpret_cast<int32_t*>(ws + L.split_first);
+  a.seq_splits = reinterpret_cast<int32_t*>(ws + L.seq_splits);
   a.part_o = reinterpret_cast<float*>(ws + L.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
   a.B = p.batch;
@@ -397,6 +406,54 @@ size_t writer_ws_bytes(const mla_cache_write_params& p) {
 }
 
 }  // namespace
+
+namespace mla {
+
+void split_plan_host(const int32_t* tiles, int32_t B, int32_t S, int32_t* split_first,
+                     int32_t* seq_splits) {
+  int32_t tot = 0, mx = 0;
+  for (int32_t b = 0; b < B; b++) {
+    tot += tiles[b];
+    mx = tiles[b] > mx ? tiles[b] : mx;
+  }
+  const bool aligned = B <= S && B <= kAlignedMaxBatch;
+  int32_t L = 1;
+  if (aligned && tot > 0) {
+    int32_t lo = (tot + S - 1) / S, hi = mx;
+    while (lo < hi) {
+      const int32_t mid = lo + (hi - lo) / 2;
+      int64_t cnt = 0;
+      for (int32_t b = 0; b < B; b++) cnt += aligned_splits(tiles[b], mid);
+      if (cnt <= S) hi = mid; else lo = mid + 1;
+    }
+    L = lo;
+  }
+  int32_t G = 0, C = 0;
+  for (int32_t b = 0; b < B; b++) {
+    const int32_t n = tiles[b];
+    if (aligned) {
+      const int32_t k = aligned_splits(n, L);
+      for (int32_t i = 0; i < k; i++) split_first[G + i] = C + aligned_first(n, k, i);
+      seq_splits[2 * b] = G;
+      seq_splits[2 * b + 1] = G + k - 1;
+      G += k;
+    } else if (n == 0) {
+      seq_splits[2 * b] = 0;
+      seq_splits[2 * b + 1] = -1;
+    } else {
+      seq_splits[2 * b] = split_owner(tot, S, C);
+      seq_splits[2 * b + 1] = split_owner(tot, S, C + n - 1);
+    }
+    C += n;
+  }
+  if (aligned) {
+    for (int32_t g = G; g <= S; g++) split_first[g] = tot;
+  } else {
+    for (int32_t g = 0; g <= S; g++) split_first[g] = (int32_t)split_begin(tot, S, g);
+  }
+}
+
+}  // namespace mla
 
 extern "C" {
 
@@ -833,6 +890,22 @@ int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g) {
 int32_t mla_split_owner(int64_t n_tiles, int32_t splits, int64_t tile) {
   if (n_tiles < 1 || splits < 1) return -1;
   return mla::split_owner(n_tiles, splits, tile);
+}
+
+mla_status mla_split_plan(const int32_t* tiles, int32_t batch, int32_t splits,
+                          int32_t* split_first, int32_t* seq_splits) {
+  g_last_error.clear();
+  if (batch < 1 || splits < 1 || !tiles || !split_first || !seq_splits)
+    return fail(MLA_ERR_INVALID_ARG, "batch=%d splits=%d and three non-null arrays required",
+                batch, splits);
+  int64_t tot = 0;
+  for (int32_t b = 0; b < batch; b++) {
+    if (tiles[b] < 0) return fail(MLA_ERR_INVALID_ARG, "tiles[%d] < 0", b);
+    tot += tiles[b];
+  }
+  if (tot >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "2^31 tiles or more");
+  mla::split_plan_host(tiles, batch, splits, split_first, seq_splits);
+  return MLA_OK;
 }
 
 }  // extern "C"

@@ -239,8 +239,8 @@ void attend_fp8_kernel(AttnArgs a) {
   select_latent_group(a, hg * 32 * HB);  // the host keeps a head group inside one latent group
   const int32_t n_total = load_ro(a.cu_tiles, a.B);
   if (n_total == 0) return;
-  const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);
-  const int32_t t_end = (int32_t)split_begin(n_total, a.splits, g + 1);
+  const int32_t t_begin = load_ro(a.split_first, g);
+  const int32_t t_end = load_ro(a.split_first, g + 1);
   if (t_begin >= t_end) return;
   const int32_t n = t_end - t_begin;
 
@@ -592,17 +592,13 @@ hipError_t launch_attend_fp8(const AttnArgs& a, hipStream_t s, hipEvent_t ev_sta
   const dim3 grid(a.splits * HG);
   const bool sp = a.slots != nullptr;
   if (hpg == 64 && !sp)
-    hipExtLaunchKernelGGL((attend_fp8_kernel<2, false>), grid, dim3(Shape8<2>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend_fp8_kernel<2, false>, grid, dim3(Shape8<2>::NW * 64), s, ev_start, ev_stop, a);
   else if (hpg == 64)
-    hipExtLaunchKernelGGL((attend_fp8_kernel<2, true>), grid, dim3(Shape8<2>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend_fp8_kernel<2, true>, grid, dim3(Shape8<2>::NW * 64), s, ev_start, ev_stop, a);
   else if (!sp)
-    hipExtLaunchKernelGGL((attend_fp8_kernel<1, false>), grid, dim3(Shape8<1>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend_fp8_kernel<1, false>, grid, dim3(Shape8<1>::NW * 64), s, ev_start, ev_stop, a);
   else
-    hipExtLaunchKernelGGL((attend_fp8_kernel<1, true>), grid, dim3(Shape8<1>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend_fp8_kernel<1, true>, grid, dim3(Shape8<1>::NW * 64), s, ev_start, ev_stop, a);
   return hipGetLastError();
 }
 

@@ -4,12 +4,12 @@
 // heads a multiple of 32, bf16 latent/rope rows, bf16 absorbed query.
 //
 // Work decomposition.  A token split g owns a contiguous run of 32-token tiles
-// of the concatenated sequences ("split plan" in mla_common.hpp); one tile is
-// one pipeline step.  Its heads are served by HG work groups of 32*HB heads
-// each (HB = 2 for 64 heads, 1 for 32); the HG groups of one split get
-// workgroup ids that differ by a multiple of 8 and are dispatched together, so
-// they run on the same XCD and the second read of every tile is served by that
-// XCD's L2.
+// (the split table the planner writes, mla_common.hpp); one tile is one
+// pipeline step.  Its heads are served by HG work groups of 64 heads (or 32
+// when the head count is not a multiple of 64); the HG groups of one split
+// get workgroup ids that differ by a multiple of 8 and are dispatched
+// together, so they run on the same XCD and the second read of every tile is
+// served by that XCD's L2.
 //
 // Every step is described by the tile descriptor the planning kernel wrote
 // (page, sequence, first token, valid tokens, last-of-sequence flag).  The
@@ -17,29 +17,20 @@
 // LDS window of 64 tiles by direct global->LDS loads, so the per-step
 // bookkeeping of every wave is one LDS read.
 //
-// Inside a work group the waves specialise:
-//  * 2*HB score waves.  Wave (hb, kh) holds the absorbed query of 32 heads for
-//    one part of the 576-wide key (kh = 0: latent 0..255; kh = 1: latent
-//    256..511 and the 64 rope values) in registers and computes, for each step,
-//      S^T[t, i] = sum_d KV[t, d] Q[i, d]      (MFMA 32x32x16 bf16, M = tokens,
-//                                              N = heads, K = its key part)
-//    The kh = 1 wave hands its partial scores to its partner through LDS; in
-//    the next step the partner adds them to its own, runs the online softmax
-//    (one lane = one head) and publishes the bf16 weights P, the per-head
-//    rescale factors and, at the end of a sequence segment, 1/l and the
-//    log-sum-exp.  The kh = 0 part is the shorter one: its wave also runs the
-//    softmax.
-//  * 4*HB value waves.  Each owns a slice of 64 (HB = 2) or 128 (HB = 1)
-//    latent rows of the output for all heads of the group and computes
-//      O^T[d, i] += sum_t C[t, d] P[i, t]      (M = latent rows, N = heads,
-//                                              K = tokens)
-//    two steps behind the score waves.  It reads its latent fragments of a
-//    step with the transposing LDS read in the step of that tile and keeps
-//    them in registers until the weights arrive; each such read feeds HB
-//    MFMAs.  The weights are in a permuted token order (slot i of lane group
-//    g is token 8*(i/4) + 4*g + i%4 of the 16-token k-step) that matches the
-//    score accumulator layout, and the latent tile is read in the same order.
-//    The first four value waves issue the tile loads.
+// Two kernels share the tile loads, the swizzled LDS ring and the online
+// softmax:
+//  * attend64_kernel (64 heads per work group, eight waves; the decode
+//    workloads with 128 or 64 heads) -- its roles are described above it.
+//  * attend_mfma_kernel<1> (32 heads, six waves): two score waves split the
+//    576-wide key in two parts (latent 0..255; latent 256..511 and the rope
+//    values), the first adding the second's partial scores, running the online
+//    softmax and publishing the bf16 weights; four value waves own 128 latent
+//    rows each, two steps behind the scores.
+//
+// The value products read the latent tile with the transposing LDS read; the
+// weights are in a permuted token order (slot i of lane group g is token
+// 8*(i/4) + 4*g + i%4 of the 16-token k-step) that matches the score
+// accumulator layout, and the latent tile is read in the same order.
 //
 // LDS ring.  Three stages of one step: 32 latent rows of 1 KiB and 32 rope
 // rows of 128 B, written by direct global->LDS 16-byte loads (one instruction
@@ -50,15 +41,6 @@
 // the score product and the 4-row transposing reads of the value product
 // free of bank conflicts (64 four-byte banks).  The partial scores, weights
 // and rescale factors are double-buffered by step parity.
-//
-// Step j (one work-group barrier; every wave runs n + 2 steps):
-//   loader waves wait for their loads of step j; barrier
-//   loader waves: issue the loads of step j + 2
-//   score waves kh = 0: softmax of step j - 1, publish P(j-1); partial S(j)
-//   score waves kh = 1: partial S(j), hand it over
-//   value waves: read P(j-2) and the latent fragments of step j;
-//                O += C(j-2) P(j-2); at a segment end, store the partial.
-// The barrier of step j + 1 orders what step j published before its readers.
 //
 // Softmax rescaling is lazy: after the first four steps of a sequence segment
 // (which track the exact maximum, so an early dominant token gets weight
@@ -227,17 +209,21 @@ struct Loader {
   // of step i+1 and sb groups of KS partial-output stores issued after the
   // awaited batch (the hardware counter retires in issue order).  The counts
   // are exact or smaller, so the wait never ends early; an extra window load
-  // in the newer batch only makes it longer.
+  // in the newer batch only makes it longer, and so does a count clamped to
+  // the counter's range of 63.
   template <int KS>
   __device__ void wait_current(int sb) {
+    constexpr int C0 = kPerWave, C1 = kPerWave + KS < 63 ? kPerWave + KS : 63,
+                  C2 = kPerWave + 2 * KS < 63 ? kPerWave + 2 * KS : 63;
+    constexpr int D1 = KS < 63 ? KS : 63, D2 = 2 * KS < 63 ? 2 * KS : 63;
     if (newer_issued) {
-      if (sb == 0) wait_vmcnt<kPerWave>();
-      else if (sb == 1) wait_vmcnt<kPerWave + KS>();
-      else wait_vmcnt<kPerWave + 2 * KS>();
+      if (sb == 0) wait_vmcnt<C0>();
+      else if (sb == 1) wait_vmcnt<C1>();
+      else wait_vmcnt<C2>();
     } else {
       if (sb == 0) wait_vmcnt<0>();
-      else if (sb == 1) wait_vmcnt<KS>();
-      else wait_vmcnt<2 * KS>();
+      else if (sb == 1) wait_vmcnt<D1>();
+      else wait_vmcnt<D2>();
     }
   }
   // In step i: issue step i+2.
@@ -285,8 +271,8 @@ void attend_mfma_kernel(AttnArgs a) {
   select_latent_group(a, hg * 32 * HB);  // the host keeps a head group inside one latent group
   const int32_t n_total = load_ro(a.cu_tiles, a.B);
   if (n_total == 0) return;
-  const int32_t t_begin = (int32_t)split_begin(n_total, a.splits, g);
-  const int32_t t_end = (int32_t)split_begin(n_total, a.splits, g + 1);
+  const int32_t t_begin = load_ro(a.split_first, g);
+  const int32_t t_end = load_ro(a.split_first, g + 1);
   if (t_begin >= t_end) return;
   const int32_t n = t_end - t_begin;  // steps of this split
 
@@ -580,6 +566,373 @@ void attend_mfma_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 64 heads per work group, eight waves (two per SIMD; wave w runs on SIMD w % 4).
+//
+//  * w0, w1: score waves, one per key part kh: kh = 0 is latent 0..287 (18
+//    k-steps), kh = 1 latent 288..511 and the 64 rope values (18 k-steps).  Each
+//    holds the absorbed query of all 64 heads over its key part (144 VGPRs) and
+//    computes the partial scores of both 32-head blocks from one A fragment
+//    read (32 tokens x 16 key values), so a tile is read from LDS twice per 64
+//    heads and every fragment feeds two MFMAs.  The two partials of a step go
+//    to LDS.
+//  * w4, w5: softmax waves for head blocks 0 and 1 (on the score waves'
+//    SIMDs, whose matrix cores they leave free): in step j they add the two
+//    partial scores of step j - 1, run the online softmax and publish the bf16
+//    weights.
+//  * w2, w3, w6, w7: value waves v = 0..3, latent rows 128 v .. 128 v + 127 of
+//    both head blocks, and the four loader waves.  Each reads its latent
+//    fragments of tile j with the transposing LDS read in step j (the tile is
+//    then free for the loads of step j + 3) and consumes them in step j + 2,
+//    with the weights of that step; every fragment feeds two MFMAs.  The
+//    weights are read first in a step, so its products wait only for them.
+//
+// Step j (one barrier): loaders wait for their loads of step j; barrier;
+// loaders issue step j + 2 into the stage tile j - 1 used; score waves S(j);
+// softmax waves softmax(j - 1); value waves O += C(j-2) P(j-2) and read C(j).
+// Partial scores, weights, rescale factors and 1/l are double-buffered by
+// step parity; the barrier of a step orders what the previous step published.
+constexpr int kKs64 = 18;                         // k-steps per key part
+constexpr int kX64 = 2 * 2 * kXBytes;             // partial scores of one step: [kh][hb]
+constexpr int kP64 = 2 * kPBytes;                 // weights of one step: [hb]
+constexpr int kLds64 = kRing + kWinBytes + 2 * kX64 + 2 * kP64 + 2 * 2 * 32 * 4 * 2 + 2 * 2 * 4;
+static_assert(kLds64 <= 160 * 1024, "LDS budget of one compute unit");
+static_assert(2 * kKs64 == (kDc + kDr) / 16, "the key parts cover the whole key");
+
+template <bool SP>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLds64];
+  lds_t* ring = (lds_t*)smem;
+  lds_t* win = ring + kRing;                        // [2][kWin] tile descriptors
+  lds_t* xbuf = win + kWinBytes;                    // [2 parity][2 kh][2 hb][4][64 lanes][16 B]
+  lds_t* pbuf = xbuf + 2 * kX64;                    // [2 parity][2 hb][2 k-steps][64 lanes][16 B]
+  float* s_alpha = (float*)(smem + kRing + kWinBytes + 2 * kX64 + 2 * kP64);  // [2][2][32]
+  float* s_invl = s_alpha + 2 * 2 * 32;             // [2][2][32]
+  int* s_flag = (int*)(s_invl + 2 * 2 * 32);        // [2][2]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g32 = lane >> 5;
+
+  // workgroup id -> (split, head group); the HG groups of a split share an XCD
+  const int32_t HG = a.h / 64;
+  int32_t g, hg;
+  if (HG > 1) {
+    const int32_t L = blockIdx.x, span = 8 * HG;
+    hg = (L % span) / 8;
+    g = (L / span) * 8 + (L % 8);
+  } else {
+    hg = 0;
+    g = blockIdx.x;
+  }
+  if (g >= a.splits) return;
+  select_latent_group(a, hg * 64);
+  const int32_t n_total = load_ro(a.cu_tiles, a.B);
+  if (n_total == 0) return;
+  const int32_t t_begin = load_ro(a.split_first, g);
+  const int32_t t_end = load_ro(a.split_first, g + 1);
+  if (t_begin >= t_end) return;
+  const int32_t n = t_end - t_begin;  // steps of this split
+  const float sm = a.sm_scale_log2;
+
+  if (wave < 2) {
+    // ================================================================ score waves
+    const int kh = wave;
+    const int K0 = kh * kKs64;
+    bf16x8 qf[2][kKs64];
+    auto issue_q = [&](int32_t bb) {
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++) {
+        const int32_t head = hg * 64 + hb * 32 + (lane & 31);
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc + kDr));
+#pragma unroll
+        for (int k = 0; k < kKs64; k++) qf[hb][k] = qp[2 * (K0 + k) + g32];
+      }
+    };
+    Tile cur = global_tile(a, t_begin), prev{};
+    issue_q(cur.b);
+    if (wave == 1) {
+      load_window(a, win, t_begin, t_end, 0, lane);
+      if (n > kWin) load_window(a, win, t_begin, t_end, 1, lane);
+    }
+    wait_vmcnt<0>();
+    wg_barrier();
+    const int row = lane & 31;
+    for (int32_t j = 0; j <= n + 1; j++) {
+      wg_barrier();
+      if (j < n) {
+        if (j > 0 && prev.last) wait_vmcnt<0>();  // the new segment's query
+        const lds_t* st = ring + (j % kStages) * kStage;
+        auto ld_a = [&](int k) -> bf16x8 {
+          const int ks = K0 + k;
+          const lds_t* p = ks < 32
+              ? st + row * kCRow + (((2 * ks + g32) ^ swz_c(row)) << 4)
+              : st + kStageC + row * kRRow + (((2 * (ks - 32) + g32) ^ swz_r(row)) << 4);
+          return *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(p);
+        };
+        // the next descriptor, read before the products hide its latency
+        const Tile nxt = j + 1 < n ? read_tile(win, j + 1) : Tile{};
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        constexpr int D = 6;
+        bf16x8 av[D];
+#pragma unroll
+        for (int k = 0; k < D; k++) av[k] = ld_a(k);
+#pragma unroll
+        for (int k = 0; k < kKs64; k++) {
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k % D], qf[0][k], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k % D], qf[1][k], s1, 0, 0, 0);
+          if (k + D < kKs64) av[k % D] = ld_a(k + D);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_t* xb = xbuf + (j & 1) * kX64 + kh * 2 * kXBytes + lane * 16;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + 1024 * q) =
+              f32x4{s0[4 * q], s0[4 * q + 1], s0[4 * q + 2], s0[4 * q + 3]};
+          *reinterpret_cast<f32x4 __attribute__((address_space(3)))*>(xb + kXBytes + 1024 * q) =
+              f32x4{s1[4 * q], s1[4 * q + 1], s1[4 * q + 2], s1[4 * q + 3]};
+        }
+        prev = cur;
+        if (j + 1 < n) {
+          cur = nxt;
+          // the products above have read the query registers: the next
+          // segment's query can be requested now, a step ahead of its use
+          if (prev.last) issue_q(cur.b);
+        }
+      }
+    }
+  } else if (wave == 4 || wave == 5) {
+    // ================================================================ softmax + loader waves
+    const int hb = wave - 4;
+    const int32_t head = hg * 64 + hb * 32 + (lane & 31);
+    wg_barrier();
+    float m_run = -INFINITY, l_run = 0.f;
+    int32_t seg_step = 0;
+    for (int32_t j = 0; j <= n + 1; j++) {
+      wg_barrier();
+      if (j >= 1 && j <= n) {
+        const int par = (j - 1) & 1;
+        const Tile pv = read_tile(win, j - 1);
+        const bool seg_last = pv.last || j == n;
+        f32x16 s;
+        const lds_t* x0 = xbuf + par * kX64 + hb * kXBytes + lane * 16;
+        const lds_t* x1 = x0 + 2 * kXBytes;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const f32x4 u = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(x0 + 1024 * q);
+          const f32x4 w = *reinterpret_cast<const f32x4 __attribute__((address_space(3)))*>(x1 + 1024 * q);
+          s[4 * q] = u[0] + w[0];
+          s[4 * q + 1] = u[1] + w[1];
+          s[4 * q + 2] = u[2] + w[2];
+          s[4 * q + 3] = u[3] + w[3];
+        }
+        // mask the tokens past the end (only the last step of a sequence)
+        if (pv.nv < kStep) {
+#pragma unroll
+          for (int jj = 0; jj < 16; jj++)
+            if (8 * (jj >> 2) + 4 * g32 + (jj & 3) >= pv.nv) s[jj] = -INFINITY;
+        }
+        // step maximum per head: over the lane's 16 tokens, then across the
+        // two lane halves that hold the same head (the scale is positive)
+        float mx = s[0];
+#pragma unroll
+        for (int jj = 1; jj < 16; jj++) mx = fmaxf(mx, s[jj]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mt = mx * sm;
+        // exact running maximum for the first steps of a segment (the largest
+        // weight is then exactly 1 in bf16), lazy afterwards
+        const float thr = seg_step < kExactSteps ? 0.f : kLazy;
+        const bool any = __any(mt > m_run + thr);
+        float alpha = 1.f;
+        if (any) {
+          const float m_new = fmaxf(m_run, mt);
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float mref = m_run == -INFINITY ? 0.f : m_run;
+        // weights as bf16 pairs; the normaliser sums exactly the bf16 weights
+        // the value product consumes
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+        uint32_t pk[8];
+        float lsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+          const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q], sm, -mref)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + 1], sm, -mref))};
+          const bf16x2 pr = __builtin_convertvector(e, bf16x2);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          pk[q] = __builtin_bit_cast(uint32_t, pr);
+        }
+        l_run += lsum;
+        lds_t* pb = pbuf + par * kP64 + hb * kPBytes + lane * 16;
+        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb + 64 * 16) =
+            u32x4{pk[4], pk[5], pk[6], pk[7]};
+        seg_step++;
+        if (g32 == 0) s_alpha[(par * 2 + hb) * 32 + lane] = alpha;
+        if (lane == 0) s_flag[par * 2 + hb] = any ? 1 : 0;
+        if (seg_last) {
+          const float ltot = l_run + __shfl_xor(l_run, 32);
+          if (g32 == 0) {
+            s_invl[(par * 2 + hb) * 32 + lane] = ltot > 0.f ? 1.f / ltot : 0.f;
+            const int64_t slot = (int64_t)(g + pv.b);
+            a.part_lse[slot * a.h + head] =
+                ltot > 0.f ? (m_run + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+          }
+          m_run = -INFINITY;
+          l_run = 0.f;
+          seg_step = 0;
+        }
+      }
+    }
+  } else {
+    // ================================================================ value waves
+    const int v = (wave & 1) | ((wave >> 2) << 1);  // w2 -> 0, w3 -> 1, w6 -> 2, w7 -> 3
+    constexpr int MD = 4;                            // 32-row output blocks of this wave
+    // latent fragments of two steps: slot j % 2 holds those of step j - 2
+    // until its products are issued, then receives those of step j
+    bf16x8 cb[2][MD][2];
+    // fragment (md, kk) of the tile in stage st; ln is this lane, recomputed
+    // from an opaque copy in every step so that the compiler does not keep
+    // sixteen read addresses live across the loop
+    auto ld_c = [&](const lds_t* st, int ln, int md, int kk) -> bf16x8 {
+      const int j16 = ln & 15, grp = ln >> 4, e = j16 >> 2, qd = j16 & 3, gg = ln >> 5;
+      const int dd = 32 * (v * MD + md) + 16 * (grp & 1) + 4 * qd;
+      const int chunk = dd >> 3, hoff = (dd & 7) * 2;
+      const int r0 = 16 * kk + 4 * gg + e;
+      const int r1 = r0 + 8;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+              const_cast<lds_t*>(st) + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+              const_cast<lds_t*>(st) + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
+      const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, cat);
+    };
+    auto stage_of = [&](int32_t j) -> const lds_t* {
+      int off = (j % kStages) * kStage;
+      asm volatile("" : "+s"(off));
+      return ring + off;
+    };
+    // the value waves are the four loader waves: every step they wait for
+    // their loads of that step before its barrier and then issue the loads
+    // two steps ahead; a segment end adds one group of kVStores stores
+    constexpr int kVStores = 2 * MD * 4;
+    Loader<4, SP> ld;
+    ld.start(a, ring, win, t_begin, n, v, lane);
+    int sb1 = 0, sb2 = 0;  // partial-store groups issued in the previous two steps
+    wg_barrier();
+    // steps 0 and 1: fragments only
+    ld.template wait_current<kVStores>(0);
+    wg_barrier();
+    ld.issue_ahead(a, ring, win, t_begin, v, lane);
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int md = 0; md < MD; md++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) cb[0][md][kk] = ld_c(stage_of(0), ln, md, kk);
+    }
+    ld.template wait_current<kVStores>(0);
+    wg_barrier();
+    ld.issue_ahead(a, ring, win, t_begin, v, lane);
+    if (n > 1) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int md = 0; md < MD; md++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) cb[1][md][kk] = ld_c(stage_of(1), ln, md, kk);
+    }
+    f32x16 o[MD][2];
+#pragma unroll
+    for (int md = 0; md < MD; md++) o[md][0] = o[md][1] = f32x16{};
+    // step j >= 2: O += C(j-2) P(j-2), then the fragments of step j
+    auto step = [&](auto slot_c, int32_t j) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slot_c)::value;  // j % 2, also the parity of step j - 2
+      ld.template wait_current<kVStores>(sb1 + sb2);
+      wg_barrier();
+      ld.issue_ahead(a, ring, win, t_begin, v, lane);
+      const bool load = j < n;
+      const lds_t* st = stage_of(j);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      // the weights and the rescale flag of step j - 2 first: the products
+      // wait for nothing else
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+          pf[hb][kk] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+              pbuf + SL * kP64 + hb * kPBytes + (kk * 64 + lane) * 16);
+      if (__builtin_amdgcn_readfirstlane(s_flag[SL * 2] | s_flag[SL * 2 + 1])) {
+        const float a0 = s_alpha[(SL * 2) * 32 + (lane & 31)];
+        const float a1 = s_alpha[(SL * 2 + 1) * 32 + (lane & 31)];
+#pragma unroll
+        for (int md = 0; md < MD; md++) {
+          o[md][0] *= a0;
+          o[md][1] *= a1;
+        }
+      }
+      // per latent block: the products of step j - 2, then that block's
+      // fragments of step j into the same registers
+#pragma unroll
+      for (int md = 0; md < MD; md++) {
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+          for (int hb = 0; hb < 2; hb++)
+            o[md][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[SL][md][kk], pf[hb][kk],
+                                                                o[md][hb], 0, 0, 0);
+        if (load) {
+#pragma unroll
+          for (int kk = 0; kk < 2; kk++) cb[SL][md][kk] = ld_c(st, ln, md, kk);
+        }
+        // keep the reads behind the products that free their registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const Tile pv = read_tile(win, j - 2);
+      int sb = 0;
+      if (pv.last || j - 2 == n - 1) {
+        const int64_t slot = (int64_t)(g + pv.b);
+        sb = 1;
+#pragma unroll
+        for (int hb = 0; hb < 2; hb++) {
+          const float inv = s_invl[(SL * 2 + hb) * 32 + (lane & 31)];
+          float* dst = a.part_o + slot * a.h * kDc + frag_offset(hg * 2 + hb, v * MD, 0, lane);
+#pragma unroll
+          for (int md = 0; md < MD; md++) {
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              const f32x4 val = {o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
+                                 o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv};
+              *reinterpret_cast<f32x4*>(dst + (md * 4 + jj) * 256) = val;
+            }
+            o[md][hb] = f32x16{};
+          }
+        }
+      }
+      sb2 = sb1;
+      sb1 = sb;
+    };
+    for (int32_t j = 2; j <= n + 1; j += 2) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 > n + 1) break;
+      step(std::integral_constant<int, 1>{}, j + 1);
+    }
+  }
+}
+
 // heads served by one work group
 int32_t heads_per_group(int32_t heads) { return heads % 64 == 0 ? 64 : 32; }
 
@@ -606,17 +959,13 @@ hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_
   // sparse index lists get their own instantiations (slot-list loads)
   const bool sp = a.slots != nullptr;
   if (hpg == 64 && !sp)
-    hipExtLaunchKernelGGL((attend_mfma_kernel<2, false>), grid, dim3(Shape<2>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend64_kernel<false>, grid, dim3(512), s, ev_start, ev_stop, a);
   else if (hpg == 64)
-    hipExtLaunchKernelGGL((attend_mfma_kernel<2, true>), grid, dim3(Shape<2>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend64_kernel<true>, grid, dim3(512), s, ev_start, ev_stop, a);
   else if (!sp)
-    hipExtLaunchKernelGGL((attend_mfma_kernel<1, false>), grid, dim3(Shape<1>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend_mfma_kernel<1, false>, grid, dim3(Shape<1>::NW * 64), s, ev_start, ev_stop, a);
   else
-    hipExtLaunchKernelGGL((attend_mfma_kernel<1, true>), grid, dim3(Shape<1>::NW * 64), 0, s,
-                          ev_start, ev_stop, 0, a);
+    launch_timed(attend_mfma_kernel<1, true>, grid, dim3(Shape<1>::NW * 64), s, ev_start, ev_stop, a);
   return hipGetLastError();
 }
 

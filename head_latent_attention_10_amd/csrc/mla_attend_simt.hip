@@ -24,8 +24,8 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
   select_latent_group(a, head);
   const int32_t n_total = a.cu_tiles[a.B];
   if (n_total == 0) return;
-  const int64_t t_begin = split_begin(n_total, a.splits, g);
-  const int64_t t_end = split_begin(n_total, a.splits, g + 1);
+  const int64_t t_begin = load_ro(a.split_first, g);
+  const int64_t t_end = load_ro(a.split_first, g + 1);
   if (t_begin >= t_end) return;
   const int32_t d_c = a.d_c, d_r = a.d_r, dl = d_c + d_r;
   const float sm = a.sm_scale_log2 * 0.69314718055994530942f;  // back to natural units

@@ -37,13 +37,37 @@ __host__ __device__ inline int64_t frag_offset(int32_t hblk, int32_t mdg, int32_
 }
 
 // ---------------------------------------------------------------- split plan
-// Tiles of all sequences are numbered in order; split g owns a contiguous run.
+// Tiles of all sequences are numbered in order, and every split owns a
+// contiguous run of them: split g owns [split_first[g], split_first[g + 1]).
+// Two rules, chosen by the batch size:
+//  * sequence-aligned (batch <= splits and batch <= kAlignedMaxBatch): no split
+//    crosses a sequence.  With
+//    n_b tiles in sequence b, L is the least bound such that
+//    sum_b ceil(n_b / L) <= splits, sequence b gets k_b = ceil(n_b / L)
+//    splits in order, and its i-th split owns tiles [n_b i / k_b,
+//    n_b (i + 1) / k_b) of it; splits left over own nothing.  A work group
+//    then serves one sequence, and the longest split is as short as it can be
+//    without crossing one.
+//  * contiguous (otherwise): split g owns [n g / splits, n (g + 1) /
+//    splits) of all n tiles, whatever sequences they belong to.
+// seq_splits[2 b], seq_splits[2 b + 1] are the first and last split holding
+// a tile of sequence b (last < first when it has none).
 __host__ __device__ inline int64_t split_begin(int64_t n_tiles, int32_t splits, int32_t g) {
   return (n_tiles * (int64_t)g) / (int64_t)splits;
 }
 // The largest g whose run starts at or before `tile`; that run contains it.
 __host__ __device__ inline int32_t split_owner(int64_t n_tiles, int32_t splits, int64_t tile) {
   return (int32_t)(((tile + 1) * (int64_t)splits - 1) / n_tiles);
+}
+// Split count of a sequence of n tiles under the sequence-aligned rule with bound L.
+// (The aligned rule applies when the batch is at most the split count and at
+// most kAlignedMaxBatch, defined with the planner below.)
+__host__ __device__ inline int32_t aligned_splits(int32_t n, int32_t L) {
+  return n > 0 ? (n + L - 1) / L : 0;
+}
+// First tile (within its sequence of n tiles split k ways) of split i.
+__host__ __device__ inline int32_t aligned_first(int32_t n, int32_t k, int32_t i) {
+  return (int32_t)(((int64_t)n * i) / k);
 }
 
 // Everything the attention kernels need to know about the problem.
@@ -56,6 +80,8 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* cu_tiles;   // [B + 1] prefix sums of ceil(T_b / kTile) (workspace)
   const int32_t* tiles;      // [n_tiles][4] tile descriptors (workspace)
+  const int32_t* split_first;  // [splits + 1] first tile of each split (workspace)
+  const int32_t* seq_splits;   // [B][2] first and last split of each sequence (workspace)
   float* part_o;             // [slots, h, d_c]
   float* part_lse;           // [slots, h]
   int32_t B, h, d_c, d_r, P, max_blocks, num_blocks;
@@ -145,14 +171,144 @@ struct PlanInput {
   int32_t* slots;
   int32_t* cu_tiles;
   int32_t* tiles;
+  int32_t splits;
+  int32_t* split_first;  // [splits + 1]
+  int32_t* seq_splits;   // [B][2]
 };
+
+// Sequences the sequence-aligned split rule serves (above it, and above the
+// split count, the contiguous rule applies).
+constexpr int kAlignedMaxBatch = 2048;
 
 // LDS of one planning work group.
 struct PlanShared {
   int32_t scan[kPlanThreads];
   int32_t cu[kPlanThreads + 1];  // tile prefix sums of the current chunk of sequences
   int32_t len[kPlanThreads];
+  int32_t ntile[kAlignedMaxBatch];      // tiles per sequence (split table, aligned rule)
+  int32_t gfirst[kAlignedMaxBatch + 1];  // first split of each sequence, then the total
+  int32_t tfirst[kAlignedMaxBatch];      // first tile of each sequence
 };
+
+// Tiles of sequence b as the planner counts them.
+__device__ inline int32_t plan_tiles(const PlanInput& in, int32_t b) {
+  int32_t T;
+  if (in.indices) {
+    T = in.seq_lens[b];
+    T = T < 0 ? 0 : (T > in.idx_stride ? in.idx_stride : T);
+  } else {
+    T = seq_len_clamped(in.seq_lens, b, in.max_blocks, in.P);
+  }
+  return (T + kTile - 1) / kTile;
+}
+
+// Sum (or maximum) of one value per thread over the work group: across each
+// wave by lane exchanges, then across the waves through LDS.
+__device__ inline int32_t plan_reduce(int32_t v, bool is_max, PlanShared& sh) {
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int off = 32; off > 0; off >>= 1) {
+    const int32_t o = __shfl_xor(v, off);
+    v = is_max ? (o > v ? o : v) : v + o;
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) sh.scan[w] = v;
+  __syncthreads();
+  int32_t r = sh.scan[0];
+  for (int i = 1; i < kPlanThreads / 64; i++) r = is_max ? (sh.scan[i] > r ? sh.scan[i] : r) : r + sh.scan[i];
+  return r;
+}
+
+// Inclusive prefix sum of one value per thread over the work group.
+__device__ inline int32_t plan_scan(int32_t v, PlanShared& sh) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(v, off);
+    if (l >= off) v += o;
+  }
+  __syncthreads();
+  if (l == 63) sh.scan[w] = v;
+  __syncthreads();
+  for (int i = 0; i < w; i++) v += sh.scan[i];
+  return v;
+}
+
+// The split table (split rules above), written by one planning work group.
+__device__ inline void plan_splits(const PlanInput& in, PlanShared& sh) {
+  const int32_t B = in.B, S = in.splits;
+  const int tid = threadIdx.x;
+  const bool aligned = B <= S && B <= kAlignedMaxBatch;
+  int32_t tot = 0, mx = 0;
+  for (int32_t b = tid; b < B; b += kPlanThreads) {
+    const int32_t n = plan_tiles(in, b);
+    if (aligned) sh.ntile[b] = n;
+    tot += n;
+    mx = n > mx ? n : mx;
+  }
+  tot = plan_reduce(tot, false, sh);
+  mx = plan_reduce(mx, true, sh);
+  int32_t L = 1;
+  if (aligned && tot > 0) {
+    // least L with sum_b ceil(n_b / L) <= S; L = max n_b always qualifies
+    int32_t lo = (tot + S - 1) / S, hi = mx;
+    while (lo < hi) {
+      const int32_t mid = lo + (hi - lo) / 2;
+      int32_t cnt = 0;
+      for (int32_t b = tid; b < B; b += kPlanThreads) cnt += aligned_splits(sh.ntile[b], mid);
+      cnt = plan_reduce(cnt, false, sh);
+      if (cnt <= S) hi = mid; else lo = mid + 1;
+    }
+    L = lo;
+  }
+  if (aligned) {
+    // split counts k_b and their exclusive prefix sums (first split, first
+    // tile of each sequence) in LDS, a chunk of kPlanThreads sequences at a time
+    int32_t gcarry = 0, tcarry = 0;
+    for (int32_t base = 0; base < B; base += kPlanThreads) {
+      const int32_t b = base + tid;
+      const int32_t n = b < B ? sh.ntile[b] : 0;
+      const int32_t k = aligned_splits(n, L);
+      const int32_t sk = plan_scan(k, sh), sn = plan_scan(n, sh);
+      if (b < B) {
+        sh.gfirst[b] = gcarry + sk - k;
+        sh.tfirst[b] = tcarry + sn - n;
+        in.seq_splits[2 * b] = gcarry + sk - k;
+        in.seq_splits[2 * b + 1] = gcarry + sk - 1;
+      }
+      gcarry += plan_reduce(k, false, sh);
+      tcarry += plan_reduce(n, false, sh);
+    }
+    if (tid == 0) sh.gfirst[B] = gcarry;
+    __syncthreads();
+    // one split per thread: its sequence by binary search over the first splits
+    for (int32_t g = tid; g <= S; g += kPlanThreads) {
+      int32_t first = tot;
+      if (g < gcarry) {
+        int32_t lo = 0, hi = B - 1;  // last b with gfirst[b] <= g
+        while (lo < hi) {
+          const int32_t mid = (lo + hi + 1) >> 1;
+          if (sh.gfirst[mid] <= g) lo = mid; else hi = mid - 1;
+        }
+        const int32_t n = sh.ntile[lo], k = sh.gfirst[lo + 1] - sh.gfirst[lo];
+        first = sh.tfirst[lo] + aligned_first(n, k, g - sh.gfirst[lo]);
+      }
+      in.split_first[g] = first;
+    }
+    return;
+  }
+  for (int32_t g = tid; g <= S; g += kPlanThreads) in.split_first[g] = (int32_t)split_begin(tot, S, g);
+  int32_t tcarry = 0;
+  for (int32_t base = 0; base < B; base += kPlanThreads) {
+    const int32_t b = base + tid;
+    const int32_t n = b < B ? plan_tiles(in, b) : 0;
+    const int32_t sn = plan_scan(n, sh);
+    if (b < B) {
+      const int32_t C = tcarry + sn - n;
+      in.seq_splits[2 * b] = n == 0 ? 0 : split_owner(tot, S, C);
+      in.seq_splits[2 * b + 1] = n == 0 ? -1 : split_owner(tot, S, C + n - 1);
+    }
+    tcarry += plan_reduce(n, false, sh);
+  }
+}
 
 // Work group `wg` of `nwg` (kPlanThreads threads each) of the planner.  The
 // sequences are taken in chunks of kPlanThreads; every planning group scans
@@ -169,6 +325,13 @@ __device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, 
   const bool sparse = in.indices != nullptr;
   const int tid = threadIdx.x;
   const bool one_page = !sparse && P % kTile == 0;
+  // with more than one planning group, the last one writes the split table
+  // and the others the tile descriptors, at the same time
+  if (nwg > 1 && wg == nwg - 1) {
+    plan_splits(in, sh);
+    return;
+  }
+  const int32_t ntile_groups = nwg > 1 ? nwg - 1 : 1;
   int32_t carry = 0;
   if (wg == 0 && tid == 0) cu_tiles[0] = 0;
   for (int32_t base = 0; base < B; base += kPlanThreads) {
@@ -186,23 +349,17 @@ __device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, 
       sh.len[tid] = T;
       n = (T + kTile - 1) / kTile;
     }
-    sh.scan[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int32_t v = tid >= off ? sh.scan[tid - off] : 0;
-      __syncthreads();
-      sh.scan[tid] += v;
-      __syncthreads();
-    }
-    sh.cu[tid + 1] = carry + sh.scan[tid];
+    const int32_t inc = plan_scan(n, sh);
+    sh.cu[tid + 1] = carry + inc;
     if (tid == 0) sh.cu[0] = carry;
-    if (wg == 0 && tid < cnt) cu_tiles[b + 1] = carry + sh.scan[tid];
+    if (wg == 0 && tid < cnt) cu_tiles[b + 1] = carry + inc;
     __syncthreads();
     // tile t of this chunk belongs to the last local sequence j with cu[j] <= t
     // (sequences without tiles share their start with the next one)
     const int32_t t_end = sh.cu[cnt];
 #pragma unroll 4
-    for (int32_t t = sh.cu[0] + wg * kPlanThreads + tid; t < t_end; t += nwg * kPlanThreads) {
+    for (int32_t t = sh.cu[0] + wg * kPlanThreads + tid; t < t_end;
+         t += ntile_groups * kPlanThreads) {
       int32_t lo = 0, hi = cnt - 1;
       while (lo < hi) {
         const int32_t mid = (lo + hi + 1) >> 1;
@@ -223,12 +380,13 @@ __device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, 
     carry = t_end;
     __syncthreads();
   }
+  if (nwg == 1) plan_splits(in, sh);
   if (!sparse) return;
   // slot list: entries e = b * idx_stride + n, eight per thread at a time so
   // that their index and table loads are in flight together
   const int32_t cap = max_blocks * P;
   const int32_t total = B * in.idx_stride;  // < 2^31 (checked on the host)
-  const int32_t nthr = nwg * kPlanThreads;
+  const int32_t nthr = ntile_groups * kPlanThreads;
   for (int32_t e0 = wg * kPlanThreads + tid; e0 < total; e0 += 8 * nthr) {
     int32_t t[8], bb[8];
     bool ok[8];

@@ -16,6 +16,9 @@ struct PlanRequest {
   const int32_t* block_table;
   int32_t* cu_tiles;
   int32_t* tiles;
+  int32_t splits;
+  int32_t* split_first;
+  int32_t* seq_splits;
   const int32_t* indices = nullptr;  // sparse mode
   int32_t idx_stride = 0;
   int32_t* slots = nullptr;
@@ -23,8 +26,14 @@ struct PlanRequest {
 
 inline PlanInput plan_input(const mla_decode_params& p, const PlanRequest& r) {
   return PlanInput{r.seq_lens, r.block_table, p.batch, p.max_blocks_per_seq, p.page_size,
-                   p.num_blocks, r.indices, r.idx_stride, r.slots, r.cu_tiles, r.tiles};
+                   p.num_blocks, r.indices, r.idx_stride, r.slots, r.cu_tiles, r.tiles,
+                   r.splits, r.split_first, r.seq_splits};
 }
+
+// The split table on the host (the planner's rules, for tests): tiles[b] =
+// tiles of sequence b; writes split_first[splits + 1] and seq_splits[2 B].
+void split_plan_host(const int32_t* tiles, int32_t B, int32_t splits, int32_t* split_first,
+                     int32_t* seq_splits);
 
 // q_lat[b,i,:d_c] = W_UK[i]^T q_nope[b,i,:]; q_lat[b,i,d_c:] = q_rope[b,i,:].
 // With plan != null the matrix-core absorption also runs the split planner in

@@ -5,6 +5,8 @@
 
 #include "mla_kernels.hpp"
 
+#include <hip/hip_ext.h>
+
 namespace mla {
 namespace {
 
@@ -72,6 +74,18 @@ __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");  // LDS written by the awaited loads is read after this
+}
+
+// Launch with the two optional events stamped by the dispatch itself (start
+// and end of the kernel's execution); without events, a plain launch, which
+// adds no packets around the kernel.
+template <typename... KArgs, typename... Args>
+inline void launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                         hipEvent_t ev_start, hipEvent_t ev_stop, Args... args) {
+  if (!ev_start && !ev_stop)
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  else
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev_start, ev_stop, 0, args...);
 }
 
 // ------------------------------------------------------------------ tiles

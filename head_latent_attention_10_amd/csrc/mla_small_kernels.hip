@@ -176,19 +176,18 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t d_c = a.d_c;
   float* dst = o_lat + ((int64_t)b * a.h + head) * d_c;
-  const int32_t n_total = a.cu_tiles[a.B];
   const int32_t first = a.cu_tiles[b], last = a.cu_tiles[b + 1] - 1;
   if (last < first) {
     for (int32_t d = tid; d < d_c; d += kCombThreads) dst[d] = 0.f;
     return;
   }
-  const int32_t g_lo = split_owner(n_total, a.splits, first);
-  const int32_t g_hi = split_owner(n_total, a.splits, last);
+  const int32_t g_lo = a.seq_splits[2 * b];
+  const int32_t g_hi = a.seq_splits[2 * b + 1];
   const int32_t n_cand = (g_hi - g_lo + 1) * a.streams;
   // candidate slot k -> (split, stream); splits that own no tile wrote nothing
   auto cand_lse = [&](int32_t k, int64_t* slot_out) -> float {
     const int32_t gg = g_lo + k / a.streams, ts = k % a.streams;
-    const bool owns = split_begin(n_total, a.splits, gg) < split_begin(n_total, a.splits, gg + 1);
+    const bool owns = a.split_first[gg] < a.split_first[gg + 1];
     const int64_t slot = (int64_t)(gg + b) * a.streams + ts;
     *slot_out = slot;
     return owns ? a.part_lse[slot * a.h + head] : -INFINITY;
@@ -292,14 +291,13 @@ __global__ __launch_bounds__(256) void combine_frag_chunk_kernel(AttnArgs a, flo
   const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of this thread's weights
   const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
   float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * a.h + hblk * 32 + r) * kFragLat + d);
-  const int32_t n_total = load_ro(a.cu_tiles, a.B);
   const int32_t first = load_ro(a.cu_tiles, b), last = load_ro(a.cu_tiles, b + 1) - 1;
   if (last < first) {
     *dst = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const int32_t g_lo = split_owner(n_total, a.splits, first);
-  const int32_t n_cand = split_owner(n_total, a.splits, last) - g_lo + 1;
+  const int32_t g_lo = load_ro(a.seq_splits, 2 * b);
+  const int32_t n_cand = load_ro(a.seq_splits, 2 * b + 1) - g_lo + 1;
   const int64_t slot_stride = (int64_t)a.h * kFragLat;
   const float* src = a.part_o + (int64_t)(g_lo + b) * slot_stride + frag_offset(hblk, mdg, jj, lane);
   const float* lse = a.part_lse + (int64_t)(g_lo + b) * a.h + hblk * 32 + wr;
@@ -311,8 +309,7 @@ __global__ __launch_bounds__(256) void combine_frag_chunk_kernel(AttnArgs a, flo
     // splits in the range that own no tile wrote nothing: weight 0
     if (tid < kFragChunk) {
       const int32_t gg = g_lo + c0 + tid;
-      s_own[tid] = tid < n && split_begin(n_total, a.splits, gg) <
-                                  split_begin(n_total, a.splits, gg + 1);
+      s_own[tid] = tid < n && load_ro(a.split_first, gg) < load_ro(a.split_first, gg + 1);
     }
     __syncthreads();
     float4 v[kFragChunk];
@@ -388,20 +385,16 @@ __global__ __launch_bounds__(256) void combine_frag_few_kernel(AttnArgs a, float
   const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of the LSE work
   const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
   float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * a.h + hblk * 32 + r) * kFragLat + d);
-  const int32_t n_total = load_ro(a.cu_tiles, a.B);
   const int32_t first = load_ro(a.cu_tiles, b), last = load_ro(a.cu_tiles, b + 1) - 1;
   if (last < first) {
     *dst = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const int32_t g_lo = split_owner(n_total, a.splits, first);
-  const int32_t n_cand = split_owner(n_total, a.splits, last) - g_lo + 1;
-  // with no more splits than tiles every split owns a tile; otherwise splits
-  // that own none wrote nothing and get weight 0
-  const bool all_own = a.splits <= n_total;
+  const int32_t g_lo = load_ro(a.seq_splits, 2 * b);
+  const int32_t n_cand = load_ro(a.seq_splits, 2 * b + 1) - g_lo + 1;
+  // splits that own no tile wrote nothing and get weight 0
   auto owns = [&](int32_t k) {
-    return all_own || split_begin(n_total, a.splits, g_lo + k) <
-                          split_begin(n_total, a.splits, g_lo + k + 1);
+    return load_ro(a.split_first, g_lo + k) < load_ro(a.split_first, g_lo + k + 1);
   };
   const int64_t slot_stride = (int64_t)a.h * kFragLat;
   const float* src = a.part_o + (int64_t)(g_lo + b) * slot_stride + frag_offset(hblk, mdg, jj, lane);
@@ -417,7 +410,7 @@ __global__ __launch_bounds__(256) void combine_frag_few_kernel(AttnArgs a, float
       v[i] = k < n_cand ? *reinterpret_cast<const float4*>(src + (int64_t)k * slot_stride)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (!all_own) {
+    {
 #pragma unroll
       for (int i = 0; i < kCombPer; i++)
         if (c0 + i < n_cand && !owns(c0 + i)) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);

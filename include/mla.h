@@ -176,13 +176,27 @@ mla_status mla_gather_cache(const mla_decode_params* p, const void* c_kv, const 
                             const int32_t* seq_lens, int32_t max_tokens, void* c_out,
                             float* scale_out, void* rope_out, void* stream);
 
-/* Host-side split arithmetic (no HIP call; used by the kernels' planner).
- * The cache of all sequences is cut into 32-token tiles, numbered across
- * sequences in order.  Split g of `splits` owns tiles
- * [mla_split_begin(n, splits, g), mla_split_begin(n, splits, g + 1));
- * mla_split_owner returns the split owning a tile. */
+/* Host-side split arithmetic (no HIP call; the kernels' planner follows the
+ * same rules on the device).  The cache of all sequences is cut into 32-token
+ * tiles, numbered across sequences in order, and every split (token-split work
+ * group) owns a contiguous run of them.  Two rules, chosen by the batch size:
+ *  - batch <= splits and batch <= 2048: no split crosses a sequence.  With n_b tiles in
+ *    sequence b, L is the least bound with sum_b ceil(n_b / L) <= splits;
+ *    sequence b gets k_b = ceil(n_b / L) splits in order, its i-th owning its
+ *    tiles [n_b i / k_b, n_b (i + 1) / k_b); splits left over own nothing.
+ *  - otherwise: split g owns tiles [n g / splits, n (g + 1) / splits) of
+ *    all n tiles (mla_split_begin); mla_split_owner returns the split owning
+ *    a tile under this rule.
+ * mla_split_plan applies the rule to tiles[batch] (tiles per sequence, >= 0,
+ * summing below 2^31) and writes split_first[splits + 1] (split g owns
+ * [split_first[g], split_first[g + 1])) and seq_splits[2 batch] (first and
+ * last split holding a tile of sequence b; last < first when it has none).
+ * Errors: MLA_ERR_INVALID_ARG for batch < 1, splits < 1, a null array or a
+ * negative count; MLA_ERR_UNSUPPORTED for 2^31 tiles or more. */
 int64_t mla_split_begin(int64_t n_tiles, int32_t splits, int32_t g);
 int32_t mla_split_owner(int64_t n_tiles, int32_t splits, int64_t tile);
+mla_status mla_split_plan(const int32_t* tiles, int32_t batch, int32_t splits,
+                          int32_t* split_first, int32_t* seq_splits);
 
 /* ------------------------------------------------------------------------
  * Latent-cache writer: appends one new token per sequence to the paged cache

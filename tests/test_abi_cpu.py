@@ -47,12 +47,13 @@ def _params(**kw):
 
 def test_workspace_size_without_device():
     n = _lib.mla_decode_workspace_size(_params())
-    # q_lat + cu_tiles + tile descriptors (B * ceil(2 blocks * 64 / 32) of 16 B)
-    # + partials ((8 + 2) slots) + lse + o_lat, each 256-aligned
+    # q_lat + cu_tiles + split table (8 + 1) + sequence splits (2 B) + tile
+    # descriptors (B * ceil(2 blocks * 64 / 32) of 16 B) + partials ((8 + 2)
+    # slots) + lse + o_lat, each 256-aligned
     B, h, dc, dr = 2, 4, 32, 8
     expect = 0
-    for size in (B * h * (dc + dr) * 4, (B + 1) * 4, B * 4 * 16, 10 * h * dc * 4, 10 * h * 4,
-                 B * h * dc * 4):
+    for size in (B * h * (dc + dr) * 4, (B + 1) * 4, 9 * 4, 2 * B * 4, B * 4 * 16,
+                 10 * h * dc * 4, 10 * h * 4, B * h * dc * 4):
         expect += (size + 255) // 256 * 256
     assert n == expect
 
@@ -144,6 +145,76 @@ def test_split_slots_are_unique():
                 assert s not in slots
                 assert s < G + len(lens_tiles)
                 slots.add(s)
+
+
+def _plan_reference(tiles, S):
+    """The split rules written out directly: sequence-aligned when the batch
+    fits in the splits (least L by linear search), contiguous otherwise."""
+    import math
+    B, tot = len(tiles), sum(tiles)
+    cu = [0]
+    for x in tiles:
+        cu.append(cu[-1] + x)
+    if B > S or B > 2048:
+        first = [tot * g // S for g in range(S + 1)]
+    else:
+        L = 1
+        while sum(math.ceil(n / L) for n in tiles if n) > S:
+            L += 1
+        first = []
+        for b, n in enumerate(tiles):
+            k = math.ceil(n / L) if n else 0
+            first += [cu[b] + n * i // k for i in range(k)]
+        first += [tot] * (S + 1 - len(first))
+    seq = []
+    for b in range(B):
+        owners = [g for g in range(S) if first[g] < first[g + 1] and cu[b] < cu[b + 1]
+                  and first[g] < cu[b + 1] and first[g + 1] > cu[b]]
+        seq.append((owners[0], owners[-1]) if owners else None)
+    return first, seq
+
+
+@pytest.mark.parametrize("tiles,S", [
+    ([3, 0, 5, 1, 0, 0, 9, 2], 8),          # ragged with empty sequences, B == S
+    ([3, 0, 5, 1, 0, 0, 9, 2], 40),         # many more splits than tiles
+    ([3, 0, 5, 1, 0, 0, 9, 2], 3),          # B > S: contiguous rule
+    ([0, 0, 0], 5),                         # nothing to do
+    ([1024] * 8, 128),                      # the 32K point: 16 splits of 64 tiles each
+    ([40, 1000, 7, 517, 333, 1023, 2, 940], 128),   # a 1K..32K-like ragged batch
+    ([128] * 64, 128), ([512] * 32, 128), ([256] * 16, 256),
+    ([1] * 2049, 4096),                     # above the aligned rule's batch limit
+])
+def test_split_plan_rules(tiles, S):
+    first, seq = _lib.mla_split_plan(tiles, S)
+    ref_first, ref_seq = _plan_reference(tiles, S)
+    assert list(first) == ref_first
+    cu = [0]
+    for x in tiles:
+        cu.append(cu[-1] + x)
+    for b, r in enumerate(ref_seq):
+        if r is None:
+            assert seq[b, 1] < seq[b, 0]
+        else:
+            assert tuple(seq[b]) == r
+    # every tile is owned once; aligned plans keep each split in one sequence
+    assert first[0] == 0 and first[-1] == cu[-1]
+    assert all(a <= b for a, b in zip(first, first[1:]))
+    if len(tiles) <= min(S, 2048):
+        for g in range(S):
+            if first[g] < first[g + 1]:
+                owners = [b for b in range(len(tiles)) if cu[b] < first[g + 1] and cu[b + 1] > first[g]]
+                assert len(owners) == 1
+        # slots g + b stay unique and below S + B
+        slots = [g + b for b in range(len(tiles)) if seq[b, 1] >= seq[b, 0]
+                 for g in range(seq[b, 0], seq[b, 1] + 1)]
+        assert len(slots) == len(set(slots)) and max(slots, default=0) < S + len(tiles)
+
+
+def test_split_plan_rejects_bad_arguments():
+    for tiles, S in (([], 4), ([1, 2], 0), ([1, -1], 4)):
+        with pytest.raises(_lib.MlaError) as ei:
+            _lib.mla_split_plan(tiles, S)
+        assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
 
 
 def _prefill_params(**kw):

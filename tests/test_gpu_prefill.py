@@ -19,11 +19,15 @@ from oracle.prefill import mha_prefill
 pytestmark = pytest.mark.gpu
 
 # Bars (bf16 arithmetic with fp32 accumulation, as for the decode step):
-#  * whole output: max |err| <= 2e-2 RMS over every computed output value;
-#  * per output row (b, l, i): max |err| <= 2e-2 RMS of that row.  Rows that
-#    average many keys are small, and so are their rounding errors; the MHA
-#    form rounds the reconstructed keys, values and softmax weights to bf16,
-#    which the per-row bar still has to absorb.
+#  * per output row (b, l, i): max |err| <= 2e-2 RMS of that row, on every
+#    case.  Rows that average many keys are small, and so are their rounding
+#    errors;
+#  * whole output: max |err| <= 2e-2 RMS over every computed value, on the
+#    cases where every row sees many keys (the 128-head long contexts, the
+#    benchmark's call, the small-page fp8 case).  On the small ragged cases a
+#    row with one or a few keys has outputs ~15x the overall RMS, and the bf16
+#    rounding of its value vectors alone exceeds 2e-2 of that RMS
+#    (tests/test_prefill_bar_cpu.py shows it on the oracle's own output).
 TOL = 2e-2
 
 
@@ -59,7 +63,7 @@ def run_prefill(pi, q_lens=None):
     return (out if c.out_dtype == "f32" else out.view(torch.bfloat16)).float().double().cpu().numpy()
 
 
-def check(pi, got, heads=None, batches=None, rows=None, label=""):
+def check(pi, got, heads=None, batches=None, rows=None, label="", whole=False):
     c = pi.cfg
     ref = mha_prefill(pi.q, pi.q_lens, pi.c_kv, pi.c_kv_scale, pi.k_rope, pi.block_table,
                       pi.seq_lens, pi.W_UK, pi.W_UV, c.sm_scale, c.page_size, q_tag=c.q_dtype,
@@ -81,8 +85,9 @@ def check(pi, got, heads=None, batches=None, rows=None, label=""):
          f"row RMS {rms[worst]:.3e}, ratio {ratio[worst]:.3e}; overall max err "
          f"{float(err[rows_done].max()):.3e}, RMS {float(np.sqrt(np.mean(ref[mask] ** 2))):.3e}")
     assert ratio[worst] <= TOL
-    whole = float(err[rows_done].max()) / float(np.sqrt(np.mean(ref[mask] ** 2)))
-    assert whole <= TOL, whole
+    if whole:
+        w = float(err[rows_done].max()) / float(np.sqrt(np.mean(ref[mask] ** 2)))
+        assert w <= TOL, w
     # rows past each chunk are never written
     for b in range(c.batch):
         assert np.isnan(got[b, int(pi.q_lens[b]):]).all(), b
@@ -136,7 +141,7 @@ def test_prefill_dsv3_heads_long_context_sampled(cache):
     got = run_prefill(pi)
     for b in range(2):
         assert np.all(np.isfinite(got[b, :int(pi.q_lens[b])])), b
-    check(pi, got, heads=[0, 37, 127], rows=[0, 63, 64, 255, 299, 511], label=f"dsv3 long {cache}")
+    check(pi, got, heads=[0, 37, 127], rows=[0, 63, 64, 255, 299, 511], label=f"dsv3 long {cache}", whole=True)
 
 
 def test_prefill_fp8_small_pages_many_tiles():
@@ -146,7 +151,7 @@ def test_prefill_fp8_small_pages_many_tiles():
     cfg = DSV3.replace(heads=4, batch=2, seed=5206, cache_dtype="e4m3", page_size=16)
     _say("prefill fp8 small pages")
     pi = generate_prefill(cfg, 400, seq_lens=[1500, 2047], q_lens=[400, 257])
-    check(pi, run_prefill(pi), label="fp8 p16")
+    check(pi, run_prefill(pi), label="fp8 p16", whole=True)
 
 
 def test_prefill_empty_sequences():
@@ -172,4 +177,4 @@ def test_prefill_bench_configuration_sampled(cache):
     got = run_prefill(pi)
     assert np.all(np.isfinite(got))
     check(pi, got, heads=[0, 127], batches=[0, 1], rows=[0, 255, 256, 4095],
-          label=f"bench config {cache}")
+          label=f"bench config {cache}", whole=True)
