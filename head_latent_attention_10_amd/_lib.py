@@ -98,6 +98,12 @@ _SIGNATURES = {
     "mla_decode_timed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
     "mla_absorb_q": (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     "mla_attend_latent": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_attend_partial": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_combine": (ctypes.c_int, [_PP, _P, _P, ctypes.c_size_t, _P]),
+    "mla_partials_layout": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_int32)]),
     "mla_up_project": (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     "mla_gather_cache": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "mla_split_begin": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
@@ -238,6 +244,32 @@ def mla_attend_latent(p, q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens,
         ctypes.byref(p), _ptr(q_lat), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope),
         _ptr(block_table), _ptr(seq_lens), _ptr(o_lat), _ptr(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def mla_attend_partial(p, q_lat, c_kv, c_kv_scale, k_rope, block_table, seq_lens, workspace,
+                       workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("mla_attend_partial", load_library().mla_attend_partial(
+        ctypes.byref(p), _ptr(q_lat), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope),
+        _ptr(block_table), _ptr(seq_lens), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mla_combine(p, o_lat, workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("mla_combine", load_library().mla_combine(
+        ctypes.byref(p), _ptr(o_lat), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mla_partials_layout(p):
+    """(part_o byte offset, part_lse byte offset, slots, fragment_major) of the
+    partials mla_attend_partial writes into the workspace for *p."""
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    n, f = ctypes.c_int32(), ctypes.c_int32()
+    _check("mla_partials_layout", load_library().mla_partials_layout(
+        ctypes.byref(p), ctypes.byref(a), ctypes.byref(b), ctypes.byref(n), ctypes.byref(f)))
+    return a.value, b.value, n.value, f.value
 
 
 def mla_up_project(p, o_lat, W_UV, out, stream=None):

@@ -182,19 +182,11 @@ mla::PlanRequest plan_request(const Layout& L, char* ws, const int32_t* block_ta
   return r;
 }
 
-// `groups` > 1: grouped latent, group-major pools (mla_grouped_decode).
-mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat, const void* c_kv,
-                  const float* c_kv_scale, const void* k_rope, const mla::PlanRequest& req,
-                  float* o_lat, char* ws, hipStream_t s, bool planned = false,
-                  hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
-                  int32_t groups = 1) {
-  const int32_t* block_table = req.block_table;
-  const int32_t* seq_lens = req.seq_lens;
-  mla::AttnArgs a;
-  a.q_lat = q_lat;
-  a.c_kv = c_kv;
-  a.c_kv_scale = c_kv_scale;
-  a.k_rope = k_rope;
+// Everything the attention and combine kernels need to know about the problem
+// and the workspace, but the cache pointers.
+mla::AttnArgs attn_args(const mla_decode_params& p, const Layout& L, char* ws,
+                        const int32_t* block_table, const int32_t* seq_lens) {
+  mla::AttnArgs a{};
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.cu_tiles = reinterpret_cast<int32_t*>(ws + L.cu_tiles);
@@ -213,6 +205,25 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   a.num_blocks = p.num_blocks;
   a.splits = L.splits;
   a.streams = L.streams;
+  // the partial layout follows the shape: fragment-major for the shapes the
+  // matrix-core kernels serve (whichever kernel runs), row-major otherwise
+  a.frag_layout = mla::mfma_any_supported(p) ? 1 : 0;
+  a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
+  return a;
+}
+
+// The split attention into the workspace's partials (a2..a6).
+// `groups` > 1: grouped latent, group-major pools (mla_grouped_decode).
+mla_status attend_partial(const mla_decode_params& p, const Layout& L, const void* q_lat,
+                          const void* c_kv, const float* c_kv_scale, const void* k_rope,
+                          const mla::PlanRequest& req, char* ws, hipStream_t s,
+                          bool planned = false, hipEvent_t ev_before = nullptr,
+                          hipEvent_t ev_after = nullptr, int32_t groups = 1) {
+  mla::AttnArgs a = attn_args(p, L, ws, req.block_table, req.seq_lens);
+  a.q_lat = q_lat;
+  a.c_kv = c_kv;
+  a.c_kv_scale = c_kv_scale;
+  a.k_rope = k_rope;
   a.slots = req.indices ? req.slots : nullptr;
   a.idx_stride = req.indices ? req.idx_stride : 0;
   a.group_heads = groups > 1 ? p.num_heads / groups : 0;
@@ -226,8 +237,6 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
   const bool groups_fit = groups <= 1 || (p.num_heads / groups) % mla::mfma_heads_per_group(p.num_heads) == 0;
   const bool use_bf16 = aligned && groups_fit && mla::mfma_supported(p);
   const bool use_fp8 = aligned && groups_fit && mla::mfma_fp8_supported(p);
-  a.frag_layout = use_bf16 || use_fp8 ? 1 : 0;
-  a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
 
   hipError_t e = hipSuccess;
   if (!planned) {
@@ -246,9 +255,27 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
     if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  e = mla::launch_combine(a, o_lat, s);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MLA_OK;
+}
+
+// The log-sum-exp merge of the workspace's partials into o_lat (a7).
+mla_status combine(const mla_decode_params& p, const Layout& L, char* ws, float* o_lat,
+                   hipStream_t s) {
+  const mla::AttnArgs a = attn_args(p, L, ws, nullptr, nullptr);
+  const hipError_t e = mla::launch_combine(a, o_lat, s);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "combine launch");
+}
+
+// Split attention and merge (a2..a7).
+mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat, const void* c_kv,
+                  const float* c_kv_scale, const void* k_rope, const mla::PlanRequest& req,
+                  float* o_lat, char* ws, hipStream_t s, bool planned = false,
+                  hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
+                  int32_t groups = 1) {
+  mla_status st = attend_partial(p, L, q_lat, c_kv, c_kv_scale, k_rope, req, ws, s, planned,
+                                 ev_before, ev_after, groups);
+  if (st != MLA_OK) return st;
+  return combine(p, L, ws, o_lat, s);
 }
 
 }  // namespace
@@ -528,6 +555,58 @@ mla_status mla_attend_latent(const mla_decode_params* p, const void* q_lat, cons
   char* ws = static_cast<char*>(workspace);
   return attend(*p, L, q_lat, c_kv, c_kv_scale, k_rope, plan_request(L, ws, block_table, seq_lens),
                 o_lat, ws, static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_attend_partial(const mla_decode_params* p, const void* q_lat, const void* c_kv,
+                              const float* c_kv_scale, const void* k_rope,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
+  if (st != MLA_OK) return st;
+  if (!q_lat) return fail(MLA_ERR_INVALID_ARG, "null q_lat");
+  Layout L;
+  st = layout(*p, &L);
+  if (st != MLA_OK) return st;
+  st = check_workspace(L, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  return attend_partial(*p, L, q_lat, c_kv, c_kv_scale, k_rope,
+                        plan_request(L, ws, block_table, seq_lens), ws,
+                        static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_combine(const mla_decode_params* p, float* o_lat, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!o_lat) return fail(MLA_ERR_INVALID_ARG, "null o_lat");
+  Layout L;
+  st = layout(*p, &L);
+  if (st != MLA_OK) return st;
+  st = check_workspace(L, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  return combine(*p, L, static_cast<char*>(workspace), o_lat, static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_partials_layout(const mla_decode_params* p, size_t* part_o_offset,
+                               size_t* part_lse_offset, int32_t* slots, int32_t* fragment_major) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!part_o_offset || !part_lse_offset || !slots || !fragment_major)
+    return fail(MLA_ERR_INVALID_ARG, "null output pointer");
+  Layout L;
+  st = layout(*p, &L);
+  if (st != MLA_OK) return st;
+  *part_o_offset = L.part_o;
+  *part_lse_offset = L.part_lse;
+  *slots = (int32_t)L.slots;
+  *fragment_major = mla::mfma_any_supported(*p) ? 1 : 0;
+  return MLA_OK;
 }
 
 mla_status mla_up_project(const mla_decode_params* p, const float* o_lat, const void* W_UV,

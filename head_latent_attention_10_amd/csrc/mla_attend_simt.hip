@@ -116,7 +116,13 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < kSimtPerThread; k++) {
         const int32_t d = tid + 256 * k;
-        if (d < d_c) a.part_o[(slot * a.h + head) * d_c + d] = o[k] * inv;
+        if (d >= d_c) continue;
+        // the matrix-core shapes keep their partials fragment-major (the
+        // layout the combine reads for them), whichever kernel wrote them
+        const int64_t off = a.frag_layout
+            ? frag_offset(head >> 5, d >> 5, (d >> 3) & 3, ((d >> 2) & 1) * 32 + (head & 31)) + (d & 3)
+            : (int64_t)head * d_c + d;
+        a.part_o[slot * a.h * d_c + off] = o[k] * inv;
       }
       if (tid == 0) a.part_lse[slot * a.h + head] = l > 0.f ? m + logf(l) : -INFINITY;
       fresh = true;

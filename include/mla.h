@@ -149,7 +149,7 @@ mla_status mla_absorb_q(const mla_decode_params* p, const void* q, const void* W
 
 /* Stage: attention in the latent space over the paged cache, split along
  * tokens, partial results merged by their log-sum-exp ("The RoPE handling"
- * score, softmax, p . c_KV).
+ * score, softmax, p . c_KV): mla_attend_partial followed by mla_combine.
  *   q_lat [B, h, d_latent + d_rope] as written by mla_absorb_q
  *   o_lat [B, h, d_latent] fp32 (written)
  *   workspace as for mla_decode. */
@@ -158,6 +158,41 @@ mla_status mla_attend_latent(const mla_decode_params* p, const void* q_lat, cons
                              const int32_t* block_table, const int32_t* seq_lens,
                              float* o_lat, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* Stage: the split attention alone ("The RoPE handling" score, the softmax
+ * over each split's tokens and p . c_KV over them; TPLA section 3.4, Eq. 5):
+ * plans the token splits (split rules above) and writes, for every
+ * (split, sequence) pair that shares tokens, the split's normalised partial
+ * output o_s = sum_t p_t c_t / sum_t p_t and its log-sum-exp
+ * lse_s = m + ln sum_t exp(s_t - m) into the workspace.  q_lat, the cache
+ * arguments and the workspace as for mla_attend_latent; the partials stay in
+ * the workspace for mla_combine (mla_partials_layout says where). */
+mla_status mla_attend_partial(const mla_decode_params* p, const void* q_lat, const void* c_kv,
+                              const float* c_kv_scale, const void* k_rope,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage: the log-sum-exp merge of the partials that mla_attend_partial left
+ * in `workspace` (same *p, enqueued after it):
+ *   o_lat[b,i,:] = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M),  M = max_s lse_s
+ * over the splits s holding tokens of sequence b -- the exact merge of
+ * softmax partials over disjoint token ranges.  A sequence with one split gets
+ * its partial back unchanged; one with no tokens gets zeros.
+ *   o_lat [B, h, d_latent] fp32 (written). */
+mla_status mla_combine(const mla_decode_params* p, float* o_lat, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Where mla_attend_partial keeps the partials of *p in the workspace: o_s of
+ * slot k at byte offset part_o_offset + k h d_latent 4 (fp32), lse_s of slot k
+ * and head i at part_lse_offset + (k h + i) 4; slots = splits + batch; the
+ * pair (split g, sequence b) uses slot g + b.  fragment_major = 1 for the
+ * shapes the matrix-core kernels serve (d_latent 512, heads a multiple of 32,
+ * bf16 or fp8 cache): a slot's [h, 512] block is then stored as
+ * [h/32][16][4][64][4] (head block, 32-value latent block m, 8-value group j,
+ * lane 32 g + r, 4 values): head 32 hb + r, latent 32 m + 8 j + 4 g + 0..3.
+ * Otherwise the block is row-major [h][d_latent]. */
+mla_status mla_partials_layout(const mla_decode_params* p, size_t* part_o_offset,
+                               size_t* part_lse_offset, int32_t* slots, int32_t* fragment_major);
 
 /* Stage: value up-projection, kept apart from W_O ("MLA Matrix Absorption":
  * W_UV is in practice not folded into the output projection).

@@ -279,3 +279,60 @@ def test_prefill_rejects_bad_arguments_before_launch():
                          _lib.mla_prefill_workspace_size(p8))
     assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
     assert "aligned" in _lib.mla_last_error()
+
+
+def test_stage_entry_points_validate_before_launch():
+    """mla_attend_partial / mla_combine reject null pointers and short
+    workspaces before any HIP call."""
+    p = _params()
+    fake = 0x10000
+    need = _lib.mla_decode_workspace_size(p)
+    with pytest.raises(_lib.MlaError) as ei:      # null q_lat
+        _lib.mla_attend_partial(p, None, fake, None, fake, fake, fake, fake, need)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    with pytest.raises(_lib.MlaError) as ei:      # null latent cache
+        _lib.mla_attend_partial(p, fake, None, None, fake, fake, fake, fake, need)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    with pytest.raises(_lib.MlaError) as ei:      # one byte short
+        _lib.mla_attend_partial(p, fake, fake, None, fake, fake, fake, fake, need - 1)
+    assert ei.value.status == _lib.MLA_ERR_WORKSPACE
+    with pytest.raises(_lib.MlaError) as ei:      # no workspace
+        _lib.mla_attend_partial(p, fake, fake, None, fake, fake, fake, None, need)
+    assert ei.value.status == _lib.MLA_ERR_WORKSPACE
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_combine(p, None, fake, need)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_combine(p, fake, fake, need - 1)
+    assert ei.value.status == _lib.MLA_ERR_WORKSPACE
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_combine(_params(batch=0), fake, fake, need)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_partials_layout_lies_inside_the_workspace():
+    """The partials sit inside the decode workspace: (splits + batch) slots of
+    h x d_c floats, then their h log-sum-exps; fragment-major exactly when a
+    matrix-core kernel serves the shape (64 or 32 heads of a 512-latent bf16
+    or fp8 cache)."""
+    for kw, frag in ((dict(), 0),
+                     (dict(num_heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128,
+                           cache_dtype="bf16", q_dtype="bf16", rope_dtype="bf16",
+                           weight_dtype="bf16"), 1),
+                     (dict(num_heads=32, d_latent=512, d_rope=64, d_nope=128, d_v=128,
+                           cache_dtype="e4m3", q_dtype="bf16", rope_dtype="bf16",
+                           weight_dtype="bf16"), 1),
+                     (dict(num_heads=3, d_latent=512, d_rope=64, d_nope=128, d_v=128,
+                           cache_dtype="bf16", q_dtype="bf16", rope_dtype="bf16",
+                           weight_dtype="bf16"), 0)):
+        p = _params(**kw)
+        off_o, off_l, slots, f = _lib.mla_partials_layout(p)
+        h, dc = p.num_heads, p.d_latent
+        assert slots == p.num_splits + p.batch
+        assert off_o % 256 == 0 and off_l % 256 == 0
+        assert off_l >= off_o + slots * h * dc * 4
+        assert off_l + slots * h * 4 <= _lib.mla_decode_workspace_size(p)
+        assert f == frag, kw
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_partials_layout(_params(num_heads=0))
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
