@@ -95,6 +95,7 @@ _SIGNATURES = {
     "mla_decode_num_splits": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int32)]),
     "mla_absorbed_dtype": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int32)]),
     "mla_decode": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_decode_no_alloc": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mla_decode_timed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
     "mla_absorb_q": (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     "mla_attend_latent": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -229,6 +230,18 @@ def mla_decode_timed(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK
         ctypes.byref(p), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope), _ptr(block_table),
         _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _ptr(workspace), workspace_bytes,
         _stream(stream), evb, eva))
+
+
+# Size of the fixed device array mla_decode_no_alloc works in (the header's
+# MLA_NO_ALLOC_SCRATCH_BYTES).
+MLA_NO_ALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def mla_decode_no_alloc(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK, W_UV, out,
+                        stream=None):
+    _check("mla_decode_no_alloc", load_library().mla_decode_no_alloc(
+        ctypes.byref(p), _ptr(q), _ptr(c_kv), _ptr(c_kv_scale), _ptr(k_rope), _ptr(block_table),
+        _ptr(seq_lens), _ptr(W_UK), _ptr(W_UV), _ptr(out), _stream(stream)))
 
 
 def mla_absorb_q(p, q, W_UK, q_lat, stream=None):

@@ -3,9 +3,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "mla_kernels.hpp"
+
+// Workspace of mla_decode_no_alloc: a fixed array of device memory that comes
+// with the code object, so that call allocates nothing.  Each device holds its
+// own copy at its own address, from the library's first use of the array on
+// it until the process ends.  In host code this name is a stand-in, never a
+// device address: host code uses the per-device address that
+// hipGetSymbolAddress returns (no_alloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MLA_NO_ALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -344,6 +353,33 @@ mla_status decode_impl(const mla_decode_params* p, const void* q, const void* c_
   return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
 }
 
+// ---------------------------------------------------------------- no-allocation decode
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current.
+mla_status no_alloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "device %d: the scratch table holds devices 0..%d", dev,
+                kScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255))
+      return fail(MLA_ERR_HIP, "scratch array at %p is not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 // ---------------------------------------------------------------- DSA
 mla_status validate_dsa(const mla_dsa_params* d, bool need_topk) {
   if (!d) return fail(MLA_ERR_INVALID_ARG, "dsa params is NULL");
@@ -635,6 +671,31 @@ mla_status mla_decode(const mla_decode_params* p, const void* q, const void* c_k
                       void* workspace, size_t workspace_bytes, void* stream) {
   return mla_decode_timed(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, W_UK, W_UV, out,
                           workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+mla_status mla_decode_no_alloc(const mla_decode_params* p, const void* q, const void* c_kv,
+                               const float* c_kv_scale, const void* k_rope,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const void* W_UK, const void* W_UV, void* out, void* stream) {
+  g_last_error.clear();
+  mla_status st = validate(p);
+  if (st != MLA_OK) return st;
+  st = check_cache_ptrs(p, c_kv, c_kv_scale, k_rope, block_table, seq_lens);
+  if (st != MLA_OK) return st;
+  if (!q || !W_UK || !W_UV || !out) return fail(MLA_ERR_INVALID_ARG, "null q, W_UK, W_UV or out");
+  Layout L;
+  st = layout(*p, &L);
+  if (st != MLA_OK) return st;
+  if (L.total > (size_t)MLA_NO_ALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE,
+                "the step needs %zu bytes of workspace; the fixed scratch holds %zu "
+                "(fewer splits or a smaller batch fit)",
+                L.total, (size_t)MLA_NO_ALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = no_alloc_scratch(&ws);
+  if (st != MLA_OK) return st;
+  return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, seq_lens, nullptr, 0, W_UK,
+                     W_UV, out, ws, (size_t)MLA_NO_ALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
 }
 
 mla_status mla_decode_sparse_workspace_size(const mla_decode_params* p, int32_t index_stride,

@@ -127,6 +127,25 @@ mla_status mla_decode(const mla_decode_params* p, const void* q, const void* c_k
                       const void* W_UK, const void* W_UV, void* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mla_decode
+ * with the workspace taken from a fixed array of MLA_NO_ALLOC_SCRATCH_BYTES
+ * bytes of device memory that the library holds on each device it runs on
+ * (from its first use there until the process ends).  The call makes no
+ * allocation of its own.  Arguments, results and errors as for mla_decode,
+ * less the workspace; MLA_ERR_WORKSPACE when mla_decode_workspace_size(p)
+ * exceeds MLA_NO_ALLOC_SCRATCH_BYTES (checked before any HIP call when
+ * num_splits > 0; fewer splits or a smaller batch fit).  Every call on one
+ * device shares that device's array and nothing in it needs to start at zero
+ * (each call writes what it reads), so calls that overlap on one device --
+ * on two streams, or from two threads -- race and must be ordered by the
+ * caller.  Devices 0..63. */
+#define MLA_NO_ALLOC_SCRATCH_BYTES (128u << 20)
+mla_status mla_decode_no_alloc(const mla_decode_params* p, const void* q, const void* c_kv,
+                               const float* c_kv_scale, const void* k_rope,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const void* W_UK, const void* W_UV, void* out, void* stream);
+
 /* mla_decode that also records two caller-created hipEvent_t (may be NULL)
  * at the start and end of the split-attention kernel, so the caller can time
  * that kernel alone (hipEventElapsedTime).  The matrix-core kernels take the

@@ -336,3 +336,28 @@ def test_partials_layout_lies_inside_the_workspace():
     with pytest.raises(_lib.MlaError) as ei:
         _lib.mla_partials_layout(_params(num_heads=0))
     assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_no_alloc_decode_checks_before_any_hip_call():
+    """mla_decode_no_alloc: the scratch size matches the header; null pointers
+    and a step whose workspace exceeds the fixed scratch are rejected before
+    any HIP call."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MLA_NO_ALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.MLA_NO_ALLOC_SCRATCH_BYTES
+    fake = 0x10000
+    p = _params()
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_decode_no_alloc(p, None, fake, None, fake, fake, fake, fake, fake, fake)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_decode_no_alloc(p, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG      # scale pointer with an fp32 cache
+    big = _params(batch=512, num_heads=128, d_nope=128, d_rope=64, d_latent=512, d_v=128,
+                  cache_dtype="bf16", q_dtype="bf16", rope_dtype="bf16", weight_dtype="bf16",
+                  num_splits=128)
+    assert _lib.mla_decode_workspace_size(big) > _lib.MLA_NO_ALLOC_SCRATCH_BYTES
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_decode_no_alloc(big, fake, fake, None, fake, fake, fake, fake, fake, fake)
+    assert ei.value.status == _lib.MLA_ERR_WORKSPACE
+    assert "scratch" in _lib.mla_last_error()
