@@ -131,7 +131,8 @@ mla_status layout(const mla_decode_params& p, Layout* L, int32_t sparse_stride =
   const size_t tiles_per_seq = (cap + mla::kTile - 1) / mla::kTile;
   off = align256(off + B * tiles_per_seq * 4 * sizeof(int32_t));
   L->part_o = off;
-  off = align256(off + (size_t)L->slots * h * dc * sizeof(float));
+  // fragment-major partials (the matrix-core shapes) are bf16, others fp32
+  off = align256(off + (size_t)L->slots * h * dc * (mla::mfma_any_supported(p) ? 2 : 4));
   L->part_lse = off;
   off = align256(off + (size_t)L->slots * h * sizeof(float));
   L->o_lat = off;
@@ -202,7 +203,7 @@ mla::AttnArgs attn_args(const mla_decode_params& p, const Layout& L, char* ws,
   a.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   a.split_first = reinterpret_cast<int32_t*>(ws + L.split_first);
   a.seq_splits = reinterpret_cast<int32_t*>(ws + L.seq_splits);
-  a.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  a.part_o = ws + L.part_o;
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
   a.B = p.batch;
   a.h = p.num_heads;

@@ -556,15 +556,15 @@ void attend_fp8_kernel(AttnArgs a) {
           const int64_t slot = (int64_t)(g + prev.b);
 #pragma unroll
           for (int hb = 0; hb < HB; hb++) {
-            float* dst = a.part_o + slot * a.h * kDc8 + frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
+            uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc8 +
+                            frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
 #pragma unroll
             for (int md = 0; md < MDP; md++) {
 #pragma unroll
-              for (int jj = 0; jj < 4; jj++) {
-                const f32x4 v = {o[md][hb][4 * jj] * inv[hb], o[md][hb][4 * jj + 1] * inv[hb],
-                                 o[md][hb][4 * jj + 2] * inv[hb], o[md][hb][4 * jj + 3] * inv[hb]};
-                *reinterpret_cast<f32x4*>(dst + (md * 4 + jj) * 256) = v;
-              }
+              for (int jj = 0; jj < 4; jj++)
+                *reinterpret_cast<uint2*>(dst + (md * 4 + jj) * 256) =
+                    pack_bf16x4(o[md][hb][4 * jj] * inv[hb], o[md][hb][4 * jj + 1] * inv[hb],
+                                o[md][hb][4 * jj + 2] * inv[hb], o[md][hb][4 * jj + 3] * inv[hb]);
               o[md][hb] = f32x16{};
             }
           }

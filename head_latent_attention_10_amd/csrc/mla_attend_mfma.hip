@@ -536,17 +536,16 @@ void attend_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int hb = 0; hb < HB; hb++) {
             const float inv = s_invl[(par * HB + hb) * 32 + (lane & 31)];
-            // fragment-major partial: one store instruction writes 1 KiB contiguous
-            float* dst = a.part_o + slot * a.h * kDc +
-                         frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
+            // fragment-major bf16 partial: one store instruction writes 512 B contiguous
+            uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc +
+                            frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
 #pragma unroll
             for (int md = 0; md < MDP; md++) {
 #pragma unroll
-              for (int jj = 0; jj < 4; jj++) {
-                const f32x4 v = {o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
-                                 o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv};
-                *reinterpret_cast<f32x4*>(dst + (md * 4 + jj) * 256) = v;
-              }
+              for (int jj = 0; jj < 4; jj++)
+                *reinterpret_cast<uint2*>(dst + (md * 4 + jj) * 256) =
+                    pack_bf16x4(o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
+                                o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv);
               o[md][hb] = f32x16{};
             }
           }
@@ -909,15 +908,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
 #pragma unroll
         for (int hb = 0; hb < 2; hb++) {
           const float inv = s_invl[(SL * 2 + hb) * 32 + (lane & 31)];
-          float* dst = a.part_o + slot * a.h * kDc + frag_offset(hg * 2 + hb, v * MD, 0, lane);
+          uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc +
+                          frag_offset(hg * 2 + hb, v * MD, 0, lane);
 #pragma unroll
           for (int md = 0; md < MD; md++) {
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              const f32x4 val = {o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
-                                 o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv};
-              *reinterpret_cast<f32x4*>(dst + (md * 4 + jj) * 256) = val;
-            }
+            for (int jj = 0; jj < 4; jj++)
+              *reinterpret_cast<uint2*>(dst + (md * 4 + jj) * 256) =
+                  pack_bf16x4(o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
+                              o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv);
             o[md][hb] = f32x16{};
           }
         }

@@ -12,7 +12,7 @@ constexpr int kTile = 32;  // tokens per planning tile (one step of the attentio
 
 // Planning: kPlanGroups work groups of kPlanThreads threads (see plan_block).
 constexpr int kPlanThreads = 256;
-constexpr int kPlanGroups = 8;
+constexpr int kPlanGroups = 32;
 
 // Per-tile descriptor written by the planning kernel, tiles numbered across
 // the sequences in order (four int32):
@@ -82,13 +82,13 @@ struct AttnArgs {
   const int32_t* tiles;      // [n_tiles][4] tile descriptors (workspace)
   const int32_t* split_first;  // [splits + 1] first tile of each split (workspace)
   const int32_t* seq_splits;   // [B][2] first and last split of each sequence (workspace)
-  float* part_o;             // [slots, h, d_c]
+  void* part_o;              // [slots, h, d_c]: bf16 fragment-major when frag_layout, else fp32 row-major
   float* part_lse;           // [slots, h]
   int32_t B, h, d_c, d_r, P, max_blocks, num_blocks;
   int32_t log2P;             // log2(P) when P is a power of two, else -1
   int32_t splits;            // work groups along tokens (gridDim.x)
   int32_t streams;           // partial slots per (split, sequence)
-  int32_t frag_layout;       // part_o in fragment-major layout (frag_offset), else row-major
+  int32_t frag_layout;       // part_o bf16 in fragment-major layout (frag_offset), else fp32 row-major
   float sm_scale_log2;       // sm_scale * log2(e)
   // Sparse mode (slots != null): sequence b attends to seq_lens[b] entries
   // (at most idx_stride) whose physical slots (block * P + offset) the planner
@@ -182,7 +182,7 @@ constexpr int kAlignedMaxBatch = 2048;
 
 // LDS of one planning work group.
 struct PlanShared {
-  int32_t scan[kPlanThreads];
+  int32_t red[8];                // per-wave partial results of the reductions
   int32_t cu[kPlanThreads + 1];  // tile prefix sums of the current chunk of sequences
   int32_t len[kPlanThreads];
   int32_t ntile[kAlignedMaxBatch];      // tiles per sequence (split table, aligned rule)
@@ -202,34 +202,103 @@ __device__ inline int32_t plan_tiles(const PlanInput& in, int32_t b) {
   return (T + kTile - 1) / kTile;
 }
 
-// Sum (or maximum) of one value per thread over the work group: across each
-// wave by lane exchanges, then across the waves through LDS.
-__device__ inline int32_t plan_reduce(int32_t v, bool is_max, PlanShared& sh) {
+// Work-group reductions of the planner: across each wave by lane exchanges,
+// then across the four waves through LDS (two barriers each).
+__device__ inline int2 plan_sum_max(int32_t s, int32_t m, PlanShared& sh) {
   const int tid = threadIdx.x, w = tid >> 6;
   for (int off = 32; off > 0; off >>= 1) {
-    const int32_t o = __shfl_xor(v, off);
-    v = is_max ? (o > v ? o : v) : v + o;
+    s += __shfl_xor(s, off);
+    const int32_t o = __shfl_xor(m, off);
+    m = o > m ? o : m;
   }
   __syncthreads();
-  if ((tid & 63) == 0) sh.scan[w] = v;
+  if ((tid & 63) == 0) {
+    sh.red[w] = s;
+    sh.red[4 + w] = m;
+  }
   __syncthreads();
-  int32_t r = sh.scan[0];
-  for (int i = 1; i < kPlanThreads / 64; i++) r = is_max ? (sh.scan[i] > r ? sh.scan[i] : r) : r + sh.scan[i];
+  int2 r = make_int2(sh.red[0], sh.red[4]);
+  for (int i = 1; i < kPlanThreads / 64; i++) {
+    r.x += sh.red[i];
+    r.y = sh.red[4 + i] > r.y ? sh.red[4 + i] : r.y;
+  }
   return r;
 }
 
-// Inclusive prefix sum of one value per thread over the work group.
-__device__ inline int32_t plan_scan(int32_t v, PlanShared& sh) {
+// Number of threads of the work group whose `pred` holds.
+__device__ inline int32_t plan_count(bool pred, PlanShared& sh) {
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int32_t c = __popcll(__ballot(pred));
+  __syncthreads();
+  if ((tid & 63) == 0) sh.red[w] = c;
+  __syncthreads();
+  int32_t r = 0;
+  for (int i = 0; i < kPlanThreads / 64; i++) r += sh.red[i];
+  return r;
+}
+
+// Inclusive prefix sums of two values per thread over the work group, and
+// their totals.
+__device__ inline void plan_scan2(int32_t& a, int32_t& b, int32_t* tot_a, int32_t* tot_b,
+                                  PlanShared& sh) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   for (int off = 1; off < 64; off <<= 1) {
-    const int32_t o = __shfl_up(v, off);
-    if (l >= off) v += o;
+    const int32_t oa = __shfl_up(a, off), ob = __shfl_up(b, off);
+    if (l >= off) {
+      a += oa;
+      b += ob;
+    }
   }
   __syncthreads();
-  if (l == 63) sh.scan[w] = v;
+  if (l == 63) {
+    sh.red[w] = a;
+    sh.red[4 + w] = b;
+  }
   __syncthreads();
-  for (int i = 0; i < w; i++) v += sh.scan[i];
-  return v;
+  int32_t ta = 0, tb = 0;
+  for (int i = 0; i < kPlanThreads / 64; i++) {
+    if (i < w) {
+      a += sh.red[i];
+      b += sh.red[4 + i];
+    }
+    ta += sh.red[i];
+    tb += sh.red[4 + i];
+  }
+  *tot_a = ta;
+  *tot_b = tb;
+}
+
+// Least L in [lo, hi] with sum_b ceil(ntile[b] / L) <= S, given that hi
+// qualifies (the count does not grow with L).  Each round tests up to
+// kPlanThreads / T evenly spaced candidates at once, T threads sharing the
+// sequences of one candidate; the candidates that fail form a prefix, whose
+// length narrows [lo, hi] to one step.
+__device__ inline int32_t plan_least_bound(int32_t B, int32_t S, int32_t lo, int32_t hi,
+                                           PlanShared& sh) {
+  const int tid = threadIdx.x;
+  // threads per candidate: at most 16 sequences each, or more threads when
+  // few candidates are left
+  int32_t tb = 1;
+  while (tb < 64 && B > 16 * tb) tb *= 2;
+  while (lo < hi) {
+    const int32_t span = hi - lo;  // candidates lo .. hi - 1; hi qualifies
+    int32_t T = 1;
+    while (T < 64 && (int64_t)span * (2 * T) <= kPlanThreads) T *= 2;
+    if (T < tb) T = tb;
+    const int32_t ncand = kPlanThreads / T;
+    const int32_t step = (span + ncand - 1) / ncand;
+    const int32_t sub = tid & (T - 1);
+    const int32_t c = lo + (tid / T) * step;
+    int32_t cnt = 0;
+    if (c < hi)
+      for (int32_t b = sub; b < B; b += T) cnt += aligned_splits(sh.ntile[b], c);
+    for (int off = 1; off < T; off <<= 1) cnt += __shfl_xor(cnt, off);
+    const int32_t nf = plan_count(c < hi && sub == 0 && cnt > S, sh);
+    const int32_t first_ok = lo + nf * step;  // first candidate that qualifies (or past hi)
+    if (first_ok < hi) hi = first_ok;
+    if (nf > 0) lo = lo + (nf - 1) * step + 1;
+  }
+  return lo;
 }
 
 // The split table (split rules above), written by one planning work group.
@@ -244,22 +313,22 @@ __device__ inline void plan_splits(const PlanInput& in, PlanShared& sh) {
     tot += n;
     mx = n > mx ? n : mx;
   }
-  tot = plan_reduce(tot, false, sh);
-  mx = plan_reduce(mx, true, sh);
-  int32_t L = 1;
-  if (aligned && tot > 0) {
-    // least L with sum_b ceil(n_b / L) <= S; L = max n_b always qualifies
-    int32_t lo = (tot + S - 1) / S, hi = mx;
-    while (lo < hi) {
-      const int32_t mid = lo + (hi - lo) / 2;
-      int32_t cnt = 0;
-      for (int32_t b = tid; b < B; b += kPlanThreads) cnt += aligned_splits(sh.ntile[b], mid);
-      cnt = plan_reduce(cnt, false, sh);
-      if (cnt <= S) hi = mid; else lo = mid + 1;
-    }
-    L = lo;
-  }
+  const int2 tm = plan_sum_max(tot, mx, sh);  // its barriers also publish ntile
+  tot = tm.x;
+  mx = tm.y;
   if (aligned) {
+    // L = max n_b qualifies, and so does any L >= tot / (S - B), since
+    // sum_b ceil(n_b / L) < tot / L + B
+    int32_t L = 1;
+    if (tot > 0) {
+      const int32_t lo = (tot + S - 1) / S;
+      int32_t hi = mx;
+      if (S > B) {
+        const int32_t ub = (int32_t)(((int64_t)tot + (S - B) - 1) / (S - B));
+        if (ub < hi) hi = ub;
+      }
+      L = plan_least_bound(B, S, lo, hi < lo ? lo : hi, sh);
+    }
     // split counts k_b and their exclusive prefix sums (first split, first
     // tile of each sequence) in LDS, a chunk of kPlanThreads sequences at a time
     int32_t gcarry = 0, tcarry = 0;
@@ -267,15 +336,16 @@ __device__ inline void plan_splits(const PlanInput& in, PlanShared& sh) {
       const int32_t b = base + tid;
       const int32_t n = b < B ? sh.ntile[b] : 0;
       const int32_t k = aligned_splits(n, L);
-      const int32_t sk = plan_scan(k, sh), sn = plan_scan(n, sh);
+      int32_t sk = k, sn = n, tk, tn;
+      plan_scan2(sk, sn, &tk, &tn, sh);
       if (b < B) {
         sh.gfirst[b] = gcarry + sk - k;
         sh.tfirst[b] = tcarry + sn - n;
         in.seq_splits[2 * b] = gcarry + sk - k;
         in.seq_splits[2 * b + 1] = gcarry + sk - 1;
       }
-      gcarry += plan_reduce(k, false, sh);
-      tcarry += plan_reduce(n, false, sh);
+      gcarry += tk;
+      tcarry += tn;
     }
     if (tid == 0) sh.gfirst[B] = gcarry;
     __syncthreads();
@@ -300,13 +370,14 @@ __device__ inline void plan_splits(const PlanInput& in, PlanShared& sh) {
   for (int32_t base = 0; base < B; base += kPlanThreads) {
     const int32_t b = base + tid;
     const int32_t n = b < B ? plan_tiles(in, b) : 0;
-    const int32_t sn = plan_scan(n, sh);
+    int32_t sn = n, unused = 0, tn, tu;
+    plan_scan2(sn, unused, &tn, &tu, sh);
     if (b < B) {
       const int32_t C = tcarry + sn - n;
       in.seq_splits[2 * b] = n == 0 ? 0 : split_owner(tot, S, C);
       in.seq_splits[2 * b + 1] = n == 0 ? -1 : split_owner(tot, S, C + n - 1);
     }
-    tcarry += plan_reduce(n, false, sh);
+    tcarry += tn;
   }
 }
 
@@ -315,7 +386,9 @@ __device__ inline void plan_splits(const PlanInput& in, PlanShared& sh) {
 // each chunk (cu_tiles[b] = sum_{j<b} ceil(T_j / kTile), written by group 0),
 // and the groups share out the chunk's tiles, writing one descriptor per tile
 // (tile_word).  The tile's page is resolved here when no tile can span two
-// pages (P a multiple of kTile).
+// pages (P a multiple of kTile).  A thread takes four tiles at a time: their
+// sequences first (LDS), then all four table loads, then the stores, so the
+// loads are in flight together.
 __device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, PlanShared& sh) {
   const int32_t* __restrict__ seq_lens = in.seq_lens;
   const int32_t* __restrict__ block_table = in.block_table;
@@ -332,6 +405,7 @@ __device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, 
     return;
   }
   const int32_t ntile_groups = nwg > 1 ? nwg - 1 : 1;
+  const int32_t stride = ntile_groups * kPlanThreads;
   int32_t carry = 0;
   if (wg == 0 && tid == 0) cu_tiles[0] = 0;
   for (int32_t base = 0; base < B; base += kPlanThreads) {
@@ -349,33 +423,51 @@ __device__ inline void plan_block(const PlanInput& in, int32_t wg, int32_t nwg, 
       sh.len[tid] = T;
       n = (T + kTile - 1) / kTile;
     }
-    const int32_t inc = plan_scan(n, sh);
+    int32_t inc = n, unused = 0, tot, tu;
+    plan_scan2(inc, unused, &tot, &tu, sh);
     sh.cu[tid + 1] = carry + inc;
     if (tid == 0) sh.cu[0] = carry;
     if (wg == 0 && tid < cnt) cu_tiles[b + 1] = carry + inc;
     __syncthreads();
     // tile t of this chunk belongs to the last local sequence j with cu[j] <= t
     // (sequences without tiles share their start with the next one)
-    const int32_t t_end = sh.cu[cnt];
-#pragma unroll 4
-    for (int32_t t = sh.cu[0] + wg * kPlanThreads + tid; t < t_end;
-         t += ntile_groups * kPlanThreads) {
-      int32_t lo = 0, hi = cnt - 1;
-      while (lo < hi) {
-        const int32_t mid = (lo + hi + 1) >> 1;
-        if (sh.cu[mid] <= t) lo = mid; else hi = mid - 1;
+    const int32_t t_end = carry + tot;
+    for (int32_t t4 = carry + wg * kPlanThreads + tid; t4 < t_end; t4 += 4 * stride) {
+      int32_t seq[4], tok[4], raw[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int32_t t = t4 + u * stride;
+        int32_t lo = 0;
+        if (t < t_end) {
+          int32_t hi = cnt - 1;
+          while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if (sh.cu[mid] <= t) lo = mid; else hi = mid - 1;
+          }
+        }
+        seq[u] = lo;
+        tok[u] = (t - sh.cu[lo]) * kTile;
       }
-      const int32_t T = sh.len[lo];
-      const int32_t t0 = (t - sh.cu[lo]) * kTile;
-      const int32_t nv = min(kTile, T - t0);
-      int32_t blk = -1, off = 0;
-      if (one_page) {
-        const int32_t raw = block_table[(int64_t)(base + lo) * max_blocks + t0 / P];
-        blk = raw < 0 ? 0 : (raw >= num_blocks ? num_blocks - 1 : raw);
-        off = t0 % P;
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        raw[u] = one_page && t4 + u * stride < t_end
+                     ? block_table[(int64_t)(base + seq[u]) * max_blocks + tok[u] / P]
+                     : 0;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int32_t t = t4 + u * stride;
+        if (t < t_end) {
+          const int32_t T = sh.len[seq[u]], t0 = tok[u];
+          const int32_t nv = min(kTile, T - t0);
+          int32_t blk = -1, off = 0;
+          if (one_page) {
+            blk = raw[u] < 0 ? 0 : (raw[u] >= num_blocks ? num_blocks - 1 : raw[u]);
+            off = t0 % P;
+          }
+          reinterpret_cast<int4*>(tiles)[t] =
+              make_int4(blk, base + seq[u], t0, tile_word(nv, t0 + kTile >= T, off));
+        }
       }
-      reinterpret_cast<int4*>(tiles)[t] =
-          make_int4(blk, base + lo, t0, tile_word(nv, t0 + kTile >= T, off));
     }
     carry = t_end;
     __syncthreads();
@@ -420,6 +512,16 @@ __device__ inline uint16_t f32_to_bf16_bits(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Four fp32 values -> four bf16 (round to nearest even) in 8 bytes, the first
+// in the low half of the first word: two packed conversions (v_cvt_pk_bf16_f32).
+__device__ inline uint2 pack_bf16x4(float a, float b, float c, float d) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t lo = __builtin_convertvector((f32x2_t{a, b}), bf16x2_t);
+  const bf16x2_t hi = __builtin_convertvector((f32x2_t{c, d}), bf16x2_t);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // OCP E4M3FN byte -> fp32 using the gfx950 hardware conversion.

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
             const int32_t k = k0b + u;
             v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (k < n && s_w[k] != 0.f) {
-              const float* src = a.part_o + (s_slot[k] * a.h + head) * d_c + d;
+              const float* src = static_cast<const float*>(a.part_o) + (s_slot[k] * a.h + head) * d_c + d;
               if (v4) {
                 v[u] = *reinterpret_cast<const float4*>(src);
               } else {
@@ -268,210 +268,94 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
   }
 }
 
-// The same merge over fragment-major partials (frag_offset; 512 latent values,
-// heads a multiple of 32), two variants.  Work group = (sequence, 32-head
-// block, 32-value latent block); a thread owns one 16-byte piece (4 latent
-// values of one head), so each wave reads 1 KiB contiguous per slot.
-//
-// For sequences that span many splits: slots are taken in chunks of 32; a
-// thread first issues the loads of its piece in every slot of the chunk, then
-// the chunk's weights are formed in LDS (running maximum per head across
-// chunks) while the loads are in flight.
+// The same merge over fragment-major bf16 partials (frag_offset; 512 latent
+// values, heads a multiple of 32).  Work group = (sequence, 32-head block,
+// 32-value latent block); a thread owns one 4-value piece (head 32 hblk + r,
+// latent 32 mdg + 8 jj + 4 g + 0..3), so each wave reads 512 B contiguous
+// per slot.  Two dependent memory round trips: the sequence's split range,
+// then, all in flight together, the pieces of up to kCombPass slots, their
+// LSEs and the split table entries that say whether a split owns tiles (one
+// that owns none wrote nothing: weight 0, and its stale piece is never
+// multiplied in).  Longer ranges take further passes with a running maximum.
 constexpr int kFragLat = 512;
-constexpr int kFragChunk = 32;
+constexpr int kCombPass = 16;
 
-__global__ __launch_bounds__(256) void combine_frag_chunk_kernel(AttnArgs a, float* __restrict__ o_lat) {
-  __shared__ float s_w[kFragChunk][32];
-  __shared__ int32_t s_own[kFragChunk];
-  __shared__ float s_red[8][32];
-  __shared__ float s_M[32], s_alpha[32];
+__global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __restrict__ o_lat) {
+  __shared__ float s_w[kCombPass][32];  // LSEs of the pass's slots, then their weights
+  __shared__ float s_M[32], s_W[32], s_alpha[32];
   const int32_t b = blockIdx.x, hblk = blockIdx.y, mdg = blockIdx.z;
   const int tid = threadIdx.x, jj = tid >> 6, lane = tid & 63;
   const int r = lane & 31;                 // head of this thread's piece
-  const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of this thread's weights
+  const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of the LSE loads
   const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
   float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * a.h + hblk * 32 + r) * kFragLat + d);
-  const int32_t first = load_ro(a.cu_tiles, b), last = load_ro(a.cu_tiles, b + 1) - 1;
-  if (last < first) {
+  const int2 range = *reinterpret_cast<const int2*>(a.seq_splits + 2 * b);
+  const int32_t g_lo = range.x, n_cand = range.y - range.x + 1;
+  if (n_cand <= 0) {  // no tokens
     *dst = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const int32_t g_lo = load_ro(a.seq_splits, 2 * b);
-  const int32_t n_cand = load_ro(a.seq_splits, 2 * b + 1) - g_lo + 1;
   const int64_t slot_stride = (int64_t)a.h * kFragLat;
-  const float* src = a.part_o + (int64_t)(g_lo + b) * slot_stride + frag_offset(hblk, mdg, jj, lane);
+  const uint16_t* src = static_cast<const uint16_t*>(a.part_o) + (int64_t)(g_lo + b) * slot_stride +
+                        frag_offset(hblk, mdg, jj, lane);
   const float* lse = a.part_lse + (int64_t)(g_lo + b) * a.h + hblk * 32 + wr;
-  if (tid < 32) s_M[tid] = -INFINITY;
-  float wsum = 0.f;
+  if (tid < 32) {
+    s_M[tid] = -INFINITY;
+    s_W[tid] = 0.f;
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int32_t c0 = 0; c0 < n_cand; c0 += kFragChunk) {
-    const int32_t n = min(kFragChunk, n_cand - c0);
-    // splits in the range that own no tile wrote nothing: weight 0
-    if (tid < kFragChunk) {
-      const int32_t gg = g_lo + c0 + tid;
-      s_own[tid] = tid < n && load_ro(a.split_first, gg) < load_ro(a.split_first, gg + 1);
-    }
-    __syncthreads();
-    float4 v[kFragChunk];
+  for (int32_t c0 = 0; c0 < n_cand; c0 += kCombPass) {
+    const int32_t n = min(kCombPass, n_cand - c0);  // uniform
+    uint2 v[kCombPass];
 #pragma unroll
-    for (int k = 0; k < kFragChunk; k++)
-      v[k] = s_own[k] ? *reinterpret_cast<const float4*>(src + (int64_t)(c0 + k) * slot_stride)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-    float l4[kFragChunk / 8];
-    float mc = -INFINITY;
+    for (int k = 0; k < kCombPass; k++)
+      v[k] = k < n ? *reinterpret_cast<const uint2*>(src + (int64_t)(c0 + k) * slot_stride)
+                   : make_uint2(0u, 0u);
 #pragma unroll
-    for (int u = 0; u < kFragChunk / 8; u++) {
+    for (int u = 0; u < kCombPass / 8; u++) {
       const int k = wk + 8 * u;
-      l4[u] = s_own[k] ? lse[(int64_t)(c0 + k) * a.h] : -INFINITY;
-      mc = fmaxf(mc, l4[u]);
-    }
-    s_red[wk][wr] = mc;
-    __syncthreads();
-    if (tid < 32) {
-      float m = s_red[0][tid];
-      for (int i = 1; i < 8; i++) m = fmaxf(m, s_red[i][tid]);
-      const float m_old = s_M[tid], m_new = fmaxf(m_old, m);
-      s_alpha[tid] = m_old == -INFINITY ? 0.f : expf(m_old - m_new);
-      s_M[tid] = m_new;
-    }
-    __syncthreads();
-    {
-      const float m = s_M[wr];
-      float ws = 0.f;
-#pragma unroll
-      for (int u = 0; u < kFragChunk / 8; u++) {
-        const float w = l4[u] == -INFINITY ? 0.f : expf(l4[u] - m);
-        s_w[wk + 8 * u][wr] = w;
-        ws += w;
+      if (k < n) {
+        const int32_t gg = g_lo + c0 + k;
+        const bool owns = load_ro(a.split_first, gg) < load_ro(a.split_first, gg + 1);
+        const float l = lse[(int64_t)(c0 + k) * a.h];
+        s_w[k][wr] = owns ? l : -INFINITY;
       }
-      wsum = wsum * s_alpha[wr] + ws;
+    }
+    __syncthreads();
+    if (tid < 32) {  // per head: running maximum, rescale factor and weights
+      const float m_old = s_M[tid];
+      float m = m_old;
+      for (int k = 0; k < n; k++) m = fmaxf(m, s_w[k][tid]);
+      const float al = m_old == -INFINITY ? 0.f : expf(m_old - m);
+      float W = s_W[tid] * al;
+      for (int k = 0; k < n; k++) {
+        const float l = s_w[k][tid];
+        const float w = l == -INFINITY ? 0.f : expf(l - m);
+        s_w[k][tid] = w;
+        W += w;
+      }
+      s_M[tid] = m;
+      s_W[tid] = W;
+      s_alpha[tid] = al;
     }
     __syncthreads();
     const float al = s_alpha[r];
-    acc.x *= al; acc.y *= al; acc.z *= al; acc.w *= al;
+    acc.x *= al;
+    acc.y *= al;
+    acc.z *= al;
+    acc.w *= al;
 #pragma unroll
-    for (int k = 0; k < kFragChunk; k++) {
-      const float w = s_w[k][r];
-      acc.x = fmaf(w, v[k].x, acc.x);
-      acc.y = fmaf(w, v[k].y, acc.y);
-      acc.z = fmaf(w, v[k].z, acc.z);
-      acc.w = fmaf(w, v[k].w, acc.w);
-    }
-    __syncthreads();
-  }
-  s_red[wk][wr] = wsum;
-  __syncthreads();
-  float W = 0.f;
-  for (int i = 0; i < 8; i++) W += s_red[i][r];
-  const float inv = W > 0.f ? 1.f / W : 0.f;
-  *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-}
-
-// For sequences that span few splits (many work groups, few slots each): a
-// thread holds at most 12 slots' pieces, which keeps registers and so
-// occupancy high.  It issues their loads first; while they are in flight the
-// work group forms, per head, the largest LSE over all slots and the sum of
-// exp(lse - largest) in one read of the LSEs, then the weights in LDS.
-constexpr int kCombPer = 12;  // slots per pass
-
-__global__ __launch_bounds__(256) void combine_frag_few_kernel(AttnArgs a, float* __restrict__ o_lat) {
-  constexpr int NPH = 8;  // slot phases of the LSE work
-  __shared__ float s_w[kCombPer][32];  // LSE of the pass's slots, then their weights
-  __shared__ float s_red[2][NPH][32];
-  __shared__ float s_M[32], s_W[32];
-  const int32_t b = blockIdx.x, hblk = blockIdx.y, mdg = blockIdx.z;
-  const int tid = threadIdx.x, jj = tid >> 6, lane = tid & 63;
-  const int r = lane & 31;                 // head of this thread's piece
-  const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of the LSE work
-  const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
-  float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * a.h + hblk * 32 + r) * kFragLat + d);
-  const int32_t first = load_ro(a.cu_tiles, b), last = load_ro(a.cu_tiles, b + 1) - 1;
-  if (last < first) {
-    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
-  const int32_t g_lo = load_ro(a.seq_splits, 2 * b);
-  const int32_t n_cand = load_ro(a.seq_splits, 2 * b + 1) - g_lo + 1;
-  // splits that own no tile wrote nothing and get weight 0
-  auto owns = [&](int32_t k) {
-    return load_ro(a.split_first, g_lo + k) < load_ro(a.split_first, g_lo + k + 1);
-  };
-  const int64_t slot_stride = (int64_t)a.h * kFragLat;
-  const float* src = a.part_o + (int64_t)(g_lo + b) * slot_stride + frag_offset(hblk, mdg, jj, lane);
-  const float* lse = a.part_lse + (int64_t)(g_lo + b) * a.h + hblk * 32 + wr;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int32_t c0 = 0; c0 < n_cand; c0 += kCombPer) {
-    // the pass's slots (the condition is uniform); slots that own no tile
-    // hold no data and get weight 0
-    float4 v[kCombPer];
-#pragma unroll
-    for (int i = 0; i < kCombPer; i++) {
-      const int32_t k = c0 + i;
-      v[i] = k < n_cand ? *reinterpret_cast<const float4*>(src + (int64_t)k * slot_stride)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    {
-#pragma unroll
-      for (int i = 0; i < kCombPer; i++)
-        if (c0 + i < n_cand && !owns(c0 + i)) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (c0 == 0) {
-      // per head: the largest LSE over all slots and the sum of
-      // exp(lse - largest), online per slot phase, then merged; the first
-      // pass's LSEs stay in LDS
-      float mx = -INFINITY, sum = 0.f;
-      for (int32_t k = wk; k < n_cand; k += NPH) {
-        const float l = owns(k) ? lse[(int64_t)k * a.h] : -INFINITY;
-        if (k < kCombPer) s_w[k][wr] = l;
-        if (l > mx) {
-          sum = sum * expf(mx - l) + 1.f;  // exp(-inf) = 0 for the first one
-          mx = l;
-        } else if (l != -INFINITY) {
-          sum += expf(l - mx);
-        }
+    for (int k = 0; k < kCombPass; k++) {
+      if (k < n) {
+        const float w = s_w[k][r];
+        const float x0 = __uint_as_float(v[k].x << 16), x1 = __uint_as_float(v[k].x & 0xffff0000u);
+        const float x2 = __uint_as_float(v[k].y << 16), x3 = __uint_as_float(v[k].y & 0xffff0000u);
+        // a split without tiles has weight 0 and an undefined piece: selected out
+        acc.x += w != 0.f ? w * x0 : 0.f;
+        acc.y += w != 0.f ? w * x1 : 0.f;
+        acc.z += w != 0.f ? w * x2 : 0.f;
+        acc.w += w != 0.f ? w * x3 : 0.f;
       }
-      s_red[0][wk][wr] = mx;
-      s_red[1][wk][wr] = sum;
-      __syncthreads();
-      if (tid < 32) {
-        float m = -INFINITY;
-        for (int i = 0; i < NPH; i++) m = fmaxf(m, s_red[0][i][tid]);
-        float W = 0.f;
-        for (int i = 0; i < NPH; i++) {
-          const float mi = s_red[0][i][tid];
-          if (mi != -INFINITY) W += s_red[1][i][tid] * expf(mi - m);
-        }
-        s_M[tid] = m;
-        s_W[tid] = W;
-      }
-      __syncthreads();
-      for (int i = tid; i < kCombPer * 32; i += 256) {
-        const int32_t k = i >> 5;
-        const int hh = i & 31;
-        const float l = k < n_cand ? s_w[k][hh] : -INFINITY;
-        s_w[k][hh] = l == -INFINITY ? 0.f : expf(l - s_M[hh]);
-      }
-    } else {
-      // a later pass's weights (0 past the end and for slots that own no tile)
-      for (int i = tid; i < kCombPer * 32; i += 256) {
-        const int32_t k = c0 + (i >> 5);
-        const int hh = i & 31;
-        float w = 0.f;
-        if (k < n_cand && owns(k)) {
-          const float l = a.part_lse[(int64_t)(g_lo + b + k) * a.h + hblk * 32 + hh];
-          w = l == -INFINITY ? 0.f : expf(l - s_M[hh]);
-        }
-        s_w[i >> 5][hh] = w;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kCombPer; i++) {
-      const float w = s_w[i][r];
-      acc.x = fmaf(w, v[i].x, acc.x);
-      acc.y = fmaf(w, v[i].y, acc.y);
-      acc.z = fmaf(w, v[i].z, acc.z);
-      acc.w = fmaf(w, v[i].w, acc.w);
     }
     __syncthreads();
   }
@@ -483,12 +367,8 @@ __global__ __launch_bounds__(256) void combine_frag_few_kernel(AttnArgs a, float
 hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s) {
   if (a.frag_layout) {
     if (a.d_c != kFragLat || a.h % 32 || a.streams != 1) return hipErrorInvalidValue;
-    // chunked merge when sequences span four or more splits on average
-    const dim3 grid(a.B, a.h / 32, kFragLat / 32);
-    if (a.splits >= 4 * a.B)
-      hipLaunchKernelGGL(combine_frag_chunk_kernel, grid, dim3(256), 0, s, a, o_lat);
-    else
-      hipLaunchKernelGGL(combine_frag_few_kernel, grid, dim3(256), 0, s, a, o_lat);
+    hipLaunchKernelGGL(combine_frag_kernel, dim3(a.B, a.h / 32, kFragLat / 32), dim3(256), 0, s, a,
+                       o_lat);
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3(a.B, a.h), dim3(kCombThreads), 0, s, a, o_lat);
   }

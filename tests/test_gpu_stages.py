@@ -3,8 +3,8 @@ attention (mla_attend_partial) followed by the log-sum-exp merge (mla_combine)
 is mla_attend_latent bit for bit, and with the up-projection it is mla_decode
 bit for bit; a merge over a single split returns the split's partial
 unchanged; the generic kernel, serving misaligned pools of a matrix-core
-shape, writes the partials in the same fragment-major layout and the step
-still meets the oracle."""
+shape, writes the partials in the same bf16 fragment-major layout and the
+step still meets the oracle."""
 import sys
 
 import numpy as np
@@ -92,8 +92,8 @@ def _fragment_partial(block, h, dc):
 @pytest.mark.parametrize("case", ["dsv3_bf16", "tiny_fp32"])
 def test_single_split_combine_returns_the_partial(case):
     """A sequence that one split holds whole gets that split's partial back
-    bit for bit; the partial is read at the offsets mla_partials_layout gives
-    and un-permuted from the fragment layout it states."""
+    bit for bit; the partial is read at the offsets mla_partials_layout gives,
+    in the type (bf16 or fp32) and layout it states."""
     cfg = CASES[case].replace(batch=8)
     _say(f"single split {case}")
     inp = generate(cfg)
@@ -106,7 +106,10 @@ def test_single_split_combine_returns_the_partial(case):
     tiles = [(int(t) + 31) // 32 for t in inp.seq_lens]
     _, seq = _lib.mla_split_plan(tiles, splits)
     h, dc = cfg.heads, cfg.d_latent
-    part = ws[off_o: off_o + slots * h * dc * 4].view(torch.float32).cpu().numpy()
+    if frag:   # bf16 pieces, widened exactly
+        part = ws[off_o: off_o + slots * h * dc * 2].view(torch.bfloat16).float().cpu().numpy()
+    else:
+        part = ws[off_o: off_o + slots * h * dc * 4].view(torch.float32).cpu().numpy()
     part = part.reshape(slots, h * dc)
     got = olat.cpu().numpy()
     whole = 0
