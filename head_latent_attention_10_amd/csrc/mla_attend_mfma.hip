@@ -189,11 +189,11 @@ struct Loader {
   int32_t n;           // steps of the split
   bool newer_issued;   // the batch after the awaited one was issued
 
+  // Issue the loads of step `next`, described by d.
   __device__ void issue_next(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
-                             int lane, bool from_table = false) {
+                             int lane, const Tile& d) {
     if (lw == 0 && next >= kWin + 4 && next % kWin == 4 && next + kWin - 4 < n)
       load_window(a, win, t_begin, t_begin + n, next / kWin + 1, lane);
-    const Tile d = from_table ? global_tile(a, t_begin + next) : read_tile(win, next);
     issue_step<NL, SP>(a, ring + (next % kStages) * kStage, d, lw, lane);
     next++;
   }
@@ -202,9 +202,15 @@ struct Loader {
                         int lw, int lane) {
     next = 0;
     n = steps;
-    for (int s = 0; s < 2 && next < n; s++) issue_next(a, ring, win, t_begin, lw, lane, true);
+    for (int s = 0; s < 2 && next < n; s++)
+      issue_next(a, ring, win, t_begin, lw, lane, global_tile(a, t_begin + next));
     newer_issued = next == 2;
   }
+  // The descriptor of the next step to load, read from the window in step
+  // i right after its barrier: reading it early lets the loads be issued
+  // later in the step without waiting for the LDS reads issued in between
+  // (the LDS counter retires in order).
+  __device__ Tile peek(const lds_t* win) const { return next < n ? read_tile(win, next) : Tile{}; }
   // Wait for this wave's loads of step i.  What may stay in flight: the batch
   // of step i+1 and sb groups of KS partial-output stores issued after the
   // awaited batch (the hardware counter retires in issue order).  The counts
@@ -226,15 +232,19 @@ struct Loader {
       else wait_vmcnt<D2>();
     }
   }
-  // In step i: issue step i+2.
+  // In step i: issue step i+2, described by d (peek, read after the barrier of step i).
   __device__ void issue_ahead(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
-                              int lane) {
+                              int lane, const Tile& d) {
     if (next < n) {
-      issue_next(a, ring, win, t_begin, lw, lane);
+      issue_next(a, ring, win, t_begin, lw, lane, d);
       newer_issued = true;
     } else {
       newer_issued = false;
     }
+  }
+  __device__ void issue_ahead(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
+                              int lane) {
+    issue_ahead(a, ring, win, t_begin, lw, lane, peek(win));
   }
 };
 
@@ -580,15 +590,22 @@ void attend_mfma_kernel(AttnArgs a) {
 //    partial scores of step j - 1, run the online softmax and publish the bf16
 //    weights.
 //  * w2, w3, w6, w7: value waves v = 0..3, latent rows 128 v .. 128 v + 127 of
-//    both head blocks, and the four loader waves.  Each reads its latent
-//    fragments of tile j with the transposing LDS read in step j (the tile is
-//    then free for the loads of step j + 3) and consumes them in step j + 2,
-//    with the weights of that step; every fragment feeds two MFMAs.  The
-//    weights are read first in a step, so its products wait only for them.
+//    both head blocks.  Each reads its latent fragments of tile j with the
+//    transposing LDS read in step j (the tile is then free for the loads of
+//    step j + 3) and consumes them in step j + 2, with the weights of that
+//    step; every fragment feeds two MFMAs.  The weights are read first in a
+//    step, so its products wait only for them.
+//  * Loaders: w2, w3 (loader lanes 0, 1) and w4, w5 (2, 3), nine 1 KiB loads
+//    each per step.  A compute unit accepts about one such load per 20 clocks,
+//    so a wave that issues them stalls for most of that time: the two value
+//    waves that load issue theirs after their products (w6 and w7, the
+//    second value wave of each value SIMD, finish later and issue none), and
+//    the softmax waves, which have time to spare, right after the barrier.
 //
 // Step j (one barrier): loaders wait for their loads of step j; barrier;
-// loaders issue step j + 2 into the stage tile j - 1 used; score waves S(j);
-// softmax waves softmax(j - 1); value waves O += C(j-2) P(j-2) and read C(j).
+// softmax waves issue their part of step j + 2 into the stage tile j - 1 used,
+// then softmax(j - 1); score waves S(j); value waves O += C(j-2) P(j-2) and
+// read C(j), then w2 and w3 issue their part of step j + 2.
 // Partial scores, weights, rescale factors and 1/l are double-buffered by
 // step parity; the barrier of a step orders what the previous step published.
 constexpr int kKs64 = 18;                         // k-steps per key part
@@ -706,11 +723,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     // ================================================================ softmax + loader waves
     const int hb = wave - 4;
     const int32_t head = hg * 64 + hb * 32 + (lane & 31);
+    // loader lanes 2 and 3; a segment end adds one store (the LSE) after the
+    // loads of its step
+    Loader<4, SP> ld;
+    ld.start(a, ring, win, t_begin, n, 2 + hb, lane);
+    int sb1 = 0, sb2 = 0;
     wg_barrier();
     float m_run = -INFINITY, l_run = 0.f;
     int32_t seg_step = 0;
     for (int32_t j = 0; j <= n + 1; j++) {
+      ld.template wait_current<1>(sb1 + sb2);
       wg_barrier();
+      ld.issue_ahead(a, ring, win, t_begin, 2 + hb, lane);
+      int sb = 0;
       if (j >= 1 && j <= n) {
         const int par = (j - 1) & 1;
         const Tile pv = read_tile(win, j - 1);
@@ -788,8 +813,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
           m_run = -INFINITY;
           l_run = 0.f;
           seg_step = 0;
+          sb = 1;
         }
       }
+      sb2 = sb1;
+      sb1 = sb;
     }
   } else {
     // ================================================================ value waves
@@ -821,18 +849,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
       asm volatile("" : "+s"(off));
       return ring + off;
     };
-    // the value waves are the four loader waves: every step they wait for
-    // their loads of that step before its barrier and then issue the loads
-    // two steps ahead; a segment end adds one group of kVStores stores
+    // w2 and w3 are loader lanes 0 and 1: every step they wait for their
+    // loads of that step before its barrier and issue the loads two steps
+    // ahead after their products; a segment end adds one group of kVStores
+    // stores after those loads
     constexpr int kVStores = 2 * MD * 4;
+    const bool loader = v < 2;
     Loader<4, SP> ld;
-    ld.start(a, ring, win, t_begin, n, v, lane);
+    if (loader) ld.start(a, ring, win, t_begin, n, v, lane);
     int sb1 = 0, sb2 = 0;  // partial-store groups issued in the previous two steps
     wg_barrier();
     // steps 0 and 1: fragments only
-    ld.template wait_current<kVStores>(0);
+    if (loader) ld.template wait_current<kVStores>(0);
     wg_barrier();
-    ld.issue_ahead(a, ring, win, t_begin, v, lane);
+    if (loader) ld.issue_ahead(a, ring, win, t_begin, v, lane);
     {
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -841,9 +871,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) cb[0][md][kk] = ld_c(stage_of(0), ln, md, kk);
     }
-    ld.template wait_current<kVStores>(0);
+    if (loader) ld.template wait_current<kVStores>(0);
     wg_barrier();
-    ld.issue_ahead(a, ring, win, t_begin, v, lane);
+    if (loader) ld.issue_ahead(a, ring, win, t_begin, v, lane);
     if (n > 1) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -858,9 +888,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     // step j >= 2: O += C(j-2) P(j-2), then the fragments of step j
     auto step = [&](auto slot_c, int32_t j) __attribute__((always_inline)) {
       constexpr int SL = decltype(slot_c)::value;  // j % 2, also the parity of step j - 2
-      ld.template wait_current<kVStores>(sb1 + sb2);
+      if (loader) ld.template wait_current<kVStores>(sb1 + sb2);
       wg_barrier();
-      ld.issue_ahead(a, ring, win, t_begin, v, lane);
       const bool load = j < n;
       const lds_t* st = stage_of(j);
       int ln = lane;
@@ -874,7 +903,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
         for (int kk = 0; kk < 2; kk++)
           pf[hb][kk] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
               pbuf + SL * kP64 + hb * kPBytes + (kk * 64 + lane) * 16);
-      if (__builtin_amdgcn_readfirstlane(s_flag[SL * 2] | s_flag[SL * 2 + 1])) {
+      const int flag = s_flag[SL * 2] | s_flag[SL * 2 + 1];
+      // the descriptor of the loads issued after the products, read with the
+      // weights (one LDS round trip before the first product)
+      const Tile nd = loader ? ld.peek(win) : Tile{};
+      if (__builtin_amdgcn_readfirstlane(flag)) {
         const float a0 = s_alpha[(SL * 2) * 32 + (lane & 31)];
         const float a1 = s_alpha[(SL * 2 + 1) * 32 + (lane & 31)];
 #pragma unroll
@@ -900,6 +933,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
         // keep the reads behind the products that free their registers
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (loader) ld.issue_ahead(a, ring, win, t_begin, v, lane, nd);
       const Tile pv = read_tile(win, j - 2);
       int sb = 0;
       if (pv.last || j - 2 == n - 1) {
