@@ -50,6 +50,20 @@ def attn_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def measured_counters(workload: str):
+    """The committed rocprofv3 counter summary of the attention kernel on
+    `workload` (profiles/attend_<workload>_counters.json), if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != attn_source_hash():
+        return None
+    return rec
+
+
 def measured_traffic(workload: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
@@ -123,6 +137,19 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
     torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg = sum(attn_ms) / len(attn_ms)
+    # per-step spread: the same steps once more, each between two events
+    sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
+    for a, b in sevs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        sevs[k][0].record(stream)
+        step(warmup + k)
+        sevs[k][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in sevs]
     cache_bytes = inp.cache_bytes()
     ms_per_step = total_ms / steps
     return {
@@ -132,6 +159,8 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
         "tokens_per_s": cfg.batch / (ms_per_step * 1e-3),
         "attn_ms": attn_avg,
         "attn_ms_min": min(attn_ms),
+        "attn_ms_pct": percentiles(attn_ms),
+        "step_ms_pct": percentiles(step_ms),
         "cache_bytes": cache_bytes,
         "attn_gbps": cache_bytes / (attn_avg * 1e-3) / 1e9,
         "step_cache_gbps": cache_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -139,6 +168,52 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
         "copies": copies,
         "inp": inp,
     }
+
+
+def percentiles(xs):
+    """Median, 10th and 90th percentile (ms) of per-call times."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def copy_bandwidth(mib: int = 1024, reps: int = 10):
+    """A plain device-to-device copy of `mib` MiB, timed with events over
+    `reps` copies: (read + written bytes) / time in GB/s, the median call."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del src, dst
+    times.sort()
+    ms = times[len(times) // 2]
+    return {"GBps": round(2 * n / (ms * 1e-3) / 1e9, 1), "bytes": 2 * n, "ms_median": round(ms, 4),
+            "how": f"torch copy_ of {mib} MiB device to device, median of {reps}, read + write bytes"}
+
+
+def host_cpu():
+    """(logical CPUs, CPU model) of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
 
 
 def cpu_baseline(inp, seconds: float):
@@ -170,8 +245,10 @@ def cpu_baseline(inp, seconds: float):
     t_full = elapsed * work_full / max(work_done, 1)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
+    nproc, model = host_cpu()
     return {
         "value": cfg.batch / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "threads": threads, "nproc": nproc, "cpu_model": model,
         "sample": (f"{pairs} (sequence, head) pairs in order over {passes} pass(es) of the "
                    f"step ({work_done} token-heads; one step is {work_full}) in {elapsed:.1f} s, "
                    f"fp64 numpy oracle, scaled by token-heads to one step"),
@@ -530,37 +607,91 @@ def measure_prefill(spec: str, steps: int, warmup: int):
             "workspace_bytes": n}
 
 
+def kernel_class(name: str):
+    """The decode-step stage a rocprofv3 kernel name belongs to (None: other)."""
+    for key, cls in (("attend64_kernel", "attention"), ("attend_mfma_kernel", "attention"),
+                     ("attend_fp8_kernel", "attention"), ("attend_simt_kernel", "attention"),
+                     ("absorb", "absorb"), ("combine", "combine"), ("up_project", "up_project"),
+                     ("plan_kernel", "plan"), ("copyBuffer", "copy")):
+        if key in name:
+            return cls
+    return None
+
+
 def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: int, commands):
-    """HBM bytes per attention launch from two rocprofv3 --pmc runs of
-    `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB
-    per dispatch).  Each counter is scaled by what it reads for the plain copy
-    of copy_mb MiB in the same run (the largest copy dispatch)."""
+    """HBM bytes per launch of every stage of the decode step from two
+    rocprofv3 --pmc runs of `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by what it reads
+    for the plain copy of copy_mb MiB that ends the run (its last copy
+    dispatch); the attention launch's bytes go to hbm_bytes_per_launch."""
     import statistics
 
     out = {}
     for name, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(directory) if r[2] == name]
-        attn = [v for _, k, _, v in rows if "attend_mfma_kernel" in k]
-        copies = [(v, d) for d, k, _, v in rows if "copyBuffer" in k]
-        if not attn or not copies:
-            raise SystemExit(f"{name}: attention or copy dispatches missing")
-        copy_kib = max(copies)[0]
+        copies = [(d, v) for d, k, _, v in rows if kernel_class(k) == "copy"]
+        if not copies:
+            raise SystemExit(f"{name}: copy dispatch missing")
+        copy_kib = max(copies)[1]   # the calibration copy is the run's last dispatch
         factor = copy_mb * 1024.0 / copy_kib
-        out[name] = {"attention_kib_median": statistics.median(attn), "dispatches": len(attn),
-                     "copy_kib": copy_kib, "factor": factor,
-                     "bytes_per_launch": statistics.median(attn) * 1024.0 * factor}
+        per = {}
+        for cls in ("attention", "absorb", "combine", "up_project", "plan"):
+            vals = [v for _, k, _, v in rows if kernel_class(k) == cls]
+            if vals:
+                per[cls] = {"kib_median": statistics.median(vals), "dispatches": len(vals),
+                            "bytes_per_launch": round(statistics.median(vals) * 1024.0 * factor)}
+        if "attention" not in per:
+            raise SystemExit(f"{name}: attention dispatches missing")
+        out[name] = {"copy_kib": copy_kib, "factor": factor, "kernels": per}
+    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    step = {cls: fetch["kernels"].get(cls, {}).get("bytes_per_launch", 0) +
+            write["kernels"].get(cls, {}).get("bytes_per_launch", 0)
+            for cls in set(fetch["kernels"]) | set(write["kernels"])}
     rec = {
         "workload": workload,
-        "kernel": "attend_mfma_kernel",
         "kernel_source_sha256_16": attn_source_hash(),
         "copy_calibration_mib": copy_mb,
-        "fetch": out["FETCH_SIZE"],
-        "write": out["WRITE_SIZE"],
-        "hbm_bytes_per_launch": round(out["FETCH_SIZE"]["bytes_per_launch"] +
-                                      out["WRITE_SIZE"]["bytes_per_launch"]),
+        "fetch": fetch,
+        "write": write,
+        "hbm_bytes_per_launch": step["attention"],
+        "hbm_bytes_per_step_by_stage": step,
+        "hbm_bytes_per_step": sum(step.values()),
         "commands": commands,
     }
     path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def summarize_counters(workload: str, dirs, commands):
+    """Median per dispatch of every counter in rocprofv3 --pmc runs of this
+    script (`dirs`), per decode-step stage, into
+    profiles/attend_<workload>_counters.json.  MfmaUtil (rocprofv3's
+    SQ_VALU_MFMA_BUSY_CYCLES summed over SIMDs / (GRBM_GUI_ACTIVE x SIMDs), in
+    percent) becomes mfma_util, a fraction, for the attention kernel."""
+    import statistics
+
+    rows = []
+    for d in dirs:
+        rows += _counter_rows(d)
+    per = {}
+    for _, k, c, v in rows:
+        cls = kernel_class(k)
+        if cls and cls != "copy":
+            per.setdefault(cls, {}).setdefault(c, []).append(v)
+    stages = {cls: {c: statistics.median(vs) for c, vs in cs.items()} for cls, cs in per.items()}
+    if "attention" not in stages:
+        raise SystemExit("no attention dispatches in the counter runs")
+    att = stages["attention"]
+    rec = {
+        "workload": workload,
+        "kernel_source_sha256_16": attn_source_hash(),
+        "mfma_util": round(att["MfmaUtil"] / 100.0, 4) if "MfmaUtil" in att else None,
+        "stages": stages,
+        "commands": commands,
+    }
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_counters.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -602,6 +733,9 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/attend_<workload>_traffic.json from two rocprofv3 --pmc "
                          "runs (FETCH_SIZE, WRITE_SIZE) of this script; no GPU needed")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="write profiles/attend_<workload>_counters.json from rocprofv3 --pmc runs "
+                         "of this script (one directory per run); no GPU needed")
     ap.add_argument("--profile-command", action="append", default=[],
                     help="command line recorded with --summarize-traffic (repeatable)")
     args = ap.parse_args()
@@ -609,6 +743,9 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(args.workload, args.summarize_traffic[0], args.summarize_traffic[1],
                           args.calibrate_copy_mb, args.profile_command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.workload, args.summarize_counters, args.profile_command)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -652,7 +789,9 @@ def main():
         r = measure(w, max(10, args.steps // 2), max(3, args.warmup // 2), args.num_splits)
         extra[w] = {"tokens_per_s": round(r["tokens_per_s"], 1),
                     "ms_per_step": round(r["ms_per_step"], 4),
+                    "ms_per_step_pct": r["step_ms_pct"],
                     "attn_kernel_ms": round(r["attn_ms"], 4),
+                    "attn_kernel_ms_pct": r["attn_ms_pct"],
                     "attn_cache_GBps": round(r["attn_gbps"], 1),
                     "attn_frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4)}
         del r
@@ -672,17 +811,10 @@ def main():
     for w in [w for w in args.prefill.split(",") if w]:
         extra[f"prefill_dsv3_{w.replace(':', '_')}"] = measure_prefill(w, 5, 2)
 
-    if args.calibrate_copy_mb > 0:
-        n = args.calibrate_copy_mb << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     cfg = main_run["cfg"]
     traffic = measured_traffic(args.workload)
+    counters = measured_counters(args.workload)
+    copy = copy_bandwidth()
     roofline = {
         "bound": "hbm",
         "achieved": round(main_run["attn_gbps"], 1),
@@ -690,10 +822,29 @@ def main():
         "unit": "GB/s",
         "frac": round(main_run["attn_gbps"] / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
-        "kernel": "attend_mfma_kernel",
+        "kernel": "attend64_kernel" if cfg.heads % 64 == 0 else "attend_mfma_kernel<1>",
         "algorithmic_bytes_per_launch": main_run["cache_bytes"],
         "kernel_ms": round(main_run["attn_ms"], 4),
+        "kernel_ms_pct": main_run["attn_ms_pct"],
+        # a second denominator: what a plain copy reaches on this GPU in this run
+        "copy_GBps": copy["GBps"],
+        "frac_of_copy": round(main_run["attn_gbps"] / copy["GBps"], 4),
+        "copy": copy,
+        # matrix-core busy share of the kernel (SQ_VALU_MFMA_BUSY_CYCLES over
+        # every SIMD's active cycles) from the committed counter run, if taken
+        # on this kernel source
+        "mfma_util": counters.get("mfma_util") if counters else None,
     }
+    if args.calibrate_copy_mb > 0:
+        # the last copy dispatch of the run: a plain copy of known size that
+        # scales the byte counters of a rocprofv3 --pmc run
+        n = args.calibrate_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(main_run["inp"], args.cpu_seconds)
@@ -705,6 +856,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(main_run["ms_per_step"], 4),
+        "ms_per_step_pct": main_run["step_ms_pct"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
