@@ -69,6 +69,14 @@ __device__ inline void dma16s(const void* sbase, uint32_t voff, uint32_t m0) {
                : "memory");
 }
 
+// One 4-byte-per-lane direct global->LDS load (lane l writes lds + 4 l), for
+// the lanes active at the call.
+__device__ inline void dma4(const void* g, lds_t* l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0)
+               : "memory");
+}
+
 template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
