@@ -5,12 +5,14 @@
 // values per token, heads a multiple of 32, bf16 absorbed query.
 //
 // The work decomposition, split plan, tile descriptors and head groups are
-// those of the bf16 kernel (mla_attend_mfma.hip).  The step schedule is not:
-// this kernel takes two work-group barriers per step (one when the step's tile
-// is in LDS, one after the softmax wave has published the weights, after which
-// the value waves run the value product of that same step), where the bf16
-// kernel takes one and runs its value product two steps behind.  What else
-// differs is how the 8-bit latent tile is consumed:
+// those of the bf16 kernels (mla_attend_mfma.hip).  Two schedules:
+//  * attend64_fp8_kernel (64-head work groups, dense tables): the pipelined
+//    schedule of the bf16 64-head kernel, described above it.
+//  * attend_fp8_kernel (32-head work groups, and index lists): two work-group
+//    barriers per step (one when the step's tile is in LDS, one after the
+//    softmax wave has published the weights, after which the value waves run
+//    the value product of that same step).
+// Both consume the 8-bit latent tile the same way:
 //
 //  * Scores.  S^T[t, i] = scale_t * sum_d e4m3[t, d] q[i, d] + rope term.  The
 //    latent part runs on the fp8 matrix core (32x32x64, both operands E4M3):
@@ -26,15 +28,14 @@
 //    8-bit transposing LDS read (8 tokens of one latent column per lane) and
 //    widened to bf16 exactly (every E4M3 value is a bf16 value), feeding the
 //    bf16 matrix core.
-//  * The per-token scales of a step are loaded from global memory by the
-//    softmax waves at the end of the previous step and used after the score
-//    products (these waves issue no direct-to-LDS loads, so the wait for the
-//    scales never waits for the tile prefetch); the kh = 1 waves hand over
-//    their latent and rope partial scores separately and the softmax wave
-//    applies the scales.
+//  * The per-token scales multiply the latent part of the score only, so the
+//    latent and rope partial scores are handed to the softmax wave separately
+//    and it applies the scales.  attend_fp8_kernel's softmax waves load the
+//    scales from global memory one step ahead; attend64_fp8_kernel loads them
+//    into the tile's LDS stage together with the tile.
 //
-// LDS ring: six stages of 32 latent rows of 512 B plus 32 rope rows of 128 B
-// (20 KiB), loaded four steps ahead.  The 16-byte chunk index of a latent row
+// LDS ring of attend_fp8_kernel: six stages of 32 latent rows of 512 B plus 32
+// rope rows of 128 B (20 KiB), loaded four steps ahead.  The 16-byte chunk index of a latent row
 // is XOR-swizzled with a permutation of the row's low four bits chosen so that
 // the 16-row reads of the score product and the 8-row transposing reads of the
 // value product both spread over the 64 banks.
