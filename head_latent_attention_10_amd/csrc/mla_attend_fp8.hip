@@ -444,16 +444,23 @@ void attend_fp8_kernel(AttnArgs a) {
           m_run = m_new;
         }
         const float mref = m_run == -INFINITY ? 0.f : m_run;
-        // weights p (normaliser) and p * scale_t (value product operand, bf16)
+        // weights p * scale_t rounded to bf16 (the value product's operand);
+        // the normaliser sums the weights that product consumes, those bf16
+        // values divided by scale_t (p where the scale is 0), so that their
+        // rounding cancels in the normalised output as in the bf16 path
         uint32_t pk[8];
         float lsum = 0.f;
 #pragma unroll
         for (int q = 0; q < 8; q++) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q], sm, -mref));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + 1], sm, -mref));
-          lsum += p0 + p1;
-          const f32x2 e = {p0 * sc[2 * q], p1 * sc[2 * q + 1]};
-          pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(e, bf16x2));
+          const float c0 = sc[2 * q], c1 = sc[2 * q + 1];
+          const f32x2 e = {p0 * c0, p1 * c1};
+          const bf16x2 pr = __builtin_convertvector(e, bf16x2);
+          pk[q] = __builtin_bit_cast(uint32_t, pr);
+          const f32x2 back = __builtin_convertvector(pr, f32x2);
+          lsum += (c0 != 0.f ? back[0] * __builtin_amdgcn_rcpf(c0) : p0) +
+                  (c1 != 0.f ? back[1] * __builtin_amdgcn_rcpf(c1) : p1);
         }
         l_run += lsum;
         *reinterpret_cast<u32x4 __attribute__((address_space(3)))*>(pb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
@@ -925,16 +932,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
           m_run = m_new;
         }
         const float mref = m_run == -INFINITY ? 0.f : m_run;
-        // weights p (normaliser) and p * scale_t (value product operand, bf16)
+        // weights p * scale_t rounded to bf16 (the value product's operand);
+        // the normaliser sums the weights that product consumes, those bf16
+        // values divided by scale_t (p where the scale is 0), so that their
+        // rounding cancels in the normalised output as in the bf16 path
         uint32_t pk[8];
         float lsum = 0.f;
 #pragma unroll
         for (int q = 0; q < 8; q++) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q], sm, -mref));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + 1], sm, -mref));
-          lsum += p0 + p1;
-          const f32x2 e = {p0 * sc[2 * q], p1 * sc[2 * q + 1]};
-          pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(e, bf16x2));
+          const float c0 = sc[2 * q], c1 = sc[2 * q + 1];
+          const f32x2 e = {p0 * c0, p1 * c1};
+          const bf16x2 pr = __builtin_convertvector(e, bf16x2);
+          pk[q] = __builtin_bit_cast(uint32_t, pr);
+          const f32x2 back = __builtin_convertvector(pr, f32x2);
+          lsum += (c0 != 0.f ? back[0] * __builtin_amdgcn_rcpf(c0) : p0) +
+                  (c1 != 0.f ? back[1] * __builtin_amdgcn_rcpf(c1) : p1);
         }
         l_run += lsum;
         lds_t* pb = pbuf + par * kPF + hb * kP8Bytes + lane * 16;
