@@ -579,32 +579,43 @@ def measure_prefill(spec: str, steps: int, warmup: int):
     ql = to_device_array(pi.q_lens, dev.device)
     p = dev.params()
     n = _lib.mla_prefill_workspace_size(p)
-    ws = torch.empty(n, dtype=torch.uint8, device=dev.device)
+    unit = _lib.prefill_unit_bytes(dev.max_blocks_per_seq, cfg.page_size)
     out = torch.empty((B, L, cfg.heads, cfg.d_v), dtype=out_torch_dtype(cfg.out_dtype),
                       device=dev.device)
     stream = torch.cuda.current_stream()
 
-    def step():
-        _lib.mla_prefill(p, L, q, ql, dev.c_kv, dev.c_kv_scale, dev.k_rope, dev.block_table,
-                         dev.seq_lens,
-                         dev.W_UK, dev.W_UV, out, ws, n, stream)
+    def timed(nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev.device)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        step()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+        def step():
+            _lib.mla_prefill(p, L, q, ql, dev.c_kv, dev.c_kv_scale, dev.k_rope, dev.block_table,
+                             dev.seq_lens, dev.W_UK, dev.W_UV, out, ws, nbytes, stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        del ws
+        return a.elapsed_time(b) / steps
+
+    # the default workspace (the call in chunks of (sequence, head) units once
+    # every unit's keys and values pass its size), then one holding them all
+    ms = timed(n)
+    units = B * cfg.heads
+    ms_one_pass = timed(units * unit) if units * unit != n else ms
     dec, att = prefill_flops(pi.seq_lens, pi.q_lens, cfg.heads)
     return {"ms_per_call": round(ms, 4), "new_tokens_per_s": round(B * L / (ms * 1e-3), 1),
             "decompress_tflop": round(dec / 1e12, 4), "attention_tflop": round(att / 1e12, 4),
             "TFLOPs": round((dec + att) / (ms * 1e-3) / 1e12, 1),
             "frac_of_bf16_peak": round((dec + att) / (ms * 1e-3) / BF16_PEAK_TFLOPS / 1e12, 4),
-            "workspace_bytes": n}
+            "workspace_bytes": n, "units": units, "units_per_chunk_max": n // unit,
+            "ms_per_call_one_pass": round(ms_one_pass, 4),
+            "workspace_bytes_one_pass": units * unit}
 
 
 def kernel_class(name: str):

@@ -450,6 +450,20 @@ def mla_grouped_decode(p, latent_groups: int, q, c_kv, c_kv_scale, k_rope, block
 
 # ------------------------------------------------------------------ prefill
 
+# The workspace mla_prefill_workspace_size asks for at most (the header's
+# MLA_PREFILL_DEFAULT_WORKSPACE_BYTES); any workspace of one (sequence, head)
+# unit or more works, the call then running in chunks of units.
+MLA_PREFILL_DEFAULT_WORKSPACE_BYTES = 1 << 30
+
+
+def prefill_unit_bytes(max_blocks_per_seq: int, page_size: int) -> int:
+    """Workspace bytes of one (sequence, head) unit of mla_prefill: its keys
+    (192 wide) and values (128 wide) in bf16 over Tpad tokens, Tpad the cache
+    capacity of a sequence rounded up to 128."""
+    tpad = -(-max_blocks_per_seq * page_size // 128) * 128
+    return tpad * (192 + 128) * 2
+
+
 def mla_prefill_workspace_size(p) -> int:
     n = ctypes.c_size_t(0)
     _check("mla_prefill_workspace_size",

@@ -1,4 +1,5 @@
 // C ABI: host-side validation, workspace layout and launch sequencing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -228,8 +229,10 @@ mla_status attend_partial(const mla_decode_params& p, const Layout& L, const voi
                           const void* c_kv, const float* c_kv_scale, const void* k_rope,
                           const mla::PlanRequest& req, char* ws, hipStream_t s,
                           bool planned = false, hipEvent_t ev_before = nullptr,
-                          hipEvent_t ev_after = nullptr, int32_t groups = 1) {
+                          hipEvent_t ev_after = nullptr, int32_t groups = 1,
+                          int32_t shards = 1) {
   mla::AttnArgs a = attn_args(p, L, ws, req.block_table, req.seq_lens);
+  a.shards = shards;
   a.q_lat = q_lat;
   a.c_kv = c_kv;
   a.c_kv_scale = c_kv_scale;
@@ -269,9 +272,11 @@ mla_status attend_partial(const mla_decode_params& p, const Layout& L, const voi
 }
 
 // The log-sum-exp merge of the workspace's partials into o_lat (a7).
+// shards > 1: TPLA shard heads, merged into the h / shards heads' output.
 mla_status combine(const mla_decode_params& p, const Layout& L, char* ws, float* o_lat,
-                   hipStream_t s) {
-  const mla::AttnArgs a = attn_args(p, L, ws, nullptr, nullptr);
+                   hipStream_t s, int32_t shards = 1) {
+  mla::AttnArgs a = attn_args(p, L, ws, nullptr, nullptr);
+  a.shards = shards;
   const hipError_t e = mla::launch_combine(a, o_lat, s);
   return e == hipSuccess ? MLA_OK : hip_fail(e, "combine launch");
 }
@@ -281,11 +286,11 @@ mla_status attend(const mla_decode_params& p, const Layout& L, const void* q_lat
                   const float* c_kv_scale, const void* k_rope, const mla::PlanRequest& req,
                   float* o_lat, char* ws, hipStream_t s, bool planned = false,
                   hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
-                  int32_t groups = 1) {
+                  int32_t groups = 1, int32_t shards = 1) {
   mla_status st = attend_partial(p, L, q_lat, c_kv, c_kv_scale, k_rope, req, ws, s, planned,
-                                 ev_before, ev_after, groups);
+                                 ev_before, ev_after, groups, shards);
   if (st != MLA_OK) return st;
-  return combine(p, L, ws, o_lat, s);
+  return combine(p, L, ws, o_lat, s, shards);
 }
 
 }  // namespace
@@ -956,18 +961,31 @@ mla_status mla_tpla_decode(const mla_decode_params* p, const mla_tpla_params* t,
                               t->shards, p->d_latent, p->d_rope, mu, s);
   if (e != hipSuccess) return hip_fail(e, "expand launch");
   float* o2 = reinterpret_cast<float*>(ws + L.dec.o_lat);
-  st = attend(p2, L.dec, ws + L.dec.q_lat, c_kv, c_kv_scale, k_rope, plan, o2, ws, s, planned);
-  if (st != MLA_OK) return st;
   float* o1 = reinterpret_cast<float*>(ws + L.o_lat1);
-  e = mla::launch_tpla_gather(o2, o1, p->batch, p->num_heads, t->shards, p->d_latent, s);
-  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  // With bf16 fragment-major partials and whole 32-head blocks the merge takes
+  // each head's own shard columns straight into o1 (and the 64-head attention
+  // reads only its shard); otherwise every shard head is merged whole and the
+  // gather picks the columns.
+  const bool by_shard = t->shards > 1 && mla::mfma_any_supported(p2) && p->num_heads % 32 == 0;
+  st = attend(p2, L.dec, ws + L.dec.q_lat, c_kv, c_kv_scale, k_rope, plan, by_shard ? o1 : o2, ws,
+              s, planned, nullptr, nullptr, 1, by_shard ? t->shards : 1);
+  if (st != MLA_OK) return st;
+  if (!by_shard) {
+    e = mla::launch_tpla_gather(o2, o1, p->batch, p->num_heads, t->shards, p->d_latent, s);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+  }
   e = mla::launch_up_project(*p, o1, W_UV, out, s);
   return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
 }
 
+// The workspace size asked for by default: every (sequence, head) unit's keys
+// and values when they fit in MLA_PREFILL_DEFAULT_WORKSPACE_BYTES, else as many
+// units as fit there (at least one); the call then runs in chunks of units.
 static size_t prefill_ws_bytes(const mla_decode_params& p) {
-  const size_t per_head = (size_t)p.batch * p.num_heads * mla::prefill_tpad(p) * sizeof(uint16_t);
-  return align256(per_head * 192) + align256(per_head * 128);
+  const size_t unit = mla::prefill_unit_bytes(p);
+  const size_t units = (size_t)p.batch * p.num_heads;
+  const size_t fit = std::max<size_t>(1, MLA_PREFILL_DEFAULT_WORKSPACE_BYTES / unit);
+  return unit * std::max<size_t>(1, std::min(units, fit));
 }
 
 mla_status mla_prefill_workspace_size(const mla_decode_params* p, size_t* bytes) {
@@ -996,8 +1014,7 @@ mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void
     return fail(MLA_ERR_INVALID_ARG, "max_q_len %d outside [1, 2^24]", max_q_len);
   if ((int64_t)p->batch * max_q_len * p->num_heads * 192 >= ((int64_t)1 << 40))
     return fail(MLA_ERR_UNSUPPORTED, "query tensor too large");
-  if (p->batch > 65535 || 2 * (int64_t)p->num_heads > 65535 ||
-      (int64_t)p->batch * p->num_heads * ((max_q_len + 127) / 128) >= ((int64_t)1 << 31))
+  if ((int64_t)p->batch * p->num_heads * ((max_q_len + 127) / 128) >= ((int64_t)1 << 31))
     return fail(MLA_ERR_UNSUPPORTED, "prefill grid too large (batch %d, heads %d, max_q_len %d)",
                 p->batch, p->num_heads, max_q_len);
   if (!q || !q_lens || !c_kv || !k_rope || !block_table || !seq_lens || !W_UK || !W_UV || !out)
@@ -1008,18 +1025,15 @@ mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void
     return fail(MLA_ERR_INVALID_ARG, "c_kv_scale is required for an fp8 cache and only then");
   if (reinterpret_cast<uintptr_t>(c_kv_scale) & 3)
     return fail(MLA_ERR_INVALID_ARG, "c_kv_scale must be 4-byte aligned");
-  const size_t need = prefill_ws_bytes(*p);
+  const size_t need = mla::prefill_unit_bytes(*p);
   if (!workspace || workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+    return fail(MLA_ERR_WORKSPACE, "workspace of at least %zu bytes (one sequence and head) needed",
+                need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
     return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  char* ws = static_cast<char*>(workspace);
   const hipError_t e = mla::launch_prefill(*p, max_q_len, q, q_lens, c_kv, c_kv_scale, k_rope,
-                                           block_table,
-                                           seq_lens, W_UK, W_UV, out, ws,
-                                           ws + align256((size_t)p->batch * p->num_heads *
-                                                         mla::prefill_tpad(*p) * 2 * 192),
-                                           static_cast<hipStream_t>(stream));
+                                           block_table, seq_lens, W_UK, W_UV, out, workspace,
+                                           workspace_bytes, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "prefill launch");
 }
 

@@ -65,7 +65,6 @@ constexpr int kStageC = kStep * kCRow;            // 32768
 constexpr int kStage = kStageC + kStep * kRRow;   // 36864
 constexpr int kStages = 3;
 constexpr int kRing = kStages * kStage;           // 110592
-constexpr int kLoadsPerStep = kStep + kStep / 8;  // 32 latent rows + 4 rope groups
 constexpr int kKs0 = 16, kKs1 = 20;               // score k-steps of the two key parts (36 in all)
 constexpr int kNL = 4;                            // loader waves (the first value waves)
 constexpr int kXBytes = 64 * 64;                  // one wave's partial scores
@@ -87,6 +86,25 @@ struct Shape {
       kRing + kWinBytes + 2 * HB * (kXBytes + kPBytes) + 2 * HB * 32 * 4 * 2 + 2 * HB * 4;
 };
 
+// One latent shard of the 64-head kernel: the latent columns [c0, c0 + W) of
+// a cache row, W = d_c / G, that a work group whose heads are all shard-j
+// heads of a G-shard TPLA step reads (G = 1: the whole latent row).  In LDS a
+// stage holds the 32 rows' shard pieces (2 W bytes each) and their rope rows.
+template <int G>
+struct Shard {
+  static_assert(G == 1 || G == 2 || G == 4, "1, 2 or 4 shards");
+  static constexpr int W = kDc / G;                   // latent values per row
+  static constexpr int KL = W / 16;                   // latent k-steps of the scores
+  static constexpr int KPW = (KL + kDr / 16) / 2;     // k-steps per score wave
+  static constexpr int CRow = 2 * W;                  // bytes per latent row in LDS
+  static constexpr int StageC = kStep * CRow;
+  static constexpr int Stage = StageC + kStep * kRRow;
+  static constexpr int Ring = kStages * Stage;
+  static constexpr int Loads = kStep / G + kStep / 8;  // 1 KiB loads per step
+  static constexpr int MD = 4 / G;                    // 32-column output blocks per value wave
+  static_assert((KL + kDr / 16) % 2 == 0, "the score waves split the k-steps evenly");
+};
+
 // Chunk swizzles (LDS of 64 four-byte banks, one 256-byte bank line).  Latent
 // rows: row bits (b3 b2 b1 b0) -> chunk bits (b1 b0 b3 b2), so 16 consecutive
 // rows read at one chunk index hit 16 different chunks of the bank line (the
@@ -103,15 +121,55 @@ __device__ inline int swz_r(int r) { return (r >> 1) & 7; }
 // row.  Otherwise rows past the end repeat the last valid token (finite data,
 // masked in the softmax) and, when a step can span pages, every lane looks up
 // its own block.
-template <int NL, bool SP>
+//
+// With G > 1 shards a load carries the shard pieces of G rows (64 / G lanes a
+// row), row G m + lane / (64 / G) of load m at byte c0b of the cache row; the
+// piece swizzle stays inside the shard (it changes the low four piece bits
+// only, and a shard spans 16 or 32 pieces).
+template <int NL, bool SP, int G = 1>
 __device__ __forceinline__ void issue_step(const AttnArgs& a, lds_t* stage, const Tile& d, int lw,
-                                  int lane) {
+                                  int lane, uint32_t c0b = 0) {
   static_assert(kStep % NL == 0 && (kStep / 8) % NL == 0, "uniform row assignment");
+  static_assert(G == 1 || (kStep / G) % NL == 0, "uniform shard load assignment");
+  static_assert(G == 1 || !SP, "sharded loads serve the dense cache");
   // recompute the per-lane offsets in every call instead of keeping them live
   // across the step loop (they would cost registers in every wave)
   asm volatile("" : "+v"(lane));
   const uint32_t st = (uint32_t)(uintptr_t)stage;
   const int64_t base = (int64_t)d.blk * a.P + d.off;
+  if constexpr (G > 1) {
+    constexpr int LPR = 64 / G;  // lanes per row
+    const int rl = lane / LPR, pc = lane % LPR;
+    const char* ckv = static_cast<const char*>(a.c_kv);
+    const char* krp = static_cast<const char*>(a.k_rope);
+    const bool full = d.blk >= 0 && d.nv == kStep;
+    const int32_t rmax = d.nv - 1;
+#pragma unroll
+    for (int m = 0; m < kStep / G / NL; m++) {
+      const int mi = lw + NL * m;
+      const int r = G * mi + rl;
+      if (full) {
+        dma16s(ckv + base * kCRow, (uint32_t)(r * kCRow) + c0b + ((uint32_t)(pc ^ swz_c(r)) << 4),
+               st + mi * 1024);
+      } else {
+        const int64_t slot = d.blk >= 0 ? base + min(r, rmax)
+                                        : phys_slot(a.block_table, d.b, d.t0 + min(r, rmax), a.P,
+                                                    a.max_blocks, a.num_blocks);
+        dma16(ckv + slot * kCRow + c0b + ((pc ^ swz_c(r)) << 4), stage + mi * 1024);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kStep / 8 / NL; m++) {
+      const int j = lw + NL * m;
+      const int r = 8 * j + (lane >> 3);
+      const int64_t slot = full ? base + r
+                           : d.blk >= 0 ? base + min(r, rmax)
+                                        : phys_slot(a.block_table, d.b, d.t0 + min(r, rmax), a.P,
+                                                    a.max_blocks, a.num_blocks);
+      dma16(krp + slot * kRRow + (((lane & 7) ^ swz_r(r)) << 4), stage + Shard<G>::StageC + j * 1024);
+    }
+    return;
+  }
   if (d.blk >= 0 && d.nv == kStep) {
     const char* cb = static_cast<const char*>(a.c_kv) + base * kCRow;
     const char* rb = static_cast<const char*>(a.k_rope) + base * kRRow;
@@ -181,20 +239,24 @@ __device__ __forceinline__ void issue_step(const AttnArgs& a, lds_t* stage, cons
 // step kWin w + 2, when every wave has moved past window w - 1 (the value
 // waves, the furthest behind, then consume step kWin w).  It is complete
 // before step kWin w + 4 starts, long before its first use.
-template <int NL, bool SP>
+template <int NL, bool SP, int G = 1>
 struct Loader {
-  static_assert(kLoadsPerStep % NL == 0, "equal load counts per wave");
-  static constexpr int kPerWave = kLoadsPerStep / NL;
+  static_assert(Shard<G>::Loads % NL == 0, "equal load counts per wave");
+  static constexpr int kPerWave = Shard<G>::Loads / NL;
   int32_t next;        // split-local index of the next step to load
   int32_t n;           // steps of the split
   bool newer_issued;   // the batch after the awaited one was issued
+  uint32_t c0b = 0;    // byte offset of the shard in a cache row (G > 1)
 
   // Issue the loads of step `next`, described by d.
   __device__ void issue_next(const AttnArgs& a, lds_t* ring, lds_t* win, int32_t t_begin, int lw,
                              int lane, const Tile& d) {
     if (lw == 0 && next >= kWin + 4 && next % kWin == 4 && next + kWin - 4 < n)
       load_window(a, win, t_begin, t_begin + n, next / kWin + 1, lane);
-    issue_step<NL, SP>(a, ring + (next % kStages) * kStage, d, lw, lane);
+    if constexpr (G == 1)
+      issue_step<NL, SP>(a, ring + (next % kStages) * kStage, d, lw, lane);
+    else
+      issue_step<NL, SP, G>(a, ring + (next % kStages) * Shard<G>::Stage, d, lw, lane, c0b);
     next++;
   }
   // The first two steps, issued at kernel entry from the planner's table.
@@ -608,21 +670,29 @@ void attend_mfma_kernel(AttnArgs a) {
 // read C(j), then w2 and w3 issue their part of step j + 2.
 // Partial scores, weights, rescale factors and 1/l are double-buffered by
 // step parity; the barrier of a step orders what the previous step published.
-constexpr int kKs64 = 18;                         // k-steps per key part
 constexpr int kX64 = 2 * 2 * kXBytes;             // partial scores of one step: [kh][hb]
 constexpr int kP64 = 2 * kPBytes;                 // weights of one step: [hb]
-constexpr int kLds64 = kRing + kWinBytes + 2 * kX64 + 2 * kP64 + 2 * 2 * 32 * 4 * 2 + 2 * 2 * 4;
-static_assert(kLds64 <= 160 * 1024, "LDS budget of one compute unit");
-static_assert(2 * kKs64 == (kDc + kDr) / 16, "the key parts cover the whole key");
+template <int G>
+constexpr int lds64() {
+  return Shard<G>::Ring + kWinBytes + 2 * kX64 + 2 * kP64 + 2 * 2 * 32 * 4 * 2 + 2 * 2 * 4;
+}
+static_assert(lds64<1>() <= 160 * 1024, "LDS budget of one compute unit");
+static_assert(Shard<1>::KPW == 18 && Shard<1>::Stage == kStage, "the whole-row kernel's shape");
 
-template <bool SP>
+// G > 1: the G-shard TPLA step with shard-major heads (expanded head j h / G + i
+// is head i's shard-j head), h / G a multiple of 64, so that the 64 heads of a
+// work group share one shard j: it reads that shard's latent columns and the
+// rope part only, computes its score k-steps (the query is zero elsewhere) and
+// its output columns, and writes the shard's columns of its partials.
+template <bool SP, int G = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kLds64];
+  using Sh = Shard<G>;
+  __shared__ __attribute__((aligned(1024))) char smem[lds64<G>()];
   lds_t* ring = (lds_t*)smem;
-  lds_t* win = ring + kRing;                        // [2][kWin] tile descriptors
+  lds_t* win = ring + Sh::Ring;                     // [2][kWin] tile descriptors
   lds_t* xbuf = win + kWinBytes;                    // [2 parity][2 kh][2 hb][4][64 lanes][16 B]
   lds_t* pbuf = xbuf + 2 * kX64;                    // [2 parity][2 hb][2 k-steps][64 lanes][16 B]
-  float* s_alpha = (float*)(smem + kRing + kWinBytes + 2 * kX64 + 2 * kP64);  // [2][2][32]
+  float* s_alpha = (float*)(smem + Sh::Ring + kWinBytes + 2 * kX64 + 2 * kP64);  // [2][2][32]
   float* s_invl = s_alpha + 2 * 2 * 32;             // [2][2][32]
   int* s_flag = (int*)(s_invl + 2 * 2 * 32);        // [2][2]
 
@@ -644,6 +714,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
   }
   if (g >= a.splits) return;
   select_latent_group(a, hg * 64);
+  // the shard of this work group's heads (0 for the whole row)
+  const int32_t shard = G > 1 ? (hg * 64) / (a.h / G) : 0;
   const int32_t n_total = load_ro(a.cu_tiles, a.B);
   if (n_total == 0) return;
   const int32_t t_begin = load_ro(a.split_first, g);
@@ -655,8 +727,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
   if (wave < 2) {
     // ================================================================ score waves
     const int kh = wave;
-    const int K0 = kh * kKs64;
-    bf16x8 qf[2][kKs64];
+    constexpr int KPW = Sh::KPW, KL = Sh::KL;
+    const int K0 = kh * KPW;
+    bf16x8 qf[2][KPW];
     auto issue_q = [&](int32_t bb) {
 #pragma unroll
       for (int hb = 0; hb < 2; hb++) {
@@ -664,7 +737,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
             static_cast<const uint16_t*>(a.q_lat) + ((int64_t)bb * a.h + head) * (kDc + kDr));
 #pragma unroll
-        for (int k = 0; k < kKs64; k++) qf[hb][k] = qp[2 * (K0 + k) + g32];
+        for (int k = 0; k < KPW; k++) {
+          // k-step K0 + k of the shard: latent k-step shard KL + ks, or rope
+          const int ks = K0 + k;
+          const int gk = ks < KL ? shard * KL + ks : kDc / 16 + (ks - KL);
+          qf[hb][k] = qp[2 * gk + g32];
+        }
       }
     };
     Tile cur = global_tile(a, t_begin), prev{};
@@ -680,12 +758,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
       wg_barrier();
       if (j < n) {
         if (j > 0 && prev.last) wait_vmcnt<0>();  // the new segment's query
-        const lds_t* st = ring + (j % kStages) * kStage;
+        const lds_t* st = ring + (j % kStages) * Sh::Stage;
         auto ld_a = [&](int k) -> bf16x8 {
           const int ks = K0 + k;
-          const lds_t* p = ks < 32
-              ? st + row * kCRow + (((2 * ks + g32) ^ swz_c(row)) << 4)
-              : st + kStageC + row * kRRow + (((2 * (ks - 32) + g32) ^ swz_r(row)) << 4);
+          const lds_t* p = ks < KL
+              ? st + row * Sh::CRow + (((2 * ks + g32) ^ swz_c(row)) << 4)
+              : st + Sh::StageC + row * kRRow + (((2 * (ks - KL) + g32) ^ swz_r(row)) << 4);
           return *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(p);
         };
         // the next descriptor, read before the products hide its latency
@@ -696,10 +774,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
 #pragma unroll
         for (int k = 0; k < D; k++) av[k] = ld_a(k);
 #pragma unroll
-        for (int k = 0; k < kKs64; k++) {
+        for (int k = 0; k < KPW; k++) {
           s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k % D], qf[0][k], s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k % D], qf[1][k], s1, 0, 0, 0);
-          if (k + D < kKs64) av[k % D] = ld_a(k + D);
+          if (k + D < KPW) av[k % D] = ld_a(k + D);
           __builtin_amdgcn_sched_barrier(0);
         }
         lds_t* xb = xbuf + (j & 1) * kX64 + kh * 2 * kXBytes + lane * 16;
@@ -725,7 +803,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     const int32_t head = hg * 64 + hb * 32 + (lane & 31);
     // loader lanes 2 and 3; a segment end adds one store (the LSE) after the
     // loads of its step
-    Loader<4, SP> ld;
+    Loader<4, SP, G> ld;
+    ld.c0b = (uint32_t)(shard * Sh::CRow);
     ld.start(a, ring, win, t_begin, n, 2 + hb, lane);
     int sb1 = 0, sb2 = 0;
     wg_barrier();
@@ -822,7 +901,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
   } else {
     // ================================================================ value waves
     const int v = (wave & 1) | ((wave >> 2) << 1);  // w2 -> 0, w3 -> 1, w6 -> 2, w7 -> 3
-    constexpr int MD = 4;                            // 32-row output blocks of this wave
+    constexpr int MD = Sh::MD;                       // 32-row output blocks of this wave
     // latent fragments of two steps: slot j % 2 holds those of step j - 2
     // until its products are issued, then receives those of step j
     bf16x8 cb[2][MD][2];
@@ -831,21 +910,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     // sixteen read addresses live across the loop
     auto ld_c = [&](const lds_t* st, int ln, int md, int kk) -> bf16x8 {
       const int j16 = ln & 15, grp = ln >> 4, e = j16 >> 2, qd = j16 & 3, gg = ln >> 5;
-      const int dd = 32 * (v * MD + md) + 16 * (grp & 1) + 4 * qd;
+      const int dd = 32 * (v * MD + md) + 16 * (grp & 1) + 4 * qd;  // within the shard
       const int chunk = dd >> 3, hoff = (dd & 7) * 2;
       const int r0 = 16 * kk + 4 * gg + e;
       const int r1 = r0 + 8;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-              const_cast<lds_t*>(st) + r0 * kCRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
+              const_cast<lds_t*>(st) + r0 * Sh::CRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-              const_cast<lds_t*>(st) + r1 * kCRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
+              const_cast<lds_t*>(st) + r1 * Sh::CRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
       const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       return __builtin_bit_cast(bf16x8, cat);
     };
     auto stage_of = [&](int32_t j) -> const lds_t* {
-      int off = (j % kStages) * kStage;
+      int off = (j % kStages) * Sh::Stage;
       asm volatile("" : "+s"(off));
       return ring + off;
     };
@@ -855,7 +934,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     // stores after those loads
     constexpr int kVStores = 2 * MD * 4;
     const bool loader = v < 2;
-    Loader<4, SP> ld;
+    Loader<4, SP, G> ld;
+    ld.c0b = (uint32_t)(shard * Sh::CRow);
     if (loader) ld.start(a, ring, win, t_begin, n, v, lane);
     int sb1 = 0, sb2 = 0;  // partial-store groups issued in the previous two steps
     wg_barrier();
@@ -943,7 +1023,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
         for (int hb = 0; hb < 2; hb++) {
           const float inv = s_invl[(SL * 2 + hb) * 32 + (lane & 31)];
           uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc +
-                          frag_offset(hg * 2 + hb, v * MD, 0, lane);
+                          frag_offset(hg * 2 + hb, shard * (Sh::W / 32) + v * MD, 0, lane);
 #pragma unroll
           for (int md = 0; md < MD; md++) {
 #pragma unroll
@@ -991,7 +1071,13 @@ hipError_t launch_attend_mfma(const AttnArgs& a, int32_t cache_dtype, hipStream_
   const dim3 grid(a.splits * HG);
   // sparse index lists get their own instantiations (slot-list loads)
   const bool sp = a.slots != nullptr;
-  if (hpg == 64 && !sp)
+  // TPLA steps whose shard heads come in whole 64-head groups read their shard only
+  const bool sharded = a.shards > 1 && (a.h / a.shards) % 64 == 0 && !sp && hpg == 64;
+  if (sharded && a.shards == 2)
+    launch_timed(attend64_kernel<false, 2>, grid, dim3(512), s, ev_start, ev_stop, a);
+  else if (sharded && a.shards == 4)
+    launch_timed(attend64_kernel<false, 4>, grid, dim3(512), s, ev_start, ev_stop, a);
+  else if (hpg == 64 && !sp)
     launch_timed(attend64_kernel<false>, grid, dim3(512), s, ev_start, ev_stop, a);
   else if (hpg == 64)
     launch_timed(attend64_kernel<true>, grid, dim3(512), s, ev_start, ev_stop, a);

@@ -101,6 +101,13 @@ struct AttnArgs {
   int32_t group_heads;
   int64_t c_group_bytes;
   int64_t c_group_scales;
+  // TPLA (shards > 1): the h heads are the shard heads of h / shards heads in
+  // shard-major order (head j h / shards + i: head i, shard j), whose queries
+  // are zero outside their shard's d_c / shards latent columns.  Kernels may
+  // then leave a shard head's other latent columns of its partials unwritten;
+  // the combine merges each head's own shard columns into an [B, h / shards,
+  // d_c] output.
+  int32_t shards;
 };
 
 // Point a's latent pool (and scales) at the group of the heads starting at

@@ -10,14 +10,21 @@
 // at position T_b - L_b + l and sees positions 0 .. T_b - L_b + l.
 //
 // Two kernels:
-//  * decompress: K[b, i, t, :] = [W_UK[i] c_t ; k_rope_t] and V^T[b, i, :, t] =
-//    W_UV[i] c_t for every cached t < T_b, a bf16 matrix-core GEMM per (128
-//    tokens, head, K or V) tile, both operands arriving in LDS by direct loads,
-//    the next latent chunk in flight while the current one is multiplied;
-//  * attention: a work group per (256 queries, head, sequence), a wave per 32
-//    queries; per 64-key tile S^T = K Q^T (16x16x32 MFMA, keys on M), the
-//    causal mask, an online softmax per query, and O^T += V^T P^T (the key
-//    order of this product is the one the score fragments already hold).
+//  * decompress: K[u, t, :] = [W_UK[i] c_t ; k_rope_t] and V^T[u, :, t] =
+//    W_UV[i] c_t for every cached t < T_b of unit u = (sequence b, head i), a
+//    bf16 matrix-core GEMM per (128 tokens, unit, K or V) tile, both operands
+//    arriving in LDS by direct loads, the next latent chunk in flight while the
+//    current one is multiplied;
+//  * attention: a work group per (256 queries, unit), a wave per 32 queries;
+//    per 64-key tile S^T = K Q^T (16x16x32 MFMA, keys on M), the causal mask,
+//    an online softmax per query, and O^T += V^T P^T (the key order of this
+//    product is the one the score fragments already hold).
+// The units u = b h + i are taken in chunks of consecutive units, the two
+// kernels run per chunk, and the reconstructed keys and values of one chunk
+// live in the workspace at a time: its size sets the chunk, not B h T.
+#include <algorithm>
+#include <numeric>
+
 #include "mla_mfma_util.hpp"
 
 namespace mla {
@@ -49,10 +56,11 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   const uint16_t* W_UK;     // [h, 128, 512]
   const uint16_t* W_UV;     // [h, 128, 512]
-  uint16_t* Kn;             // [B, h, Tpad, 192]: reconstructed nope part, then rope
-  uint16_t* Vt;             // [B, h, 128, Tpad]: tokens permuted within 32 (vt_pos)
+  uint16_t* Kn;             // [units, Tpad, 192]: reconstructed nope part, then rope
+  uint16_t* Vt;             // [units, 128, Tpad]: tokens permuted within 32 (vt_pos)
   void* out;                // [B, Lq, h, 128]
   int32_t B, h, Lq, P, max_blocks, num_blocks, Tpad;
+  int32_t u0;               // first unit (b h + head) of this launch's chunk
   float sm_log2;            // sm_scale * log2(e)
 };
 
@@ -86,7 +94,8 @@ __device__ inline T lds_read(const lds_t* p) {
 }
 
 // ------------------------------------------------------------------ decompress
-// blockIdx = (token tile, i, b); WHICH 0 reconstructs keys, 1 values.  Wave
+// blockIdx = (token tile, unit within the chunk); WHICH 0 reconstructs keys,
+// 1 values.  Wave
 // (wm, wn) computes tokens 64 wm .. +63 by outputs 64 wn .. +63 of the
 // 128 x 128 tile, as outputs x tokens for keys and tokens x outputs for values,
 // so that each lane holds four adjacent values of its output row (key row
@@ -99,7 +108,8 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
   __shared__ __attribute__((aligned(1024))) char smem[4 * kDecHalf];  // two stages of A | B
   __shared__ float s_scale[kDecTok];  // fp8: the tile's per-token scales
   const PrefillArgs a = args;
-  const int32_t b = blockIdx.z, head = blockIdx.y;
+  const int32_t ul = blockIdx.y, unit = a.u0 + ul;
+  const int32_t b = unit / a.h, head = unit - b * a.h;
   const int32_t T = cached_len(a, b);
   const int32_t t0 = blockIdx.x * kDecTok;
   if (t0 >= T) return;
@@ -223,10 +233,10 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
         *reinterpret_cast<bf16x4 __attribute__((address_space(3)))*>(ot + row * kORow + 2 * col) = v;
       }
   wg_barrier();
-  const int64_t bh = (int64_t)b * a.h + head;
+  const int64_t bh = ul;  // the unit's place in the chunk's workspace
 #pragma unroll
-  for (int u = 0; u < 8; u++) {
-    const int pi = tid + 256 * u, row = pi >> 4, pc = pi & 15;
+  for (int k = 0; k < 8; k++) {
+    const int pi = tid + 256 * k, row = pi >> 4, pc = pi & 15;
     const u32x4 v = lds_read<u32x4>(ot + row * kORow + 16 * pc);
     if (WHICH == 0)  // key row t0 + row, reconstructed part
       *reinterpret_cast<u32x4*>(a.Kn + (bh * a.Tpad + t0 + row) * kPDq + 8 * pc) = v;
@@ -237,8 +247,8 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
     // the key's rope part, copied beside the reconstructed part (rows past T
     // repeat the last token, as above)
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int32_t idx = tid + 256 * u, row = idx >> 3, pc = idx & 7;
+    for (int k = 0; k < 4; k++) {
+      const int32_t idx = tid + 256 * k, row = idx >> 3, pc = idx & 7;
       const int32_t t = min(t0 + row, T - 1);
       const int64_t slot = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks);
       *reinterpret_cast<uint4*>(a.Kn + (bh * a.Tpad + t0 + row) * kPDq + kPDn + 8 * pc) =
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(256) void prefill_decompress_kernel(PrefillArgs arg
 }
 
 // ------------------------------------------------------------------ attention
-// One work group per (256 queries, head, sequence) on a 1-D grid, a wave per
+// One work group per (256 queries, unit) on a 1-D grid, a wave per
 // 32 queries (two 16-query MFMA column blocks sharing every key fragment).
 // Key and value tiles arrive by direct-to-LDS loads into three stages, the
 // tiles of steps n + 1 and n + 2 in flight while step n is multiplied, one
@@ -292,15 +302,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char smem[kAStages * (kKStage + kVStage)];
   const PrefillArgs a = args;
   // Block order: the 8 XCDs take block ids round-robin; regroup so that each
-  // XCD runs a contiguous range of (q-tile, head, sequence) work, the q-tiles
-  // of one head (which read the same keys and values) sharing its L2, and the
-  // causally heaviest q-tile of each head first.
+  // XCD runs a contiguous range of (q-tile, unit) work, the q-tiles of one
+  // unit (which read the same keys and values) sharing its L2, and the
+  // causally heaviest q-tile of each unit first.
   const uint32_t nwg = gridDim.x, per = nwg / 8;
   uint32_t id = blockIdx.x;
   if (id < per * 8) id = (id % 8) * per + id / 8;
   const int32_t qt = n_qtiles - 1 - (int32_t)(id % n_qtiles);
-  const int32_t head = (int32_t)((id / n_qtiles) % a.h);
-  const int32_t b = (int32_t)(id / n_qtiles / a.h);
+  const int32_t ul = (int32_t)(id / n_qtiles), unit = a.u0 + ul;
+  const int32_t b = unit / a.h, head = unit - b * a.h;
   const int32_t T = cached_len(a, b);
   const int32_t Lb = query_len(a, b, T);
   const int32_t q0 = qt * kQTile;
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int64_t bh = (int64_t)b * a.h + head;
+  const int64_t bh = ul;  // the unit's place in the chunk's workspace
   lds_t* ring = (lds_t*)smem;
   constexpr int kStage = kKStage + kVStage;
   const int32_t t_end = T - Lb + min(q0 + kQTile, Lb);  // keys this work group needs
@@ -469,11 +479,35 @@ int32_t prefill_tpad(const mla_decode_params& p) {
   return (int32_t)((cap + kDecTok - 1) / kDecTok * kDecTok);
 }
 
+size_t prefill_unit_bytes(const mla_decode_params& p) {
+  // keys [Tpad, 192] and transposed values [128, Tpad], bf16; a multiple of 256
+  return (size_t)prefill_tpad(p) * (kPDq + kPDv) * sizeof(uint16_t);
+}
+
+int64_t prefill_chunk_units(const mla_decode_params& p, int32_t max_q_len, size_t workspace_bytes) {
+  const int64_t units = (int64_t)p.batch * p.num_heads;
+  const int64_t fit = std::min<int64_t>((int64_t)(workspace_bytes / prefill_unit_bytes(p)), 65535);
+  if (units == 0 || fit < 1) return 0;
+  if (fit >= units) return units;
+  // The fewest chunks the workspace allows.  An attention work group fills a
+  // compute unit (its LDS ring), so a chunk's (256 queries, unit) work groups
+  // are taken as whole rounds of the compute units where the workspace
+  // allows: the unit count of a chunk a multiple of m.
+  constexpr int64_t kComputeUnits = 256;  // MI355X
+  const int64_t n_qtiles = (max_q_len + kQTile - 1) / kQTile;
+  int64_t m = kComputeUnits / std::gcd(kComputeUnits, n_qtiles);
+  if (fit < m) m = 1;
+  const int64_t cap = fit / m * m;
+  const int64_t chunks = (units + cap - 1) / cap;
+  const int64_t even = (units + chunks - 1) / chunks;
+  return (even + m - 1) / m * m;  // <= cap, since cap is a multiple of m
+}
+
 hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const void* q,
                           const int32_t* q_lens, const void* c_kv, const float* c_kv_scale,
                           const void* k_rope, const int32_t* block_table, const int32_t* seq_lens,
-                          const void* W_UK, const void* W_UV, void* out, void* Kn, void* Vt,
-                          hipStream_t s) {
+                          const void* W_UK, const void* W_UV, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t s) {
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.q_lens = q_lens;
@@ -485,8 +519,6 @@ hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const v
   a.seq_lens = seq_lens;
   a.W_UK = static_cast<const uint16_t*>(W_UK);
   a.W_UV = static_cast<const uint16_t*>(W_UV);
-  a.Kn = static_cast<uint16_t*>(Kn);
-  a.Vt = static_cast<uint16_t*>(Vt);
   a.out = out;
   a.B = p.batch;
   a.h = p.num_heads;
@@ -497,23 +529,33 @@ hipError_t launch_prefill(const mla_decode_params& p, int32_t max_q_len, const v
   a.Tpad = prefill_tpad(p);
   const float sm = p.sm_scale > 0.f ? p.sm_scale : 1.0f / sqrtf((float)(p.d_nope + p.d_rope));
   a.sm_log2 = sm * 1.4426950408889634f;
-  const dim3 dgrid(a.Tpad / kDecTok, p.num_heads, p.batch);
-  if (p.cache_dtype == MLA_FP8_E4M3) {
-    hipLaunchKernelGGL((prefill_decompress_kernel<0, true>), dgrid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL((prefill_decompress_kernel<1, true>), dgrid, dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((prefill_decompress_kernel<0, false>), dgrid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL((prefill_decompress_kernel<1, false>), dgrid, dim3(256), 0, s, a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)p.batch * p.num_heads;
+  const int64_t per = prefill_chunk_units(p, max_q_len, workspace_bytes);
+  if (per < 1) return hipErrorInvalidValue;
+  a.Kn = static_cast<uint16_t*>(workspace);
+  a.Vt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                     (size_t)per * a.Tpad * kPDq * sizeof(uint16_t));
   const int32_t n_qtiles = (max_q_len + kQTile - 1) / kQTile;
-  const dim3 grid((uint32_t)((int64_t)n_qtiles * p.num_heads * p.batch));
-  if (p.out_dtype == MLA_BF16)
-    hipLaunchKernelGGL(prefill_attn_kernel<MLA_BF16>, grid, dim3(512), 0, s, a, n_qtiles);
-  else
-    hipLaunchKernelGGL(prefill_attn_kernel<MLA_F32>, grid, dim3(512), 0, s, a, n_qtiles);
-  return hipGetLastError();
+  for (int64_t u0 = 0; u0 < units; u0 += per) {
+    const int32_t n = (int32_t)std::min(per, units - u0);
+    a.u0 = (int32_t)u0;
+    const dim3 dgrid(a.Tpad / kDecTok, n);
+    if (p.cache_dtype == MLA_FP8_E4M3) {
+      hipLaunchKernelGGL((prefill_decompress_kernel<0, true>), dgrid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prefill_decompress_kernel<1, true>), dgrid, dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((prefill_decompress_kernel<0, false>), dgrid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prefill_decompress_kernel<1, false>), dgrid, dim3(256), 0, s, a);
+    }
+    const dim3 grid((uint32_t)((int64_t)n_qtiles * n));
+    if (p.out_dtype == MLA_BF16)
+      hipLaunchKernelGGL(prefill_attn_kernel<MLA_BF16>, grid, dim3(512), 0, s, a, n_qtiles);
+    else
+      hipLaunchKernelGGL(prefill_attn_kernel<MLA_F32>, grid, dim3(512), 0, s, a, n_qtiles);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -280,15 +280,23 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
 constexpr int kFragLat = 512;
 constexpr int kCombPass = 16;
 
+// With TPLA shards (a.shards > 1) block (b, hblk, mdg) merges the columns of
+// output head block hblk that lie in shard j = mdg / (16 / shards), from the
+// partials of shard head block j (h / shards) / 32 + hblk, into an output of
+// h / shards heads: the shard heads' other columns are neither read nor written.
 __global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __restrict__ o_lat) {
   __shared__ float s_w[kCombPass][32];  // LSEs of the pass's slots, then their weights
   __shared__ float s_M[32], s_W[32], s_alpha[32];
-  const int32_t b = blockIdx.x, hblk = blockIdx.y, mdg = blockIdx.z;
+  const int32_t b = blockIdx.x, mdg = blockIdx.z;
+  const int32_t G = a.shards > 1 ? a.shards : 1, h_out = a.h / G;
+  const int32_t hblk_out = blockIdx.y;
+  const int32_t hblk = (mdg / (kFragLat / 32 / G)) * (h_out / 32) + hblk_out;  // partials' head block
   const int tid = threadIdx.x, jj = tid >> 6, lane = tid & 63;
   const int r = lane & 31;                 // head of this thread's piece
   const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of the LSE loads
   const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
-  float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * a.h + hblk * 32 + r) * kFragLat + d);
+  float4* dst =
+      reinterpret_cast<float4*>(o_lat + ((int64_t)b * h_out + hblk_out * 32 + r) * kFragLat + d);
   const int2 range = *reinterpret_cast<const int2*>(a.seq_splits + 2 * b);
   const int32_t g_lo = range.x, n_cand = range.y - range.x + 1;
   if (n_cand <= 0) {  // no tokens
@@ -366,9 +374,10 @@ __global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __
 
 hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s) {
   if (a.frag_layout) {
-    if (a.d_c != kFragLat || a.h % 32 || a.streams != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(combine_frag_kernel, dim3(a.B, a.h / 32, kFragLat / 32), dim3(256), 0, s, a,
-                       o_lat);
+    const int32_t G = a.shards > 1 ? a.shards : 1;
+    if (a.d_c != kFragLat || a.h % (32 * G) || a.streams != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_frag_kernel, dim3(a.B, a.h / G / 32, kFragLat / 32), dim3(256), 0, s,
+                       a, o_lat);
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3(a.B, a.h), dim3(kCombThreads), 0, s, a, o_lat);
   }

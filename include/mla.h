@@ -415,10 +415,20 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
  * Supported: bf16 q, rope and weights, a bf16 or fp8 (E4M3 with c_kv_scale,
  * which must be NULL otherwise) cache, with d_latent 512, d_nope 128, d_rope
  * 64, d_v 128 (else MLA_ERR_UNSUPPORTED); q, c_kv, k_rope, W_UK and W_UV
- * 16-byte aligned.  The workspace holds the keys (reconstructed part and
- * rope part) and values of every cached token: batch x h x Tpad x (192 + 128)
- * bf16 values, Tpad = max_blocks_per_seq x page_size rounded up to 128.
+ * 16-byte aligned.  The work is taken in chunks of consecutive units (b, i),
+ * unit b h + i; for each chunk the workspace (256-byte aligned, caller-owned)
+ * holds the reconstructed keys (nope and rope parts) and values of every
+ * cached token of the chunk's units: Tpad x (192 + 128) bf16 values a unit,
+ * Tpad = max_blocks_per_seq x page_size rounded up to 128.  Any workspace of
+ * at least one unit works (MLA_ERR_WORKSPACE below that); a larger one means
+ * fewer, larger chunks (at most 65535 units each, split evenly).
+ * mla_prefill_workspace_size returns every unit's size when that is at most
+ * MLA_PREFILL_DEFAULT_WORKSPACE_BYTES, else the most units that fit in it (at
+ * least one).  Chunks run in order on the stream; the workspace is free once
+ * the call's work on the stream has completed.
  * ------------------------------------------------------------------------ */
+#define MLA_PREFILL_DEFAULT_WORKSPACE_BYTES ((size_t)1 << 30)
+
 mla_status mla_prefill_workspace_size(const mla_decode_params* p, size_t* bytes);
 
 mla_status mla_prefill(const mla_decode_params* p, int32_t max_q_len, const void* q,

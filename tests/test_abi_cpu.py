@@ -227,9 +227,23 @@ def _prefill_params(**kw):
 
 
 def test_prefill_workspace_size_without_device():
-    # keys with their rope part and transposed values: B x h x Tpad x (192 + 128)
-    # bf16, Tpad = 5 blocks x 64 rounded up to 128
-    assert _lib.mla_prefill_workspace_size(_prefill_params()) == 3 * 4 * 384 * (192 + 128) * 2
+    # keys with their rope part and transposed values of every (sequence, head)
+    # unit: B x h x Tpad x (192 + 128) bf16, Tpad = 5 blocks x 64 rounded up to 128
+    unit = 384 * (192 + 128) * 2
+    assert _lib.prefill_unit_bytes(5, 64) == unit
+    assert _lib.mla_prefill_workspace_size(_prefill_params()) == 3 * 4 * unit
+    text = open(HEADER).read()
+    m = re.search(r"#define MLA_PREFILL_DEFAULT_WORKSPACE_BYTES \(\(size_t\)1 << (\d+)\)", text)
+    assert m and 1 << int(m.group(1)) == _lib.MLA_PREFILL_DEFAULT_WORKSPACE_BYTES
+    # 2 x 128 units of 16K tokens (10 MiB each) ask for the most units that
+    # fit in the default, not all 2.7 GB
+    big = _prefill_params(batch=2, num_heads=128, max_blocks_per_seq=256, num_blocks=512)
+    unit = _lib.prefill_unit_bytes(256, 64)
+    assert unit == 16384 * 640
+    assert _lib.mla_prefill_workspace_size(big) == (_lib.MLA_PREFILL_DEFAULT_WORKSPACE_BYTES // unit) * unit
+    # a unit larger than the default still gets one unit
+    huge = _prefill_params(batch=1, num_heads=2, max_blocks_per_seq=40000, num_blocks=40000)
+    assert _lib.mla_prefill_workspace_size(huge) == _lib.prefill_unit_bytes(40000, 64)
 
 
 @pytest.mark.parametrize("bad", [dict(cache_dtype="f32"), dict(q_dtype="f32"),
@@ -258,8 +272,8 @@ def test_prefill_rejects_bad_arguments_before_launch():
         with pytest.raises(_lib.MlaError) as ei:
             _lib.mla_prefill(p, 16, *a, fake, n)
         assert ei.value.status == _lib.MLA_ERR_INVALID_ARG, i
-    with pytest.raises(_lib.MlaError) as ei:
-        _lib.mla_prefill(p, 16, *args, fake, n - 1)
+    with pytest.raises(_lib.MlaError) as ei:  # less than one (sequence, head) unit
+        _lib.mla_prefill(p, 16, *args, fake, _lib.prefill_unit_bytes(5, 64) - 1)
     assert ei.value.status == _lib.MLA_ERR_WORKSPACE
     with pytest.raises(_lib.MlaError) as ei:
         _lib.mla_prefill(p, 16, *args, fake + 128, n)

@@ -43,13 +43,17 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_prefill(pi, q_lens=None):
+def run_prefill(pi, q_lens=None, units=None):
+    """Run mla_prefill; `units` sizes the workspace at that many (sequence,
+    head) units (the call then runs in chunks), else the size the library asks for."""
     dev = DeviceInputs(pi.dense)
     c = pi.cfg
     q = to_device_array(pi.q, dev.device)
     ql = to_device_array(np.asarray(pi.q_lens if q_lens is None else q_lens, np.int32), dev.device)
     p = dev.params()
     n = _lib.mla_prefill_workspace_size(p)
+    if units is not None:
+        n = units * _lib.prefill_unit_bytes(dev.max_blocks_per_seq, c.page_size)
     ws = torch.empty(n, dtype=torch.uint8, device=dev.device)
     out = torch.empty((c.batch, pi.max_q_len, c.heads, c.d_v), dtype=out_torch_dtype(c.out_dtype),
                       device=dev.device)
@@ -115,6 +119,24 @@ def test_prefill_matches_oracle(case):
     _say(f"prefill {case}")
     pi = generate_prefill(k["cfg"], k["max_q_len"], seq_lens=k["seq_lens"], q_lens=k["q_lens"])
     check(pi, run_prefill(pi), label=case)
+
+
+@pytest.mark.parametrize("case", ["ragged_bf16", "fp8_ragged"])
+def test_prefill_in_unit_chunks_matches_one_pass(case):
+    """A workspace of 1, 3 or 5 (sequence, head) units runs the call in chunks
+    of consecutive units (16 units: chunks of 1; 3 with a last chunk of 1; 4);
+    each unit's keys, values and attention are computed as in one pass, so the
+    outputs are the same bits, and they match the oracle."""
+    k = CASES[case]
+    pi = generate_prefill(k["cfg"], k["max_q_len"], seq_lens=k["seq_lens"], q_lens=k["q_lens"])
+    units = pi.cfg.batch * pi.cfg.heads
+    _say(f"prefill {case} in one pass ({units} units)")
+    full = run_prefill(pi, units=units)
+    check(pi, full, label=f"{case} one pass")
+    for per in (1, 3, 5):
+        _say(f"prefill {case} with a workspace of {per} units")
+        got = run_prefill(pi, units=per)
+        np.testing.assert_array_equal(got, full)
 
 
 def test_prefill_clamps_q_lens():

@@ -80,6 +80,14 @@ CASES = {
                   page_size=16),
     "bf16": small("dsv3_ragged_32k", seq_len_range=(1, 700), batch=3, seed=4101),
     "fp8": small("dsv3_fp8_16k", seq_len=None, seq_len_range=(1, 600), batch=3, seed=4102),
+    # 64 heads on 16-token pages: the shard heads still come in whole 64-head
+    # groups (one per shard for two shards), and steps span pages
+    "bf16_h64_p16": small("dsv3_ragged_32k", heads=64, page_size=16, seq_len_range=(1, 500),
+                          batch=3, seed=4103),
+    # 32 heads: whole 32-head blocks (merged by shard) but no 64-head shard groups
+    "bf16_h32": small("dsv3_ragged_32k", heads=32, seq_len_range=(1, 400), batch=2, seed=4104),
+    # 16 heads: shard heads merged whole, then gathered
+    "bf16_h16": small("dsv3_ragged_32k", heads=16, seq_len_range=(1, 400), batch=2, seed=4105),
 }
 
 
@@ -90,7 +98,8 @@ def test_tpla_matches_oracle(case, shards, mu):
     _say(f"tpla {case} shards={shards} mu={mu}")
     inp = generate(cfg)
     out = run_tpla(inp, shards, mu)
-    heads = None if cfg.heads <= 8 else [0, 1, 63, 64, 127]
+    h = cfg.heads
+    heads = None if h <= 16 else sorted({0, 1, h // 2 - 1, h // 2, h - 1})
     check(inp, out, shards, mu, heads=heads, label=f"{case} g={shards}")
 
 
@@ -109,8 +118,10 @@ def test_tpla_is_deterministic():
     assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
-def test_tpla_full_size_sampled():
-    """The 32K ragged DeepSeek-V3 workload, two shards, sampled pairs."""
+@pytest.mark.parametrize("shards", [2, 4])
+def test_tpla_full_size_sampled(shards):
+    """The 32K ragged DeepSeek-V3 workload, two or four shards, sampled pairs."""
+    _say(f"tpla dsv3_ragged_32k shards={shards}")
     inp = generate(CONFIGS["dsv3_ragged_32k"])
-    out = run_tpla(inp, 2)
-    check(inp, out, 2, batches=[0, 5], heads=[3, 77], label="dsv3_ragged_32k g=2")
+    out = run_tpla(inp, shards)
+    check(inp, out, shards, batches=[0, 5], heads=[3, 77, 127], label=f"dsv3_ragged_32k g={shards}")
