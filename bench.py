@@ -425,6 +425,10 @@ def measure_dsa(name: str, steps: int, warmup: int):
         dev.block_table, dev.seq_lens, scores, cap, stream))
     t_topk = stage(lambda j: _lib.mla_topk_select(scores, cap, dev.seq_lens, cfg.batch, k, idx, k,
                                                   cnt, stream))
+    tws = _lib.mla_topk_select_split_workspace_size(cfg.batch, cap)
+    tw = torch.empty(tws, dtype=torch.uint8, device=dev.device)
+    t_topk_split = stage(lambda j: _lib.mla_topk_select_split(
+        scores, cap, dev.seq_lens, cfg.batch, k, idx, k, cnt, tw, tws, stream))
     t_dec = stage(lambda j: _lib.mla_decode_sparse(
         p, dev.q, c_copies[j % copies], s_copies[j % copies], r_copies[j % copies],
         dev.block_table, idx, k, cnt, dev.W_UK, dev.W_UV, out, sw, sws, stream))
@@ -438,7 +442,9 @@ def measure_dsa(name: str, steps: int, warmup: int):
             "selected_tokens": int(sel.sum()), "cache_dtype": cfg.cache_dtype,
             "algorithmic_bytes": alg, "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
             "stage_us": {"indexer": round(t_idx * 1e3, 2), "topk": round(t_topk * 1e3, 2),
+                         "topk_split": round(t_topk_split * 1e3, 2),
                          "sparse_decode": round(t_dec * 1e3, 2)},
+            "topk_in_step": "split" if cfg.batch <= 64 else "one work group per sequence",
             "indexer_key_GBps": round(idx_bytes / (t_idx * 1e-3) / 1e9, 1),
             "copies_rotated": copies}
 

@@ -116,6 +116,10 @@ _SIGNATURES = {
     "mla_quantize_e4m3_rows": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
     "mla_indexer_scores": (ctypes.c_int, [_PP, _DP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "mla_topk_select": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P]),
+    "mla_topk_select_split_workspace_size": (ctypes.c_int,
+                                             [_I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_topk_select_split": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P,
+                                             ctypes.c_size_t, _P]),
     "mla_decode_sparse_workspace_size": (ctypes.c_int, [_PP, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "mla_decode_sparse": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
@@ -374,6 +378,23 @@ def mla_topk_select(scores, score_stride: int, seq_lens, batch: int, k: int, ind
     _check("mla_topk_select", load_library().mla_topk_select(
         _ptr(scores), int(score_stride), _ptr(seq_lens), int(batch), int(k), _ptr(indices),
         int(index_stride), _ptr(counts), _stream(stream)))
+
+
+def mla_topk_select_split_workspace_size(batch: int, score_stride: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_topk_select_split_workspace_size",
+           load_library().mla_topk_select_split_workspace_size(int(batch), int(score_stride),
+                                                               ctypes.byref(n)))
+    return n.value
+
+
+def mla_topk_select_split(scores, score_stride: int, seq_lens, batch: int, k: int, indices,
+                          index_stride: int, counts, workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    _check("mla_topk_select_split", load_library().mla_topk_select_split(
+        _ptr(scores), int(score_stride), _ptr(seq_lens), int(batch), int(k), _ptr(indices),
+        int(index_stride), _ptr(counts), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def mla_decode_sparse_workspace_size(p, index_stride: int) -> int:

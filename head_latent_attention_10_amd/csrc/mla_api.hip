@@ -410,8 +410,12 @@ mla_status check_indexer_ptrs(const mla_decode_params& p, const mla_dsa_params& 
 
 int32_t score_cap(const mla_decode_params& p) { return p.max_blocks_per_seq * p.page_size; }
 
+// Batches up to this size take the top-k with its candidate pass spread over
+// several work groups per sequence (one work group per sequence above).
+constexpr int32_t kTopkSplitMaxBatch = 64;
+
 struct DsaLayout {
-  size_t scores, indices, counts, decode, total;
+  size_t scores, indices, counts, topk, decode, total;
   Layout dec;
 };
 
@@ -424,6 +428,8 @@ mla_status dsa_layout(const mla_decode_params& p, const mla_dsa_params& d, DsaLa
   off = align256(off + B * (size_t)d.topk * sizeof(int32_t));
   L->counts = off;
   off = align256(off + B * sizeof(int32_t));
+  L->topk = off;  // the split top-k's candidate lists
+  if (p.batch <= kTopkSplitMaxBatch) off = align256(off + mla::topk_split_ws_bytes(p.batch, score_cap(p)));
   L->decode = off;
   mla_status st = layout(p, &L->dec, d.topk);
   if (st != MLA_OK) return st;
@@ -834,20 +840,60 @@ mla_status mla_indexer_scores(const mla_decode_params* p, const mla_dsa_params* 
   return e == hipSuccess ? MLA_OK : hip_fail(e, "indexer launch");
 }
 
-mla_status mla_topk_select(const float* scores, int32_t score_stride, const int32_t* seq_lens,
-                           int32_t batch, int32_t k, int32_t* indices, int32_t index_stride,
-                           int32_t* counts, void* stream) {
-  g_last_error.clear();
+static mla_status check_topk_args(const float* scores, int32_t score_stride,
+                                  const int32_t* seq_lens, int32_t batch, int32_t k,
+                                  int32_t* indices, int32_t index_stride, int32_t* counts) {
   if (batch < 0 || batch > (1 << 24) || k < 1 || k > (1 << 24) || score_stride < 1 ||
       index_stride < k)
     return fail(MLA_ERR_INVALID_ARG,
                 "batch=%d k=%d score_stride=%d index_stride=%d (need k >= 1, index_stride >= k)",
                 batch, k, score_stride, index_stride);
-  if (batch == 0) return MLA_OK;
-  if (!scores || !seq_lens || !indices || !counts)
+  if (batch > 0 && (!scores || !seq_lens || !indices || !counts))
     return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL");
+  return MLA_OK;
+}
+
+mla_status mla_topk_select(const float* scores, int32_t score_stride, const int32_t* seq_lens,
+                           int32_t batch, int32_t k, int32_t* indices, int32_t index_stride,
+                           int32_t* counts, void* stream) {
+  g_last_error.clear();
+  mla_status st = check_topk_args(scores, score_stride, seq_lens, batch, k, indices, index_stride,
+                                  counts);
+  if (st != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
   const hipError_t e = mla::launch_topk(scores, score_stride, seq_lens, batch, k, indices,
                                         index_stride, counts, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "top-k launch");
+}
+
+mla_status mla_topk_select_split_workspace_size(int32_t batch, int32_t score_stride, size_t* bytes) {
+  g_last_error.clear();
+  if (batch < 0 || batch > 65535 || score_stride < 1)
+    return fail(MLA_ERR_INVALID_ARG, "batch=%d (0..65535) score_stride=%d (>= 1)", batch,
+                score_stride);
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = mla::topk_split_ws_bytes(batch, score_stride);
+  return MLA_OK;
+}
+
+mla_status mla_topk_select_split(const float* scores, int32_t score_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t k,
+                                 int32_t* indices, int32_t index_stride, int32_t* counts,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status st = check_topk_args(scores, score_stride, seq_lens, batch, k, indices, index_stride,
+                                  counts);
+  if (st != MLA_OK) return st;
+  if (batch > 65535) return fail(MLA_ERR_INVALID_ARG, "batch %d above 65535", batch);
+  if (batch == 0) return MLA_OK;
+  const size_t need = mla::topk_split_ws_bytes(batch, score_stride);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, %zu required", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const hipError_t e = mla::launch_topk_split(scores, score_stride, seq_lens, batch, k, indices,
+                                              index_stride, counts, workspace,
+                                              static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "top-k launch");
 }
 
@@ -903,7 +949,10 @@ mla_status mla_dsa_decode(const mla_decode_params* p, const mla_dsa_params* d, c
                                      scores, p->batch, d->index_heads, d->index_dim,
                                      p->page_size, p->max_blocks_per_seq, p->num_blocks, cap, s);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
-  e = mla::launch_topk(scores, cap, seq_lens, p->batch, d->topk, idx, d->topk, counts, s);
+  e = p->batch <= kTopkSplitMaxBatch
+          ? mla::launch_topk_split(scores, cap, seq_lens, p->batch, d->topk, idx, d->topk, counts,
+                                   ws + L.topk, s)
+          : mla::launch_topk(scores, cap, seq_lens, p->batch, d->topk, idx, d->topk, counts, s);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return decode_impl(p, q, c_kv, c_kv_scale, k_rope, block_table, counts, idx, d->topk, W_UK,
                      W_UV, out, ws + L.decode, workspace_bytes - L.decode, stream, nullptr,

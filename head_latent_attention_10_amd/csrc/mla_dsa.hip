@@ -23,6 +23,8 @@
 // the k-th largest key K and how many keys equal to K are taken (the earliest
 // positions) are found there by counting; the selected positions come out in
 // increasing order (details at topk_kernel).
+#include <algorithm>
+
 #include "mla_mfma_util.hpp"
 
 namespace mla {
@@ -202,6 +204,27 @@ __device__ inline uint32_t block_max_u32(uint32_t v, uint32_t* s_wave) {
   return t;
 }
 
+// Two maxima over the work group in one exchange (two barriers); s_wave holds
+// 2 kTopkWaves values.
+__device__ inline void block_max2_u32(uint32_t& a, uint32_t& b, uint32_t* s_wave) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a = max(a, (uint32_t)__shfl_xor((int)a, o));
+    b = max(b, (uint32_t)__shfl_xor((int)b, o));
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    s_wave[threadIdx.x >> 6] = a;
+    s_wave[kTopkWaves + (threadIdx.x >> 6)] = b;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; w++) {
+    a = max(a, s_wave[w]);
+    b = max(b, s_wave[kTopkWaves + w]);
+  }
+}
+
 struct TopkArgs {
   const float* scores;
   int32_t score_stride;
@@ -212,6 +235,13 @@ struct TopkArgs {
   int32_t* counts;
 };
 
+// What a radix round over register-held keys shares (radix_rank).
+struct RadixShared {
+  uint32_t whist[kTopkWaves][256];  // per-wave digit histograms
+  uint32_t wave[2 * kTopkWaves];    // per-wave values of the work-group reductions
+  uint32_t pick[4];
+};
+
 struct TopkShared {
   uint32_t cand_key[kCandCap];
   int32_t cand_pos[kCandCap];
@@ -219,10 +249,8 @@ struct TopkShared {
     uint32_t bits[kFastMaxT / 32];  // selected positions (fast path)
     uint32_t hist[kBins];           // radix histogram (general path)
   };
-  uint32_t whist[kTopkWaves][256];  // per-wave digit histograms (fast path)
-  uint32_t wave[kTopkWaves];
+  RadixShared r;
   uint32_t seg[kTopkWaves];  // candidates of each wave's segment
-  uint32_t pick[4];
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave (DPP: row shifts, then
@@ -247,7 +275,7 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v) {
 // #(keys > K) and *eq = #(keys == K).
 template <int N>
 __device__ uint32_t radix_rank(const uint32_t (&key)[N], const bool (&ok)[N], int n, uint32_t rank,
-                               uint32_t base, int top, int low, TopkShared& sh, uint32_t* rem_out,
+                               uint32_t base, int top, int low, RadixShared& sh, uint32_t* rem_out,
                                uint32_t* eq_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t K = base, rem = rank, eq = 0;
@@ -293,7 +321,8 @@ __device__ uint32_t radix_rank(const uint32_t (&key)[N], const bool (&ok)[N], in
 
 // Radix select over all T keys in global memory (11 + 11 + 10 bits, LDS
 // histograms): the k-th largest key K and how many keys equal to K are taken.
-__device__ void radix_select_global(const float* sc, int32_t T, uint32_t k, TopkShared& sh,
+template <typename SH>
+__device__ void radix_select_global(const float* sc, int32_t T, uint32_t k, SH& sh,
                                     uint32_t* K_out, uint32_t* rem_out) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, rem = k;
@@ -313,29 +342,119 @@ __device__ void radix_select_global(const float* sc, int32_t T, uint32_t k, Topk
     // counts from the top bin down: thread t owns bins 2047 - 2t and 2046 - 2t
     const int hb = kBins - 1 - 2 * tid;
     const uint32_t c0 = sh.hist[hb], c1 = sh.hist[hb - 1];
-    const uint32_t incl = block_scan(c0 + c1, sh.wave);  // keys in bins >= hb - 1
+    const uint32_t incl = block_scan(c0 + c1, sh.r.wave);  // keys in bins >= hb - 1
     const uint32_t above = incl - c0 - c1;                // keys in bins > hb
     if (above < rem && rem <= above + c0) {
-      sh.pick[0] = hb;
-      sh.pick[1] = above;
+      sh.r.pick[0] = hb;
+      sh.r.pick[1] = above;
     } else if (above + c0 < rem && rem <= incl) {
-      sh.pick[0] = hb - 1;
-      sh.pick[1] = above + c0;
+      sh.r.pick[0] = hb - 1;
+      sh.r.pick[1] = above + c0;
     }
     __syncthreads();
-    prefix |= sh.pick[0] << shift;
-    rem -= sh.pick[1];
+    prefix |= sh.r.pick[0] << shift;
+    rem -= sh.r.pick[1];
     __syncthreads();
   }
   *K_out = prefix;
   *rem_out = rem;
 }
 
+// Step 1 of the fast path below: a lower bound L of the k-th largest key, the
+// top 16 bits of the R-th largest of 4096 keys at evenly spaced positions, R
+// a few standard deviations above the sample rank of the k-th largest key, so
+// that at least k keys are >= L and not many more (L = 0, every key, when
+// T <= 6144).  False when the fast path does not apply (T too long, or R past
+// the sample).  The same scores always give the same L.
+__device__ bool sample_bound(const float* sc, int32_t T, uint32_t k, RadixShared& sh, uint32_t* L) {
+  const int tid = threadIdx.x;
+  *L = 0;
+  if (T > kFastMaxT) return false;
+  if (T <= kAllCand) return true;
+  const uint32_t r = (uint32_t)(((uint64_t)k * kSample + T - 1) / T);
+  const uint32_t R = r + 4 * (uint32_t)ceilf(sqrtf((float)r)) + 16;
+  if (R >= kSample) return false;
+  uint32_t key[4];
+  bool ok[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    key[e] = score_key(sc[((int64_t)(tid + kTopkThreads * e) * T) / kSample]);
+    ok[e] = true;
+  }
+  // the top 16 bits of the R-th largest sampled key: a lower bound is all
+  // the candidate pass needs
+  *L = radix_rank<4>(key, ok, 4, R, 0u, 32, 16, sh, nullptr, nullptr);
+  return true;
+}
+
+// The general path: a radix select over all T keys in global memory gives the
+// k-th largest key K and how many keys equal to K are taken, then thread t
+// walks positions [t chunk, (t + 1) chunk) twice, counting and then writing
+// the selected positions in increasing order.
+template <typename SH>
+__device__ void select_general(const float* sc, int32_t T, uint32_t k, int32_t* out, SH& sh) {
+  const int tid = threadIdx.x;
+  uint32_t K, rem;
+  radix_select_global(sc, T, k, sh, &K, &rem);
+  const int32_t chunk = (T + kTopkThreads - 1) / kTopkThreads;
+  const int32_t p0 = min(T, tid * chunk), p1 = min(T, p0 + chunk);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int32_t i = p0; i < p1; i++) {
+    const uint32_t key = score_key(sc[i]);
+    n_gt += key > K;
+    n_eq += key == K;
+  }
+  uint32_t gt = block_scan(n_gt, sh.r.wave) - n_gt;
+  uint32_t eq = block_scan(n_eq, sh.r.wave) - n_eq;
+  for (int32_t i = p0; i < p1; i++) {
+    const uint32_t key = score_key(sc[i]);
+    if (key > K) {
+      out[gt + min(eq, rem)] = i;
+      gt++;
+    } else if (key == K) {
+      if (eq < rem) out[gt + eq] = i;
+      eq++;
+    }
+  }
+}
+
+// Over candidates held N per thread (key, position, ok; every key >= L), the
+// k-th largest key K and the last position `last` up to which keys equal to K
+// are taken: a position is selected when its key is > K, or == K at a
+// position <= last.  ne (wave-uniform) bounds the register slots in use.  The
+// radix select runs on key - L (order kept, all candidates being >= L): only
+// the bits of max - L are searched, and its leading digit spreads the
+// candidates over many bins.
+// kmax: the largest candidate key.
+template <int N>
+__device__ void candidate_cut(const uint32_t (&key)[N], const int32_t (&pos)[N], const bool (&ok)[N],
+                              int ne, uint32_t k, uint32_t L, uint32_t kmax_key, RadixShared& sh,
+                              uint32_t* K_out, uint32_t* last_out) {
+  uint32_t dk[N];
+#pragma unroll
+  for (int e = 0; e < N; e++) dk[e] = ok[e] ? key[e] - L : 0u;
+  const uint32_t kmax = kmax_key - L;
+  const int bits = kmax == 0 ? 0 : 32 - __clz(kmax);
+  const int top = max(8, bits);  // at least one pass (it counts the equal keys)
+  uint32_t rem, eq;
+  const uint32_t K = L + radix_rank<N>(dk, ok, ne, k, 0u, top, 0, sh, &rem, &eq);
+  uint32_t last = 0xffffffffu;  // equal keys at positions <= last are taken
+  if (eq > rem) {
+    uint32_t pk[N];  // larger for earlier positions, among the equal keys
+    bool pok[N];
+#pragma unroll
+    for (int e = 0; e < N; e++) {
+      pok[e] = ok[e] && key[e] == K;
+      pk[e] = ~(uint32_t)pos[e];
+    }
+    last = ~radix_rank<N>(pk, pok, ne, rem, 0u, 32, 0, sh, nullptr, nullptr);
+  }
+  *K_out = K;
+  *last_out = last;
+}
+
 // One work group per sequence.  Fast path (k < T <= 262144):
-//  1. L = the R-th largest of 4096 keys at evenly spaced positions, R a few
-//     standard deviations above the sample rank of the k-th largest key, so
-//     that at least k keys are >= L and not many more (L = 0, every key, when
-//     T <= 6144);
+//  1. L = sample_bound;
 //  2. one pass over the scores: each wave appends its keys >= L (the
 //     candidates) with their positions to its own LDS segment (ballots, no
 //     atomics);
@@ -345,8 +464,7 @@ __device__ void radix_select_global(const float* sc, int32_t T, uint32_t k, Topk
 //     a bitmap of the positions;
 //  4. a scan of the bitmap writes the positions in increasing order.
 // When the sample bound misses (fewer than k candidates, or a full segment)
-// or T is larger, a radix select over global memory gives K and rem and the
-// output pass walks all T positions.
+// or T is larger, select_general.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   __shared__ TopkShared sh;
   const int32_t b = blockIdx.x;
@@ -361,26 +479,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     return;
   }
   const float* sc = a.scores + (int64_t)b * a.score_stride;
-  bool fast = T <= kFastMaxT;
-  uint32_t L = 0;
-  if (fast && T > kAllCand) {
-    const uint32_t r = (uint32_t)(((uint64_t)k * kSample + T - 1) / T);
-    const uint32_t R = r + 4 * (uint32_t)ceilf(sqrtf((float)r)) + 16;
-    if (R >= kSample) {
-      fast = false;
-    } else {
-      uint32_t key[4];
-      bool ok[4];
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        key[e] = score_key(sc[((int64_t)(tid + kTopkThreads * e) * T) / kSample]);
-        ok[e] = true;
-      }
-      // the top 16 bits of the R-th largest sampled key: a lower bound is all
-      // the candidate pass needs
-      L = radix_rank<4>(key, ok, 4, R, 0u, 32, 16, sh, nullptr, nullptr);
-    }
-  }
+  uint32_t L;
+  bool fast = sample_bound(sc, T, k, sh.r, &L);
   if (fast) {
     const int32_t nwords = (T + 31) / 32;
     for (int32_t w = tid; w < nwords; w += kTopkThreads) sh.bits[w] = 0;
@@ -428,33 +528,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     uint32_t key[kSegLane];
     int32_t pos[kSegLane];
     bool ok[kSegLane];
-    uint32_t kmax = 0;
 #pragma unroll
     for (int e = 0; e < kSegLane; e++) {
       const uint32_t x = lane + 64 * e;
       ok[e] = x < n_seg;
       key[e] = ok[e] ? sh.cand_key[wave * kSeg + x] : 0u;
       pos[e] = ok[e] ? sh.cand_pos[wave * kSeg + x] : 0;
-      kmax = max(kmax, key[e]);
     }
-    // every candidate lies in [L, max]; K shares their common leading bits
-    kmax = block_max_u32(kmax, sh.wave);
-    const int common = (L ^ kmax) == 0 ? 32 : __clz(L ^ kmax);
-    const int top = max(8, 32 - common);  // at least one pass (it counts the equal keys)
-    const uint32_t base = top == 32 ? 0u : (L & ~((1u << top) - 1u));
-    uint32_t rem, eq;
-    const uint32_t K = radix_rank<kSegLane>(key, ok, ne, k, base, top, 0, sh, &rem, &eq);
-    uint32_t last = 0xffffffffu;  // equal keys at positions <= last are taken
-    if (eq > rem) {
-      uint32_t pk[kSegLane];      // larger for earlier positions, among the equal keys
-      bool pok[kSegLane];
+    uint32_t kmax = 0;
 #pragma unroll
-      for (int e = 0; e < kSegLane; e++) {
-        pok[e] = ok[e] && key[e] == K;
-        pk[e] = ~(uint32_t)pos[e];
-      }
-      last = ~radix_rank<kSegLane>(pk, pok, ne, rem, 0u, 32, 0, sh, nullptr, nullptr);
-    }
+    for (int e = 0; e < kSegLane; e++) kmax = max(kmax, key[e]);
+    kmax = block_max_u32(kmax, sh.r.wave);
+    uint32_t K, last;
+    candidate_cut<kSegLane>(key, pos, ok, ne, k, L, kmax, sh.r, &K, &last);
 #pragma unroll
     for (int e = 0; e < kSegLane; e++) {
       if (ok[e] && (key[e] > K || (key[e] == K && (uint32_t)pos[e] <= last)))
@@ -470,7 +556,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       wv[e] = w < nwords ? sh.bits[w] : 0u;
       nb += (uint32_t)__popc(wv[e]);
     }
-    uint32_t o = block_scan(nb, sh.wave) - nb;
+    uint32_t o = block_scan(nb, sh.r.wave) - nb;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       uint32_t x = wv[e];
@@ -481,33 +567,199 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       }
     }
   } else {
-    uint32_t K, rem;
-    radix_select_global(sc, T, k, sh, &K, &rem);
-    // thread t walks positions [t * chunk, (t + 1) * chunk)
-    const int32_t chunk = (T + kTopkThreads - 1) / kTopkThreads;
-    const int32_t p0 = min(T, tid * chunk), p1 = min(T, p0 + chunk);
-    uint32_t n_gt = 0, n_eq = 0;
-    for (int32_t i = p0; i < p1; i++) {
-      const uint32_t key = score_key(sc[i]);
-      n_gt += key > K;
-      n_eq += key == K;
-    }
-    uint32_t gt = block_scan(n_gt, sh.wave) - n_gt;
-    uint32_t eq = block_scan(n_eq, sh.wave) - n_eq;
-    for (int32_t i = p0; i < p1; i++) {
-      const uint32_t key = score_key(sc[i]);
-      if (key > K) {
-        out[gt + min(eq, rem)] = i;
-        gt++;
-      } else if (key == K) {
-        if (eq < rem) out[gt + eq] = i;
-        eq++;
-      }
-    }
+    select_general(sc, T, k, out, sh);
   }
   if (tid == 0) a.counts[b] = a.k;
 }
 
+// ------------------------------------------------------------------ split top-k
+// The same selection with the candidate pass spread over work groups of
+// kSplitChunk positions each (several per sequence), for batches too small
+// to fill the chip with one work group per sequence:
+//  * topk_cand_kernel, work group (chunk c, sequence b): L = sample_bound
+//    (every chunk of a sequence computes the same L), then the positions of
+//    the chunk whose keys are >= L, in increasing order, into the chunk's
+//    region of the candidate list and their count into ccount; chunk 0 also
+//    records whether the fast path applies;
+//  * topk_pick_kernel, work group b: the chunks' candidates concatenated in
+//    LDS (in position order), kCandCap at most, thread t holding candidates
+//    [12 t, 12 t + 12); K and last as above (candidate_cut); the selected
+//    positions written in order by a scan over the threads.  Fewer than k or
+//    more than kCandCap candidates, or no fast path: select_general.
+constexpr int kSplitChunk = 2048;                        // positions per candidate work group
+constexpr int kSplitMaxChunks = kFastMaxT / kSplitChunk;  // 128
+constexpr int kPickLane = kCandCap / kTopkThreads;       // 12
+
+struct TopkSplit {
+  int32_t* cand;    // [B][nch * kSplitChunk] candidate positions
+  uint32_t* ckey;   // [B][nch * kSplitChunk] their keys
+  int32_t* ccount;  // [B][nch] candidates per chunk
+  int32_t* fast;    // [B] the fast path applies (written by chunk 0)
+  int32_t nch;      // chunks per sequence: those of the longest sequence the fast path takes
+};
+
+__device__ inline int32_t topk_len(const TopkArgs& a, int32_t b) {
+  const int32_t T = a.seq_lens[b];
+  return T < 0 ? 0 : (T > a.score_stride ? a.score_stride : T);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_cand_kernel(TopkArgs a, TopkSplit sp) {
+  __shared__ RadixShared sh;
+  __shared__ uint32_t s_cnt[kSplitChunk / kTopkThreads][kTopkWaves];
+  const int32_t c = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t T = topk_len(a, b);
+  const int32_t p0 = c * kSplitChunk;
+  if (T <= a.k || p0 >= T) return;
+  const float* sc = a.scores + (int64_t)b * a.score_stride;
+  // the chunk's keys (position p0 + 1024 e + tid), requested with the sample's
+  constexpr int E = kSplitChunk / kTopkThreads;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    const int32_t i = p0 + kTopkThreads * e + tid;
+    v[e] = i < T ? sc[i] : 0.f;
+  }
+  uint32_t L;
+  const bool fast = sample_bound(sc, T, (uint32_t)a.k, sh, &L);
+  if (c == 0 && tid == 0) sp.fast[b] = fast ? 1 : 0;
+  if (!fast) return;
+  // wave w's candidates of round e go after those of the rounds before and of
+  // the waves before it in round e
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  bool cnd[E];
+  uint32_t kv[E];
+  uint32_t rank[E];  // among the wave's candidates of its round
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    const int32_t i = p0 + kTopkThreads * e + tid;
+    kv[e] = score_key(v[e]);
+    cnd[e] = i < T && kv[e] >= L;
+    const uint64_t m = __ballot(cnd[e]);
+    rank[e] = (uint32_t)__popcll(m & below);
+    if (lane == 0) s_cnt[e][wave] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  const int64_t base = ((int64_t)b * sp.nch + c) * kSplitChunk;
+  uint32_t total = 0;  // candidates of the rounds before e, then of the chunk
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    uint32_t waves_before = 0, round = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; w++) {
+      const uint32_t n = s_cnt[e][w];
+      waves_before += w < wave ? n : 0u;
+      round += n;
+    }
+    if (cnd[e]) {
+      sp.cand[base + total + waves_before + rank[e]] = p0 + kTopkThreads * e + tid;
+      sp.ckey[base + total + waves_before + rank[e]] = kv[e];
+    }
+    total += round;
+  }
+  if (tid == 0) sp.ccount[(int64_t)b * sp.nch + c] = (int32_t)total;
+}
+
+struct PickShared {
+  uint32_t cand_key[kCandCap];
+  int32_t cand_pos[kCandCap];
+  uint32_t hist[kBins];  // radix histogram (general path)
+  RadixShared r;
+  uint32_t first[kSplitMaxChunks + 1];  // first candidate of each chunk
+};
+
+__global__ __launch_bounds__(kTopkThreads) void topk_pick_kernel(TopkArgs a, TopkSplit sp) {
+  __shared__ PickShared sh;
+  const int32_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t T = topk_len(a, b);
+  int32_t* out = a.indices + (int64_t)b * a.index_stride;
+  const uint32_t k = (uint32_t)a.k;
+  if (T <= a.k) {  // everything is selected
+    for (int32_t i = tid; i < T; i += kTopkThreads) out[i] = i;
+    if (tid == 0) a.counts[b] = T;
+    return;
+  }
+  const float* sc = a.scores + (int64_t)b * a.score_stride;
+  bool fast = sp.fast[b] != 0;  // uniform
+  if (fast) {
+    const int32_t nc = (T + kSplitChunk - 1) / kSplitChunk;  // <= nch <= 128 on the fast path
+    if (tid < 64) {  // wave 0: chunks 2 l and 2 l + 1, scanned across the lanes
+      const int32_t c0 = 2 * tid, c1 = 2 * tid + 1;
+      const uint32_t n0 = c0 < nc ? (uint32_t)sp.ccount[(int64_t)b * sp.nch + c0] : 0u;
+      const uint32_t n1 = c1 < nc ? (uint32_t)sp.ccount[(int64_t)b * sp.nch + c1] : 0u;
+      const uint32_t incl = wave_incl_scan(n0 + n1);
+      const uint32_t f0 = incl - n0 - n1;
+      if (c0 <= nc) sh.first[c0] = f0;
+      if (c1 <= nc) sh.first[c1] = f0 + n0;  // entry nc: the total
+      if (c1 + 1 == nc) sh.first[nc] = incl;  // (nc = 128: past the last lane's pair)
+    }
+    __syncthreads();
+    const uint32_t n = sh.first[nc];
+    fast = n >= k && n <= (uint32_t)kCandCap;
+    if (fast) {
+      // the chunks' lists concatenated in LDS (position order): G threads a
+      // chunk, each copying every G-th candidate, eight requests in flight
+      const int lg = 32 - __clz((uint32_t)(nc - 1));  // ceil(log2(nc)), nc >= 1
+      const int G = kTopkThreads >> lg;
+      const int32_t c = tid / G, j = tid % G;
+      if (c < nc) {
+        const uint32_t f = sh.first[c], m = sh.first[c + 1] - f;
+        const int64_t src = ((int64_t)b * sp.nch + c) * kSplitChunk;
+        for (uint32_t i0 = (uint32_t)j; i0 < m; i0 += 8u * G) {
+          int32_t pv[8];
+          uint32_t kv[8];
+#pragma unroll
+          for (int u = 0; u < 8; u++) {
+            const uint32_t i = i0 + (uint32_t)(u * G);
+            pv[u] = i < m ? sp.cand[src + i] : 0;
+            kv[u] = i < m ? sp.ckey[src + i] : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; u++) {
+            const uint32_t i = i0 + (uint32_t)(u * G);
+            if (i < m) {
+              sh.cand_pos[f + i] = pv[u];
+              sh.cand_key[f + i] = kv[u];
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // candidates 12 t .. 12 t + 11, in position order
+      uint32_t key[kPickLane];
+      int32_t pos[kPickLane];
+      bool ok[kPickLane];
+      uint32_t nmin = 0, kmax = 0;  // ~least and largest key
+#pragma unroll
+      for (int e = 0; e < kPickLane; e++) {
+        const uint32_t x = (uint32_t)(kPickLane * tid + e);
+        ok[e] = x < n;
+        pos[e] = ok[e] ? sh.cand_pos[x] : 0;
+        key[e] = ok[e] ? sh.cand_key[x] : 0u;
+        nmin = max(nmin, ok[e] ? ~key[e] : 0u);
+        kmax = max(kmax, key[e]);
+      }
+      block_max2_u32(nmin, kmax, sh.r.wave);
+      // every candidate is >= the bound; the least candidate key is one too
+      uint32_t K, last;
+      candidate_cut<kPickLane>(key, pos, ok, kPickLane, k, ~nmin, kmax, sh.r, &K, &last);
+      bool sel[kPickLane];
+      uint32_t ns = 0;
+#pragma unroll
+      for (int e = 0; e < kPickLane; e++) {
+        sel[e] = ok[e] && (key[e] > K || (key[e] == K && (uint32_t)pos[e] <= last));
+        ns += sel[e];
+      }
+      uint32_t o = block_scan(ns, sh.r.wave) - ns;
+#pragma unroll
+      for (int e = 0; e < kPickLane; e++)
+        if (sel[e]) out[o++] = pos[e];
+    }
+  }
+  if (!fast) select_general(sc, T, k, out, sh);
+  if (tid == 0) a.counts[b] = a.k;
+}
 }  // namespace
 
 bool indexer_mfma_ok(int32_t heads, int32_t dim) { return heads == kIdxHeads && dim == kIdxDim; }
@@ -535,6 +787,31 @@ hipError_t launch_topk(const float* scores, int32_t score_stride, const int32_t*
                        int32_t* counts, hipStream_t s) {
   TopkArgs a{scores, score_stride, seq_lens, k, indices, index_stride, counts};
   hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kTopkThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+static int32_t split_chunks(int32_t score_stride) {
+  return (std::min(score_stride, kFastMaxT) + kSplitChunk - 1) / kSplitChunk;
+}
+
+size_t topk_split_ws_bytes(int32_t B, int32_t score_stride) {
+  const size_t nch = (size_t)split_chunks(score_stride);
+  return (size_t)B * (2 * nch * kSplitChunk + nch + 1) * sizeof(int32_t);
+}
+
+hipError_t launch_topk_split(const float* scores, int32_t score_stride, const int32_t* seq_lens,
+                             int32_t B, int32_t k, int32_t* indices, int32_t index_stride,
+                             int32_t* counts, void* workspace, hipStream_t s) {
+  TopkArgs a{scores, score_stride, seq_lens, k, indices, index_stride, counts};
+  TopkSplit sp;
+  int32_t* w = static_cast<int32_t*>(workspace);
+  sp.nch = split_chunks(score_stride);  // longer sequences go the general way
+  sp.cand = w;
+  sp.ckey = reinterpret_cast<uint32_t*>(w + (size_t)B * sp.nch * kSplitChunk);
+  sp.ccount = w + 2 * (size_t)B * sp.nch * kSplitChunk;
+  sp.fast = sp.ccount + (size_t)B * sp.nch;
+  hipLaunchKernelGGL(topk_cand_kernel, dim3(sp.nch, B), dim3(kTopkThreads), 0, s, a, sp);
+  hipLaunchKernelGGL(topk_pick_kernel, dim3(B), dim3(kTopkThreads), 0, s, a, sp);
   return hipGetLastError();
 }
 

@@ -141,5 +141,12 @@ hipError_t launch_indexer(const uint8_t* q, const float* q_scale, const float* w
 hipError_t launch_topk(const float* scores, int32_t score_stride, const int32_t* seq_lens,
                        int32_t B, int32_t k, int32_t* indices, int32_t index_stride,
                        int32_t* counts, hipStream_t s);
+// The same selection with the candidate pass spread over several work groups
+// per sequence; workspace of topk_split_ws_bytes(B, score_stride) bytes,
+// 4-byte aligned.
+size_t topk_split_ws_bytes(int32_t B, int32_t score_stride);
+hipError_t launch_topk_split(const float* scores, int32_t score_stride, const int32_t* seq_lens,
+                             int32_t B, int32_t k, int32_t* indices, int32_t index_stride,
+                             int32_t* counts, void* workspace, hipStream_t s);
 
 }  // namespace mla

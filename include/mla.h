@@ -366,6 +366,21 @@ mla_status mla_topk_select(const float* scores, int32_t score_stride, const int3
                            int32_t batch, int32_t k, int32_t* indices, int32_t index_stride,
                            int32_t* counts, void* stream);
 
+/* The same selection (same results bit for bit) with each sequence's
+ * candidate pass spread over work groups of 2048 positions, for batches too
+ * small to fill the GPU with one work group per sequence ("TransMLA & Sparse
+ * Latent Attention", Chapter 6, "Fine-grained token selection": the k
+ * highest-scoring positions).  batch <= 65535.  The workspace (device memory,
+ * caller-owned, 256-byte aligned, contents on entry irrelevant) holds the
+ * candidate positions and keys: mla_topk_select_split_workspace_size bytes,
+ * about 8 x min(score_stride, 262144) bytes per sequence. */
+mla_status mla_topk_select_split_workspace_size(int32_t batch, int32_t score_stride, size_t* bytes);
+
+mla_status mla_topk_select_split(const float* scores, int32_t score_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t k,
+                                 int32_t* indices, int32_t index_stride, int32_t* counts,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace mla_decode_sparse needs for index lists of row stride
  * index_stride (>= 1). */
 mla_status mla_decode_sparse_workspace_size(const mla_decode_params* p, int32_t index_stride,

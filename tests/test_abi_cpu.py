@@ -375,3 +375,42 @@ def test_no_alloc_decode_checks_before_any_hip_call():
         _lib.mla_decode_no_alloc(big, fake, fake, None, fake, fake, fake, fake, fake, fake)
     assert ei.value.status == _lib.MLA_ERR_WORKSPACE
     assert "scratch" in _lib.mla_last_error()
+
+
+def test_topk_entry_points_validate_before_launch():
+    """mla_topk_select and mla_topk_select_split reject bad sizes, null
+    pointers and a short or misaligned workspace before any HIP call; the
+    split workspace is 8 bytes (position and key) per candidate position of
+    min(score_stride, 262144) (whole chunks of 2048) plus the chunk counts."""
+    nch = -(-300 // 2048)
+    assert _lib.mla_topk_select_split_workspace_size(3, 300) == 3 * (2 * nch * 2048 + nch + 1) * 4
+    nch = 262144 // 2048
+    assert _lib.mla_topk_select_split_workspace_size(2, 10 ** 6) == 2 * (2 * nch * 2048 + nch + 1) * 4
+    for bad in ((-1, 300), (65536, 300), (2, 0)):
+        with pytest.raises(_lib.MlaError) as ei:
+            _lib.mla_topk_select_split_workspace_size(*bad)
+        assert ei.value.status == _lib.MLA_ERR_INVALID_ARG
+    fake = 0x10000
+    n = _lib.mla_topk_select_split_workspace_size(2, 5000)
+    for call in (lambda **kw: _lib.mla_topk_select(**kw),
+                 lambda **kw: _lib.mla_topk_select_split(**kw, workspace=fake, workspace_bytes=n)):
+        base = dict(scores=fake, score_stride=5000, seq_lens=fake, batch=2, k=64, indices=fake,
+                    index_stride=64, counts=fake)
+        for key, val in (("k", 0), ("index_stride", 63), ("score_stride", 0), ("batch", -1),
+                         ("scores", None), ("counts", None)):
+            kw = dict(base)
+            kw[key] = val
+            with pytest.raises(_lib.MlaError) as ei:
+                call(**kw)
+            assert ei.value.status == _lib.MLA_ERR_INVALID_ARG, key
+    base = dict(scores=fake, score_stride=5000, seq_lens=fake, batch=2, k=64, indices=fake,
+                index_stride=64, counts=fake)
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_topk_select_split(**base, workspace=fake, workspace_bytes=n - 1)
+    assert ei.value.status == _lib.MLA_ERR_WORKSPACE
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_topk_select_split(**base, workspace=None, workspace_bytes=n)
+    assert ei.value.status == _lib.MLA_ERR_WORKSPACE
+    with pytest.raises(_lib.MlaError) as ei:
+        _lib.mla_topk_select_split(**base, workspace=fake + 16, workspace_bytes=n)
+    assert ei.value.status == _lib.MLA_ERR_INVALID_ARG

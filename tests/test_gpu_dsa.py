@@ -107,13 +107,31 @@ def _scores_with_ties(rng, T):
     return s
 
 
+TOPK = ["one_group", "split"]
+
+
+def run_topk(variant, scores, stride, lens, B, k, idx, index_stride, cnt):
+    """mla_topk_select (one work group per sequence) or mla_topk_select_split
+    (candidate pass over several work groups per sequence)."""
+    if variant == "one_group":
+        _lib.mla_topk_select(scores, stride, lens, B, k, idx, index_stride, cnt)
+    else:
+        n = _lib.mla_topk_select_split_workspace_size(B, stride)
+        ws = torch.empty(n, dtype=torch.uint8, device=scores.device)
+        ws.fill_(0xAB)  # stale contents must not matter
+        _lib.mla_topk_select_split(scores, stride, lens, B, k, idx, index_stride, cnt, ws, n)
+
+
+@pytest.mark.parametrize("variant", TOPK)
 @pytest.mark.parametrize("k,lens", [
     (300, [0, 1, 299, 300, 301, 5000, 4096, 777]),
     (2048, [131072, 2047, 2049, 65536]),
     (1, [1, 2, 50, 9]),
+    # one candidate chunk, chunk edges, a ragged last chunk, 128 chunks
+    (700, [2048, 2049, 4095, 6145, 262144, 9000]),
 ])
-def test_topk_bit_exact(k, lens):
-    _say(f"top-k k={k} lens={lens}")
+def test_topk_bit_exact(k, lens, variant):
+    _say(f"top-k {variant} k={k} lens={lens}")
     rng = np.random.default_rng(900 + k)
     B, stride = len(lens), max(lens) + 3
     scores = np.full((B, stride), np.nan, np.float32)
@@ -124,7 +142,7 @@ def test_topk_bit_exact(k, lens):
     lt = torch.tensor(lens, dtype=torch.int32, device=dev)
     idx = torch.full((B, k + 5), -7, dtype=torch.int32, device=dev)
     cnt = torch.full((B,), -7, dtype=torch.int32, device=dev)
-    _lib.mla_topk_select(st, stride, lt, B, k, idx, k + 5, cnt)
+    run_topk(variant, st, stride, lt, B, k, idx, k + 5, cnt)
     torch.cuda.synchronize()
     idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
     for b, T in enumerate(lens):
@@ -134,10 +152,12 @@ def test_topk_bit_exact(k, lens):
         assert (idx[b, len(want):] == -7).all()
 
 
-def test_topk_paths_past_the_sample_bound():
+@pytest.mark.parametrize("variant", TOPK)
+def test_topk_paths_past_the_sample_bound(variant):
     """Inputs the sampled lower bound cannot serve: a sequence longer than the
     in-LDS path allows, large scores only between the sampled positions, and k
     close to T -- all must still match the oracle bit for bit."""
+    _say(f"top-k {variant} past the sample bound")
     rng = np.random.default_rng(4242)
     T1, T2, T3 = 300000, 20000, 20000
     lens, ks = [T1, T2, T3], 2048
@@ -156,7 +176,7 @@ def test_topk_paths_past_the_sample_bound():
         lt = torch.tensor(lens, dtype=torch.int32, device=dev)
         idx = torch.full((3, k), -7, dtype=torch.int32, device=dev)
         cnt = torch.empty((3,), dtype=torch.int32, device=dev)
-        _lib.mla_topk_select(st, stride, lt, 3, k, idx, k, cnt)
+        run_topk(variant, st, stride, lt, 3, k, idx, k, cnt)
         torch.cuda.synchronize()
         got, c = idx.cpu().numpy(), cnt.cpu().numpy()
         for b, T in enumerate(lens):
@@ -164,7 +184,9 @@ def test_topk_paths_past_the_sample_bound():
             assert c[b] == len(want) and np.array_equal(got[b, :len(want)], want), (k, b)
 
 
-def test_topk_all_equal_scores_take_the_earliest():
+@pytest.mark.parametrize("variant", TOPK)
+def test_topk_all_equal_scores_take_the_earliest(variant):
+    _say(f"top-k {variant} all equal")
     dev = torch.device("cuda")
     T, k = 10000, 2048
     s = torch.zeros((2, T), dtype=torch.float32, device=dev)
@@ -172,7 +194,7 @@ def test_topk_all_equal_scores_take_the_earliest():
     lens = torch.tensor([T, T], dtype=torch.int32, device=dev)
     idx = torch.empty((2, k), dtype=torch.int32, device=dev)
     cnt = torch.empty((2,), dtype=torch.int32, device=dev)
-    _lib.mla_topk_select(s, T, lens, 2, k, idx, k, cnt)
+    run_topk(variant, s, T, lens, 2, k, idx, k, cnt)
     torch.cuda.synchronize()
     assert (cnt.cpu().numpy() == k).all()
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(k), (2, 1)))
