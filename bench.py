@@ -42,11 +42,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), DSV3 shape @32K ctx"
-ATTN_SOURCE = os.path.join(ROOT, "head_latent_attention_10_amd", "csrc", "mla_attend_mfma.hip")
+CSRC = os.path.join(ROOT, "head_latent_attention_10_amd", "csrc")
 
 
-def attn_source_hash() -> str:
-    with open(ATTN_SOURCE, "rb") as f:
+def attn_source(workload: str) -> str:
+    """The source file of the attention kernel that serves `workload`: the fp8
+    kernel's for an fp8 cache, the bf16 matrix-core kernel's otherwise."""
+    from mla_inputs import CONFIGS
+    cfg = CONFIGS.get(workload)
+    fp8 = cfg is not None and cfg.cache_dtype == "e4m3"
+    return os.path.join(CSRC, "mla_attend_fp8.hip" if fp8 else "mla_attend_mfma.hip")
+
+
+def attn_source_hash(workload: str) -> str:
+    with open(attn_source(workload), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -59,7 +68,7 @@ def measured_counters(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != attn_source_hash():
+    if rec.get("kernel_source_sha256_16") != attn_source_hash(workload):
         return None
     return rec
 
@@ -72,7 +81,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != attn_source_hash():
+    if rec.get("kernel_source_sha256_16") != attn_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -626,7 +635,8 @@ def measure_prefill(spec: str, steps: int, warmup: int):
 
 def kernel_class(name: str):
     """The decode-step stage a rocprofv3 kernel name belongs to (None: other)."""
-    for key, cls in (("attend64_kernel", "attention"), ("attend_mfma_kernel", "attention"),
+    for key, cls in (("attend64_kernel", "attention"), ("attend64_fp8_kernel", "attention"),
+                     ("attend_mfma_kernel", "attention"),
                      ("attend_fp8_kernel", "attention"), ("attend_simt_kernel", "attention"),
                      ("absorb", "absorb"), ("combine", "combine"), ("up_project", "up_project"),
                      ("plan_kernel", "plan"), ("copyBuffer", "copy")):
@@ -666,7 +676,8 @@ def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: in
             for cls in set(fetch["kernels"]) | set(write["kernels"])}
     rec = {
         "workload": workload,
-        "kernel_source_sha256_16": attn_source_hash(),
+        "kernel_source": os.path.basename(attn_source(workload)),
+        "kernel_source_sha256_16": attn_source_hash(workload),
         "copy_calibration_mib": copy_mb,
         "fetch": fetch,
         "write": write,
@@ -703,7 +714,8 @@ def summarize_counters(workload: str, dirs, commands):
     att = stages["attention"]
     rec = {
         "workload": workload,
-        "kernel_source_sha256_16": attn_source_hash(),
+        "kernel_source": os.path.basename(attn_source(workload)),
+        "kernel_source_sha256_16": attn_source_hash(workload),
         "mfma_util": round(att["MfmaUtil"] / 100.0, 4) if "MfmaUtil" in att else None,
         "stages": stages,
         "commands": commands,
@@ -811,6 +823,14 @@ def main():
                     "attn_kernel_ms_pct": r["attn_ms_pct"],
                     "attn_cache_GBps": round(r["attn_gbps"], 1),
                     "attn_frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4)}
+        # committed counter summaries of this workload's attention kernel, if
+        # taken on its current source
+        wc = measured_counters(w)
+        if wc:
+            extra[w]["attn_mfma_util"] = wc.get("mfma_util")
+        wt = measured_traffic(w)
+        if wt:
+            extra[w]["attn_hbm_bytes_per_launch"] = wt
         del r
     for w in [w for w in args.writers.split(",") if w]:
         extra["cache_" + w] = measure_writer(w, max(320, args.steps), max(5, args.warmup))
