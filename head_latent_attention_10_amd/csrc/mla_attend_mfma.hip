@@ -905,28 +905,46 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     // latent fragments of two steps: slot j % 2 holds those of step j - 2
     // until its products are issued, then receives those of step j
     bf16x8 cb[2][MD][2];
-    // fragment (md, kk) of the tile in stage st; ln is this lane, recomputed
-    // from an opaque copy in every step so that the compiler does not keep
-    // sixteen read addresses live across the loop
-    auto ld_c = [&](const lds_t* st, int ln, int md, int kk) -> bf16x8 {
-      const int j16 = ln & 15, grp = ln >> 4, e = j16 >> 2, qd = j16 & 3, gg = ln >> 5;
-      const int dd = 32 * (v * MD + md) + 16 * (grp & 1) + 4 * qd;  // within the shard
-      const int chunk = dd >> 3, hoff = (dd & 7) * 2;
-      const int r0 = 16 * kk + 4 * gg + e;
-      const int r1 = r0 + 8;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-              const_cast<lds_t*>(st) + r0 * Sh::CRow + ((chunk ^ swz_c(r0)) << 4) + hoff));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
-              const_cast<lds_t*>(st) + r1 * Sh::CRow + ((chunk ^ swz_c(r1)) << 4) + hoff));
-      const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      return __builtin_bit_cast(bf16x8, cat);
+    // The fragment reads of one step.  Lane (e, qd, grp, gg) reads rows
+    // r = 16 kk + 4 gg + e (+ 8) at latent value 32 m + 16 (grp & 1) + 4 qd of
+    // block m = v MD + md (within the shard); with the row's chunk swizzle s,
+    // that piece sits at rows(kk, h) + 64 (m ^ (s >> 2)), rows() holding the
+    // row, the swizzled low chunk bits and the 8-byte half (ring-relative
+    // offsets, computed once per step from an opaque copy of the lane so that
+    // the compiler keeps no read addresses live across the loop).
+    struct FragRows {
+      uint32_t base[2][2], t[2][2];
     };
-    auto stage_of = [&](int32_t j) -> const lds_t* {
+    auto frag_rows = [&](int32_t j) -> FragRows {
       int off = (j % kStages) * Sh::Stage;
       asm volatile("" : "+s"(off));
-      return ring + off;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int j16 = ln & 15, grp = ln >> 4, e = j16 >> 2, qd = j16 & 3, gg = ln >> 5;
+      const int c_low = 2 * (grp & 1) + (qd >> 1);
+      FragRows fr;
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+          const int r = 16 * kk + 4 * gg + e + 8 * h2;
+          const int sw = swz_c(r);
+          fr.base[kk][h2] = (uint32_t)(off + r * Sh::CRow + ((c_low ^ (sw & 3)) << 4) + 8 * (qd & 1));
+          fr.t[kk][h2] = (uint32_t)(sw >> 2);
+        }
+      return fr;
+    };
+    // fragment (md, kk): two 4-row transposing reads
+    auto ld_c = [&](const FragRows& fr, int md, int kk) -> bf16x8 {
+      const uint32_t m = (uint32_t)(v * MD + md);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+              ring + (fr.base[kk][0] + ((m ^ fr.t[kk][0]) << 6))));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<i16x4 __attribute__((address_space(3)))*>(
+              ring + (fr.base[kk][1] + ((m ^ fr.t[kk][1]) << 6))));
+      const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, cat);
     };
     // w2 and w3 are loader lanes 0 and 1: every step they wait for their
     // loads of that step before its barrier and issue the loads two steps
@@ -944,23 +962,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     wg_barrier();
     if (loader) ld.issue_ahead(a, ring, win, t_begin, v, lane);
     {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
+      const FragRows fr = frag_rows(0);
 #pragma unroll
       for (int md = 0; md < MD; md++)
 #pragma unroll
-        for (int kk = 0; kk < 2; kk++) cb[0][md][kk] = ld_c(stage_of(0), ln, md, kk);
+        for (int kk = 0; kk < 2; kk++) cb[0][md][kk] = ld_c(fr, md, kk);
     }
     if (loader) ld.template wait_current<kVStores>(0);
     wg_barrier();
     if (loader) ld.issue_ahead(a, ring, win, t_begin, v, lane);
     if (n > 1) {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
+      const FragRows fr = frag_rows(1);
 #pragma unroll
       for (int md = 0; md < MD; md++)
 #pragma unroll
-        for (int kk = 0; kk < 2; kk++) cb[1][md][kk] = ld_c(stage_of(1), ln, md, kk);
+        for (int kk = 0; kk < 2; kk++) cb[1][md][kk] = ld_c(fr, md, kk);
     }
     f32x16 o[MD][2];
 #pragma unroll
@@ -971,9 +987,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
       if (loader) ld.template wait_current<kVStores>(sb1 + sb2);
       wg_barrier();
       const bool load = j < n;
-      const lds_t* st = stage_of(j);
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
       // the weights and the rescale flag of step j - 2 first: the products
       // wait for nothing else
       bf16x8 pf[2][2];
@@ -987,6 +1000,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
       // the descriptor of the loads issued after the products, read with the
       // weights (one LDS round trip before the first product)
       const Tile nd = loader ? ld.peek(win) : Tile{};
+      const FragRows fr = frag_rows(j);
       if (__builtin_amdgcn_readfirstlane(flag)) {
         const float a0 = s_alpha[(SL * 2) * 32 + (lane & 31)];
         const float a1 = s_alpha[(SL * 2 + 1) * 32 + (lane & 31)];
@@ -1008,7 +1022,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
                                                                 o[md][hb], 0, 0, 0);
         if (load) {
 #pragma unroll
-          for (int kk = 0; kk < 2; kk++) cb[SL][md][kk] = ld_c(st, ln, md, kk);
+          for (int kk = 0; kk < 2; kk++) cb[SL][md][kk] = ld_c(fr, md, kk);
         }
         // keep the reads behind the products that free their registers
         __builtin_amdgcn_sched_barrier(0);
