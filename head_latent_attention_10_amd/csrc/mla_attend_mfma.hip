@@ -687,6 +687,7 @@ static_assert(Shard<1>::KPW == 18 && Shard<1>::Stage == kStage, "the whole-row k
 template <bool SP, int G = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_kernel(AttnArgs a) {
   using Sh = Shard<G>;
+  constexpr bool kScoreLoads = G > 1;  // loader lanes 2, 3 on the score waves
   __shared__ __attribute__((aligned(1024))) char smem[lds64<G>()];
   lds_t* ring = (lds_t*)smem;
   lds_t* win = ring + Sh::Ring;                     // [2][kWin] tile descriptors
@@ -746,6 +747,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
       }
     };
     Tile cur = global_tile(a, t_begin), prev{};
+    // Sharded steps: the score waves, idle for much of a step, issue the
+    // loads of loader lanes 2 and 3 (the softmax waves' in the whole-row
+    // kernel), after their products and the next segment's query.
+    Loader<4, SP, G> sld;
+    sld.c0b = (uint32_t)(shard * Sh::CRow);
+    if constexpr (kScoreLoads) sld.start(a, ring, win, t_begin, n, 2 + kh, lane);
     issue_q(cur.b);
     if (wave == 1) {
       load_window(a, win, t_begin, t_end, 0, lane);
@@ -755,9 +762,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     wg_barrier();
     const int row = lane & 31;
     for (int32_t j = 0; j <= n + 1; j++) {
+      // (loading: the wait for step j's loads also covers the query requested
+      // before them)
+      if constexpr (kScoreLoads) sld.template wait_current<1>(0);
       wg_barrier();
       if (j < n) {
-        if (j > 0 && prev.last) wait_vmcnt<0>();  // the new segment's query
+        if (!kScoreLoads && j > 0 && prev.last) wait_vmcnt<0>();  // the new segment's query
         const lds_t* st = ring + (j % kStages) * Sh::Stage;
         auto ld_a = [&](int k) -> bf16x8 {
           const int ks = K0 + k;
@@ -796,6 +806,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
           if (prev.last) issue_q(cur.b);
         }
       }
+      if constexpr (kScoreLoads) sld.issue_ahead(a, ring, win, t_begin, 2 + kh, lane);
     }
   } else if (wave == 4 || wave == 5) {
     // ================================================================ softmax + loader waves
@@ -805,15 +816,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     // loads of its step
     Loader<4, SP, G> ld;
     ld.c0b = (uint32_t)(shard * Sh::CRow);
-    ld.start(a, ring, win, t_begin, n, 2 + hb, lane);
+    if constexpr (!kScoreLoads) ld.start(a, ring, win, t_begin, n, 2 + hb, lane);
     int sb1 = 0, sb2 = 0;
     wg_barrier();
     float m_run = -INFINITY, l_run = 0.f;
     int32_t seg_step = 0;
     for (int32_t j = 0; j <= n + 1; j++) {
-      ld.template wait_current<1>(sb1 + sb2);
+      if constexpr (!kScoreLoads) ld.template wait_current<1>(sb1 + sb2);
       wg_barrier();
-      ld.issue_ahead(a, ring, win, t_begin, 2 + hb, lane);
+      if constexpr (!kScoreLoads) ld.issue_ahead(a, ring, win, t_begin, 2 + hb, lane);
       int sb = 0;
       if (j >= 1 && j <= n) {
         const int par = (j - 1) & 1;
