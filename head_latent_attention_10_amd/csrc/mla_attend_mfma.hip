@@ -663,6 +663,9 @@ void attend_mfma_kernel(AttnArgs a) {
 //    waves that load issue theirs after their products (w6 and w7, the
 //    second value wave of each value SIMD, finish later and issue none), and
 //    the softmax waves, which have time to spare, right after the barrier.
+//    In the sharded instantiations (G > 1) the softmax waves set the step's
+//    length instead, and the score waves issue lanes 2 and 3 after their
+//    products.
 //
 // Step j (one barrier): loaders wait for their loads of step j; barrier;
 // softmax waves issue their part of step j + 2 into the stage tile j - 1 used,
