@@ -277,13 +277,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
 // LSEs and the split table entries that say whether a split owns tiles (one
 // that owns none wrote nothing: weight 0, and its stale piece is never
 // multiplied in).  Longer ranges take further passes with a running maximum.
+// kCombPass slots a pass: 16, or 8 when sequences average at most 4 splits
+// (large batches: half the registers, twice the work groups in flight).
 constexpr int kFragLat = 512;
-constexpr int kCombPass = 16;
 
 // With TPLA shards (a.shards > 1) block (b, hblk, mdg) merges the columns of
 // output head block hblk that lie in shard j = mdg / (16 / shards), from the
 // partials of shard head block j (h / shards) / 32 + hblk, into an output of
 // h / shards heads: the shard heads' other columns are neither read nor written.
+template <int kCombPass>
 __global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __restrict__ o_lat) {
   __shared__ float s_w[kCombPass][32];  // LSEs of the pass's slots, then their weights
   __shared__ float s_M[32], s_W[32], s_alpha[32];
@@ -376,8 +378,11 @@ hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s) {
   if (a.frag_layout) {
     const int32_t G = a.shards > 1 ? a.shards : 1;
     if (a.d_c != kFragLat || a.h % (32 * G) || a.streams != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(combine_frag_kernel, dim3(a.B, a.h / G / 32, kFragLat / 32), dim3(256), 0, s,
-                       a, o_lat);
+    const dim3 grid(a.B, a.h / G / 32, kFragLat / 32);
+    if (a.splits <= 4 * a.B)
+      hipLaunchKernelGGL(combine_frag_kernel<8>, grid, dim3(256), 0, s, a, o_lat);
+    else
+      hipLaunchKernelGGL(combine_frag_kernel<16>, grid, dim3(256), 0, s, a, o_lat);
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3(a.B, a.h), dim3(kCombThreads), 0, s, a, o_lat);
   }
