@@ -17,12 +17,14 @@
 // accumulation): indexer heads on M, tokens on N, so one lane's accumulator
 // holds 16 heads of one token and the head sum is in-lane plus one exchange.
 //
-// Top-k: one work group per sequence.  Scores map to unsigned keys that order
-// like the floats (-0 taken as +0).  A sample bounds the k-th largest key from
-// below, the keys above the bound are gathered in position order in LDS, and
-// the k-th largest key K and how many keys equal to K are taken (the earliest
-// positions) are found there by counting; the selected positions come out in
-// increasing order (details at topk_kernel).
+// Top-k.  Scores map to unsigned keys that order like the floats (-0 taken as
+// +0).  A sample bounds the k-th largest key from below, the keys above the
+// bound are gathered in position order, and the k-th largest key K and how
+// many keys equal to K are taken (the earliest positions) are found by
+// counting; the selected positions come out in increasing order.  Either one
+// work group per sequence does all of it (topk_kernel), or work groups of 2048
+// positions gather the candidates and one work group per sequence selects
+// (topk_cand_kernel, topk_pick_kernel); both give the same selection.
 #include <algorithm>
 
 #include "mla_mfma_util.hpp"
