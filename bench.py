@@ -662,7 +662,9 @@ def kernel_class(name: str):
     for key, cls in (("attend64_kernel", "attention"), ("attend64_fp8_kernel", "attention"),
                      ("attend_mfma_kernel", "attention"),
                      ("attend_fp8_kernel", "attention"), ("attend_simt_kernel", "attention"),
-                     ("absorb", "absorb"), ("combine", "combine"), ("up_project", "up_project"),
+                     ("absorb", "absorb"), ("up16_mfma_kernel<true", "merge_up"),
+                     ("up16_mfma_kernel<false", "up_project"), ("merge_kernel", "combine"),
+                     ("combine", "combine"), ("up_project", "up_project"),
                      ("plan_kernel", "plan"), ("copyBuffer", "copy")):
         if key in name:
             return cls
@@ -686,7 +688,7 @@ def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, copy_mb: in
         copy_kib = max(copies)[1]   # the calibration copy is the run's last dispatch
         factor = copy_mb * 1024.0 / copy_kib
         per = {}
-        for cls in ("attention", "absorb", "combine", "up_project", "plan"):
+        for cls in ("attention", "absorb", "merge_up", "combine", "up_project", "plan"):
             vals = [v for _, k, _, v in rows if kernel_class(k) == cls]
             if vals:
                 per[cls] = {"kib_median": statistics.median(vals), "dispatches": len(vals),

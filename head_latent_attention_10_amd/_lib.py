@@ -280,10 +280,10 @@ def mla_combine(p, o_lat, workspace, workspace_bytes=None, stream=None):
 
 
 def mla_partials_layout(p):
-    """(part_o byte offset, part_lse byte offset, slots, fragment_major) of the
+    """(part_o byte offset, part_lse byte offset, slots, bf16_rows) of the
     partials mla_attend_partial writes into the workspace for *p; the partial
-    outputs are bf16 fragment-major when fragment_major is 1, else fp32
-    row-major."""
+    outputs are row-major [slot][head][d_latent], bf16 when bf16_rows is 1,
+    else fp32."""
     a, b = ctypes.c_size_t(), ctypes.c_size_t()
     n, f = ctypes.c_int32(), ctypes.c_int32()
     _check("mla_partials_layout", load_library().mla_partials_layout(

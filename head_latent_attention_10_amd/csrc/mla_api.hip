@@ -132,7 +132,7 @@ mla_status layout(const mla_decode_params& p, Layout* L, int32_t sparse_stride =
   const size_t tiles_per_seq = (cap + mla::kTile - 1) / mla::kTile;
   off = align256(off + B * tiles_per_seq * 4 * sizeof(int32_t));
   L->part_o = off;
-  // fragment-major partials (the matrix-core shapes) are bf16, others fp32
+  // partials of the matrix-core shapes are bf16, others fp32
   off = align256(off + (size_t)L->slots * h * dc * (mla::mfma_any_supported(p) ? 2 : 4));
   L->part_lse = off;
   off = align256(off + (size_t)L->slots * h * sizeof(float));
@@ -216,9 +216,9 @@ mla::AttnArgs attn_args(const mla_decode_params& p, const Layout& L, char* ws,
   a.num_blocks = p.num_blocks;
   a.splits = L.splits;
   a.streams = L.streams;
-  // the partial layout follows the shape: fragment-major for the shapes the
-  // matrix-core kernels serve (whichever kernel runs), row-major otherwise
-  a.frag_layout = mla::mfma_any_supported(p) ? 1 : 0;
+  // the partial type follows the shape: bf16 for the shapes the matrix-core
+  // kernels serve (whichever kernel runs), fp32 otherwise
+  a.part_bf16 = mla::mfma_any_supported(p) ? 1 : 0;
   a.sm_scale_log2 = resolved_scale(p) * 1.4426950408889634f;
   return a;
 }
@@ -351,9 +351,17 @@ mla_status decode_impl(const mla_decode_params* p, const void* q, const void* c_
   hipError_t e =
       mla::launch_absorb(*p, q, W_UK, ws + L.q_lat, absorbed_dtype(*p), &plan, &planned, s);
   if (e != hipSuccess) return hip_fail(e, "absorb launch");
+  st = attend_partial(*p, L, ws + L.q_lat, c_kv, c_kv_scale, k_rope, plan, ws, s, planned,
+                      static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after),
+                      groups);
+  if (st != MLA_OK) return st;
+  if (mla::merge_up_supported(*p) && aligned16(W_UV)) {
+    // merge and up-projection in one launch (the same bits as the two stages)
+    e = mla::launch_merge_up(*p, attn_args(*p, L, ws, nullptr, nullptr), W_UV, out, s);
+    return e == hipSuccess ? MLA_OK : hip_fail(e, "merge + up-projection launch");
+  }
   float* o_lat = reinterpret_cast<float*>(ws + L.o_lat);
-  st = attend(*p, L, ws + L.q_lat, c_kv, c_kv_scale, k_rope, plan, o_lat, ws, s, planned,
-              static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after), groups);
+  st = combine(*p, L, ws, o_lat, s);
   if (st != MLA_OK) return st;
   e = mla::launch_up_project(*p, o_lat, W_UV, out, s);
   return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
@@ -641,11 +649,11 @@ mla_status mla_combine(const mla_decode_params* p, float* o_lat, void* workspace
 }
 
 mla_status mla_partials_layout(const mla_decode_params* p, size_t* part_o_offset,
-                               size_t* part_lse_offset, int32_t* slots, int32_t* fragment_major) {
+                               size_t* part_lse_offset, int32_t* slots, int32_t* bf16_rows) {
   g_last_error.clear();
   mla_status st = validate(p);
   if (st != MLA_OK) return st;
-  if (!part_o_offset || !part_lse_offset || !slots || !fragment_major)
+  if (!part_o_offset || !part_lse_offset || !slots || !bf16_rows)
     return fail(MLA_ERR_INVALID_ARG, "null output pointer");
   Layout L;
   st = layout(*p, &L);
@@ -653,7 +661,7 @@ mla_status mla_partials_layout(const mla_decode_params* p, size_t* part_o_offset
   *part_o_offset = L.part_o;
   *part_lse_offset = L.part_lse;
   *slots = (int32_t)L.slots;
-  *fragment_major = mla::mfma_any_supported(*p) ? 1 : 0;
+  *bf16_rows = mla::mfma_any_supported(*p) ? 1 : 0;
   return MLA_OK;
 }
 
@@ -1011,7 +1019,7 @@ mla_status mla_tpla_decode(const mla_decode_params* p, const mla_tpla_params* t,
   if (e != hipSuccess) return hip_fail(e, "expand launch");
   float* o2 = reinterpret_cast<float*>(ws + L.dec.o_lat);
   float* o1 = reinterpret_cast<float*>(ws + L.o_lat1);
-  // With bf16 fragment-major partials and whole 32-head blocks the merge takes
+  // With bf16 partials and whole 32-head blocks the merge takes
   // each head's own shard columns straight into o1 (and the 64-head attention
   // reads only its shard); otherwise every shard head is merged whole and the
   // gather picks the columns.

@@ -565,14 +565,10 @@ void attend_fp8_kernel(AttnArgs a) {
 #pragma unroll
           for (int hb = 0; hb < HB; hb++) {
             uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc8 +
-                            frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
+                            part_row(hg * HB + hb, pw_id * MDP, lane);
 #pragma unroll
             for (int md = 0; md < MDP; md++) {
-#pragma unroll
-              for (int jj = 0; jj < 4; jj++)
-                *reinterpret_cast<uint2*>(dst + (md * 4 + jj) * 256) =
-                    pack_bf16x4(o[md][hb][4 * jj] * inv[hb], o[md][hb][4 * jj + 1] * inv[hb],
-                                o[md][hb][4 * jj + 2] * inv[hb], o[md][hb][4 * jj + 3] * inv[hb]);
+              store_block_bf16(dst + md * 32, o[md][hb], inv[hb], lane);
               o[md][hb] = f32x16{};
             }
           }
@@ -1007,7 +1003,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
       asm volatile("" : "+s"(off));
       return ring + off;
     };
-    constexpr int kVStores = 2 * MD * 4;
+    constexpr int kVStores = 2 * MD * 2;  // two 16-byte stores per 32-value block and head block
     const bool loader = v < 2;
     LoaderF<2, SP> ld;
     if (loader) ld.start(a, ring, win, t_begin, n, v, lane);
@@ -1083,14 +1079,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
         for (int hb = 0; hb < 2; hb++) {
           const float inv = s_invl[(SL * 2 + hb) * 32 + (lane & 31)];
           uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc8 +
-                          frag_offset(hg * 2 + hb, v * MD, 0, lane);
+                          part_row(hg * 2 + hb, v * MD, lane);
 #pragma unroll
           for (int md = 0; md < MD; md++) {
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++)
-              *reinterpret_cast<uint2*>(dst + (md * 4 + jj) * 256) =
-                  pack_bf16x4(o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
-                              o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv);
+            store_block_bf16(dst + md * 32, o[md][hb], inv, lane);
             o[md][hb] = f32x16{};
           }
         }

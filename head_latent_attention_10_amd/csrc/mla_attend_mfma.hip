@@ -80,7 +80,7 @@ struct Shape {
   static constexpr int NP = 4 * HB;             // value waves
   static constexpr int NW = NQ + NP;
   static constexpr int MDP = kDc / 32 / NP;     // 32-row output blocks per value wave
-  static constexpr int kStores = MDP * 4 * HB;  // partial-output stores of a value wave per segment
+  static constexpr int kStores = MDP * 2 * HB;  // partial-output stores of a value wave per segment
   // ring | descriptor window | xbuf [2][HB] | pbuf [2][HB] | alpha, 1/l [2][HB][32] | flag [2][HB]
   static constexpr int LDS =
       kRing + kWinBytes + 2 * HB * (kXBytes + kPBytes) + 2 * HB * 32 * 4 * 2 + 2 * HB * 4;
@@ -608,16 +608,12 @@ void attend_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int hb = 0; hb < HB; hb++) {
             const float inv = s_invl[(par * HB + hb) * 32 + (lane & 31)];
-            // fragment-major bf16 partial: one store instruction writes 512 B contiguous
+            // bf16 partial rows: a store writes 32 contiguous bytes of each of 32 heads
             uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc +
-                            frag_offset(hg * HB + hb, pw_id * MDP, 0, lane);
+                            part_row(hg * HB + hb, pw_id * MDP, lane);
 #pragma unroll
             for (int md = 0; md < MDP; md++) {
-#pragma unroll
-              for (int jj = 0; jj < 4; jj++)
-                *reinterpret_cast<uint2*>(dst + (md * 4 + jj) * 256) =
-                    pack_bf16x4(o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
-                                o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv);
+              store_block_bf16(dst + md * 32, o[md][hb], inv, lane);
               o[md][hb] = f32x16{};
             }
           }
@@ -964,7 +960,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
     // loads of that step before its barrier and issue the loads two steps
     // ahead after their products; a segment end adds one group of kVStores
     // stores after those loads
-    constexpr int kVStores = 2 * MD * 4;
+    constexpr int kVStores = 2 * MD * 2;  // two 16-byte stores per 32-value block and head block
     const bool loader = v < 2;
     Loader<4, SP, G> ld;
     ld.c0b = (uint32_t)(shard * Sh::CRow);
@@ -1051,14 +1047,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void attend64_
         for (int hb = 0; hb < 2; hb++) {
           const float inv = s_invl[(SL * 2 + hb) * 32 + (lane & 31)];
           uint16_t* dst = static_cast<uint16_t*>(a.part_o) + slot * a.h * kDc +
-                          frag_offset(hg * 2 + hb, shard * (Sh::W / 32) + v * MD, 0, lane);
+                          part_row(hg * 2 + hb, shard * (Sh::W / 32) + v * MD, lane);
 #pragma unroll
           for (int md = 0; md < MD; md++) {
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++)
-              *reinterpret_cast<uint2*>(dst + (md * 4 + jj) * 256) =
-                  pack_bf16x4(o[md][hb][4 * jj] * inv, o[md][hb][4 * jj + 1] * inv,
-                              o[md][hb][4 * jj + 2] * inv, o[md][hb][4 * jj + 3] * inv);
+            store_block_bf16(dst + md * 32, o[md][hb], inv, lane);
             o[md][hb] = f32x16{};
           }
         }

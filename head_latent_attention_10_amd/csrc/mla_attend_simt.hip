@@ -117,12 +117,11 @@ __global__ __launch_bounds__(256) void attend_simt_kernel(AttnArgs a) {
       for (int k = 0; k < kSimtPerThread; k++) {
         const int32_t d = tid + 256 * k;
         if (d >= d_c) continue;
-        // the matrix-core shapes keep their partials bf16 and fragment-major
-        // (what the combine reads for them), whichever kernel wrote them
-        if (a.frag_layout) {
-          const int64_t off =
-              frag_offset(head >> 5, d >> 5, (d >> 3) & 3, ((d >> 2) & 1) * 32 + (head & 31)) + (d & 3);
-          static_cast<uint16_t*>(a.part_o)[slot * a.h * d_c + off] = f32_to_bf16_bits(o[k] * inv);
+        // the matrix-core shapes keep their partials bf16 (what the merge
+        // reads for them), whichever kernel wrote them
+        if (a.part_bf16) {
+          static_cast<uint16_t*>(a.part_o)[slot * a.h * d_c + (int64_t)head * d_c + d] =
+              f32_to_bf16_bits(o[k] * inv);
         } else {
           static_cast<float*>(a.part_o)[slot * a.h * d_c + (int64_t)head * d_c + d] = o[k] * inv;
         }

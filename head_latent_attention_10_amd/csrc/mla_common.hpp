@@ -26,14 +26,13 @@ __host__ __device__ inline int32_t tile_word(int32_t nv, bool last, int32_t off)
   return nv | ((int32_t)last << 6) | (off << 7);
 }
 
-// Fragment-major layout of one slot's partial output, used by the matrix-core
-// kernel (512 latent values, heads a multiple of 32): the slot's [h, 512] fp32
-// block is stored as [h/32][16][4][64][4] = (head block, 32-value latent block
-// mdg, 8-value group jj, lane, 4 values), where lane = 32*g + r holds head
-// 32*hblk + r and latent values 32*mdg + 8*jj + 4*g + (0..3).  This is the
-// matrix-core accumulator layout, so each 64-lane store covers 1 KiB.
-__host__ __device__ inline int64_t frag_offset(int32_t hblk, int32_t mdg, int32_t jj, int32_t lane) {
-  return (((int64_t)hblk * 16 + mdg) * 4 + jj) * 256 + lane * 4;
+// bf16 partial outputs of the shapes the matrix-core kernels serve (512
+// latent values, heads a multiple of 32): slot k's [h, 512] block is
+// row-major, value (head i, latent x) at k h 512 + 512 i + x, so that one
+// head's partial is 1 KiB contiguous for the merge.  part_row: where the
+// 32-value latent block mdg of head 32 hblk + (lane % 32) starts in a slot.
+__host__ __device__ inline int64_t part_row(int32_t hblk, int32_t mdg, int32_t lane) {
+  return (int64_t)(32 * hblk + (lane & 31)) * 512 + 32 * mdg;
 }
 
 // ---------------------------------------------------------------- split plan
@@ -82,13 +81,13 @@ struct AttnArgs {
   const int32_t* tiles;      // [n_tiles][4] tile descriptors (workspace)
   const int32_t* split_first;  // [splits + 1] first tile of each split (workspace)
   const int32_t* seq_splits;   // [B][2] first and last split of each sequence (workspace)
-  void* part_o;              // [slots, h, d_c]: bf16 fragment-major when frag_layout, else fp32 row-major
+  void* part_o;              // [slots, h, d_c] row-major: bf16 when part_bf16, else fp32
   float* part_lse;           // [slots, h]
   int32_t B, h, d_c, d_r, P, max_blocks, num_blocks;
   int32_t log2P;             // log2(P) when P is a power of two, else -1
   int32_t splits;            // work groups along tokens (gridDim.x)
   int32_t streams;           // partial slots per (split, sequence)
-  int32_t frag_layout;       // part_o bf16 in fragment-major layout (frag_offset), else fp32 row-major
+  int32_t part_bf16;         // part_o bf16 (the matrix-core shapes, part_piece), else fp32
   float sm_scale_log2;       // sm_scale * log2(e)
   // Sparse mode (slots != null): sequence b attends to seq_lens[b] entries
   // (at most idx_stride) whose physical slots (block * P + offset) the planner
@@ -529,6 +528,28 @@ __device__ inline uint2 pack_bf16x4(float a, float b, float c, float d) {
   const bf16x2_t lo = __builtin_convertvector((f32x2_t{a, b}), bf16x2_t);
   const bf16x2_t hi = __builtin_convertvector((f32x2_t{c, d}), bf16x2_t);
   return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// One 32-value latent block of a matrix-core accumulator (32 latent values x
+// 32 heads; lane 32 g + r holds head r, values 8 jj + 4 g + 0..3 in elements
+// 4 jj .. 4 jj + 3), times s, stored as bf16 into the heads' partial rows
+// (dst: lane r's row at the block's first value).  Lanes r and 32 + r swap
+// halves (v_permlane32_swap) so that each lane stores 8 consecutive values,
+// 16 bytes: lane r values 16 p + 0..7 and lane 32 + r values 16 p + 8..15 of
+// each half p of the block.
+template <typename V>
+__device__ inline void store_block_bf16(uint16_t* dst, const V& o, float s, int lane) {
+#pragma unroll
+  for (int p = 0; p < 2; p++) {
+    const uint2 x = pack_bf16x4(o[8 * p] * s, o[8 * p + 1] * s, o[8 * p + 2] * s, o[8 * p + 3] * s);
+    const uint2 y = pack_bf16x4(o[8 * p + 4] * s, o[8 * p + 5] * s, o[8 * p + 6] * s, o[8 * p + 7] * s);
+    // lanes 0..31 keep x and take the upper lanes' x; lanes 32..63 take the
+    // lower lanes' y and keep their own
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<u32x4_t*>(dst + 16 * p + 8 * (lane >> 5)) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+  }
 }
 
 // OCP E4M3FN byte -> fp32 using the gfx950 hardware conversion.

@@ -85,6 +85,13 @@ hipError_t launch_up_project_mfma(const mla_decode_params& p, const float* o_lat
 // Log-sum-exp merge of the token splits -> o_lat [B, h, d_c] fp32.
 hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s);
 
+// The merge and the up-projection in one launch, from the bf16 partials of a
+// (a.shards 1): the same bits as launch_combine, then launch_up_project.
+// Matrix-core shapes with bf16 weights, d_v = 128 and at most 16 sequences.
+bool merge_up_supported(const mla_decode_params& p);
+hipError_t launch_merge_up(const mla_decode_params& p, const AttnArgs& a, const void* W_UV,
+                           void* out, hipStream_t s);
+
 // out[b,i,:] = W_UV[i] o_lat[b,i,:].
 hipError_t launch_up_project(const mla_decode_params& p, const float* o_lat, const void* W_UV,
                              void* out, hipStream_t s);

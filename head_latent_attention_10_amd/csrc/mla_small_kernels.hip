@@ -1,5 +1,6 @@
 // Planner, absorption, log-sum-exp merge, up-projection and cache gather.
 #include "mla_kernels.hpp"
+#include "mla_merge.hpp"
 
 namespace mla {
 
@@ -268,121 +269,36 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(AttnArgs a, float
   }
 }
 
-// The same merge over fragment-major bf16 partials (frag_offset; 512 latent
-// values, heads a multiple of 32).  Work group = (sequence, 32-head block,
-// 32-value latent block); a thread owns one 4-value piece (head 32 hblk + r,
-// latent 32 mdg + 8 jj + 4 g + 0..3), so each wave reads 512 B contiguous
-// per slot.  Two dependent memory round trips: the sequence's split range,
-// then, all in flight together, the pieces of up to kCombPass slots, their
-// LSEs and the split table entries that say whether a split owns tiles (one
-// that owns none wrote nothing: weight 0, and its stale piece is never
-// multiplied in).  Longer ranges take further passes with a running maximum.
-// kCombPass slots a pass: 16, or 8 when sequences average at most 4 splits
-// (large batches: half the registers, twice the work groups in flight).
-constexpr int kFragLat = 512;
-
-// With TPLA shards (a.shards > 1) block (b, hblk, mdg) merges the columns of
-// output head block hblk that lie in shard j = mdg / (16 / shards), from the
-// partials of shard head block j (h / shards) / 32 + hblk, into an output of
-// h / shards heads: the shard heads' other columns are neither read nor written.
-template <int kCombPass>
-__global__ __launch_bounds__(256) void combine_frag_kernel(AttnArgs a, float* __restrict__ o_lat) {
-  __shared__ float s_w[kCombPass][32];  // LSEs of the pass's slots, then their weights
-  __shared__ float s_M[32], s_W[32], s_alpha[32];
-  const int32_t b = blockIdx.x, mdg = blockIdx.z;
-  const int32_t G = a.shards > 1 ? a.shards : 1, h_out = a.h / G;
-  const int32_t hblk_out = blockIdx.y;
-  const int32_t hblk = (mdg / (kFragLat / 32 / G)) * (h_out / 32) + hblk_out;  // partials' head block
-  const int tid = threadIdx.x, jj = tid >> 6, lane = tid & 63;
-  const int r = lane & 31;                 // head of this thread's piece
-  const int wr = tid & 31, wk = tid >> 5;  // (head, slot phase) of the LSE loads
-  const int32_t d = mdg * 32 + jj * 8 + 4 * (lane >> 5);
-  float4* dst =
-      reinterpret_cast<float4*>(o_lat + ((int64_t)b * h_out + hblk_out * 32 + r) * kFragLat + d);
-  const int2 range = *reinterpret_cast<const int2*>(a.seq_splits + 2 * b);
-  const int32_t g_lo = range.x, n_cand = range.y - range.x + 1;
-  if (n_cand <= 0) {  // no tokens
-    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
-  const int64_t slot_stride = (int64_t)a.h * kFragLat;
-  const uint16_t* src = static_cast<const uint16_t*>(a.part_o) + (int64_t)(g_lo + b) * slot_stride +
-                        frag_offset(hblk, mdg, jj, lane);
-  const float* lse = a.part_lse + (int64_t)(g_lo + b) * a.h + hblk * 32 + wr;
-  if (tid < 32) {
-    s_M[tid] = -INFINITY;
-    s_W[tid] = 0.f;
-  }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int32_t c0 = 0; c0 < n_cand; c0 += kCombPass) {
-    const int32_t n = min(kCombPass, n_cand - c0);  // uniform
-    uint2 v[kCombPass];
-#pragma unroll
-    for (int k = 0; k < kCombPass; k++)
-      v[k] = k < n ? *reinterpret_cast<const uint2*>(src + (int64_t)(c0 + k) * slot_stride)
-                   : make_uint2(0u, 0u);
-#pragma unroll
-    for (int u = 0; u < kCombPass / 8; u++) {
-      const int k = wk + 8 * u;
-      if (k < n) {
-        const int32_t gg = g_lo + c0 + k;
-        const bool owns = load_ro(a.split_first, gg) < load_ro(a.split_first, gg + 1);
-        const float l = lse[(int64_t)(c0 + k) * a.h];
-        s_w[k][wr] = owns ? l : -INFINITY;
-      }
-    }
-    __syncthreads();
-    if (tid < 32) {  // per head: running maximum, rescale factor and weights
-      const float m_old = s_M[tid];
-      float m = m_old;
-      for (int k = 0; k < n; k++) m = fmaxf(m, s_w[k][tid]);
-      const float al = m_old == -INFINITY ? 0.f : expf(m_old - m);
-      float W = s_W[tid] * al;
-      for (int k = 0; k < n; k++) {
-        const float l = s_w[k][tid];
-        const float w = l == -INFINITY ? 0.f : expf(l - m);
-        s_w[k][tid] = w;
-        W += w;
-      }
-      s_M[tid] = m;
-      s_W[tid] = W;
-      s_alpha[tid] = al;
-    }
-    __syncthreads();
-    const float al = s_alpha[r];
-    acc.x *= al;
-    acc.y *= al;
-    acc.z *= al;
-    acc.w *= al;
-#pragma unroll
-    for (int k = 0; k < kCombPass; k++) {
-      if (k < n) {
-        const float w = s_w[k][r];
-        const float x0 = __uint_as_float(v[k].x << 16), x1 = __uint_as_float(v[k].x & 0xffff0000u);
-        const float x2 = __uint_as_float(v[k].y << 16), x3 = __uint_as_float(v[k].y & 0xffff0000u);
-        // a split without tiles has weight 0 and an undefined piece: selected out
-        acc.x += w != 0.f ? w * x0 : 0.f;
-        acc.y += w != 0.f ? w * x1 : 0.f;
-        acc.z += w != 0.f ? w * x2 : 0.f;
-        acc.w += w != 0.f ? w * x3 : 0.f;
-      }
-    }
-    __syncthreads();
-  }
-  const float W = s_W[r];
-  const float inv = W > 0.f ? 1.f / W : 0.f;
-  *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+// The same merge over bf16 partial rows (512 latent values): one wave per
+// (sequence, output head) row, merge_row; each lane writes its 8 values.
+// With TPLA shards (a.shards = G > 1) output head i takes the columns of
+// shard j from shard head j (h / G) + i, into an output of h / G heads.
+template <int G>
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, float* __restrict__ o_lat) {
+  const int32_t b = blockIdx.x, h_out = a.h / G;
+  const int32_t i = blockIdx.y * 4 + (int32_t)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= h_out) return;  // wave-uniform
+  float o[8];
+  merge_row<G>(a, b, i, lane, o);
+  float4* dst = reinterpret_cast<float4*>(o_lat + ((int64_t)b * h_out + i) * kMergeLat + 8 * lane);
+  dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
 hipError_t launch_combine(const AttnArgs& a, float* o_lat, hipStream_t s) {
-  if (a.frag_layout) {
+  if (a.part_bf16) {
     const int32_t G = a.shards > 1 ? a.shards : 1;
-    if (a.d_c != kFragLat || a.h % (32 * G) || a.streams != 1) return hipErrorInvalidValue;
-    const dim3 grid(a.B, a.h / G / 32, kFragLat / 32);
-    if (a.splits <= 4 * a.B)
-      hipLaunchKernelGGL(combine_frag_kernel<8>, grid, dim3(256), 0, s, a, o_lat);
+    if (a.d_c != kMergeLat || a.h % G || a.streams != 1) return hipErrorInvalidValue;
+    const dim3 grid(a.B, (a.h / G + 3) / 4);
+    if (G == 1)
+      hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, s, a, o_lat);
+    else if (G == 2)
+      hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, s, a, o_lat);
+    else if (G == 4)
+      hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, s, a, o_lat);
     else
-      hipLaunchKernelGGL(combine_frag_kernel<16>, grid, dim3(256), 0, s, a, o_lat);
+      return hipErrorInvalidValue;
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3(a.B, a.h), dim3(kCombThreads), 0, s, a, o_lat);
   }

@@ -202,18 +202,15 @@ mla_status mla_combine(const mla_decode_params* p, float* o_lat, void* workspace
                        size_t workspace_bytes, void* stream);
 
 /* Where mla_attend_partial keeps the partials of *p in the workspace; slots =
- * splits + batch, and the pair (split g, sequence b) uses slot g + b.
- *  - fragment_major = 1 for the shapes the matrix-core kernels serve
- *    (d_latent 512, heads a multiple of 32, bf16 or fp8 cache): o_s is bf16,
- *    slot k's [h, 512] block at byte offset part_o_offset + k h 512 2, stored
- *    as [h/32][16][4][64][4] (head block, 32-value latent block m, 8-value
- *    group j, lane 32 g + r, 4 values): head 32 hb + r, latent
- *    32 m + 8 j + 4 g + 0..3.
- *  - otherwise o_s is fp32, slot k's block row-major [h][d_latent] at
- *    part_o_offset + k h d_latent 4.
+ * splits + batch, and the pair (split g, sequence b) uses slot g + b.  Slot
+ * k's o_s block is row-major [h][d_latent], head i's row starting at element
+ * (k h + i) d_latent from part_o_offset:
+ *  - bf16_rows = 1 for the shapes the matrix-core kernels serve (d_latent
+ *    512, heads a multiple of 32, bf16 or fp8 cache): o_s is bf16;
+ *  - otherwise o_s is fp32.
  * lse_s of slot k and head i is fp32 at part_lse_offset + (k h + i) 4. */
 mla_status mla_partials_layout(const mla_decode_params* p, size_t* part_o_offset,
-                               size_t* part_lse_offset, int32_t* slots, int32_t* fragment_major);
+                               size_t* part_lse_offset, int32_t* slots, int32_t* bf16_rows);
 
 /* Stage: value up-projection, kept apart from W_O ("MLA Matrix Absorption":
  * W_UV is in practice not folded into the output projection).

@@ -326,10 +326,10 @@ def test_stage_entry_points_validate_before_launch():
 
 def test_partials_layout_lies_inside_the_workspace():
     """The partials sit inside the decode workspace: (splits + batch) slots of
-    h x d_c values (bf16 fragment-major exactly when a matrix-core kernel
-    serves the shape: 64 or 32 heads of a 512-latent bf16 or fp8 cache; fp32
-    row-major otherwise), then their h log-sum-exps."""
-    for kw, frag in ((dict(), 0),
+    h x d_c values, row-major (bf16 exactly when a matrix-core kernel serves
+    the shape: 64 or 32 heads of a 512-latent bf16 or fp8 cache; fp32
+    otherwise), then their h log-sum-exps."""
+    for kw, bf16 in ((dict(), 0),
                      (dict(num_heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128,
                            cache_dtype="bf16", q_dtype="bf16", rope_dtype="bf16",
                            weight_dtype="bf16"), 1),
@@ -344,9 +344,9 @@ def test_partials_layout_lies_inside_the_workspace():
         h, dc = p.num_heads, p.d_latent
         assert slots == p.num_splits + p.batch
         assert off_o % 256 == 0 and off_l % 256 == 0
-        assert off_l >= off_o + slots * h * dc * (2 if frag else 4)   # bf16 when fragment-major
+        assert off_l >= off_o + slots * h * dc * (2 if bf16 else 4)
         assert off_l + slots * h * 4 <= _lib.mla_decode_workspace_size(p)
-        assert f == frag, kw
+        assert f == bf16, kw
     with pytest.raises(_lib.MlaError) as ei:
         _lib.mla_partials_layout(_params(num_heads=0))
     assert ei.value.status == _lib.MLA_ERR_INVALID_ARG

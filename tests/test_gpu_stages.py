@@ -3,8 +3,8 @@ attention (mla_attend_partial) followed by the log-sum-exp merge (mla_combine)
 is mla_attend_latent bit for bit, and with the up-projection it is mla_decode
 bit for bit; a merge over a single split returns the split's partial
 unchanged; the generic kernel, serving misaligned pools of a matrix-core
-shape, writes the partials in the same bf16 fragment-major layout and the
-step still meets the oracle."""
+shape, writes the partials as the same bf16 rows and the step still meets the
+oracle."""
 import sys
 
 import numpy as np
@@ -82,13 +82,6 @@ def test_partial_then_combine_is_attend_latent_and_decode(case):
     assert torch.equal(out, dec.out)
 
 
-def _fragment_partial(block, h, dc):
-    """[h/32][16][4][64][4] fragment-major block -> [h, 512] row-major."""
-    a = block.reshape(h // 32, 16, 4, 2, 32, 4)   # hb, m, j, g, r, e
-    a = a.transpose(0, 4, 1, 2, 3, 5)              # hb, r, m, j, g, e
-    return a.reshape(h, dc)
-
-
 @pytest.mark.parametrize("case", ["dsv3_bf16", "tiny_fp32"])
 def test_single_split_combine_returns_the_partial(case):
     """A sequence that one split holds whole gets that split's partial back
@@ -100,13 +93,13 @@ def test_single_split_combine_returns_the_partial(case):
     dev = DeviceInputs(inp)
     dec = Decoder(dev, num_splits=1)
     olat, _, _, ws = _stages(dec, dev, cfg)
-    off_o, off_l, slots, frag = _lib.mla_partials_layout(dec.p)
+    off_o, off_l, slots, bf16 = _lib.mla_partials_layout(dec.p)
     splits = _lib.mla_decode_num_splits(dec.p)
     assert slots == splits + cfg.batch
     tiles = [(int(t) + 31) // 32 for t in inp.seq_lens]
     _, seq = _lib.mla_split_plan(tiles, splits)
     h, dc = cfg.heads, cfg.d_latent
-    if frag:   # bf16 pieces, widened exactly
+    if bf16:   # bf16 rows, widened exactly
         part = ws[off_o: off_o + slots * h * dc * 2].view(torch.bfloat16).float().cpu().numpy()
     else:
         part = ws[off_o: off_o + slots * h * dc * 4].view(torch.float32).cpu().numpy()
@@ -121,16 +114,16 @@ def test_single_split_combine_returns_the_partial(case):
         if g0 != g1:
             continue
         blk = part[g0 + b]                 # pair (split g, sequence b) -> slot g + b
-        ref = _fragment_partial(blk, h, dc) if frag else blk.reshape(h, dc)
+        ref = blk.reshape(h, dc)
         assert np.array_equal(got[b], ref), b
         whole += 1
     assert whole >= cfg.batch // 2, whole
 
 
-def test_misaligned_pools_take_the_generic_kernel_with_fragment_partials():
+def test_misaligned_pools_take_the_generic_kernel_with_bf16_partials():
     """A 2-byte offset of the latent pool sends a matrix-core shape to the
-    generic kernel; its partials keep the fragment-major layout, so the merge
-    and the whole step still match the oracle."""
+    generic kernel; its partials are the same bf16 rows, so the merge and the
+    whole step still match the oracle."""
     cfg = CASES["dsv3_bf16"]
     _say("misaligned pools")
     inp = generate(cfg)
