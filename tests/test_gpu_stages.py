@@ -42,6 +42,8 @@ CASES = {
     "dsv3_fp8": _cfg("dsv3_fp8_16k", seed=7101),
     "transmla_h32": _cfg("transmla_llama2_7b", seed=7102, heads=32),
     "tiny_fp32": CONFIGS["tiny_fp32"].replace(seed=7103),
+    # more than 16 sequences: the step merges and up-projects in two launches
+    "dsv3_bf16_b24": _cfg("dsv3_b64_4k", seed=7104, batch=24, seq_len_range=(1, 300)),
 }
 
 
