@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+FP8_PEAK_TFLOPS = 5000.0    # dense fp8 matrix-core peak
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), DSV3 shape @32K ctx"
 CSRC = os.path.join(ROOT, "head_latent_attention_10_amd", "csrc")
 
@@ -86,6 +87,27 @@ def measured_traffic(workload: str):
     if rec.get("kernel_source_sha256_16") != attn_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def attention_roof(r) -> dict:
+    """The attention kernel's own bound for a measured workload: the larger of
+    its HBM time (the cache bytes at 8 TB/s) and its matrix-core time.  Per
+    cached token and head the bf16 kernel multiplies 2 (d_c + d_r) score and
+    2 d_c value flops at the bf16 rate; the fp8 kernel runs the latent scores
+    on two E4M3 query terms at the fp8 rate (2 x 2 d_c) and the rope scores and
+    the values (widened to bf16) at the bf16 rate."""
+    cfg = r["cfg"]
+    th = r["total_tokens"] * cfg.heads
+    if cfg.cache_dtype == "e4m3":
+        mfma_s = th * (2 * cfg.d_rope + 2 * cfg.d_latent) / (BF16_PEAK_TFLOPS * 1e12) + \
+                 th * (2 * 2 * cfg.d_latent) / (FP8_PEAK_TFLOPS * 1e12)
+    else:
+        mfma_s = th * (2 * (cfg.d_latent + cfg.d_rope) + 2 * cfg.d_latent) / (BF16_PEAK_TFLOPS * 1e12)
+    hbm_s = r["cache_bytes"] / (HBM_PEAK_GBPS * 1e9)
+    roof_us = max(hbm_s, mfma_s) * 1e6
+    return {"attn_roof_us": round(roof_us, 1), "attn_roof_bound": "hbm" if hbm_s >= mfma_s else "mfma",
+            "attn_hbm_us": round(hbm_s * 1e6, 1), "attn_mfma_floor_us": round(mfma_s * 1e6, 1),
+            "attn_frac_of_roof": round(roof_us / (r["attn_ms"] * 1e3), 4)}
 
 
 def measure(workload: str, steps: int, warmup: int, num_splits: int = 0):
@@ -849,7 +871,8 @@ def main():
                     "attn_kernel_ms": round(r["attn_ms"], 4),
                     "attn_kernel_ms_pct": r["attn_ms_pct"],
                     "attn_cache_GBps": round(r["attn_gbps"], 1),
-                    "attn_frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4)}
+                    "attn_frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4),
+                    **attention_roof(r)}
         # committed counter summaries of this workload's attention kernel, if
         # taken on its current source
         wc = measured_counters(w)
@@ -898,6 +921,8 @@ def main():
         # every SIMD's active cycles) from the committed counter run, if taken
         # on this kernel source
         "mfma_util": counters.get("mfma_util") if counters else None,
+        # the kernel's own bound: max(HBM time, matrix-core time) and its share
+        "own_roof": attention_roof(main_run),
     }
     if args.calibrate_copy_mb > 0:
         # the last copy dispatch of the run: a plain copy of known size that
