@@ -32,9 +32,9 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_tpla(inp, shards, mu=None, repeats=1):
+def run_tpla(inp, shards, mu=None, repeats=1, num_splits=0):
     dev = DeviceInputs(inp)
-    p = dev.params()
+    p = dev.params(num_splits=num_splits)
     t = _lib.make_tpla_params(shards, mu)
     n = _lib.mla_tpla_decode_workspace_size(p, t)
     ws = torch.empty(n, dtype=torch.uint8, device=dev.device)
@@ -101,6 +101,19 @@ def test_tpla_matches_oracle(case, shards, mu):
     h = cfg.heads
     heads = None if h <= 16 else sorted({0, 1, h // 2 - 1, h // 2, h - 1})
     check(inp, out, shards, mu, heads=heads, label=f"{case} g={shards}")
+
+
+@pytest.mark.parametrize("shards", [2, 4])
+def test_tpla_many_splits_per_sequence(shards):
+    """200 splits over two long sequences: each sequence's merge runs over more
+    than 64 slots (the weights of a second 64-slot chunk) in every shard."""
+    cfg = small("dsv3_ragged_32k", batch=2, seed=4106)
+    inp = generate(cfg, seq_lens=[5000, 3100])
+    _say(f"tpla many splits shards={shards}")
+    out = run_tpla(inp, shards, num_splits=200)
+    h = cfg.heads
+    check(inp, out, shards, heads=sorted({0, 1, h // 2 - 1, h // 2, h - 1}),
+          label=f"200 splits g={shards}")
 
 
 def test_one_shard_is_mla_decode_bitwise():
