@@ -1010,13 +1010,23 @@ mla_status mla_tpla_decode(const mla_decode_params* p, const mla_tpla_params* t,
   // absorption of the num_heads heads (its planner groups plan the split)
   const mla::PlanRequest plan = plan_request(L.dec, ws, block_table, seq_lens);
   bool planned = false;
-  hipError_t e = mla::launch_absorb(*p, q, W_UK, ws + L.q_lat1, qt, &plan, &planned, s);
-  if (e != hipSuccess) return hip_fail(e, "absorb launch");
-  mla::TplaMu mu{};
-  for (int j = 0; j < t->shards; j++) mu.v[j] = t->mu[j];
-  e = mla::launch_tpla_expand(ws + L.q_lat1, ws + L.dec.q_lat, qt, p->batch, p->num_heads,
-                              t->shards, p->d_latent, p->d_rope, mu, s);
-  if (e != hipSuccess) return hip_fail(e, "expand launch");
+  hipError_t e;
+  if (mla::absorb_mfma_ok(*p, q, W_UK, ws + L.dec.q_lat)) {
+    // the matrix-core absorption writes the shard heads' queries itself
+    mla::ShardExpand ex{t->shards, {1.f, 1.f, 1.f, 1.f}};
+    for (int j = 0; j < t->shards; j++) ex.mu[j] = t->mu[j];
+    e = mla::launch_absorb_mfma(*p, q, W_UK, ws + L.dec.q_lat, qt, &plan, s, &ex);
+    if (e != hipSuccess) return hip_fail(e, "absorb launch");
+    planned = true;
+  } else {
+    e = mla::launch_absorb(*p, q, W_UK, ws + L.q_lat1, qt, &plan, &planned, s);
+    if (e != hipSuccess) return hip_fail(e, "absorb launch");
+    mla::TplaMu mu{};
+    for (int j = 0; j < t->shards; j++) mu.v[j] = t->mu[j];
+    e = mla::launch_tpla_expand(ws + L.q_lat1, ws + L.dec.q_lat, qt, p->batch, p->num_heads,
+                                t->shards, p->d_latent, p->d_rope, mu, s);
+    if (e != hipSuccess) return hip_fail(e, "expand launch");
+  }
   float* o2 = reinterpret_cast<float*>(ws + L.dec.o_lat);
   float* o1 = reinterpret_cast<float*>(ws + L.o_lat1);
   // With bf16 partials and whole 32-head blocks the merge takes

@@ -76,9 +76,19 @@ inline bool mfma_any_supported(const mla_decode_params& p) {
 // (d_nope <= 128, multiple of 16; d_v multiple of 32).
 bool proj_mfma_supported(const mla_decode_params& p);
 // With plan != null the launch also runs the planner (as launch_plan would).
+// With ex (TPLA, ex->g of at most 4 equal shards of the latent columns): q_lat receives the ex->g h shard heads' queries instead,
+// shard-major (shard head j h + i: head i's query times ex->mu[j] on shard j's
+// columns, 0 on the others, its rope part copied), the same values as
+// absorption followed by launch_tpla_expand.
+struct ShardExpand {
+  int32_t g;
+  float mu[4];
+};
 hipError_t launch_absorb_mfma(const mla_decode_params& p, const void* q, const void* W_UK,
                               void* q_lat, int32_t q_lat_dtype, const PlanRequest* plan,
-                              hipStream_t s);
+                              hipStream_t s, const ShardExpand* ex = nullptr);
+// Whether launch_absorb takes the matrix-core kernel for these pointers.
+bool absorb_mfma_ok(const mla_decode_params& p, const void* q, const void* W_UK, const void* q_lat);
 hipError_t launch_up_project_mfma(const mla_decode_params& p, const float* o_lat,
                                   const void* W_UV, void* out, hipStream_t s);
 

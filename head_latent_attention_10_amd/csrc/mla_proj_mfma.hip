@@ -258,12 +258,12 @@ struct PlanArgs {
   PlanInput in;
 };
 
-template <int OT>
+template <int OT, bool kExpand>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ W_UK,
                                                           void* __restrict__ q_lat, int32_t B,
                                                           int32_t h, int32_t d_n, int32_t d_r,
-                                                          PlanArgs pl) {
+                                                          PlanArgs pl, ShardExpand ex) {
   __shared__ __attribute__((aligned(16))) char ws[kAbsMaxN * kAbsCols * 2];
   static_assert(sizeof(PlanShared) <= sizeof(ws), "planner LDS");
   if ((int32_t)blockIdx.x < pl.groups) {
@@ -303,14 +303,19 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
     const int idx = tid + 256 * i, row = min(idx >> 4, d_n - 1), ch = idx & 15;
     *reinterpret_cast<uint4*>(ws + row * 256 + ((ch ^ abs_swz(row)) << 4)) = wv[i];
   }
-  // the rope part of the absorbed query is q_rope copied (once per head)
+  // the rope part of the absorbed query is q_rope copied (once per head, to
+  // each of its shard heads when expanding)
+  const int32_t ng = kExpand ? ex.g : 1;
+  auto out_row = [&](int32_t b, int32_t j) -> int64_t {
+    return kExpand ? (int64_t)b * ng * h + (int64_t)j * h + head : (int64_t)b * h + head;
+  };
   if (cgrp == 0 && OT == MLA_BF16 && d_r % 8 == 0) {
     const int32_t per = d_r / 8;  // 16-byte pieces per row
     for (int32_t i = tid; i < B * per; i += 256) {
       const int32_t b = i / per, k = 8 * (i % per);
       const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * h + head) * dq + d_n + k);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(q_lat) + ((int64_t)b * h + head) * dl +
-                                kLat + k) = v;
+      for (int32_t j = 0; j < ng; j++)
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(q_lat) + out_row(b, j) * dl + kLat + k) = v;
     }
   } else if (cgrp == 0) {
     for (int32_t i0 = 0; i0 < B * d_r; i0 += 4 * 256) {
@@ -325,7 +330,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
       for (int u = 0; u < 4; u++) {
         const int32_t i = i0 + u * 256 + tid;
         if (i < B * d_r)
-          store_elem<OT>(q_lat, ((int64_t)(i / d_r) * h + head) * dl + kLat + i % d_r, v[u]);
+          for (int32_t j = 0; j < ng; j++)
+            store_elem<OT>(q_lat, out_row(i / d_r, j) * dl + kLat + i % d_r, v[u]);
       }
     }
   }
@@ -359,7 +365,19 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const int32_t bb = b0 + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (bb < B) store_elem<OT>(q_lat, ((int64_t)bb * h + head) * dl + c0 + cw + r, acc[j]);
+      if (bb < B) {
+        const int32_t col = c0 + cw + r;
+        if constexpr (!kExpand) {
+          store_elem<OT>(q_lat, ((int64_t)bb * h + head) * dl + col, acc[j]);
+        } else {
+          // what absorption then expansion store: the stored query value,
+          // times the factor of its column's shard, zero in the other shards
+          const float v = OT == MLA_BF16 ? bf16_bits_to_f32(f32_to_bf16_bits(acc[j])) : acc[j];
+          const int32_t js = col / (kLat / ng);
+          for (int32_t jj = 0; jj < ng; jj++)
+            store_elem<OT>(q_lat, out_row(bb, jj) * dl + col, jj == js ? ex.mu[jj] * v : 0.f);
+        }
+      }
     }
   }
 }
@@ -372,18 +390,26 @@ bool proj_mfma_supported(const mla_decode_params& p) {
 }
 
 hipError_t launch_absorb_mfma(const mla_decode_params& p, const void* q, const void* W_UK,
-                              void* q_lat, int32_t ot, const PlanRequest* plan, hipStream_t s) {
+                              void* q_lat, int32_t ot, const PlanRequest* plan, hipStream_t s,
+                              const ShardExpand* ex) {
   PlanArgs pl{};
   if (plan) pl = PlanArgs{kPlanGroups, plan_input(p, *plan)};
   const dim3 grid(p.num_heads * kAbsColGroups + pl.groups);
-  if (ot == MLA_BF16)
-    hipLaunchKernelGGL((absorb_mfma_kernel<MLA_BF16>), grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(W_UK), q_lat,
-                       p.batch, p.num_heads, p.d_nope, p.d_rope, pl);
-  else
-    hipLaunchKernelGGL((absorb_mfma_kernel<MLA_F32>), grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(W_UK), q_lat,
-                       p.batch, p.num_heads, p.d_nope, p.d_rope, pl);
+  const ShardExpand e = ex ? *ex : ShardExpand{1, {1.f, 1.f, 1.f, 1.f}};
+  if (ex && (e.g < 1 || e.g > 4 || kLat % e.g != 0)) return hipErrorInvalidValue;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* w = static_cast<const uint16_t*>(W_UK);
+#define MLA_ABSORB_MFMA(O, X)                                                                  \
+  hipLaunchKernelGGL((absorb_mfma_kernel<O, X>), grid, dim3(256), 0, s, qq, w, q_lat, p.batch, \
+                     p.num_heads, p.d_nope, p.d_rope, pl, e)
+  if (ot == MLA_BF16) {
+    if (ex) MLA_ABSORB_MFMA(MLA_BF16, true);
+    else MLA_ABSORB_MFMA(MLA_BF16, false);
+  } else {
+    if (ex) MLA_ABSORB_MFMA(MLA_F32, true);
+    else MLA_ABSORB_MFMA(MLA_F32, false);
+  }
+#undef MLA_ABSORB_MFMA
   return hipGetLastError();
 }
 

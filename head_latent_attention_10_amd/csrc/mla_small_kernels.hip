@@ -138,11 +138,15 @@ static hipError_t absorb_t(const mla_decode_params& p, const void* q, const void
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+bool absorb_mfma_ok(const mla_decode_params& p, const void* q, const void* W_UK, const void* q_lat) {
+  return proj_mfma_supported(p) && aligned16(q) && aligned16(W_UK) && aligned16(q_lat) &&
+         (p.d_nope + p.d_rope) % 8 == 0;
+}
+
 hipError_t launch_absorb(const mla_decode_params& p, const void* q, const void* W_UK, void* q_lat,
                          int32_t ot, const PlanRequest* plan, bool* planned, hipStream_t s) {
   if (planned) *planned = false;
-  if (proj_mfma_supported(p) && aligned16(q) && aligned16(W_UK) && aligned16(q_lat) &&
-      (p.d_nope + p.d_rope) % 8 == 0) {
+  if (absorb_mfma_ok(p, q, W_UK, q_lat)) {
     if (planned) *planned = plan != nullptr;
     return launch_absorb_mfma(p, q, W_UK, q_lat, ot, plan, s);
   }
