@@ -37,7 +37,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kIdxHeads = 64;      // matrix-core indexer: H_I
 constexpr int kIdxDim = 128;       // d_I (two 64-byte k-steps)
 constexpr int kIdxWaves = 4;
-constexpr int kIdxTokWave = 64;    // tokens per wave (two 32-token N blocks)
+constexpr int kIdxBlocks = 4;      // 32-token N blocks per wave
+constexpr int kIdxTokWave = 32 * kIdxBlocks;
 constexpr int kIdxTokWG = kIdxWaves * kIdxTokWave;
 constexpr int kIdxSimt = 256;
 
@@ -60,39 +61,59 @@ __device__ inline int32_t scored_len(const IndexerArgs& a, int32_t b) {
   return T < 0 ? 0 : (T > cap ? cap : T);
 }
 
-// Work group = 256 tokens of one sequence; wave = 64 tokens (two N blocks).
+// Work group = kIdxTokWG tokens of one sequence; wave = kIdxBlocks 32-token N
+// blocks, whose key loads (table entry, then the row pieces and the scale) are
+// all issued before the first product.  The sequence's query codes (8 KiB) and
+// its per-head factors w q_scale are staged in LDS once per work group, so a
+// wave's vector-memory instructions are its keys' alone.
 // A operand: q codes of heads 32 mb + (lane & 31), bytes 64 ks + 32 (lane >> 5)
 // .. +31; B operand: key codes of token (lane & 31) of the block, same bytes.
 // (Any consistent assignment of the 64 bytes of a k-step to the two lane
 // halves gives the same dot products.)
-__global__ __launch_bounds__(64 * kIdxWaves) void indexer_mfma_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(64 * kIdxWaves) __attribute__((amdgpu_waves_per_eu(3))) void indexer_mfma_kernel(IndexerArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[kIdxHeads * kIdxDim];
+  __shared__ __attribute__((aligned(16))) float s_wq[kIdxHeads];
   const int32_t b = blockIdx.y;
   const int32_t T = scored_len(a, b);
+  const int32_t t_wg = blockIdx.x * kIdxTokWG;
+  if (t_wg >= T) return;  // the whole work group
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t t_wave = blockIdx.x * kIdxTokWG + wave * kIdxTokWave;
-  if (t_wave >= T) return;
-  // keys of the wave's 64 tokens first (their loads are the long ones)
-  i32x8 kb[2][2];
-  float ks[2];
+  const int32_t t_wave = t_wg + wave * kIdxTokWave;
+  const bool active = t_wave < T;
+  i32x8 kb[kIdxBlocks][2];
+  float ks[kIdxBlocks];
+  if (active) {
 #pragma unroll
-  for (int nb = 0; nb < 2; nb++) {
-    const int32_t t = min(t_wave + 32 * nb + c, T - 1);
-    const int64_t slot = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks);
-    const uint8_t* row = a.k + slot * kIdxDim + 32 * g;
+    for (int nb = 0; nb < kIdxBlocks; nb++) {
+      const int32_t t = min(t_wave + 32 * nb + c, T - 1);
+      const int64_t slot = phys_slot(a.block_table, b, t, a.P, a.max_blocks, a.num_blocks);
+      const uint8_t* row = a.k + slot * kIdxDim + 32 * g;
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(row + 64 * s);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(row + 64 * s + 16);
-      kb[nb][s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int s = 0; s < 2; s++) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(row + 64 * s);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(row + 64 * s + 16);
+        kb[nb][s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      ks[nb] = a.k_scale[slot];
     }
-    ks[nb] = a.k_scale[slot];
   }
+  {
+    const i32x4* src = reinterpret_cast<const i32x4*>(a.q + (int64_t)b * kIdxHeads * kIdxDim);
+    for (int i = tid; i < kIdxHeads * kIdxDim / 16; i += 64 * kIdxWaves)
+      reinterpret_cast<i32x4*>(s_q)[i] = src[i];
+    if (tid < kIdxHeads) {
+      const int64_t o = (int64_t)b * kIdxHeads + tid;
+      s_wq[tid] = a.w[o] * a.q_scale[o];
+    }
+  }
+  __syncthreads();
+  if (!active) return;
   i32x8 qa[2][2];
   float wq[2][16];
 #pragma unroll
   for (int mb = 0; mb < 2; mb++) {
-    const uint8_t* row = a.q + ((int64_t)b * kIdxHeads + 32 * mb + c) * kIdxDim + 32 * g;
+    const uint8_t* row = s_q + (32 * mb + c) * kIdxDim + 32 * g;
 #pragma unroll
     for (int s = 0; s < 2; s++) {
       const i32x4 lo = *reinterpret_cast<const i32x4*>(row + 64 * s);
@@ -101,14 +122,14 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_mfma_kernel(IndexerArg
     }
     // accumulator row j of block mb is head 32 mb + 8 (j / 4) + 4 g + j % 4
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int32_t head = 32 * mb + 8 * (j >> 2) + 4 * g + (j & 3);
-      const int64_t o = (int64_t)b * kIdxHeads + head;
-      wq[mb][j] = a.w[o] * a.q_scale[o];
+    for (int i = 0; i < 4; i++) {
+      const f32x4 f = *reinterpret_cast<const f32x4*>(s_wq + 32 * mb + 8 * i + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; r++) wq[mb][4 * i + r] = f[r];
     }
   }
 #pragma unroll
-  for (int nb = 0; nb < 2; nb++) {
+  for (int nb = 0; nb < kIdxBlocks; nb++) {
     float v = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
