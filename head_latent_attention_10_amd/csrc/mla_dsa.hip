@@ -70,7 +70,9 @@ __device__ inline int32_t scored_len(const IndexerArgs& a, int32_t b) {
 // .. +31; B operand: key codes of token (lane & 31) of the block, same bytes.
 // (Any consistent assignment of the 64 bytes of a k-step to the two lane
 // halves gives the same dot products.)
-__global__ __launch_bounds__(64 * kIdxWaves) __attribute__((amdgpu_waves_per_eu(3))) void indexer_mfma_kernel(IndexerArgs a) {
+// (At most 168 VGPRs, so that three waves fit on a SIMD: 152 without spills.)
+__global__ __launch_bounds__(64 * kIdxWaves) __attribute__((amdgpu_waves_per_eu(3)))
+void indexer_mfma_kernel(IndexerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_q[kIdxHeads * kIdxDim];
   __shared__ __attribute__((aligned(16))) float s_wq[kIdxHeads];
   const int32_t b = blockIdx.y;
