@@ -140,23 +140,29 @@ __global__ __launch_bounds__(64 * kUpWaves) void up_project_mfma_kernel(
 // over latent half w / 4 and keeps them (8 KiB) in registers as the B operand
 // of v_mfma_f32_16x16x32_bf16 (lane 16 q + c: row c of the block, latent
 // values 32 k + 8 q .. 32 k + 8 q + 7 of k-step k); the two latent halves'
-// sums are added through LDS.  The 16 o_lat rows come from o_lat (the
-// up-projection stage, kFromParts false) or are merged from the bf16 split
-// partials by merge_row (the decode step: o_lat is never written), wave w
-// producing rows w and w + 8, each lane 8 values.  The rows are staged in LDS as a bf16 high
-// part and a bf16 remainder (16-byte chunk index XOR the row), both multiplied
-// and the products summed in fp32, which keeps about 16 significant bits of
-// o_lat.  Rows past the batch are zero.  Both sources run the same conversion,
-// products and sums, so the step and its stages agree bit for bit.
+// sums are added through LDS.  In up16_mfma_kernel (the decode step up to 16
+// sequences) the 16 o_lat rows are merged from the bf16 split partials by
+// merge_row, wave w producing rows w and w + 8, each lane 8 values, so o_lat
+// is never written; up16_olat_kernel (the up-projection stage, and the step
+// of larger batches after the merge kernel) reads them from o_lat, up to
+// kUp16Blocks blocks of 16 sequences per work group, which loads its W_UV
+// rows once and the next block's rows while it multiplies the current one.
+// The rows are staged in LDS as a bf16 high part and a bf16 remainder
+// (16-byte chunk index XOR the row), both multiplied and the products summed
+// in fp32, which keeps about 16 significant bits of o_lat.  Rows past the
+// batch are zero.  Both kernels run the same conversion, products and sums,
+// so the step and its stages agree bit for bit.
 constexpr int kUp16Rows = 16;
 constexpr int kUp16Waves = 8;
 constexpr int kUp16Dv = 128;
 constexpr int kUp16Ks = kLat / 32 / 2;  // k-steps of one latent half
+constexpr int kUp16Blocks = 4;          // 16-sequence blocks per work group (rows from o_lat)
 
 template <bool kFromParts, int OT>
 __global__ __launch_bounds__(64 * kUp16Waves) void up16_mfma_kernel(
     AttnArgs a, const float* __restrict__ o_lat, const uint16_t* __restrict__ W_UV,
     void* __restrict__ out, int32_t B, int32_t h) {
+  static_assert(kFromParts, "rows from o_lat: up16_olat_kernel");
   __shared__ __attribute__((aligned(16))) char os[2][kUp16Rows * kLat * 2];  // high, low parts
   __shared__ f32x4 red[4][64];  // sums of the second latent half
   const int32_t head = blockIdx.x, vh = blockIdx.y, b0 = blockIdx.z * kUp16Rows;
@@ -175,14 +181,7 @@ __global__ __launch_bounds__(64 * kUp16Waves) void up16_mfma_kernel(
     const int r = wave + 8 * rr;
     const int32_t b = b0 + r;
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if constexpr (kFromParts) {
-      if (b < B) merge_row<1>(a, b, head, lane, x);
-    } else if (b < B) {
-      const float4* src = reinterpret_cast<const float4*>(o_lat + ((int64_t)b * h + head) * kLat + 8 * lane);
-      const float4 u = src[0], v = src[1];
-      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-      x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-    }
+    if (b < B) merge_row<1>(a, b, head, lane, x);
     uint32_t hv[4], lv[4];
 #pragma unroll
     for (int p = 0; p < 4; p++) {
@@ -221,17 +220,113 @@ __global__ __launch_bounds__(64 * kUp16Waves) void up16_mfma_kernel(
   }
 }
 
+template <int OT>
+__global__ __launch_bounds__(64 * kUp16Waves) void up16_olat_kernel(
+    const float* __restrict__ o_lat, const uint16_t* __restrict__ W_UV,
+    void* __restrict__ out, int32_t B, int32_t h) {
+  __shared__ __attribute__((aligned(16))) char os[2][kUp16Rows * kLat * 2];  // high, low parts
+  __shared__ f32x4 red[4][64];  // sums of the second latent half
+  constexpr int NB = kUp16Blocks;
+  const int32_t head = blockIdx.x, vh = blockIdx.y, bfirst = blockIdx.z * NB * kUp16Rows;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), vb = wave & 3, kh = wave >> 2;
+  const int32_t vrow = 64 * vh + 16 * vb + c;
+  bf16x8 wf[kUp16Ks];
+  auto load_w = [&] {
+    const uint16_t* wrow = W_UV + ((int64_t)head * kUp16Dv + vrow) * kLat + 256 * kh + 8 * q;
+#pragma unroll
+    for (int ks = 0; ks < kUp16Ks; ks++) wf[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
+  };
+  // the o_lat rows w and w + 8 of the block at b0 (zero past the batch)
+  float xr[2][8];
+  auto load_rows = [&](int32_t b0) {
+#pragma unroll
+    for (int rr = 0; rr < 2; rr++) {
+      const int32_t b = b0 + wave + 8 * rr;
+#pragma unroll
+      for (int e = 0; e < 8; e++) xr[rr][e] = 0.f;
+      if (b < B) {
+        const float4* src = reinterpret_cast<const float4*>(o_lat + ((int64_t)b * h + head) * kLat + 8 * lane);
+        const float4 u = src[0], v = src[1];
+        xr[rr][0] = u.x; xr[rr][1] = u.y; xr[rr][2] = u.z; xr[rr][3] = u.w;
+        xr[rr][4] = v.x; xr[rr][5] = v.y; xr[rr][6] = v.z; xr[rr][7] = v.w;
+      }
+    }
+  };
+  // row r of the block into LDS as bf16 high and low parts
+  auto stage_row = [&](int r, const float* x) {
+    uint32_t hv[4], lv[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      const f32x2 v01 = {x[2 * p], x[2 * p + 1]};
+      const bf16x2 hp = __builtin_convertvector(v01, bf16x2);
+      const bf16x2 lp = __builtin_convertvector(v01 - __builtin_convertvector(hp, f32x2), bf16x2);
+      hv[p] = __builtin_bit_cast(uint32_t, hp);
+      lv[p] = __builtin_bit_cast(uint32_t, lp);
+    }
+    const int off = r * (kLat * 2) + ((lane ^ r) << 4);
+    *reinterpret_cast<merge_u32x4*>(os[0] + off) = merge_u32x4{hv[0], hv[1], hv[2], hv[3]};
+    *reinterpret_cast<merge_u32x4*>(os[1] + off) = merge_u32x4{lv[0], lv[1], lv[2], lv[3]};
+  };
+  load_w();
+  load_rows(bfirst);
+#pragma unroll 1
+  for (int blk = 0; blk < NB; blk++) {
+    const int32_t b0 = bfirst + blk * kUp16Rows;
+    if (b0 >= B) break;  // uniform over the work group
+    if (blk > 0) __syncthreads();  // the previous block's LDS rows and sums have been read
+    stage_row(wave, xr[0]);
+    stage_row(wave + 8, xr[1]);
+    // the next block's rows, in flight during this block's products
+    if (blk + 1 < NB && b0 + kUp16Rows < B) load_rows(b0 + kUp16Rows);
+    __syncthreads();
+    f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+#pragma unroll
+    for (int kk = 0; kk < kUp16Ks; kk++) {
+      const int ks = kUp16Ks * kh + kk;
+      const int off = c * (kLat * 2) + (((4 * ks + q) ^ c) << 4);
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(os[0] + off);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(os[1] + off);
+      acc[2 * (kk & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wf[kk], acc[2 * (kk & 1)], 0, 0, 0);
+      acc[2 * (kk & 1) + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wf[kk], acc[2 * (kk & 1) + 1], 0, 0, 0);
+    }
+    const f32x4 sum = (acc[0] + acc[2]) + (acc[1] + acc[3]);
+    if (kh == 1) red[vb][lane] = sum;
+    __syncthreads();
+    if (kh == 0) {
+      const f32x4 tot = sum + red[vb][lane];
+      // D[m = sequence 4 q + j][n = row c]
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int32_t bb = b0 + 4 * q + j;
+        if (bb < B) store_elem<OT>(out, ((int64_t)bb * h + head) * kUp16Dv + vrow, tot[j]);
+      }
+    }
+  }
+}
+
 template <bool kFromParts>
 hipError_t launch_up16(const mla_decode_params& p, const AttnArgs& a, const float* o_lat,
                        const void* W_UV, void* out, hipStream_t s) {
-  const dim3 grid(p.num_heads, kUp16Dv / 64, (p.batch + kUp16Rows - 1) / kUp16Rows);
   const uint16_t* w = static_cast<const uint16_t*>(W_UV);
-  if (p.out_dtype == MLA_BF16)
-    hipLaunchKernelGGL((up16_mfma_kernel<kFromParts, MLA_BF16>), grid, dim3(64 * kUp16Waves), 0, s,
-                       a, o_lat, w, out, p.batch, p.num_heads);
-  else
-    hipLaunchKernelGGL((up16_mfma_kernel<kFromParts, MLA_F32>), grid, dim3(64 * kUp16Waves), 0, s,
-                       a, o_lat, w, out, p.batch, p.num_heads);
+  if constexpr (kFromParts) {
+    const dim3 grid(p.num_heads, kUp16Dv / 64, (p.batch + kUp16Rows - 1) / kUp16Rows);
+    if (p.out_dtype == MLA_BF16)
+      hipLaunchKernelGGL((up16_mfma_kernel<true, MLA_BF16>), grid, dim3(64 * kUp16Waves), 0, s, a,
+                         o_lat, w, out, p.batch, p.num_heads);
+    else
+      hipLaunchKernelGGL((up16_mfma_kernel<true, MLA_F32>), grid, dim3(64 * kUp16Waves), 0, s, a,
+                         o_lat, w, out, p.batch, p.num_heads);
+  } else {
+    const int32_t per = kUp16Blocks * kUp16Rows;  // sequences per work group
+    const dim3 grid(p.num_heads, kUp16Dv / 64, (p.batch + per - 1) / per);
+    if (p.out_dtype == MLA_BF16)
+      hipLaunchKernelGGL((up16_olat_kernel<MLA_BF16>), grid, dim3(64 * kUp16Waves), 0, s, o_lat, w,
+                         out, p.batch, p.num_heads);
+    else
+      hipLaunchKernelGGL((up16_olat_kernel<MLA_F32>), grid, dim3(64 * kUp16Waves), 0, s, o_lat, w,
+                         out, p.batch, p.num_heads);
+  }
   return hipGetLastError();
 }
 
